@@ -1,0 +1,342 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+Each test checks the oracle against something it does not compute itself:
+closed forms, limits, a second independent implementation (scalar brute
+force, torch's float64 scaled-dot-product attention), invariants of causal
+attention, and hand-derived bfloat16 rounding cases.  Each is chosen so that a
+plausible slip in the oracle (a dropped scale, an off-by-one in the causal
+limit, the wrong KV head, a transposed operand, a max that drops NaN) fails.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import bf16
+from synth import WORKLOADS, draw_batch, random_case
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(seed, n, Hq, Hkv, D, P=None):
+    c = random_case(seed, 1, Hq, Hkv, D, P if P is not None else n, n)
+    return c.q[0], c.k[0], c.v[0]
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_first_row_is_first_value_row_exactly():
+    """Row 0 of a chunk at position 0 sees only key 0: softmax weight 1."""
+    q, k, v = _rand(11, 7, 4, 2, 16)
+    o = oracle.attend_rows(q, k, v, np.arange(7), 0.25)
+    for h in range(4):
+        g = oracle.kv_group(h, 4, 2)
+        assert np.array_equal(o[0, h], v[0, g].astype(np.float64))
+
+
+def test_equal_scores_give_mean_of_visible_values():
+    """q = 0 makes every visible score 0, so o is the plain mean of V rows."""
+    _, k, v = _rand(12, 40, 2, 1, 32)
+    q = np.zeros((40, 2, 32), np.float32)
+    o = oracle.attend_rows(q, k, v, np.arange(40), 0.125)
+    for i in [0, 1, 5, 39]:
+        mean = np.array([math.fsum(v[:i + 1, 0, d].astype(np.float64)) / (i + 1)
+                         for d in range(32)])
+        np.testing.assert_allclose(o[i, 0], mean, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(o[i, 1], mean, rtol=0, atol=1e-14)
+
+
+def test_identical_key_rows_give_mean_of_values():
+    """Every visible K row identical: equal scores whatever q is."""
+    q, k, v = _rand(13, 20, 2, 1, 8)
+    k[:] = k[3]
+    o = oracle.attend_rows(q, k, v, np.arange(20), 0.5)
+    np.testing.assert_allclose(o[19, 1], v[:, 0].astype(np.float64).mean(axis=0),
+                               rtol=0, atol=1e-14)
+
+
+def test_two_keys_logistic_weight():
+    """Two visible keys: o = sigma(s0 - s1) v0 + (1 - sigma) v1.
+
+    q and k are axis-aligned so the scores are scale * a * b_j with no
+    rounding: with a = 2, scale = 0.5, b0 = ln 3 (as f32), b1 = 0 the weight
+    of key 0 is 3/4 up to the f32 rounding of ln 3.
+    """
+    D = 8
+    q = np.zeros((2, 1, D), np.float32)
+    k = np.zeros((2, 1, D), np.float32)
+    q[1, 0, 0] = 2.0
+    k[0, 0, 0] = np.float32(math.log(3.0))
+    v = np.zeros((2, 1, D), np.float32)
+    v[0, 0] = np.arange(D, dtype=np.float32)
+    v[1, 0] = -1.0
+    o = oracle.attend_rows(q, k, v, [0, 1], 0.5)
+    gap = 0.5 * 2.0 * float(k[0, 0, 0])
+    w0 = 1.0 / (1.0 + math.exp(-gap))
+    expect = w0 * v[0, 0].astype(np.float64) + (1 - w0) * v[1, 0].astype(np.float64)
+    np.testing.assert_allclose(o[1, 0], expect, rtol=0, atol=1e-15)
+    assert abs(w0 - 0.75) < 1e-7
+
+
+def test_dominant_key_limit():
+    """A key whose score leads every other by >= 50 takes weight 1 - O(e^-50)."""
+    q, k, v = _rand(14, 30, 1, 1, 16)
+    q[29, 0] = 0.0
+    q[29, 0, 0] = 1.0
+    k[:, 0, 0] = 0.0
+    k[17, 0, 0] = 400.0               # scale 0.125 -> score 50 vs 0
+    o = oracle.attend_rows(q, k, v, np.arange(30), 0.125)
+    err = np.abs(o[29, 0] - v[17, 0]).max()
+    assert err <= 30 * math.exp(-50.0) * np.abs(v).max()
+
+
+def test_scale_is_applied_to_scores():
+    """Doubling the scale equals doubling q (a dropped scale fails this)."""
+    q, k, v = _rand(15, 12, 2, 1, 16)
+    a = oracle.attend_rows(q, k, v, np.arange(12), 0.5)
+    b = oracle.attend_rows(q * 2, k, v, np.arange(12), 0.25)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+    c = oracle.attend_rows(q, k, v, np.arange(12), 0.25)
+    assert np.abs(a - c).max() > 1e-3
+
+
+# ------------------------------------------------------- independent routines
+
+def test_scalar_brute_force_matches_numpy_on_tiny_workload():
+    """The 128-row tiny prefill (2 heads, head_dim 64): two implementations."""
+    w = WORKLOADS[1]
+    c = draw_batch(w)
+    ks = oracle.stored_values(c.k[0], "f32")
+    vs = oracle.stored_values(c.v[0], "f32")
+    rows = list(range(0, 8)) + [63, 64, 127]
+    ref = oracle.attend_rows(c.q[0], ks, vs, np.arange(128), w.scale)
+    sc = oracle.attend_rows_scalar(c.q[0][rows], ks, vs, rows, w.scale)
+    np.testing.assert_allclose(np.array(sc), ref[rows], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_scalar_matches_numpy_random_shapes(seed):
+    g = np.random.default_rng(seed)
+    Hkv = int(g.integers(1, 3))
+    G = int(g.integers(1, 4))
+    D = int(g.choice([1, 3, 8, 16]))
+    n = int(g.integers(1, 9))
+    start = int(g.integers(0, 6))
+    q, k, v = _rand(100 + seed, n, Hkv * G, Hkv, D, P=start + n)
+    pos = np.arange(start, start + n)
+    ref = oracle.attend_rows(q, k, v, pos, 0.3, row_block=3)
+    sc = np.array(oracle.attend_rows_scalar(q, k, v, pos, 0.3))
+    np.testing.assert_allclose(sc, ref, rtol=1e-12, atol=1e-13)
+
+
+def _torch_sdpa_f64(q, k, v, pos, scale, G):
+    """torch's float64 SDPA with an explicit boolean mask (row i sees j <= pos[i])."""
+    qt = torch.from_numpy(q.astype(np.float64)).permute(1, 0, 2)          # [Hq][n][D]
+    kt = torch.from_numpy(k.astype(np.float64)).permute(1, 0, 2)          # [Hkv][P][D]
+    vt = torch.from_numpy(v.astype(np.float64)).permute(1, 0, 2)
+    kt = kt.repeat_interleave(G, dim=0).contiguous()
+    vt = vt.repeat_interleave(G, dim=0).contiguous()
+    P = k.shape[0]
+    mask = torch.arange(P)[None, :] <= torch.from_numpy(np.asarray(pos))[:, None]
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=mask, scale=float(np.float32(scale)))
+    return o.permute(1, 0, 2).numpy()
+
+
+def test_matches_torch_sdpa_tiny_workload():
+    w = WORKLOADS[1]
+    c = draw_batch(w)
+    ref = oracle.attend_rows(c.q[0], c.k[0], c.v[0], np.arange(128), w.scale)
+    t = _torch_sdpa_f64(c.q[0], c.k[0], c.v[0], np.arange(128), w.scale, 2)
+    np.testing.assert_allclose(ref, t, rtol=0, atol=1e-12)
+
+
+def test_matches_torch_sdpa_gqa_chunk_with_history():
+    """A 96-row chunk at start 160 over 2 KV heads x 3 query heads each."""
+    q, k, v = _rand(21, 96, 6, 2, 32, P=256)
+    pos = np.arange(160, 256)
+    ref = oracle.attend_rows(q, k, v, pos, 0.2, row_block=40)
+    t = _torch_sdpa_f64(q, k, v, pos, 0.2, 3)
+    np.testing.assert_allclose(ref, t, rtol=0, atol=1e-12)
+
+
+@pytest.mark.slow
+def test_matches_torch_sdpa_chunked_prefill_workload():
+    """The 768-row chunk at position 3072 (8 heads, head_dim 256), sampled rows."""
+    w = WORKLOADS[3]
+    c = draw_batch(w)
+    rows = np.r_[0:64, 700:768]
+    pos = 3072 + rows
+    ref = oracle.attend_rows(c.q[0][rows], c.k[0], c.v[0], pos, w.scale)
+    t = _torch_sdpa_f64(c.q[0][rows], c.k[0][:3840], c.v[0][:3840], pos, w.scale, 8)
+    np.testing.assert_allclose(ref, t, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------- invariants
+
+def test_causality_later_rows_do_not_leak():
+    q, k, v = _rand(31, 24, 4, 1, 16)
+    base = oracle.attend_rows(q, k, v, np.arange(24), 0.3)
+    k2, v2 = k.copy(), v.copy()
+    k2[11:] = 1e3 * np.random.default_rng(0).standard_normal(k2[11:].shape)
+    v2[11:] = np.nan
+    o = oracle.attend_rows(q, k2, v2, np.arange(24), 0.3)
+    assert np.array_equal(o[:11], base[:11])
+    assert np.isnan(o[11:]).all()
+
+
+def test_gqa_head_to_group_map():
+    """With 2 KV heads x 3 query heads each, heads 3..5 read KV head 1 only."""
+    q, k, v = _rand(32, 10, 6, 2, 8)
+    v[:, 1, :] = 0.5
+    o = oracle.attend_rows(q, k, v, np.arange(10), 0.4)
+    # weights sum to 1: a constant V row set gives that constant (to rounding)
+    np.testing.assert_allclose(o[:, 3:6, :], 0.5, rtol=0, atol=1e-15)
+    assert not np.any(np.isclose(o[1:, 0:3, :], 0.5))
+    # a wrong map (h % Hkv, say) would send head 1 to KV head 1
+    v2 = v.copy()
+    v2[:, 0, :] = 7.0
+    o2 = oracle.attend_rows(q, k, v2, np.arange(10), 0.4)
+    np.testing.assert_allclose(o2[:, 0:3, :], 7.0, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(o2[:, 3:6, :], 0.5, rtol=0, atol=1e-15)
+
+
+def test_chunked_equals_single_shot():
+    q, k, v = _rand(33, 200, 4, 1, 16)
+    one = oracle.attend_rows(q, k, v, np.arange(200), 0.25)
+    parts = []
+    for s, r in [(0, 64), (64, 64), (128, 50), (178, 22)]:
+        parts.append(oracle.prefill_chunk(q[None, s:s + r], k[None], v[None], s, 0.25)[0])
+    np.testing.assert_allclose(np.concatenate(parts), one, rtol=0, atol=1e-14)
+
+
+def test_decode_equals_prefill_row():
+    q, k, v = _rand(34, 70, 4, 2, 16)
+    full = oracle.attend_rows(q, k, v, np.arange(70), 0.25)
+    for t in [0, 1, 33, 69]:
+        d = oracle.decode(q[None, t], k[None], v[None], [t + 1], 0.25)[0]
+        np.testing.assert_allclose(d, full[t], rtol=0, atol=1e-14)
+
+
+def test_joint_permutation_of_visible_keys():
+    q, k, v = _rand(35, 16, 2, 1, 8)
+    perm = np.random.default_rng(3).permutation(16)
+    a = oracle.attend_rows(q[15:16], k, v, [15], 0.5)
+    b = oracle.attend_rows(q[15:16], k[perm], v[perm], [15], 0.5)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------- NaN and masking
+
+def test_nan_in_visible_key_makes_row_nan_only_from_there_on():
+    q, k, v = _rand(41, 12, 2, 1, 8)
+    k[5, 0, 3] = np.nan
+    o = oracle.attend_rows(q, k, v, np.arange(12), 0.5)
+    assert np.isfinite(o[:5]).all()
+    assert np.isnan(o[5:]).all()
+
+
+def test_nan_query_row_gives_nan_row():
+    q, k, v = _rand(42, 6, 2, 1, 8)
+    q[4, 1, 0] = np.nan
+    o = oracle.attend_rows(q, k, v, np.arange(6), 0.5)
+    assert np.isnan(o[4, 1]).all() and np.isfinite(o[4, 0]).all()
+
+
+def test_all_nan_scores_give_nan_not_zero():
+    q, k, v = _rand(43, 4, 1, 1, 8)
+    k[:] = np.nan
+    o = oracle.attend_rows(q, k, v, np.arange(4), 0.5)
+    assert np.isnan(o).all()
+
+
+def test_row_without_visible_key_is_exactly_zero():
+    q, k, v = _rand(44, 3, 1, 1, 8)
+    o = oracle.attend_rows(q[:1], k, v, [-1], 0.5)
+    assert np.array_equal(o, np.zeros_like(o))
+
+
+def test_rel_error_measure():
+    v = np.array([[1.0, -4.0]])
+    assert oracle.rel_error([0.5, 1.0], [0.5, 0.0], v) == 0.25
+
+
+# ------------------------------------------------------------------- bfloat16
+
+def _golden_rne():
+    rows = []
+    with open(os.path.join(GOLDEN, "bf16_rne.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, b = line.split()[:2]
+            rows.append((int(a, 16), int(b, 16)))
+    return rows
+
+
+def test_bf16_rne_golden_cases():
+    rows = _golden_rne()
+    assert len(rows) >= 20
+    src = np.array([a for a, _ in rows], dtype=np.uint32).view(np.float32)
+    got = bf16.encode_rne(src)
+    assert [int(x) for x in got] == [b for _, b in rows]
+
+
+def test_bf16_rne_matches_torch_cpu_conversion():
+    g = np.random.default_rng(5)
+    x = np.concatenate([
+        g.standard_normal(200000).astype(np.float32) * 3,
+        (g.integers(0, 2**32, 200000, dtype=np.uint64).astype(np.uint32)).view(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 3.4028235e38, 1e-45, 1.17549435e-38], np.float32),
+    ])
+    finite_or_inf = ~np.isnan(x)
+    ours = bf16.encode_rne(x)
+    theirs = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours[finite_or_inf], theirs[finite_or_inf])
+    # NaN stays NaN in both
+    dec = bf16.decode(ours)
+    assert np.isnan(dec[~finite_or_inf]).all()
+
+
+def test_bf16_round_trip_is_exact_on_representable_values():
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    vals = bf16.decode(bits)
+    back = bf16.encode_rne(vals)
+    finite = ~np.isnan(vals)
+    assert np.array_equal(back[finite], bits[finite])
+
+
+def test_stored_values_bf16_error_bound():
+    """RNE error is at most half a unit in the last place: 8 significant
+    bits, so |x - bf16(x)| <= 2^(e-8) where 2^e <= |x| < 2^(e+1)."""
+    x = np.random.default_rng(6).standard_normal(10000).astype(np.float32)
+    s = oracle.stored_values(x, "bf16").astype(np.float64)
+    e = np.floor(np.log2(np.abs(x.astype(np.float64))))
+    assert np.all(np.abs(s - x) <= 2.0 ** (e - 8))
+    # and truncation would break it somewhere: the bound is tight enough to see
+    trunc = (x.view(np.uint32) & np.uint32(0xFFFF0000)).view(np.float32).astype(np.float64)
+    assert np.any(np.abs(trunc - x) > 2.0 ** (e - 8))
+
+
+# ------------------------------------------------------------------- workloads
+
+def test_workload_recipes():
+    w4, w5 = WORKLOADS[4], WORKLOADS[5]
+    assert sum(r for _, r in w4.chunks) == 16384 and len(w4.chunks) == 22
+    assert w4.decode_positions[0] == 16384 and len(w4.decode_positions) == 64
+    assert w4.capacity >= w4.positions and w4.capacity % 64 == 0
+    assert w5.decode_positions[-1] + 1 == 131072 == w5.capacity
+    assert WORKLOADS[2].decode_positions == (4096,)
+    for w in WORKLOADS.values():
+        assert w.capacity % 64 == 0 and w.positions <= w.capacity
+
+
+def test_outlier_rows_are_drawn_without_replacement():
+    w = WORKLOADS[5]
+    from synth import draw_session
+    c = draw_session(w, 1, positions=4096)
+    assert len(np.unique(c.outlier_idx)) == c.outlier_idx.size
