@@ -1,0 +1,182 @@
+/*
+ * ka_attn.h -- C ABI of a grouped-query causal KV-cache attention library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the "states-form" attention of Karume's generation-context
+ * path for Gemma 4 E2B: the rows of a prompt chunk, and later one decode row,
+ * attend causally to the K / V rows a session keeps in its cache
+ * (Karume v0.12.0 release notes, "Performance": the tiled states-form prefill
+ * bullet and the two parallel-decode bullets; Karume v0.8.0 release notes,
+ * "Features": the conversation-window bullet, which bounds the chunk at 768
+ * rows and the cache at 131072 positions).  For a query row at absolute
+ * position p, query head h and KV head g = h / (Hq / Hkv):
+ *
+ *     out[d] = sum_{j<=p} softmax_j(scale * q . k_g[j]) * v_g[j][d]
+ *
+ * Softmax rules (Karume v0.8.0 release notes, "Breaking Changes", the softmax
+ * NaN bullet): a NaN among a row's visible scores makes that whole output row
+ * NaN (the row max propagates NaN, no NaN is dropped); a NaN visible value
+ * v[j][d] makes output dim d NaN; masked keys carry weight exactly 0, and
+ * cache positions outside a row's visible range never reach its result.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All pointers to tensors are DEVICE pointers (hipMalloc / torch memory on
+ *    the current device); ka_attn_shape and ctx_len are HOST pointers.
+ *  - The caller owns every buffer and the stream.  The library allocates no
+ *    device memory: scratch space is the caller's `workspace`.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  KA_OK means "validated and enqueued".
+ *  - Every argument is validated on the host BEFORE anything is enqueued, so
+ *    a rejected call leaves caches and outputs untouched.  The reason is kept
+ *    per thread in ka_attn_last_error().
+ *  - The library is stateless: positions are arguments.  Calls that touch the
+ *    same cache must be ordered by the caller (one stream does that).
+ *  - f32 means IEEE binary32; bf16 means the top 16 bits of binary32, written
+ *    from f32 with round-to-nearest-even (NaN stays a quiet NaN).
+ *
+ * Tensor layouts (row-major, innermost last)
+ * ------------------------------------------
+ *   q, out (prefill)    f32 [B][R][Hq][D]     R = row_count of the chunk
+ *   k_new, v_new        f32 [B][R][Hkv][D]
+ *   q, out (decode)     f32 [B][Hq][D]
+ *
+ *   Caches: one K buffer and one V buffer, each ka_attn_cache_bytes() long,
+ *   laid out in 16-byte vectors of E elements (E = 8 for bf16, 4 for f32) so
+ *   that every kernel reads whole 16-byte vectors.  Element (b, g, j, d) --
+ *   session b, KV head g, position j, dimension d -- lives at element index
+ *
+ *   K (both dtypes):  ((((b*Hkv + g)*(C/64) + j/64)*(D/E) + d/E)*64 + j%64)*E + d%E
+ *                     i.e. [B][Hkv][C/64][D/E][64][E]: per 64-position block,
+ *                     E consecutive dims of 64 consecutive positions.
+ *   V, f32:           (((b*Hkv + g)*(C/4) + j/4)*D + d)*4 + j%4
+ *                     i.e. [B][Hkv][C/4][D][4]: per 4 positions, all dims.
+ *   V, bf16:          ((((b*Hkv + g)*(C/32) + j/32)*4 + s)*D + d)*8 + t
+ *                     with r = j%32, s = (r%16)/4, t = r%4 + 4*(r/16)
+ *                     i.e. [B][Hkv][C/32][4][D][8]: each 32-position block in
+ *                     four groups of 8 positions {4s..4s+3, 16+4s..16+4s+3}.
+ *
+ *   Cache contents beyond the rows appended so far are never read into a
+ *   result (they may hold anything, NaN included).
+ *
+ * Limits: 1 <= Hkv, Hkv divides Hq, D in {64, 128, 256}, C a multiple of 64
+ * with 64 <= C <= 131072, batch >= 1.
+ */
+#ifndef KA_ATTN_H_
+#define KA_ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KA_ATTN_ABI_VERSION 1
+#define KA_ATTN_MAX_CAPACITY 131072
+
+typedef enum ka_status {
+  KA_OK = 0,
+  KA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad count, Hq % Hkv != 0, bad scale */
+  KA_ERR_OUT_OF_RANGE = 2,     /* start + R > C, ctx < 1 or ctx > C, C too large  */
+  KA_ERR_UNSUPPORTED = 3,      /* head_dim or kv dtype not built                  */
+  KA_ERR_WORKSPACE = 4,        /* workspace smaller than required                 */
+  KA_ERR_HIP = 5               /* a HIP runtime error; text in ka_attn_last_error */
+} ka_status;
+
+typedef enum ka_dtype { KA_DTYPE_F32 = 0, KA_DTYPE_BF16 = 1 } ka_dtype;
+
+typedef struct ka_attn_shape {
+  int32_t batch;        /* B: independent sessions, each with its own cache rows */
+  int32_t num_q_heads;  /* Hq                                                      */
+  int32_t num_kv_heads; /* Hkv; query heads h*G .. h*G+G-1 share KV head h, G=Hq/Hkv */
+  int32_t head_dim;     /* D in {64, 128, 256}                                     */
+  int32_t capacity;     /* C: positions per session per KV head, multiple of 64    */
+  int32_t kv_dtype;     /* ka_dtype of both caches                                 */
+} ka_attn_shape;
+
+/* Version of this ABI (KA_ATTN_ABI_VERSION of the built library). */
+int32_t ka_attn_abi_version(void);
+
+/* Bytes of ONE cache buffer (K or V) for shape s; 0 if s is invalid. */
+size_t ka_attn_cache_bytes(const ka_attn_shape* s);
+
+/*
+ * KV append (the step that puts a chunk's rows into the session state before
+ * they are attended; Karume v0.8.0 release notes, "Features": multi-turn
+ * sessions continue the KV cache, and the context tracks the KV length).
+ *
+ * Writes rows k_new[b][i], v_new[b][i] (f32 [B][R][Hkv][D]) into cache
+ * positions start_pos + i, i < row_count, of every session b: an exact copy
+ * for f32 caches, round-to-nearest-even to bf16 for bf16 caches.
+ * row_count == 0 is a no-op.  Errors: KA_ERR_INVALID_ARGUMENT (null pointer,
+ * row_count < 0, start_pos < 0), KA_ERR_OUT_OF_RANGE (start_pos + row_count
+ * > C), KA_ERR_UNSUPPORTED, KA_ERR_HIP.
+ */
+ka_status ka_attn_append_kv(const ka_attn_shape* s, void* k_cache, void* v_cache,
+                            const float* k_new, const float* v_new,
+                            int32_t start_pos, int32_t row_count, void* stream);
+
+/*
+ * Workspace bytes that ka_attn_prefill_chunk needs for any chunk of at most
+ * max_rows rows at any start position of shape s (0 if none is needed).
+ */
+size_t ka_attn_prefill_workspace_bytes(const ka_attn_shape* s, int32_t max_rows);
+
+/*
+ * Chunked prefill (Karume v0.12.0 release notes, "Performance": the
+ * states-form prefill on the GEMM tile skeleton, where the rows of a chunk
+ * share each K / V row read; Karume v0.8.0 release notes, "Features": chunks
+ * of up to 768 rows).
+ *
+ * Row i (i < row_count) of the chunk is at absolute position start_pos + i
+ * and attends to cache positions 0 .. start_pos + i, which must already hold
+ * appended rows.  q and out are f32 [B][R][Hq][D]; out may not alias q.
+ * scale must be finite and > 0 (e.g. 1/sqrt(D)).  row_count == 0 is a no-op.
+ * workspace: device scratch of at least
+ * ka_attn_prefill_workspace_bytes(s, row_count) bytes (may be NULL when that
+ * is 0).  Errors: KA_ERR_INVALID_ARGUMENT, KA_ERR_OUT_OF_RANGE (start_pos +
+ * row_count > C), KA_ERR_UNSUPPORTED, KA_ERR_WORKSPACE, KA_ERR_HIP.
+ */
+ka_status ka_attn_prefill_chunk(const ka_attn_shape* s, const float* q,
+                                const void* k_cache, const void* v_cache, float* out,
+                                int32_t start_pos, int32_t row_count, float scale,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes that ka_attn_decode needs when no session's context length
+ * exceeds max_ctx_len.
+ */
+size_t ka_attn_decode_workspace_bytes(const ka_attn_shape* s, int32_t max_ctx_len);
+
+/*
+ * Decode step (Karume v0.12.0 release notes, "Performance": the parallel QK
+ * and PV reductions for one-row plans; Karume v0.8.0 release notes,
+ * "Performance": the KV-axis parallel value accumulation).
+ *
+ * For each session b, the single query row q[b] (f32 [B][Hq][D]) sits at
+ * position ctx_len[b] - 1 and attends to cache positions 0 .. ctx_len[b]-1
+ * (so a step appends its own row first, then decodes).  ctx_len is a HOST
+ * array of B entries, each 1 <= ctx_len[b] <= C.  out is f32 [B][Hq][D].
+ * workspace: device scratch of at least
+ * ka_attn_decode_workspace_bytes(s, max_b ctx_len[b]) bytes.  The result is
+ * bitwise reproducible for the same inputs and shape.  Errors:
+ * KA_ERR_INVALID_ARGUMENT, KA_ERR_OUT_OF_RANGE, KA_ERR_UNSUPPORTED,
+ * KA_ERR_WORKSPACE, KA_ERR_HIP.
+ */
+ka_status ka_attn_decode(const ka_attn_shape* s, const float* q,
+                         const void* k_cache, const void* v_cache, float* out,
+                         const int32_t* ctx_len, float scale,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static name of a status code ("KA_OK", ...). */
+const char* ka_attn_status_string(int32_t status);
+
+/* Reason for the last non-KA_OK status returned on this thread ("" if none). */
+const char* ka_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KA_ATTN_H_ */

@@ -1,0 +1,223 @@
+"""Python binding of libka_attn: grouped-query causal KV-cache attention on
+MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI in ``include/ka_attn.h``: each
+function takes torch tensors that live on the GPU, checks dtype / size /
+contiguity, and passes raw device pointers and the current HIP stream to the
+library.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback.  If the shared library is missing the import of this
+module still works but every call raises ``KaAttnUnavailable``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+__all__ = ["Shape", "KaAttnError", "KaAttnUnavailable", "lib", "lib_path", "F32", "BF16",
+           "cache_bytes", "alloc_cache", "append_kv", "prefill_workspace_bytes",
+           "prefill_chunk", "decode_workspace_bytes", "decode", "status_string",
+           "last_error", "abi_version", "EXPORTED_SYMBOLS"]
+
+F32 = 0
+BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libka_attn.so"
+
+EXPORTED_SYMBOLS = (
+    "ka_attn_abi_version", "ka_attn_cache_bytes", "ka_attn_append_kv",
+    "ka_attn_prefill_workspace_bytes", "ka_attn_prefill_chunk",
+    "ka_attn_decode_workspace_bytes", "ka_attn_decode", "ka_attn_status_string",
+    "ka_attn_last_error",
+)
+
+STATUS = {0: "KA_OK", 1: "KA_ERR_INVALID_ARGUMENT", 2: "KA_ERR_OUT_OF_RANGE",
+          3: "KA_ERR_UNSUPPORTED", 4: "KA_ERR_WORKSPACE", 5: "KA_ERR_HIP"}
+
+
+class KaAttnUnavailable(RuntimeError):
+    """The compiled library is not present (build it first)."""
+
+
+class KaAttnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+class Shape(ctypes.Structure):
+    """Mirror of ka_attn_shape."""
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("capacity", ctypes.c_int32), ("kv_dtype", ctypes.c_int32)]
+
+    def __init__(self, batch, num_q_heads, num_kv_heads, head_dim, capacity, kv_dtype):
+        if isinstance(kv_dtype, str):
+            kv_dtype = {"f32": F32, "bf16": BF16}[kv_dtype]
+        super().__init__(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim),
+                         int(capacity), int(kv_dtype))
+
+    def __repr__(self):
+        return (f"Shape(batch={self.batch}, Hq={self.num_q_heads}, Hkv={self.num_kv_heads}, "
+                f"D={self.head_dim}, C={self.capacity}, "
+                f"kv={'bf16' if self.kv_dtype == BF16 else 'f32'})")
+
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.environ.get("KA_ATTN_LIB", os.path.join(_HERE, _LIB_NAME))
+
+
+def lib() -> ctypes.CDLL:
+    """Loads (once) and returns the shared library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise KaAttnUnavailable(
+            f"{path} not found; build it with `python -m kv_cache_attention_amd.build`")
+    L = ctypes.CDLL(path)
+    c_void_p, c_int32, c_size_t, c_float = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    P = ctypes.POINTER(Shape)
+    L.ka_attn_abi_version.restype = c_int32
+    L.ka_attn_abi_version.argtypes = []
+    L.ka_attn_cache_bytes.restype = c_size_t
+    L.ka_attn_cache_bytes.argtypes = [P]
+    L.ka_attn_append_kv.restype = c_int32
+    L.ka_attn_append_kv.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p]
+    L.ka_attn_prefill_workspace_bytes.restype = c_size_t
+    L.ka_attn_prefill_workspace_bytes.argtypes = [P, c_int32]
+    L.ka_attn_prefill_chunk.restype = c_int32
+    L.ka_attn_prefill_chunk.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
+                                        c_float, c_void_p, c_size_t, c_void_p]
+    L.ka_attn_decode_workspace_bytes.restype = c_size_t
+    L.ka_attn_decode_workspace_bytes.argtypes = [P, c_int32]
+    L.ka_attn_decode.restype = c_int32
+    L.ka_attn_decode.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 ctypes.POINTER(c_int32), c_float, c_void_p, c_size_t, c_void_p]
+    L.ka_attn_status_string.restype = ctypes.c_char_p
+    L.ka_attn_status_string.argtypes = [c_int32]
+    L.ka_attn_last_error.restype = ctypes.c_char_p
+    L.ka_attn_last_error.argtypes = []
+    _lib = L
+    return L
+
+
+def abi_version() -> int:
+    return int(lib().ka_attn_abi_version())
+
+
+def status_string(status: int) -> str:
+    return lib().ka_attn_status_string(int(status)).decode()
+
+
+def last_error() -> str:
+    return lib().ka_attn_last_error().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise KaAttnError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return ctypes.c_void_p(handle)
+
+
+def _need(t: torch.Tensor, name: str, dtype, numel: Optional[int] = None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+
+
+def cache_bytes(shape: Shape) -> int:
+    return int(lib().ka_attn_cache_bytes(ctypes.byref(shape)))
+
+
+def alloc_cache(shape: Shape, device="cuda", fill_byte: Optional[int] = None) -> torch.Tensor:
+    """A byte tensor sized for one cache buffer (K or V) of ``shape``."""
+    n = cache_bytes(shape)
+    if n == 0:
+        raise KaAttnError(1, last_error())
+    t = torch.empty(n, dtype=torch.uint8, device=device)
+    if fill_byte is not None:
+        t.fill_(int(fill_byte))
+    return t
+
+
+def append_kv(shape: Shape, k_cache: torch.Tensor, v_cache: torch.Tensor,
+              k_new: torch.Tensor, v_new: torch.Tensor, start_pos: int, row_count: int,
+              stream=None) -> None:
+    n = shape.batch * row_count * shape.num_kv_heads * shape.head_dim
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, torch.float32, n)
+    cb = cache_bytes(shape)
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, None)
+        if t.numel() * t.element_size() < cb:
+            raise ValueError(f"{nm} is smaller than {cb} bytes")
+    _check(lib().ka_attn_append_kv(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(k_new), _ptr(v_new), int(start_pos), int(row_count),
+                                   _stream(stream)))
+
+
+def prefill_workspace_bytes(shape: Shape, max_rows: int) -> int:
+    return int(lib().ka_attn_prefill_workspace_bytes(ctypes.byref(shape), int(max_rows)))
+
+
+def prefill_chunk(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                  out: torch.Tensor, start_pos: int, row_count: int, scale: float,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    n = shape.batch * row_count * shape.num_q_heads * shape.head_dim
+    _need(q, "q", torch.float32, n)
+    _need(out, "out", torch.float32, n)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", None)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().ka_attn_prefill_chunk(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                       _ptr(out), int(start_pos), int(row_count), float(scale),
+                                       _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def decode_workspace_bytes(shape: Shape, max_ctx_len: int) -> int:
+    return int(lib().ka_attn_decode_workspace_bytes(ctypes.byref(shape), int(max_ctx_len)))
+
+
+def decode(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           out: torch.Tensor, ctx_len: Sequence[int], scale: float,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    n = shape.batch * shape.num_q_heads * shape.head_dim
+    _need(q, "q", torch.float32, n)
+    _need(out, "out", torch.float32, n)
+    if len(ctx_len) != shape.batch:
+        raise ValueError(f"ctx_len has {len(ctx_len)} entries, expected {shape.batch}")
+    arr = (ctypes.c_int32 * shape.batch)(*[int(c) for c in ctx_len])
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", None)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().ka_attn_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(out), arr, float(scale), _ptr(workspace), ws_bytes,
+                                _stream(stream)))

@@ -1,0 +1,185 @@
+// C ABI of the attention library: argument validation (always before any
+// work is enqueued, so a rejected call changes nothing), plan selection and
+// the per-thread error text.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/ka_attn.h"
+#include "ka_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+ka_status fail(ka_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+ka_status ok() {
+  g_last_error[0] = '\0';
+  return KA_OK;
+}
+
+ka_status hip_fail(hipError_t e, const char* where) {
+  return fail(KA_ERR_HIP, "%s: %s (%s)", where, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+// Checks a shape; on success fills *out.
+ka_status check_shape(const ka_attn_shape* s, ka::Shape* out) {
+  if (!s) return fail(KA_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (s->batch < 1) return fail(KA_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", s->batch);
+  if (s->num_q_heads < 1 || s->num_kv_heads < 1)
+    return fail(KA_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (got Hq=%d, Hkv=%d)",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->num_q_heads % s->num_kv_heads != 0)
+    return fail(KA_ERR_INVALID_ARGUMENT, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                s->num_q_heads, s->num_kv_heads);
+  if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256)
+    return fail(KA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128 or 256)", s->head_dim);
+  if (s->kv_dtype != KA_DTYPE_F32 && s->kv_dtype != KA_DTYPE_BF16)
+    return fail(KA_ERR_UNSUPPORTED, "kv_dtype %d not supported (0 = f32, 1 = bf16)", s->kv_dtype);
+  if (s->capacity > KA_ATTN_MAX_CAPACITY)
+    return fail(KA_ERR_OUT_OF_RANGE, "capacity %d exceeds %d", s->capacity, KA_ATTN_MAX_CAPACITY);
+  if (s->capacity < 64 || s->capacity % 64 != 0)
+    return fail(KA_ERR_INVALID_ARGUMENT, "capacity %d must be a positive multiple of 64",
+                s->capacity);
+  *out = ka::Shape{s->batch, s->num_q_heads, s->num_kv_heads, s->head_dim, s->capacity,
+                   s->kv_dtype};
+  return KA_OK;
+}
+
+ka_status check_scale(float scale) {
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(KA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0 (got %g)", (double)scale);
+  return KA_OK;
+}
+
+size_t cache_bytes(const ka::Shape& s) {
+  return (size_t)s.batch * s.num_kv_heads * (size_t)s.capacity * s.head_dim *
+         (s.kv_dtype == KA_DTYPE_BF16 ? 2 : 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ka_attn_abi_version(void) { return KA_ATTN_ABI_VERSION; }
+
+size_t ka_attn_cache_bytes(const ka_attn_shape* s) {
+  ka::Shape sh;
+  if (check_shape(s, &sh) != KA_OK) return 0;
+  return cache_bytes(sh);
+}
+
+ka_status ka_attn_append_kv(const ka_attn_shape* s, void* k_cache, void* v_cache,
+                            const float* k_new, const float* v_new, int32_t start_pos,
+                            int32_t row_count, void* stream) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  if (row_count < 0) return fail(KA_ERR_INVALID_ARGUMENT, "row_count %d < 0", row_count);
+  if (start_pos < 0) return fail(KA_ERR_INVALID_ARGUMENT, "start_pos %d < 0", start_pos);
+  if ((long long)start_pos + row_count > sh.capacity)
+    return fail(KA_ERR_OUT_OF_RANGE, "start_pos %d + row_count %d exceeds capacity %d",
+                start_pos, row_count, sh.capacity);
+  if (row_count == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new)
+    return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  hipError_t e = ka::launch_append(sh, k_cache, v_cache, k_new, v_new, start_pos, row_count,
+                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+size_t ka_attn_prefill_workspace_bytes(const ka_attn_shape* s, int32_t max_rows) {
+  ka::Shape sh;
+  if (check_shape(s, &sh) != KA_OK) return 0;
+  return ka::prefill_workspace_bound(sh, max_rows);
+}
+
+ka_status ka_attn_prefill_chunk(const ka_attn_shape* s, const float* q, const void* k_cache,
+                                const void* v_cache, float* out, int32_t start_pos,
+                                int32_t row_count, float scale, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  if (row_count < 0) return fail(KA_ERR_INVALID_ARGUMENT, "row_count %d < 0", row_count);
+  if (start_pos < 0) return fail(KA_ERR_INVALID_ARGUMENT, "start_pos %d < 0", start_pos);
+  if ((long long)start_pos + row_count > sh.capacity)
+    return fail(KA_ERR_OUT_OF_RANGE, "start_pos %d + row_count %d exceeds capacity %d",
+                start_pos, row_count, sh.capacity);
+  if ((st = check_scale(scale)) != KA_OK) return st;
+  if (row_count == 0) return ok();
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if ((const void*)q == (const void*)out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "out must not alias q");
+  const ka::PrefillPlan plan = ka::plan_prefill(sh, start_pos, row_count);
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return fail(KA_ERR_WORKSPACE, "prefill needs %zu workspace bytes, got %zu", plan.workspace_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  hipError_t e = ka::launch_prefill(sh, plan, q, k_cache, v_cache, out, start_pos, row_count,
+                                    scale, workspace, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+size_t ka_attn_decode_workspace_bytes(const ka_attn_shape* s, int32_t max_ctx_len) {
+  ka::Shape sh;
+  if (check_shape(s, &sh) != KA_OK) return 0;
+  if (max_ctx_len < 1) return 0;
+  if (max_ctx_len > sh.capacity) max_ctx_len = sh.capacity;
+  return ka::plan_decode(sh, max_ctx_len).workspace_bytes;
+}
+
+ka_status ka_attn_decode(const ka_attn_shape* s, const float* q, const void* k_cache,
+                         const void* v_cache, float* out, const int32_t* ctx_len, float scale,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  if (!ctx_len) return fail(KA_ERR_INVALID_ARGUMENT, "ctx_len is NULL");
+  int max_ctx = 0;
+  for (int b = 0; b < sh.batch; ++b) {
+    if (ctx_len[b] < 1 || ctx_len[b] > sh.capacity)
+      return fail(KA_ERR_OUT_OF_RANGE, "ctx_len[%d] = %d outside 1..capacity (%d)", b, ctx_len[b],
+                  sh.capacity);
+    if (ctx_len[b] > max_ctx) max_ctx = ctx_len[b];
+  }
+  if ((st = check_scale(scale)) != KA_OK) return st;
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if ((const void*)q == (const void*)out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "out must not alias q");
+  const ka::DecodePlan plan = ka::plan_decode(sh, max_ctx);
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return fail(KA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.workspace_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  hipError_t e = ka::launch_decode(sh, plan, q, k_cache, v_cache, out, ctx_len, scale, workspace,
+                                   reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+const char* ka_attn_status_string(int32_t status) {
+  switch (status) {
+    case KA_OK: return "KA_OK";
+    case KA_ERR_INVALID_ARGUMENT: return "KA_ERR_INVALID_ARGUMENT";
+    case KA_ERR_OUT_OF_RANGE: return "KA_ERR_OUT_OF_RANGE";
+    case KA_ERR_UNSUPPORTED: return "KA_ERR_UNSUPPORTED";
+    case KA_ERR_WORKSPACE: return "KA_ERR_WORKSPACE";
+    case KA_ERR_HIP: return "KA_ERR_HIP";
+    default: return "KA_ERR_UNKNOWN";
+  }
+}
+
+const char* ka_attn_last_error(void) { return g_last_error; }
+
+}  // extern "C"

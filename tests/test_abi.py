@@ -1,0 +1,182 @@
+"""The C ABI: the library loads, exports what the header declares, and
+rejects bad arguments on the host before touching the GPU (no GPU needed:
+every call here fails validation, which runs before any HIP call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_attention_amd as ka
+from tests.cache_layout import unpack_k, unpack_v
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ka_attn.h")
+
+
+def _lib_or_skip():
+    try:
+        return ka.lib()
+    except ka.KaAttnUnavailable as e:
+        pytest.fail(f"library not built: {e}")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ka_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = header_functions()
+    for n in ["ka_attn_append_kv", "ka_attn_prefill_chunk", "ka_attn_decode",
+              "ka_attn_decode_workspace_bytes", "ka_attn_prefill_workspace_bytes",
+              "ka_attn_cache_bytes", "ka_attn_status_string", "ka_attn_last_error",
+              "ka_attn_abi_version"]:
+        assert n in names
+    assert set(names) == set(ka.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib_or_skip()
+    for n in header_functions():
+        assert hasattr(L, n), n
+    assert ka.abi_version() == 1
+
+
+def test_status_strings():
+    _lib_or_skip()
+    assert ka.status_string(0) == "KA_OK"
+    assert ka.status_string(4) == "KA_ERR_WORKSPACE"
+    assert ka.status_string(99) == "KA_ERR_UNKNOWN"
+
+
+def S(**kw):
+    d = dict(batch=1, num_q_heads=8, num_kv_heads=1, head_dim=256, capacity=4096, kv_dtype=ka.BF16)
+    d.update(kw)
+    return ka.Shape(**d)
+
+
+def test_cache_bytes():
+    _lib_or_skip()
+    assert ka.cache_bytes(S()) == 4096 * 256 * 2
+    assert ka.cache_bytes(S(kv_dtype=ka.F32, batch=3, num_kv_heads=2)) == 3 * 2 * 4096 * 256 * 4
+    assert ka.cache_bytes(S(head_dim=96)) == 0
+    assert ka.cache_bytes(S(capacity=100)) == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def _append(shape, start, rows, ptr=FAKE):
+    return ka.lib().ka_attn_append_kv(ctypes.byref(shape), ptr, ptr, ptr, ptr, start, rows, None)
+
+
+def _prefill(shape, start, rows, scale=0.0625, ws=None, ws_bytes=0, q=FAKE, out=ctypes.c_void_p(0x2000)):
+    return ka.lib().ka_attn_prefill_chunk(ctypes.byref(shape), q, FAKE, FAKE, out, start, rows,
+                                          scale, ws, ws_bytes, None)
+
+
+def _decode(shape, ctx, scale=0.0625, ws=None, ws_bytes=0, q=FAKE, out=ctypes.c_void_p(0x2000)):
+    arr = (ctypes.c_int32 * len(ctx))(*ctx)
+    return ka.lib().ka_attn_decode(ctypes.byref(shape), q, FAKE, FAKE, out, arr, scale, ws,
+                                   ws_bytes, None)
+
+
+@pytest.mark.parametrize("shape,status", [
+    (S(batch=0), 1), (S(num_q_heads=0), 1), (S(num_kv_heads=3), 1), (S(head_dim=80), 3),
+    (S(kv_dtype=7), 3), (S(capacity=131072 + 64), 2), (S(capacity=1000), 1), (S(capacity=0), 1),
+])
+def test_bad_shapes_rejected_everywhere(shape, status):
+    _lib_or_skip()
+    assert _append(shape, 0, 1) == status
+    assert _prefill(shape, 0, 1) == status
+    assert _decode(shape, [1] * max(shape.batch, 1)) == status
+    assert ka.last_error() != ""
+
+
+def test_append_argument_errors():
+    _lib_or_skip()
+    s = S()
+    assert _append(s, -1, 1) == 1
+    assert _append(s, 0, -1) == 1
+    assert _append(s, 4000, 97) == 2
+    assert _append(s, 0, 1, ptr=None) == 1
+    assert _append(s, 4096, 0) == 0          # an empty append is a no-op
+    assert ka.last_error() == ""
+
+
+def test_prefill_argument_errors():
+    _lib_or_skip()
+    s = S()
+    assert _prefill(s, 0, 1, scale=float("nan")) == 1
+    assert _prefill(s, 0, 1, scale=float("inf")) == 1
+    assert _prefill(s, 0, 1, scale=0.0) == 1
+    assert _prefill(s, 0, 1, scale=-1.0) == 1
+    assert _prefill(s, 4090, 7) == 2
+    assert _prefill(s, 0, 1, q=None) == 1
+    assert _prefill(s, 0, 1, out=FAKE) == 1      # out aliases q
+    assert _prefill(s, 0, 0) == 0                # empty chunk is a no-op
+    # a long chunk needs a workspace; a missing or short one is rejected
+    need = ka.prefill_workspace_bytes(s, 768)
+    assert need > 0
+    assert _prefill(s, 3000, 768) == 4
+    assert _prefill(s, 3000, 768, ws=FAKE, ws_bytes=16) == 4
+
+
+def test_decode_argument_errors():
+    _lib_or_skip()
+    s = S(batch=2)
+    assert _decode(s, [1, 0]) == 2
+    assert _decode(s, [4097, 3]) == 2
+    assert _decode(s, [5, 5], scale=float("nan")) == 1
+    arr = None
+    assert ka.lib().ka_attn_decode(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.c_void_p(0x2000), arr,
+                                   0.1, None, 0, None) == 1
+    need = ka.decode_workspace_bytes(s, 4096)
+    assert need > 0
+    assert _decode(s, [4096, 10]) == 4
+    assert _decode(s, [4096, 10], ws=FAKE, ws_bytes=need - 1) == 4
+
+
+def test_workspace_sizes_cover_smaller_requests():
+    _lib_or_skip()
+    s = S(batch=4, capacity=131072)
+    big = ka.decode_workspace_bytes(s, 131072)
+    for c in [1, 64, 1000, 16384, 65536]:
+        assert ka.decode_workspace_bytes(s, c) <= big
+    p = ka.prefill_workspace_bytes(s, 768)
+    for r in [1, 16, 100, 767]:
+        assert ka.prefill_workspace_bytes(s, r) <= p
+
+
+# ------------------------------------------- the test-side layout readers
+
+def test_layout_reader_round_trip_k_and_v():
+    """The readers invert the header's index formulas (checked on a marked
+    cache: each element stores its own logical coordinates)."""
+    B, Hkv, C, D = 2, 2, 64, 16
+    for dt, E in (("f32", 4), ("bf16", 8)):
+        nel = B * Hkv * C * D
+        # element index formulas from the header
+        raw_k = np.zeros(nel, np.uint16 if dt == "bf16" else np.float32)
+        raw_v = np.zeros_like(raw_k)
+        want = np.zeros((B, Hkv, C, D))
+        for b in range(B):
+            for g in range(Hkv):
+                for j in range(C):
+                    for d in range(D):
+                        val = ((b * Hkv + g) * C + j) * D + d
+                        want[b, g, j, d] = val
+                        ki = ((((b * Hkv + g) * (C // 64) + j // 64) * (D // E) + d // E) * 64 + j % 64) * E + d % E
+                        if dt == "f32":
+                            vi = (((b * Hkv + g) * (C // 4) + j // 4) * D + d) * 4 + j % 4
+                        else:
+                            r = j % 32
+                            s_, t = (r % 16) // 4, r % 4 + 4 * (r // 16)
+                            vi = ((((b * Hkv + g) * (C // 32) + j // 32) * 4 + s_) * D + d) * 8 + t
+                        raw_k[ki] = val
+                        raw_v[vi] = val
+        assert np.array_equal(unpack_k(raw_k, B, Hkv, C, D, dt).astype(np.float64), want)
+        assert np.array_equal(unpack_v(raw_v, B, Hkv, C, D, dt).astype(np.float64), want)
