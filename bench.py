@@ -1,0 +1,371 @@
+"""Benchmark of the GQA KV-cache attention path on one MI355X.
+
+One step = one pass of the whole path over the 16K session workload: a
+16384-token prompt (8 query heads sharing 1 KV head, head_dim 256, bf16
+cache) prefilled as 21 chunks of 768 rows plus one of 256 -- each chunk an
+append of its K/V rows and a prefill of its query rows -- followed by 64
+decode steps, each an append of the step's row and a decode.  Inputs are
+seeded synthetic draws (module ``synth``), resident in HBM before timing.
+
+Printed: one JSON line.  ``value`` is the 16K prefill throughput in rows/s
+(16384 rows / GPU time of the 22 append + prefill calls).  The line also
+carries the decode time per token at 16K (in-session, and cache-cold over 64
+rotated cache copies) and at 128K (4 sessions batched), the roofline of the
+prefill kernel (bf16 MFMA) and of the 128K decode (HBM), and the CPU oracle
+timed on a bounded sample of the same workload.
+
+GPU times come from HIP events recorded on the stream the library launches
+on.  While the host enqueues a timed phase the GPU is held by a short spin
+kernel (recorded before the phase's first event), so per-call times measure
+the GPU, not Python's call overhead.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import kv_cache_attention_amd as ka  # noqa: E402
+from synth import WORKLOADS, draw_batch  # noqa: E402
+
+METRIC = "prefill rows/s at 16K ctx; decode µs/token at 16K & 128K; % HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda")
+
+
+class Hold:
+    """Keeps the GPU busy while the host enqueues a phase (torch's spin kernel)."""
+
+    def __init__(self):
+        self.cycles = 0
+        if not hasattr(torch.cuda, "_sleep"):
+            return
+        # calibrate: cycles for ~1 ms
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(1_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        self.per_ms = 1_000_000 / max(ms, 1e-3)
+
+    def __call__(self, ms):
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(self.per_ms * ms))
+
+
+def prefill_flops(w):
+    """Algorithmic flops of the session's prefill: causal pairs x Hq x D x 4."""
+    pairs = sum(R * s + R * (R + 1) // 2 for s, R in w.chunks)
+    return pairs * w.num_q_heads * w.head_dim * 4 * w.batch, pairs
+
+
+def decode_bytes(w, ctx, batch):
+    """Algorithmic HBM bytes of one decode call: K and V rows once, q and out."""
+    el = 2 if w.kv_dtype == "bf16" else 4
+    kv = 2 * batch * w.num_kv_heads * ctx * w.head_dim * el
+    qo = 2 * batch * w.num_q_heads * w.head_dim * 4
+    return kv + qo
+
+
+class Session16K:
+    """Device state of the 16K session workload."""
+
+    def __init__(self):
+        self.w = w = WORKLOADS[4]
+        c = draw_batch(w)
+        self.k = dev(c.k)          # [1][P][1][256]
+        self.v = dev(c.v)
+        self.q = dev(c.q)          # [1][16448][8][256]
+        self.shape = ka.Shape(1, 8, 1, 256, w.capacity, "bf16")
+        self.kc = ka.alloc_cache(self.shape, fill_byte=0xFF)
+        self.vc = ka.alloc_cache(self.shape, fill_byte=0xFF)
+        self.out_p = torch.empty(768 * 8 * 256, device="cuda")
+        self.out_d = torch.empty(8 * 256, device="cuda")
+        n = max(ka.prefill_workspace_bytes(self.shape, 768),
+                ka.decode_workspace_bytes(self.shape, w.capacity), 1)
+        self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+        # contiguous per-call views
+        self.chunk_views = []
+        qrow = 0
+        for s, R in w.chunks:
+            self.chunk_views.append((s, R, self.k[:, s:s + R], self.v[:, s:s + R],
+                                     self.q[:, qrow:qrow + R], self.out_p[: R * 8 * 256]))
+            qrow += R
+        self.dec_views = []
+        for t, p in enumerate(w.decode_positions):
+            self.dec_views.append((p, self.k[:, p:p + 1], self.v[:, p:p + 1], self.q[0, qrow + t]))
+
+    def prefill_phase(self, ev=None):
+        sh = self.shape
+        for i, (s, R, kk, vv, qq, oo) in enumerate(self.chunk_views):
+            ka.append_kv(sh, self.kc, self.vc, kk, vv, s, R)
+            if ev is not None:
+                ev[i][0].record()
+            ka.prefill_chunk(sh, qq, self.kc, self.vc, oo, s, R, self.w.scale, self.ws)
+            if ev is not None:
+                ev[i][1].record()
+
+    def decode_phase(self, ev=None):
+        sh = self.shape
+        for i, (p, kk, vv, qq) in enumerate(self.dec_views):
+            ka.append_kv(sh, self.kc, self.vc, kk, vv, p, 1)
+            if ev is not None:
+                ev[i][0].record()
+            ka.decode(sh, qq, self.kc, self.vc, self.out_d, [p + 1], self.w.scale, self.ws)
+            if ev is not None:
+                ev[i][1].record()
+
+
+def ev_pair():
+    return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+
+
+def bench_session(steps, warmup, hold):
+    s = Session16K()
+    log("16K session: inputs resident")
+    for _ in range(warmup):
+        s.prefill_phase()
+        s.decode_phase()
+    torch.cuda.synchronize()
+    nch, ndec = len(s.chunk_views), len(s.dec_views)
+    rec = []
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        pe = [ev_pair() for _ in range(nch)]
+        de = [ev_pair() for _ in range(ndec)]
+        ph, dh = ev_pair(), ev_pair()
+        hold(3.0)
+        ph[0].record()
+        s.prefill_phase(pe)
+        ph[1].record()
+        hold(8.0)
+        dh[0].record()
+        s.decode_phase(de)
+        dh[1].record()
+        rec.append((ph, dh, pe, de))
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    phase_p = [r[0][0].elapsed_time(r[0][1]) for r in rec]
+    phase_d = [r[1][0].elapsed_time(r[1][1]) for r in rec]
+    pre_calls = np.array([[a.elapsed_time(b) for a, b in r[2]] for r in rec])     # [steps][22]
+    dec_calls = np.array([[a.elapsed_time(b) for a, b in r[3]] for r in rec])     # [steps][64]
+    return dict(w=s.w, wall_ms=wall * 1e3, prefill_phase_ms=float(np.mean(phase_p)),
+                decode_phase_ms=float(np.mean(phase_d)), prefill_calls_ms=pre_calls,
+                decode_calls_ms=dec_calls, session=s)
+
+
+def bench_decode_cold_16k(s, hold, copies=64, reps=3):
+    """Decode at 16K over `copies` caches in rotation (more bytes than the MALL)."""
+    w = s.w
+    p = w.decode_positions[-1]
+    kcs = [s.kc.clone() for _ in range(copies)]
+    vcs = [s.vc.clone() for _ in range(copies)]
+    qq = s.dec_views[-1][3]
+    torch.cuda.synchronize()
+    times = []
+    for r in range(reps + 1):
+        a, b = ev_pair()
+        hold(3.0)
+        a.record()
+        for i in range(copies):
+            ka.decode(s.shape, qq, kcs[i], vcs[i], s.out_d, [p + 1], w.scale, s.ws)
+        b.record()
+        torch.cuda.synchronize()
+        if r:
+            times.append(a.elapsed_time(b) / copies)
+    del kcs, vcs
+    return float(np.median(times))
+
+
+def bench_decode_128k(hold, steps=32):
+    w = WORKLOADS[5]
+    c = draw_batch(w)
+    log("128K: drawn")
+    shape = ka.Shape(w.batch, 8, 1, 256, w.capacity, "bf16")
+    kc = ka.alloc_cache(shape, fill_byte=0xFF)
+    vc = ka.alloc_cache(shape, fill_byte=0xFF)
+    for s0 in range(0, w.positions, 16384):
+        e = min(w.positions, s0 + 16384)
+        ka.append_kv(shape, kc, vc, dev(c.k[:, s0:e]), dev(c.v[:, s0:e]), s0, e - s0)
+    torch.cuda.synchronize()
+    # every position is now appended once; the timed steps re-append their
+    # own rows (identical values) exactly as a decode loop does
+    kd = [dev(c.k[:, p:p + 1]) for p in w.decode_positions]
+    vd = [dev(c.v[:, p:p + 1]) for p in w.decode_positions]
+    qd = [dev(c.q[:, t]) for t in range(len(w.decode_positions))]
+    out = torch.empty(w.batch * 8 * 256, device="cuda")
+    ws = torch.empty(max(ka.decode_workspace_bytes(shape, w.capacity), 1), dtype=torch.uint8, device="cuda")
+    del c
+    log("128K: filled")
+
+    def run(ev):
+        for t, p in enumerate(w.decode_positions[:steps]):
+            ka.append_kv(shape, kc, vc, kd[t], vd[t], p, 1)
+            if ev is not None:
+                ev[t][0].record()
+            ka.decode(shape, qd[t], kc, vc, out, [p + 1] * w.batch, w.scale, ws)
+            if ev is not None:
+                ev[t][1].record()
+
+    run(None)
+    torch.cuda.synchronize()
+    reps = []
+    step_ms = []
+    for _ in range(3):
+        ev = [ev_pair() for _ in range(steps)]
+        a, b = ev_pair()
+        hold(5.0)
+        a.record()
+        run(ev)
+        b.record()
+        torch.cuda.synchronize()
+        reps.append([x.elapsed_time(y) for x, y in ev])
+        step_ms.append(a.elapsed_time(b) / steps)
+    dec = np.array(reps)
+    ctx_mean = int(np.mean([p + 1 for p in w.decode_positions[:steps]]))
+    return dict(w=w, decode_ms=float(np.median(dec)), step_ms=float(np.median(step_ms)),
+                bytes=decode_bytes(w, ctx_mean, w.batch), ctx_mean=ctx_mean)
+
+
+def cpu_baseline(session_w, budget_s=12.0):
+    """The oracle (as written) on a bounded sample of the 16K prefill."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    w = session_w
+    c = draw_batch(w)
+    ks = oracle.stored_values(c.k, "bf16")[0]
+    vs = oracle.stored_values(c.v, "bf16")[0]
+    start, R = w.chunks[-2]            # the last 768-row chunk, at 15360
+    qrow = sum(r for _, r in w.chunks[:-2])
+    ctxm = threadpool_limits(limits=cores) if threadpool_limits else None
+    try:
+        n = 16
+        t = time.perf_counter()
+        oracle.attend_rows(c.q[0, qrow:qrow + n], ks, vs, np.arange(start, start + n), w.scale)
+        dt = time.perf_counter() - t
+        n2 = int(min(R, max(n, n * budget_s / max(dt, 1e-3))))
+        t = time.perf_counter()
+        oracle.attend_rows(c.q[0, qrow:qrow + n2], ks, vs, np.arange(start, start + n2), w.scale)
+        dt2 = time.perf_counter() - t
+        # one 16K decode step
+        p = w.decode_positions[0]
+        t = time.perf_counter()
+        oracle.attend_rows(c.q[0, sum(r for _, r in w.chunks)][None], ks, vs, [p], w.scale)
+        dt3 = time.perf_counter() - t
+    finally:
+        if ctxm is not None:
+            ctxm.__exit__(None, None, None)
+    return {"value": n2 / dt2, "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{n2} query rows of the 768-row chunk at positions 15360.. (16K context, "
+                       f"8 heads, head_dim 256, bf16-stored K/V), numpy float64 two-pass softmax, "
+                       f"{cores} BLAS threads; {dt2:.1f} s"),
+            "decode_16k_us_per_token": dt3 * 1e6}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-128k", action="store_true")
+    ap.add_argument("--no-cold", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not "
+              f"supported by this build", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ka.lib()
+    torch.cuda.set_device(0)
+    hold = Hold()
+
+    r = bench_session(args.steps, args.warmup, hold)
+    w = r["w"]
+    flops, pairs = prefill_flops(w)
+    pre_calls = r["prefill_calls_ms"]                   # prefill calls only (no append)
+    pre_kernel_ms = float(pre_calls.sum(axis=1).mean())
+    achieved_tf = flops / (pre_kernel_ms * 1e-3) / 1e12
+    rows = sum(R for _, R in w.chunks)
+    value = rows / (r["prefill_phase_ms"] * 1e-3)        # append + prefill, 22 chunks
+    dec16 = r["decode_calls_ms"]
+    dec16_step = float(np.median(r["decode_phase_ms"])) / len(w.decode_positions)
+    last_chunk_ms = float(np.median(pre_calls[:, -2]))
+    s_last, R_last = w.chunks[-2]
+    flops_last = (R_last * s_last + R_last * (R_last + 1) // 2) * 8 * 256 * 4
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(r["prefill_phase_ms"] + r["decode_phase_ms"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": ("16K session: 8 query heads / 1 KV head, head_dim 256, bf16 KV "
+                                "cache (f32 accumulate), 16384-row prompt as 21x768 + 256 chunks "
+                                "(append + prefill each), then 64 decode steps (append + decode)"),
+                   "global_batch": 1, "seq_len": 16384, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved_tf / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None,
+                     "kernel": "prefill (prefill_kernel + prefill_merge_kernel), 22 chunks",
+                     "algorithmic_flops_per_step": flops, "causal_pairs": pairs,
+                     "avg_launch_ms": round(pre_kernel_ms / len(w.chunks), 5)},
+        "wall_ms_per_step": round(r["wall_ms"], 3),
+        "prefill_16k_ms": round(r["prefill_phase_ms"], 4),
+        "prefill_last768_rows_per_s": round(R_last / (last_chunk_ms * 1e-3), 1),
+        "prefill_last768_tflops": round(flops_last / (last_chunk_ms * 1e-3) / 1e12, 2),
+        "decode_us_per_token_16k": round(dec16_step * 1e3, 3),
+        "decode_us_per_token_16k_kernel_median": round(float(np.median(dec16)) * 1e3, 3),
+        "decode_us_per_token_16k_p10_p90": [round(float(np.percentile(dec16, 10)) * 1e3, 3),
+                                            round(float(np.percentile(dec16, 90)) * 1e3, 3)],
+    }
+    b16 = decode_bytes(w, w.decode_positions[-1] + 1, 1)
+    if not args.no_cold:
+        cold = bench_decode_cold_16k(r["session"], hold)
+        out["decode_us_per_token_16k_cold"] = round(cold * 1e3, 3)
+        out["decode_16k_cold_hbm_frac"] = round(b16 / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    out["decode_16k_warm_hbm_frac"] = round(b16 / (float(np.median(dec16)) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    del r
+    torch.cuda.empty_cache()
+    if not args.no_128k:
+        d = bench_decode_128k(hold)
+        gbs = d["bytes"] / (d["decode_ms"] * 1e-3) / 1e9
+        out["decode_us_per_step_128k_x4"] = round(d["decode_ms"] * 1e3, 3)
+        out["decode_us_per_token_128k"] = round(d["decode_ms"] * 1e3 / d["w"].batch, 3)
+        out["decode_us_per_step_128k_x4_with_append"] = round(d["step_ms"] * 1e3, 3)
+        out["roofline_decode_128k"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                       "traffic": None, "kernel": "decode (split + merge), 4 x 131041..131072",
+                                       "algorithmic_bytes_per_launch": d["bytes"]}
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

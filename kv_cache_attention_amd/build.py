@@ -28,6 +28,14 @@ HIPCC_FLAGS = [
 ]
 
 
+# Per-source extra flags.  The prefill kernel wants LLVM's ILP-oriented
+# machine scheduler so that LDS operand reads are issued ahead of the MFMAs
+# that consume them (the default occupancy-oriented one serialises them).
+EXTRA_FLAGS = {
+    "prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -41,7 +49,7 @@ def sources():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}")

@@ -6,7 +6,7 @@
 #include <cstdio>
 #include <cstring>
 
-#include "../../include/ka_attn.h"
+#include "ka_attn.h"
 #include "ka_launch.h"
 
 namespace {

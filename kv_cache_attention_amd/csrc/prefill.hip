@@ -36,6 +36,7 @@ constexpr int kMTile = 128;
 constexpr int kNTile = 64;
 constexpr int kTargetWgs = 512;
 constexpr int kMaxSplits = 64;
+constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay below 256
 
 typedef __attribute__((ext_vector_type(4))) float v4f;
 
@@ -46,29 +47,60 @@ struct PrefillCfg {
   static constexpr int VVEC = kNTile / E * D;            // 16-byte vectors per V tile
   static constexpr int TILE_BYTES = KVEC * 16;           // same for V
   static constexpr int NDB = D / 16;                     // 16-dim output blocks
+  // double-buffered K+V tiles when two stages fit in the 160 KiB of LDS
+  static constexpr int STAGES = 4 * TILE_BYTES <= 160 * 1024 ? 2 : 1;
+  static constexpr int LDS_BYTES = STAGES * 2 * TILE_BYTES;
 };
 
+// Asynchronous copy of one K tile and one V tile (each TILE_BYTES contiguous
+// bytes in the cache) into LDS with global_load_lds: every wave instruction
+// moves 1 KiB, lane l's 16 bytes landing at the wave's LDS base + 16 l.
+template <int TILE_BYTES>
+__device__ __forceinline__ void stage_tiles(const unsigned char* ksrc, const unsigned char* vsrc,
+                                            unsigned char* kdst, unsigned char* vdst, int w,
+                                            int lane) {
+  constexpr int PER_THREAD = TILE_BYTES / (256 * 16);
+#pragma unroll
+  for (int i = 0; i < PER_THREAD; ++i) {
+    const int off = (i * 256 + w * 64) * 16;
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(ksrc + off + lane * 16),
+        (__attribute__((address_space(3))) void*)(kdst + off), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(
+        (const void*)(vsrc + off + lane * 16),
+        (__attribute__((address_space(3))) void*)(vdst + off), 16, 0, 0);
+  }
+}
+
+// s_waitcnt vmcnt(0) through the builtin (not inline asm), so the compiler's
+// own wait tracking sees it.  gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// MFMA operands (Q, P) are rounded with the hardware converter
+// (v_cvt_pk_bf16_f32, round to nearest even).
 __device__ __forceinline__ bf16x8 to_bf16x8(const float* f) {
   bf16x8 r;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = __builtin_bit_cast(__bf16, (uint16_t)f32_to_bf16_bits(f[j]));
+  for (int j = 0; j < 8; ++j) r[j] = (__bf16)f[j];
   return r;
 }
 
-// partial row layout in the workspace: acc[D], m, l, 2 pad floats
-template <int D> constexpr int part_stride() { return D + 4; }
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void prefill_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
-    int Hq, int Hkv, int C, int start, int R, int m_tiles, int S, float sl2e) {
+    float* __restrict__ part_ml, int Hq, int Hkv, int C, int start, int R, int m_tiles, int S,
+    float sl2e) {
   using Cfg = PrefillCfg<D, BF16>;
   constexpr int E = Cfg::E;
   constexpr int NDB = Cfg::NDB;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint4* k_lds = reinterpret_cast<uint4*>(smem);
-  uint4* v_lds = reinterpret_cast<uint4*>(smem + Cfg::TILE_BYTES);
+  constexpr int STAGES = Cfg::STAGES;
+  // Two distinct LDS objects (one per stage): the compiler can then tell that
+  // the asynchronous copy into one stage does not alias reads of the other,
+  // and issues no wait for it before the compute.
+  __shared__ __attribute__((aligned(16))) unsigned char stage0[2 * Cfg::TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char stage1[STAGES == 2 ? 2 * Cfg::TILE_BYTES : 16];
 
   // ---- block -> (m-tile, split), XCD-aware: blocks x, x+8, x+16, ... land on
   // one XCD; give them the same key range so its L2 serves all of them.
@@ -85,7 +117,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int M_total = R * G;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
   const int lr = lane & 15, lg = lane >> 4;
 
   const int m_base = mt * kMTile;
@@ -154,20 +187,29 @@ __global__ __launch_bounds__(256) void prefill_kernel(
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_cache) + slab * (BF16 ? 2 : 4);
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v_cache) + slab * (BF16 ? 2 : 4);
 
-  for (int kt = kt0; kt < kt1; ++kt) {
-    // ---- stage the K and V tiles (both contiguous in the cache)
-    const uint4* ksrc = reinterpret_cast<const uint4*>(kbase + (size_t)kt * Cfg::TILE_BYTES);
-    const uint4* vsrc = reinterpret_cast<const uint4*>(vbase + (size_t)kt * Cfg::TILE_BYTES);
-    const bool last = (kt + 1) * kNTile > kend;
-    __syncthreads();  // previous tile fully consumed
-#pragma unroll 4
-    for (int i = tid; i < Cfg::KVEC; i += 256) k_lds[i] = ksrc[i];
-#pragma unroll 4
-    for (int i = tid; i < Cfg::VVEC; i += 256) {
-      uint4 v = vsrc[i];
-      if (last) {
-        // vector i of the tile: group i / D holds E positions
-        const int gi = i / D;
+  if (kt0 < kt1)
+    stage_tiles<Cfg::TILE_BYTES>(kbase + (size_t)kt0 * Cfg::TILE_BYTES,
+                                 vbase + (size_t)kt0 * Cfg::TILE_BYTES, stage0,
+                                 stage0 + Cfg::TILE_BYTES, w, lane);
+
+  // One key tile; ST is the stage holding it (compile-time, so every LDS access
+  // names its own object).
+  auto tile = [&](auto stc, int kt) {
+    constexpr int ST = decltype(stc)::value;
+    unsigned char* cur = ST == 0 ? stage0 : stage1;
+    unsigned char* nxt = ST == 0 ? stage1 : stage0;
+    wait_vmem();
+    __syncthreads();  // tile kt is in LDS; every wave is done with the other stage
+    if (STAGES == 2 && kt + 1 < kt1)
+      stage_tiles<Cfg::TILE_BYTES>(kbase + (size_t)(kt + 1) * Cfg::TILE_BYTES,
+                                   vbase + (size_t)(kt + 1) * Cfg::TILE_BYTES, nxt,
+                                   nxt + Cfg::TILE_BYTES, w, lane);
+    const uint4* k_lds = reinterpret_cast<const uint4*>(cur);
+    uint4* v_lds = reinterpret_cast<uint4*>(cur + Cfg::TILE_BYTES);
+    if ((kt + 1) * kNTile > kend) {
+      // positions at or beyond start + R may hold anything: zero their values
+      for (int i = tid; i < Cfg::VVEC; i += 256) {
+        const int gi = i / D;  // vector i of the tile: group gi holds E positions
         uint32_t keep[4];
         if constexpr (BF16) {
           const int blk = kt * 2 + (gi >> 2), sg = gi & 3;
@@ -179,11 +221,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 #pragma unroll
           for (int e = 0; e < 4; ++e) keep[e] = (kt * kNTile + gi * 4 + e) < kend ? ~0u : 0u;
         }
-        v.x &= keep[0]; v.y &= keep[1]; v.z &= keep[2]; v.w &= keep[3];
+        if ((keep[0] & keep[1] & keep[2] & keep[3]) != ~0u) {
+          uint4 v = v_lds[i];
+          v.x &= keep[0]; v.y &= keep[1]; v.z &= keep[2]; v.w &= keep[3];
+          v_lds[i] = v;
+        }
       }
-      v_lds[i] = v;
+      __syncthreads();
     }
-    __syncthreads();
 
     // ---- S^T = K . Q^T for 4 key blocks x 2 column blocks
     v4f sacc[4][2];
@@ -222,7 +267,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(
 
     // ---- causal mask (only tiles that cross some row's limit), online softmax
     const bool diag = kt * kNTile + kNTile - 1 > start + row_lo;
-    float alpha[2];
+    float tile_max[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int lim = start + row_col[mb];
@@ -243,9 +288,33 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         }
       mx = fmaxf(mx, xor_shfl(mx, 16));
       mx = fmaxf(mx, xor_shfl(mx, 32));
-      const float m_new = fmaxf(m_run[mb], mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      alpha[mb] = fast_exp2(m_run[mb] - m_use);
+      tile_max[mb] = mx;
+    }
+    // Lazy rescale: the reference max of a column moves only when the tile
+    // max exceeds it by more than kRescaleSlack (log2 units), so weights stay
+    // below 2^kRescaleSlack and the accumulator pass below runs only in the
+    // rare tiles where some column of the wave needs it.  acc and l always
+    // share one reference, so the result is the same softmax.
+    bool need = false;
+    float alpha[2] = {1.f, 1.f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (tile_max[mb] > m_run[mb] + kRescaleSlack) {
+        alpha[mb] = fast_exp2(m_run[mb] - tile_max[mb]);   // 0 when m_run is -inf
+        m_run[mb] = tile_max[mb];
+        l_run[mb] *= alpha[mb];
+        need = true;
+      }
+    }
+    if (__any(need)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc_o[db][mb] *= alpha[mb];
+    }
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const float m_use = m_run[mb] == -INFINITY ? 0.f : m_run[mb];
       float ls = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
@@ -255,13 +324,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(
           sacc[kb][mb][i] = pv;
           ls += pv;
         }
-      l_run[mb] = l_run[mb] * alpha[mb] + ls;
-      m_run[mb] = m_new;
+      l_run[mb] += ls;
     }
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) acc_o[db][mb] *= alpha[mb];
 
     // ---- O^T += V^T . P^T
     if constexpr (BF16) {
@@ -303,6 +367,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(
               acc_o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], sacc[kb][mb][t], acc_o[db][mb], 0, 0, 0);
         }
     }
+    if (STAGES == 1 && kt + 1 < kt1) {
+      __syncthreads();  // every wave is done with the only stage
+      stage_tiles<Cfg::TILE_BYTES>(kbase + (size_t)(kt + 1) * Cfg::TILE_BYTES,
+                                   vbase + (size_t)(kt + 1) * Cfg::TILE_BYTES, cur,
+                                   cur + Cfg::TILE_BYTES, w, lane);
+    }
+  };
+  for (int kt = kt0; kt < kt1; kt += 2) {
+    tile(std::integral_constant<int, 0>(), kt);
+    if (kt + 1 < kt1) tile(std::integral_constant<int, STAGES == 2 ? 1 : 0>(), kt + 1);
   }
 
   // ---- epilogue: lane holds O^T[16 db + 4 lg + i][column]
@@ -323,63 +397,81 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         *reinterpret_cast<float4*>(op + 16 * db + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
       }
     } else {
-      const size_t slot = ((((size_t)b * Hkv + g) * m_tiles + mt) * S + split) * kMTile +
-                          (m_col[mb] - m_base);
-      float* pp = part + slot * part_stride<D>();
+      // acc [tile][S][128 columns][D]; (m, l) [tile][128 columns][S][2]
+      const size_t tile_id = ((size_t)b * Hkv + g) * m_tiles + mt;
+      const int col = m_col[mb] - m_base;
+      float* pp = part + ((tile_id * S + split) * kMTile + col) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const v4f o = acc_o[db][mb];
         *reinterpret_cast<float4*>(pp + 16 * db + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
       }
       if (lg == 0) {
-        pp[D] = m_run[mb];
-        pp[D + 1] = lt;
+        float* ml = part_ml + ((tile_id * kMTile + col) * S + split) * 2;
+        ml[0] = m_run[mb];
+        ml[1] = lt;
       }
     }
   }
 }
 
-// Combines the S split partials of every column of one M-tile, in split order.
+// Combines the S split partials of 16 columns of one M-tile.  Thread (c, v)
+// owns column c and the float4 dims 4 v + 64 j; splits are summed in order.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(
-    const float* __restrict__ part, float* __restrict__ out, int Hq, int Hkv, int R,
-    int m_tiles, int S) {
-  __shared__ float wgt[kMTile * kMaxSplits];
-  __shared__ float inv_l[kMTile];
-  const int mt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const float* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
+    int Hq, int Hkv, int R, int m_tiles, int S) {
+  __shared__ float wgt[16][kMaxSplits];
+  __shared__ float inv_l[16];
+  const int mt = blockIdx.x >> 3, cg = blockIdx.x & 7;
+  const int g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int M_total = R * G;
   const int tid = threadIdx.x;
-  constexpr int PS = part_stride<D>();
-  const float* pb = part + (((size_t)b * Hkv + g) * m_tiles + mt) * (size_t)S * kMTile * PS;
-  for (int c = tid; c < kMTile; c += 256) {
+  const size_t tile_id = ((size_t)b * Hkv + g) * m_tiles + mt;
+  if (tid < 16) {
+    const float* ml = part_ml + (tile_id * kMTile + cg * 16 + tid) * S * 2;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, pb[((size_t)s * kMTile + c) * PS + D]);
+    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
     float L = 0.f;
     for (int s = 0; s < S; ++s) {
-      const float* e = pb + ((size_t)s * kMTile + c) * PS;
-      const float f = e[D] == -INFINITY ? 0.f : fast_exp2(e[D] - M);
-      wgt[c * kMaxSplits + s] = f;
-      L += f * e[D + 1];
+      const float f = ml[2 * s] == -INFINITY ? 0.f : fast_exp2(ml[2 * s] - M);
+      wgt[tid][s] = f;
+      L += f * ml[2 * s + 1];
     }
-    inv_l[c] = 1.f / L;
+    inv_l[tid] = 1.f / L;
   }
   __syncthreads();
-  constexpr int NV = D / 4;
-  for (int i = tid; i < kMTile * NV; i += 256) {
-    const int c = i / NV, dv = i % NV;
-    const int m = mt * kMTile + c;
-    if (m >= M_total) continue;
+  const int c = tid >> 4, v = tid & 15;
+  const int col = cg * 16 + c;
+  const int m = mt * kMTile + col;
+  if (m >= M_total) return;
+  const int row = m / G, hh = m % G;
+  float* op = out + (((size_t)b * R + row) * Hq + g * G + hh) * D;
+  const float* pc = part + (tile_id * S * kMTile + col) * D;
+  const size_t PS = (size_t)kMTile * D;  // stride between splits
+  const float il = inv_l[c];
+#pragma unroll
+  for (int j = 0; j < D / 64; ++j) {
+    const int d = 4 * v + 64 * j;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < S; ++s) {
-      const float f = wgt[c * kMaxSplits + s];
-      const float4 v = *reinterpret_cast<const float4*>(pb + ((size_t)s * kMTile + c) * PS + 4 * dv);
-      a.x += f * v.x; a.y += f * v.y; a.z += f * v.z; a.w += f * v.w;
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+      float4 t[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t[k] = *reinterpret_cast<const float4*>(pc + (s + k) * PS + d);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float f = wgt[c][s + k];
+        a.x += f * t[k].x; a.y += f * t[k].y; a.z += f * t[k].z; a.w += f * t[k].w;
+      }
     }
-    const float il = inv_l[c];
-    const int row = m / G, hh = m % G;
-    float* op = out + (((size_t)b * R + row) * Hq + g * G + hh) * D;
-    *reinterpret_cast<float4*>(op + 4 * dv) = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
+    for (; s < S; ++s) {
+      const float f = wgt[c][s];
+      const float4 t = *reinterpret_cast<const float4*>(pc + s * PS + d);
+      a.x += f * t.x; a.y += f * t.y; a.z += f * t.z; a.w += f * t.w;
+    }
+    *reinterpret_cast<float4*>(op + d) = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
   }
 }
 
@@ -399,21 +491,19 @@ hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const 
                     const void* vc, float* out, int start, int R, float scale, void* ws,
                     hipStream_t st) {
   using Cfg = PrefillCfg<D, BF16>;
-  const size_t lds = 2 * Cfg::TILE_BYTES;
   auto kern = prefill_kernel<D, BF16>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
-  if (e != hipSuccess) return e;
   dim3 grid(p.m_tiles * p.splits, s.num_kv_heads, s.batch);
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, q, kc, vc, out,
-                     reinterpret_cast<float*>(ws), s.num_q_heads, s.num_kv_heads, s.capacity,
-                     start, R, p.m_tiles, p.splits, scale * kLog2e);
-  e = hipGetLastError();
+  float* part = reinterpret_cast<float*>(ws);
+  float* part_ml = part + (size_t)s.batch * s.num_kv_heads * p.m_tiles * p.splits * kMTile * D;
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, kc, vc, out, part, part_ml,
+                     s.num_q_heads, s.num_kv_heads, s.capacity, start, R, p.m_tiles, p.splits,
+                     scale * kLog2e);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.splits > 1) {
-    hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3(p.m_tiles, s.num_kv_heads, s.batch),
-                       dim3(256), 0, st, reinterpret_cast<const float*>(ws), out,
-                       s.num_q_heads, s.num_kv_heads, R, p.m_tiles, p.splits);
+    hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3(p.m_tiles * 8, s.num_kv_heads, s.batch),
+                       dim3(256), 0, st, part, part_ml, out, s.num_q_heads, s.num_kv_heads, R,
+                       p.m_tiles, p.splits);
     e = hipGetLastError();
   }
   return e;
@@ -430,7 +520,7 @@ PrefillPlan plan_prefill(const Shape& s, int start, int R) {
   p.splits = choose_splits(s, p.m_tiles, nkt);
   p.workspace_bytes = p.splits == 1 ? 0
       : (size_t)s.batch * s.num_kv_heads * p.m_tiles * p.splits * kMTile *
-            (size_t)(s.head_dim + 4) * sizeof(float);
+            (size_t)(s.head_dim + 2) * sizeof(float);
   return p;
 }
 
@@ -443,7 +533,7 @@ size_t prefill_workspace_bound(const Shape& s, int max_rows) {
     const int S = choose_splits(s, mt, 1 << 30);
     if (S == 1) continue;
     const size_t bytes = (size_t)s.batch * s.num_kv_heads * mt * S * kMTile *
-                         (size_t)(s.head_dim + 4) * sizeof(float);
+                         (size_t)(s.head_dim + 2) * sizeof(float);
     if (bytes > best) best = bytes;
   }
   return best;
