@@ -52,9 +52,10 @@
  *   V, f32:           (((b*Hkv + g)*(C/4) + j/4)*D + d)*4 + j%4
  *                     i.e. [B][Hkv][C/4][D][4]: per 4 positions, all dims.
  *   V, bf16:          ((((b*Hkv + g)*(C/32) + j/32)*4 + s)*D + d)*8 + t
- *                     with r = j%32, s = (r%16)/4, t = r%4 + 4*(r/16)
+ *                     with r = j%32, s = 2*(r/16) + (r%8)/4, t = r%4 + 4*((r%16)/8)
  *                     i.e. [B][Hkv][C/32][4][D][8]: each 32-position block in
- *                     four groups of 8 positions {4s..4s+3, 16+4s..16+4s+3}.
+ *                     four groups of 8 positions {16u+4h..16u+4h+3,
+ *                     16u+8+4h..16u+8+4h+3}, group s = 2u + h.
  *
  *   Cache contents beyond the rows appended so far are never read into a
  *   result (they may hold anything, NaN included).

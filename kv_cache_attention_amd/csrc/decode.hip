@@ -47,25 +47,12 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// position of lane-slot kk of unit u
-template <bool BF16>
-__device__ __forceinline__ int unit_pos(int u, int kk) {
-  if constexpr (BF16) return ((u >> 1) << 5) + ((u & 1) << 3) + (kk & 7) + ((kk >> 3) << 4);
-  else return u * kUnit + kk;
-}
-
-// last position of unit u (bf16 units interleave within 32-position blocks)
-template <bool BF16>
-__device__ __forceinline__ int unit_last_pos(int u) {
-  if constexpr (BF16) return ((u >> 1) << 5) + ((u & 1) << 3) + 23;
-  else return u * kUnit + kUnit - 1;
-}
-
-// Units covering positions 0 .. ctx-1: bf16 units come in pairs per
-// 32-position block.
-__host__ __device__ __forceinline__ int units_for(int ctx, bool bf16) {
-  return bf16 ? 2 * ((ctx + 31) / 32) : (ctx + kUnit - 1) / kUnit;
-}
+// Position of lane-slot kk of unit u: units are 16 consecutive positions.
+// With bf16 storage unit u is half s = u % 2 of 32-block u / 2, i.e. V groups
+// 2 s and 2 s + 1 of that block.
+__device__ __forceinline__ int unit_pos(int u, int kk) { return u * kUnit + kk; }
+__device__ __forceinline__ int unit_last_pos(int u) { return u * kUnit + kUnit - 1; }
+__host__ __device__ __forceinline__ int units_for(int ctx) { return (ctx + kUnit - 1) / kUnit; }
 
 template <int D, int HPW, bool BF16>
 struct alignas(16) DecodeSmem {
@@ -96,7 +83,7 @@ __device__ __forceinline__ void load_unit_k(UnitRegs<D, BF16>& r, int u, int lan
   using R = UnitRegs<D, BF16>;
   constexpr int E = R::E;
   const int kk = lane & 15, qd = lane >> 4;
-  const int pos = unit_pos<BF16>(u, kk);
+  const int pos = unit_pos(u, kk);
 #pragma unroll
   for (int i = 0; i < R::NCH; ++i)
     r.k[i] = *reinterpret_cast<const uint4*>(kc + k_vec_index(pos, qd * R::NCH + i, D, E) * E);
@@ -128,7 +115,7 @@ __device__ __forceinline__ void process_unit(UnitRegs<D, BF16>& r, int u, int la
   using R = UnitRegs<D, BF16>;
   constexpr int NCH = R::NCH, ND = R::ND, NG = R::NG;
   const int kk = lane & 15, qd = lane >> 4;
-  const int pos = unit_pos<BF16>(u, kk);
+  const int pos = unit_pos(u, kk);
   // ---- scores: partial dot over this lane's quarter of D, then 2 xor steps.
   // q is read from LDS per 16-byte chunk; the fence after each chunk keeps the
   // compiler from hoisting every chunk's q into registers at once.
@@ -183,7 +170,7 @@ __device__ __forceinline__ void process_unit(UnitRegs<D, BF16>& r, int u, int la
   // ---- weights -> LDS in V slot order (lanes 0..15 hold one copy)
   if (qd == 0) {
     int slot;
-    if constexpr (BF16) slot = ((kk & 7) >> 2) * 8 + (kk & 3) + 4 * (kk >> 3);
+    if constexpr (BF16) slot = ((kk >> 2) & 1) * 8 + (kk & 3) + 4 * ((kk >> 3) & 1);
     else slot = kk;
 #pragma unroll
     for (int h = 0; h < HPW; ++h) {
@@ -193,7 +180,7 @@ __device__ __forceinline__ void process_unit(UnitRegs<D, BF16>& r, int u, int la
   }
   wave_lds_sync();
   // ---- positions at or beyond ctx may hold anything: zero their values
-  if (unit_last_pos<BF16>(u) >= ctx) {
+  if (unit_last_pos(u) >= ctx) {
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       uint32_t keep[4];
@@ -274,7 +261,7 @@ void decode_split_kernel(
   const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;
   const T* kc = reinterpret_cast<const T*>(k_cache) + slab;
   const T* vc = reinterpret_cast<const T*>(v_cache) + slab;
-  const int n_units = units_for(ctx, BF16);
+  const int n_units = units_for(ctx);
   const int u0 = (int)((long long)split * n_units / S);
   const int u1 = (int)((long long)(split + 1) * n_units / S);
 
@@ -481,7 +468,7 @@ DecodePlan plan_decode(const Shape& s, int max_ctx) {
   const int G = s.num_q_heads / s.num_kv_heads;
   p.heads_per_wg = heads_per_wg(G);
   p.head_groups = G / p.heads_per_wg;
-  const int units = units_for(max_ctx, s.kv_dtype == 1);
+  const int units = units_for(max_ctx);
   const long long slabs = (long long)s.batch * s.num_kv_heads * p.head_groups;
   long long S = (kTargetWgs + slabs - 1) / slabs;
   const long long by_units = units / kWaves;  // at least one unit per wave

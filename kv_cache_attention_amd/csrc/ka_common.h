@@ -44,14 +44,19 @@ __device__ __forceinline__ size_t k_vec_index(int j, int c, int D, int E) {
 __device__ __forceinline__ size_t vf32_vec_index(int j, int d, int D) {
   return (size_t)(j >> 2) * D + d;
 }
-// V, bf16: [B][Hkv][C/32][4][D][8].  Position j sits in group s of its
-// 32-position block at slot t, with r = j % 32, s = (r % 16) / 4,
-// t = r % 4 + 4 * (r / 16).
-__device__ __forceinline__ int vbf16_group(int j) { return ((j >> 5) << 2) + ((j & 15) >> 2); }
-__device__ __forceinline__ int vbf16_slot(int j) { return (j & 3) + ((j & 16) >> 2); }
-// inverse: position of slot t in group s of 32-block blk
-__device__ __forceinline__ int vbf16_pos(int blk, int s, int t) {
-  return (blk << 5) + (s << 2) + (t & 3) + ((t & 4) << 2);
+// V, bf16: [B][Hkv][C/32][4][D][8].  In each 32-position block, group
+// g = 2 s + h holds positions {16 s + 4 h + 0..3, 16 s + 8 + 4 h + 0..3}
+// (slots 0..3 and 4..7) -- the positions one lane half holds in the
+// accumulator of a 32x32 MFMA, so exponentiated scores feed the value
+// product directly.  For r = j % 32: g = 2 (r / 16) + (r % 8) / 4,
+// t = r % 4 + 4 ((r % 16) / 8).
+__device__ __forceinline__ int vbf16_group(int j) {
+  return ((j >> 5) << 2) + (((j >> 4) & 1) << 1) + ((j >> 2) & 1);
+}
+__device__ __forceinline__ int vbf16_slot(int j) { return (j & 3) + (((j >> 3) & 1) << 2); }
+// inverse: position of slot t in group g of 32-block blk
+__device__ __forceinline__ int vbf16_pos(int blk, int g, int t) {
+  return (blk << 5) + ((g >> 1) << 4) + ((g & 1) << 2) + (t & 3) + ((t >> 2) << 3);
 }
 
 // ------------------------------------------------------- wave reductions

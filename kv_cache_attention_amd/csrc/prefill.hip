@@ -47,28 +47,26 @@ struct PrefillCfg {
   static constexpr int VVEC = kNTile / E * D;            // 16-byte vectors per V tile
   static constexpr int TILE_BYTES = KVEC * 16;           // same for V
   static constexpr int NDB = D / 16;                     // 16-dim output blocks
-  // double-buffered K+V tiles when two stages fit in the 160 KiB of LDS
-  static constexpr int STAGES = 4 * TILE_BYTES <= 160 * 1024 ? 2 : 1;
-  static constexpr int LDS_BYTES = STAGES * 2 * TILE_BYTES;
+  static constexpr int NQ = BF16 ? D / 32 : D / 16;      // Q^T operand registers per column block
+  // Pipelined form: K and V tiles double-buffered separately (4 tiles) when
+  // that fits the 160 KiB of LDS; otherwise one K+V stage.
+  static constexpr bool PIPE = 4 * TILE_BYTES <= 160 * 1024;
+  using QReg = typename std::conditional<BF16, bf16x8, v4f>::type;
 };
 
-// Asynchronous copy of one K tile and one V tile (each TILE_BYTES contiguous
-// bytes in the cache) into LDS with global_load_lds: every wave instruction
-// moves 1 KiB, lane l's 16 bytes landing at the wave's LDS base + 16 l.
+// Asynchronous copy of one tile (TILE_BYTES contiguous bytes of the cache)
+// into LDS with global_load_lds: every wave instruction moves 1 KiB, lane l's
+// 16 bytes landing at the wave's LDS base + 16 l.
 template <int TILE_BYTES>
-__device__ __forceinline__ void stage_tiles(const unsigned char* ksrc, const unsigned char* vsrc,
-                                            unsigned char* kdst, unsigned char* vdst, int w,
-                                            int lane) {
+__device__ __forceinline__ void load_tile(const unsigned char* src, unsigned char* dst, int w,
+                                          int lane) {
   constexpr int PER_THREAD = TILE_BYTES / (256 * 16);
 #pragma unroll
   for (int i = 0; i < PER_THREAD; ++i) {
     const int off = (i * 256 + w * 64) * 16;
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(ksrc + off + lane * 16),
-        (__attribute__((address_space(3))) void*)(kdst + off), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(
-        (const void*)(vsrc + off + lane * 16),
-        (__attribute__((address_space(3))) void*)(vdst + off), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void*)(src + off + lane * 16),
+                                     (__attribute__((address_space(3))) void*)(dst + off), 16, 0,
+                                     0);
   }
 }
 
@@ -86,77 +84,68 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* f) {
 }
 
 
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void prefill_kernel(
-    const float* __restrict__ q, const void* __restrict__ k_cache,
-    const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
-    float* __restrict__ part_ml, int Hq, int Hkv, int C, int start, int R, int m_tiles, int S,
-    float sl2e) {
-  using Cfg = PrefillCfg<D, BF16>;
-  constexpr int E = Cfg::E;
-  constexpr int NDB = Cfg::NDB;
-  constexpr int STAGES = Cfg::STAGES;
-  // Two distinct LDS objects (one per stage): the compiler can then tell that
-  // the asynchronous copy into one stage does not alias reads of the other,
-  // and issues no wait for it before the compute.
-  __shared__ __attribute__((aligned(16))) unsigned char stage0[2 * Cfg::TILE_BYTES];
-  __shared__ __attribute__((aligned(16))) unsigned char stage1[STAGES == 2 ? 2 * Cfg::TILE_BYTES : 16];
-
-  // ---- block -> (m-tile, split), XCD-aware: blocks x, x+8, x+16, ... land on
-  // one XCD; give them the same key range so its L2 serves all of them.
-  const int x = blockIdx.x;
-  int mt, split;
-  if (S >= 8 && S % 8 == 0) {
-    const int spx = S / 8, xcd = x & 7, j = x >> 3;
-    split = xcd * spx + j % spx;
-    mt = j / spx;
-  } else {
-    mt = x / S;
-    split = x % S;
-  }
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int G = Hq / Hkv;
-  const int M_total = R * G;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept in an SGPR
-  const int lr = lane & 15, lg = lane >> 4;
-
-  const int m_base = mt * kMTile;
-  const int row_lo = m_base / G;
-  const int row_hi = min(R - 1, (m_base + kMTile - 1) / G);
-  const int nkt = (start + row_hi) / kNTile + 1;
-  const int kt0 = (int)((long long)split * nkt / S);
-  const int kt1 = (int)((long long)(split + 1) * nkt / S);
-  const int kend = start + R;  // first position not appended by this chunk
-
-  // this lane's two M columns (mb = 0, 1)
+// Per-block constants of the tiling.
+struct Tiling {
+  int mt, split, g, b, G, M_total, lr, lg, w, lane, tid;
+  int m_base, row_lo, kt0, kt1, kend;
   int m_col[2], row_col[2];
   bool valid_col[2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    m_col[mb] = m_base + w * 32 + mb * 16 + lr;
-    valid_col[mb] = m_col[mb] < M_total;
-    row_col[mb] = valid_col[mb] ? m_col[mb] / G : 0;
-  }
-  auto q_row_ptr = [&](int mb) -> const float* {
-    const int m = m_col[mb];
-    const int row = m / G, hh = m % G;
-    return q + (((size_t)b * R + row) * Hq + g * G + hh) * D;
-  };
+};
 
-  // ---- stationary Q^T operand in registers
-  constexpr int NQ = BF16 ? D / 32 : D / 16;
-  typename std::conditional<BF16, bf16x8, v4f>::type qreg[2][NQ];
+__device__ __forceinline__ Tiling make_tiling(int Hq, int Hkv, int start, int R, int S) {
+  Tiling t;
+  // block -> (m-tile, split), XCD-aware: blocks x, x+8, x+16, ... land on one
+  // XCD; give them the same key range so its L2 serves all of them.
+  const int x = blockIdx.x;
+  if (S >= 8 && S % 8 == 0) {
+    const int spx = S / 8, xcd = x & 7, j = x >> 3;
+    t.split = xcd * spx + j % spx;
+    t.mt = j / spx;
+  } else {
+    t.mt = x / S;
+    t.split = x % S;
+  }
+  t.g = blockIdx.y;
+  t.b = blockIdx.z;
+  t.G = Hq / Hkv;
+  t.M_total = R * t.G;
+  t.tid = threadIdx.x;
+  t.lane = t.tid & 63;
+  t.w = __builtin_amdgcn_readfirstlane(t.tid >> 6);  // wave index, kept in an SGPR
+  t.lr = t.lane & 15;
+  t.lg = t.lane >> 4;
+  t.m_base = t.mt * kMTile;
+  t.row_lo = t.m_base / t.G;
+  const int row_hi = min(R - 1, (t.m_base + kMTile - 1) / t.G);
+  const int nkt = (start + row_hi) / kNTile + 1;
+  t.kt0 = (int)((long long)t.split * nkt / S);
+  t.kt1 = (int)((long long)(t.split + 1) * nkt / S);
+  t.kend = start + R;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    const float* qp = q_row_ptr(mb);
+    t.m_col[mb] = t.m_base + t.w * 32 + mb * 16 + t.lr;
+    t.valid_col[mb] = t.m_col[mb] < t.M_total;
+    t.row_col[mb] = t.valid_col[mb] ? t.m_col[mb] / t.G : 0;
+  }
+  return t;
+}
+
+// Stationary Q^T operand: this lane's slice of its two columns.
+template <int D, bool BF16>
+__device__ __forceinline__ void load_q(const Tiling& t, const float* __restrict__ q, int R, int Hq,
+                                       typename PrefillCfg<D, BF16>::QReg (&qreg)[2][PrefillCfg<D, BF16>::NQ]) {
+  constexpr int NQ = PrefillCfg<D, BF16>::NQ;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = t.m_col[mb];
+    const float* qp = q + (((size_t)t.b * R + m / t.G) * Hq + t.g * t.G + m % t.G) * D;
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks) {
       if constexpr (BF16) {
         float f[8];
-        if (valid_col[mb]) {
-          const float4 a = *reinterpret_cast<const float4*>(qp + 32 * ks + 8 * lg);
-          const float4 c = *reinterpret_cast<const float4*>(qp + 32 * ks + 8 * lg + 4);
+        if (t.valid_col[mb]) {
+          const float4 a = *reinterpret_cast<const float4*>(qp + 32 * ks + 8 * t.lg);
+          const float4 c = *reinterpret_cast<const float4*>(qp + 32 * ks + 8 * t.lg + 4);
           f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
           f[4] = c.x; f[5] = c.y; f[6] = c.z; f[7] = c.w;
         } else {
@@ -166,15 +155,377 @@ __global__ __launch_bounds__(256) void prefill_kernel(
         qreg[mb][ks] = to_bf16x8(f);
       } else {
         v4f a = {0.f, 0.f, 0.f, 0.f};
-        if (valid_col[mb]) {
-          const float4 t = *reinterpret_cast<const float4*>(qp + 16 * ks + 4 * lg);
-          a[0] = t.x; a[1] = t.y; a[2] = t.z; a[3] = t.w;
+        if (t.valid_col[mb]) {
+          const float4 v = *reinterpret_cast<const float4*>(qp + 16 * ks + 4 * t.lg);
+          a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
         }
         qreg[mb][ks] = a;
       }
     }
   }
+}
 
+// S^T = K . Q^T for one 64-position tile: 4 key blocks x 2 column blocks.
+template <int D, bool BF16>
+__device__ __forceinline__ void qk_tile(const uint4* __restrict__ k_lds,
+                                        const typename PrefillCfg<D, BF16>::QReg (&qreg)[2][PrefillCfg<D, BF16>::NQ],
+                                        v4f (&sacc)[4][2], int lr, int lg) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) sacc[kb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  if constexpr (BF16) {
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, k_lds[(4 * ks + lg) * 64 + 16 * kb + lr]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[mb][ks], sacc[kb][mb], 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c4 = 0; c4 < D / 16; ++c4) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint4 a = k_lds[(4 * c4 + lg) * 64 + 16 * kb + lr];
+        const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                             __uint_as_float(a.w)};
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qreg[mb][c4][u], sacc[kb][mb], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Causal mask (only on tiles that cross a row's limit) and online softmax of
+// one tile: turns the scores into weights in place, updates m and l, and
+// returns the accumulator rescale factors (1 where the reference max stayed).
+__device__ __forceinline__ void softmax_tile(const Tiling& t, int kt, int start, float sl2e,
+                                             v4f (&sacc)[4][2], float (&m_run)[2],
+                                             float (&l_run)[2], float (&alpha)[2]) {
+  const bool diag = kt * kNTile + kNTile - 1 > start + t.row_lo;
+  float tile_max[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int lim = start + t.row_col[mb];
+    // scores to the log2 domain first, so a column's largest term is
+    // exactly exp2(0) = 1
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float sv = sacc[kb][mb][i] * sl2e;
+        if (diag) {
+          const int key = kt * kNTile + 16 * kb + 4 * t.lg + i;
+          if (key > lim || !t.valid_col[mb]) sv = -INFINITY;
+        }
+        sacc[kb][mb][i] = sv;
+        mx = fmaxf(mx, sv);
+      }
+    mx = fmaxf(mx, xor_shfl(mx, 16));
+    mx = fmaxf(mx, xor_shfl(mx, 32));
+    tile_max[mb] = mx;
+  }
+  // Lazy rescale: a column's reference max moves only when the tile max
+  // exceeds it by more than kRescaleSlack (log2 units), so weights stay below
+  // 2^kRescaleSlack and the accumulator pass (rescale_acc) runs only in the
+  // rare tiles where some column of the wave needs it.  acc and l always
+  // share one reference, so the result is the same softmax.
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    alpha[mb] = 1.f;
+    if (tile_max[mb] > m_run[mb] + kRescaleSlack) {
+      alpha[mb] = fast_exp2(m_run[mb] - tile_max[mb]);  // 0 when m_run is -inf
+      m_run[mb] = tile_max[mb];
+      l_run[mb] *= alpha[mb];
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const float m_use = m_run[mb] == -INFINITY ? 0.f : m_run[mb];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pv = fast_exp2(sacc[kb][mb][i] - m_use);
+        sacc[kb][mb][i] = pv;
+        ls += pv;
+      }
+    l_run[mb] += ls;
+  }
+}
+
+// Applies the rescale factors softmax_tile chose (a uniform branch: skipped
+// when no column of the wave moved its reference max).
+template <int NDB>
+__device__ __forceinline__ void rescale_acc(const float (&alpha)[2], v4f (&acc_o)[NDB][2]) {
+  if (__any(alpha[0] != 1.f || alpha[1] != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) acc_o[db][mb] *= alpha[mb];
+  }
+}
+
+// O^T += V^T . P^T for one tile (P = the weights left in sacc).
+template <int D, bool BF16>
+__device__ __forceinline__ void pv_tile(const uint4* __restrict__ v_lds, const v4f (&p)[4][2],
+                                        v4f (&acc_o)[D / 16][2], int lr, int lg) {
+  constexpr int NDB = D / 16;
+  if constexpr (BF16) {
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        float f[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[i] = p[2 * k2][mb][i];
+          f[4 + i] = p[2 * k2 + 1][mb][i];
+        }
+        pb[mb][k2] = to_bf16x8(f);
+      }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, v_lds[(k2 * 4 + lg) * D + 16 * db + lr]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          acc_o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[mb][k2], acc_o[db][mb], 0, 0, 0);
+      }
+  } else {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const uint4 a = v_lds[(4 * kb + lg) * D + 16 * db + lr];
+        const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                             __uint_as_float(a.w)};
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            acc_o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], p[kb][mb][u], acc_o[db][mb], 0, 0, 0);
+      }
+  }
+}
+
+// Positions at or beyond kend may hold anything: zero their values in the
+// staged V tile kt (every thread of the block takes part).
+template <int D, bool BF16>
+__device__ __forceinline__ void zero_v_beyond(uint4* v_lds, int kt, int kend, int tid) {
+  constexpr int VVEC = PrefillCfg<D, BF16>::VVEC;
+  for (int i = tid; i < VVEC; i += 256) {
+    const int gi = i / D;  // vector i of the tile: group gi holds E positions
+    uint32_t keep[4];
+    if constexpr (BF16) {
+      const int blk = kt * 2 + (gi >> 2), sg = gi & 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        keep[e] = (vbf16_pos(blk, sg, 2 * e) < kend ? 0x0000ffffu : 0u) |
+                  (vbf16_pos(blk, sg, 2 * e + 1) < kend ? 0xffff0000u : 0u);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) keep[e] = (kt * kNTile + gi * 4 + e) < kend ? ~0u : 0u;
+    }
+    if ((keep[0] & keep[1] & keep[2] & keep[3]) != ~0u) {
+      uint4 v = v_lds[i];
+      v.x &= keep[0]; v.y &= keep[1]; v.z &= keep[2]; v.w &= keep[3];
+      v_lds[i] = v;
+    }
+  }
+}
+
+// Epilogue: normalised output (one split) or the split's partial.
+template <int D>
+__device__ __forceinline__ void store_result(const Tiling& t, float* __restrict__ out,
+                                             float* __restrict__ part, float* __restrict__ part_ml,
+                                             const v4f (&acc_o)[D / 16][2], const float (&m_run)[2],
+                                             const float (&l_run)[2], int R, int Hq, int Hkv,
+                                             int m_tiles, int S) {
+  constexpr int NDB = D / 16;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    float lt = l_run[mb];
+    lt += xor_shfl(lt, 16);
+    lt += xor_shfl(lt, 32);
+    if (!t.valid_col[mb]) continue;
+    if (S == 1) {
+      const int m = t.m_col[mb];
+      float* op = out + (((size_t)t.b * R + m / t.G) * Hq + t.g * t.G + m % t.G) * D;
+      const float inv = 1.f / lt;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const v4f o = acc_o[db][mb] * inv;
+        *reinterpret_cast<float4*>(op + 16 * db + 4 * t.lg) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+    } else {
+      // acc [tile][S][128 columns][D]; (m, l) [tile][128 columns][S][2]
+      const size_t tile_id = ((size_t)t.b * Hkv + t.g) * m_tiles + t.mt;
+      const int col = t.m_col[mb] - t.m_base;
+      float* pp = part + ((tile_id * S + t.split) * kMTile + col) * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const v4f o = acc_o[db][mb];
+        *reinterpret_cast<float4*>(pp + 16 * db + 4 * t.lg) = make_float4(o[0], o[1], o[2], o[3]);
+      }
+      if (t.lg == 0) {
+        float* ml = part_ml + ((tile_id * kMTile + col) * S + t.split) * 2;
+        ml[0] = m_run[mb];
+        ml[1] = lt;
+      }
+    }
+  }
+}
+
+// Scores of the next tile fused with the softmax of the current one.  The
+// K-operand reads run one chunk ahead in registers; each chunk (one k-step of
+// the score product: 8 MFMAs with bf16) carries a slice of the softmax work,
+// and a scheduling fence closes it, so the VALU work of the softmax issues in
+// the cycles between MFMA issues instead of after all of them.
+//   softmax phases: 0, 1 scale + mask + local max of column block 0 / 1;
+//   2 cross-lane max; 3 reference-max update; 4..7 exponentials of key
+//   block 0..3.
+template <int D, bool BF16>
+__device__ __forceinline__ void qk_next_softmax_cur(
+    const Tiling& t, const uint4* __restrict__ k_lds,
+    const typename PrefillCfg<D, BF16>::QReg (&qreg)[2][PrefillCfg<D, BF16>::NQ],
+    v4f (&nxt)[4][2], v4f (&cur)[4][2], int kt, int start, float sl2e, float (&m_run)[2],
+    float (&l_run)[2], float (&alpha)[2]) {
+  constexpr int NKS = BF16 ? D / 32 : D / 16;  // k-steps of the score product
+  const int lr = t.lr, lg = t.lg;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) nxt[kb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  const bool diag = kt * kNTile + kNTile - 1 > start + t.row_lo;
+  float lmax[2] = {-INFINITY, -INFINITY};
+  float ls[2] = {0.f, 0.f};
+  float m_use[2];
+  uint4 kbuf[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) kbuf[0][kb] = k_lds[(4 * 0 + lg) * 64 + 16 * kb + lr];
+
+  auto phase = [&](int ph) {
+    if (ph == 0 || ph == 1) {
+      const int mb = ph;
+      const int lim = start + t.row_col[mb];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // scores to the log2 domain first, so a column's largest term is
+          // exactly exp2(0) = 1
+          float sv = cur[kb][mb][i] * sl2e;
+          if (diag) {
+            const int key = kt * kNTile + 16 * kb + 4 * lg + i;
+            if (key > lim || !t.valid_col[mb]) sv = -INFINITY;
+          }
+          cur[kb][mb][i] = sv;
+          lmax[mb] = fmaxf(lmax[mb], sv);
+        }
+    } else if (ph == 2) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        lmax[mb] = fmaxf(lmax[mb], xor_shfl(lmax[mb], 16));
+        lmax[mb] = fmaxf(lmax[mb], xor_shfl(lmax[mb], 32));
+      }
+    } else if (ph == 3) {
+      // Lazy rescale: a column's reference max moves only when the tile max
+      // exceeds it by more than kRescaleSlack (log2 units); weights stay
+      // below 2^kRescaleSlack.  acc and l share one reference throughout.
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        alpha[mb] = 1.f;
+        if (lmax[mb] > m_run[mb] + kRescaleSlack) {
+          alpha[mb] = fast_exp2(m_run[mb] - lmax[mb]);  // 0 when m_run is -inf
+          m_run[mb] = lmax[mb];
+          l_run[mb] *= alpha[mb];
+        }
+        m_use[mb] = m_run[mb] == -INFINITY ? 0.f : m_run[mb];
+      }
+    } else {
+      const int kb = ph - 4;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = fast_exp2(cur[kb][mb][i] - m_use[mb]);
+          cur[kb][mb][i] = pv;
+          ls[mb] += pv;
+        }
+    }
+  };
+
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (ks + 1 < NKS) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        kbuf[(ks + 1) & 1][kb] = k_lds[(4 * (ks + 1) + lg) * 64 + 16 * kb + lr];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      if constexpr (BF16) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, kbuf[ks & 1][kb]);
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+          nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[mb][ks], nxt[kb][mb], 0, 0, 0);
+      } else {
+        const uint4 a = kbuf[ks & 1][kb];
+        const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                             __uint_as_float(a.w)};
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qreg[mb][ks][u], nxt[kb][mb], 0, 0, 0);
+      }
+    }
+    // softmax phases assigned to this chunk (all 8 spread over NKS chunks)
+#pragma unroll
+    for (int ph = 0; ph < 8; ++ph)
+      if (ph * NKS / 8 == ks) phase(ph);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) l_run[mb] += ls[mb];
+}
+
+// Pipelined prefill.  K runs one tile ahead of V: while the weights of tile i
+// are formed (VALU), the score MFMAs of tile i+1 are already issued, and the
+// copies of K(i+2) and V(i+1) are in flight.  K and V each have two LDS
+// buffers; the loop is unrolled by two so every access names its buffer.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void prefill_pipe_kernel(
+    const float* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
+    float* __restrict__ part_ml, int Hq, int Hkv, int C, int start, int R, int m_tiles, int S,
+    float sl2e) {
+  using Cfg = PrefillCfg<D, BF16>;
+  constexpr int NDB = Cfg::NDB, TB = Cfg::TILE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char kb0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char kb1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char vb0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char vb1[TB];
+
+  const Tiling t = make_tiling(Hq, Hkv, start, R, S);
+  const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;  // elements
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_cache) + slab * (BF16 ? 2 : 4);
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v_cache) + slab * (BF16 ? 2 : 4);
+  const int n = t.kt1 - t.kt0;
+
+  typename Cfg::QReg qreg[2][Cfg::NQ];
   v4f acc_o[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -182,237 +533,374 @@ __global__ __launch_bounds__(256) void prefill_kernel(
     for (int mb = 0; mb < 2; ++mb) acc_o[db][mb] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
+  v4f sa[4][2], sb[4][2];
 
-  const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;  // elements
+  if (n > 0) {
+    load_tile<TB>(kbase + (size_t)t.kt0 * TB, kb0, t.w, t.lane);
+    load_q<D, BF16>(t, q, R, Hq, qreg);
+    wait_vmem();
+    __syncthreads();
+    load_tile<TB>(vbase + (size_t)t.kt0 * TB, vb0, t.w, t.lane);
+    if (n > 1) load_tile<TB>(kbase + (size_t)(t.kt0 + 1) * TB, kb1, t.w, t.lane);
+    qk_tile<D, BF16>(reinterpret_cast<const uint4*>(kb0), qreg, sa, t.lr, t.lg);
+  }
+
+  // step i: V(i) in vb[i&1], K(i+1) in kb[(i+1)&1], scores of tile i in cur
+  auto step = [&](auto par, int i, v4f (&cur)[4][2], v4f (&nxt)[4][2]) {
+    constexpr int P = decltype(par)::value;
+    unsigned char* k_next = P == 0 ? kb1 : kb0;   // holds K(i+1)
+    unsigned char* k_free = P == 0 ? kb0 : kb1;   // held K(i): free for K(i+2)
+    unsigned char* v_cur = P == 0 ? vb0 : vb1;    // holds V(i)
+    unsigned char* v_free = P == 0 ? vb1 : vb0;   // held V(i-1): free for V(i+1)
+    const int kt = t.kt0 + i;
+    wait_vmem();
+    __syncthreads();  // V(i), K(i+1) landed; every wave is done with step i-1
+    if (i + 2 < n) load_tile<TB>(kbase + (size_t)(kt + 2) * TB, k_free, t.w, t.lane);
+    if (i + 1 < n) load_tile<TB>(vbase + (size_t)(kt + 1) * TB, v_free, t.w, t.lane);
+    if ((kt + 1) * kNTile > t.kend) {
+      zero_v_beyond<D, BF16>(reinterpret_cast<uint4*>(v_cur), kt, t.kend, t.tid);
+      __syncthreads();
+    }
+    // The next tile's score MFMAs and this tile's softmax are independent
+    // and run interleaved (the last step computes one spare tile of scores
+    // from a stale buffer, which is never used).
+    float alpha[2];
+    qk_next_softmax_cur<D, BF16>(t, reinterpret_cast<const uint4*>(k_next), qreg, nxt, cur, kt,
+                                 start, sl2e, m_run, l_run, alpha);
+    rescale_acc<NDB>(alpha, acc_o);
+    pv_tile<D, BF16>(reinterpret_cast<const uint4*>(v_cur), cur, acc_o, t.lr, t.lg);
+  };
+  for (int i = 0; i < n; i += 2) {
+    step(std::integral_constant<int, 0>(), i, sa, sb);
+    if (i + 1 < n) step(std::integral_constant<int, 1>(), i + 1, sb, sa);
+  }
+  store_result<D>(t, out, part, part_ml, acc_o, m_run, l_run, R, Hq, Hkv, m_tiles, S);
+}
+
+// ============================================================================
+// bf16 caches: 32x32x16 MFMA (v_mfma_f32_32x32x16_bf16).  A wave owns 32
+// (row, head) columns, one per lane (lane l: column l % 32, half h = l / 32).
+//   S^T = K . Q^T per 32-key block: A = K[key][16 ks + 8 h + 0..7] (16 bytes
+//     of the K layout), B = Q^T (stationary, 8 dims of the lane's column);
+//     the lane then holds keys 8 a + 4 h + 0..3 (a = 0..3) of its column.
+//   O^T += V^T . P^T per 16-key step s: A = V[group 2 s + h][dim], B = the
+//     lane's own weights for keys {16 s + 4 h + 0..3, 16 s + 8 + 4 h + 0..3},
+//     which are accumulator registers 8 s .. 8 s + 7: no data movement.
+// ============================================================================
+typedef __attribute__((ext_vector_type(16))) float v16f;
+
+struct ColB {
+  int m, row;
+  bool valid;
+  int lc, lh;
+};
+
+__device__ __forceinline__ ColB col_b(const Tiling& t) {
+  ColB c;
+  c.lc = t.lane & 31;
+  c.lh = t.lane >> 5;
+  c.m = t.m_base + t.w * 32 + c.lc;
+  c.valid = c.m < t.M_total;
+  c.row = c.valid ? c.m / t.G : 0;
+  return c;
+}
+
+template <int D>
+__device__ __forceinline__ void load_q_b(const Tiling& t, const ColB& c, const float* __restrict__ q,
+                                         int R, int Hq, bf16x8 (&qreg)[D / 16]) {
+  const float* qp = q + (((size_t)t.b * R + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    float f[8];
+    if (c.valid) {
+      const float4 a = *reinterpret_cast<const float4*>(qp + 16 * ks + 8 * c.lh);
+      const float4 b = *reinterpret_cast<const float4*>(qp + 16 * ks + 8 * c.lh + 4);
+      f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+      f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = 0.f;
+    }
+    qreg[ks] = to_bf16x8(f);
+  }
+}
+
+// Scores of the next tile (2 key blocks x D/16 k-steps) fused with the
+// softmax of the current tile, chunk by chunk (see qk_next_softmax_cur).
+//   phases: 0, 1 scale + mask + local max of key block 0 / 1; 2 cross-half
+//   max; 3 reference-max update; 4..7 exponentials of registers 8 p .. 8 p + 7
+//   of key block p / 2 (p = phase - 4).
+template <int D>
+__device__ __forceinline__ void qk_next_softmax_cur_b(
+    const Tiling& t, const ColB& c, const uint4* __restrict__ k_lds, const bf16x8 (&qreg)[D / 16],
+    v16f (&nxt)[2], v16f (&cur)[2], int kt, int start, float sl2e, float& m_run, float& l_run,
+    float& alpha) {
+  constexpr int NKS = D / 16;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) nxt[kb][i] = 0.f;
+  const bool diag = kt * kNTile + kNTile - 1 > start + t.row_lo;
+  const int lim = start + c.row;
+  float lmax = -INFINITY, ls = 0.f, m_use = 0.f;
+  uint4 kbuf[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) kbuf[0][kb] = k_lds[(c.lh) * 64 + 32 * kb + c.lc];
+
+  auto phase = [&](int ph) {
+    if (ph < 2) {
+      const int kb = ph;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        // scores to the log2 domain first, so a column's largest term is
+        // exactly exp2(0) = 1
+        float sv = cur[kb][i] * sl2e;
+        if (diag) {
+          const int key = kt * kNTile + 32 * kb + 8 * (i >> 2) + 4 * c.lh + (i & 3);
+          if (key > lim || !c.valid) sv = -INFINITY;
+        }
+        cur[kb][i] = sv;
+        lmax = fmaxf(lmax, sv);
+      }
+    } else if (ph == 2) {
+      lmax = fmaxf(lmax, xor_shfl(lmax, 32));
+    } else if (ph == 3) {
+      // Lazy rescale: the reference max moves only when the tile max exceeds
+      // it by more than kRescaleSlack (log2 units), so weights stay below
+      // 2^kRescaleSlack.  acc and l share one reference throughout.
+      alpha = 1.f;
+      if (lmax > m_run + kRescaleSlack) {
+        alpha = fast_exp2(m_run - lmax);  // 0 when m_run is -inf
+        m_run = lmax;
+        l_run *= alpha;
+      }
+      m_use = m_run == -INFINITY ? 0.f : m_run;
+    } else {
+      const int kb = (ph - 4) >> 1, i0 = ((ph - 4) & 1) * 8;
+#pragma unroll
+      for (int i = i0; i < i0 + 8; ++i) {
+        const float pv = fast_exp2(cur[kb][i] - m_use);
+        cur[kb][i] = pv;
+        ls += pv;
+      }
+    }
+  };
+
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (ks + 1 < NKS) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kbuf[(ks + 1) & 1][kb] = k_lds[(2 * (ks + 1) + c.lh) * 64 + 32 * kb + c.lc];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+      nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kbuf[ks & 1][kb]),
+                                                         qreg[ks], nxt[kb], 0, 0, 0);
+#pragma unroll
+    for (int ph = 0; ph < 8; ++ph)
+      if (ph * NKS / 8 == ks) phase(ph);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  l_run += ls;
+}
+
+template <int D>
+__device__ __forceinline__ void rescale_acc_b(float alpha, v16f (&acc_o)[D / 32]) {
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) acc_o[db] *= alpha;
+  }
+}
+
+// O^T += V^T . P^T for one tile; the weights are the registers of p.
+template <int D>
+__device__ __forceinline__ void pv_tile_b(const uint4* __restrict__ v_lds, const v16f (&p)[2],
+                                          v16f (&acc_o)[D / 32], const ColB& c) {
+  bf16x8 pb[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pb[kb][s][j] = (__bf16)p[kb][8 * s + j];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const bf16x8 av =
+            __builtin_bit_cast(bf16x8, v_lds[(kb * 4 + 2 * s + c.lh) * D + 32 * db + c.lc]);
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][s], acc_o[db], 0, 0, 0);
+      }
+}
+
+template <int D>
+__device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c,
+                                               float* __restrict__ out, float* __restrict__ part,
+                                               float* __restrict__ part_ml,
+                                               const v16f (&acc_o)[D / 32], float m_run,
+                                               float l_run, int R, int Hq, int Hkv, int m_tiles,
+                                               int S) {
+  const float lt = l_run + xor_shfl(l_run, 32);
+  if (!c.valid) return;
+  // lane holds dims 32 db + 8 a + 4 h + 0..3
+  if (S == 1) {
+    float* op = out + (((size_t)t.b * R + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D;
+    const float inv = 1.f / lt;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<float4*>(op + 32 * db + 8 * a + 4 * c.lh) =
+            make_float4(acc_o[db][4 * a] * inv, acc_o[db][4 * a + 1] * inv,
+                        acc_o[db][4 * a + 2] * inv, acc_o[db][4 * a + 3] * inv);
+  } else {
+    // acc [tile][S][128 columns][D]; (m, l) [tile][128 columns][S][2]
+    const size_t tile_id = ((size_t)t.b * Hkv + t.g) * m_tiles + t.mt;
+    const int col = c.m - t.m_base;
+    float* pp = part + ((tile_id * S + t.split) * kMTile + col) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<float4*>(pp + 32 * db + 8 * a + 4 * c.lh) =
+            make_float4(acc_o[db][4 * a], acc_o[db][4 * a + 1], acc_o[db][4 * a + 2],
+                        acc_o[db][4 * a + 3]);
+    if (c.lh == 0) {
+      float* ml = part_ml + ((tile_id * kMTile + col) * S + t.split) * 2;
+      ml[0] = m_run;
+      ml[1] = lt;
+    }
+  }
+}
+
+// Pipelined bf16 prefill, same schedule as prefill_pipe_kernel.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_bf16_kernel(
+    const float* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
+    float* __restrict__ part_ml, int Hq, int Hkv, int C, int start, int R, int m_tiles, int S,
+    float sl2e) {
+  constexpr int TB = PrefillCfg<D, true>::TILE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char kb0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char kb1[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char vb0[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char vb1[TB];
+
+  const Tiling t = make_tiling(Hq, Hkv, start, R, S);
+  const ColB c = col_b(t);
+  const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;  // elements
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_cache) + slab * 2;
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v_cache) + slab * 2;
+  const int n = t.kt1 - t.kt0;
+
+  bf16x8 qreg[D / 16];
+  v16f acc_o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  v16f sa[2], sb[2];
+
+  if (n > 0) {
+    load_tile<TB>(kbase + (size_t)t.kt0 * TB, kb0, t.w, t.lane);
+    load_q_b<D>(t, c, q, R, Hq, qreg);
+    wait_vmem();
+    __syncthreads();
+    load_tile<TB>(vbase + (size_t)t.kt0 * TB, vb0, t.w, t.lane);
+    if (n > 1) load_tile<TB>(kbase + (size_t)(t.kt0 + 1) * TB, kb1, t.w, t.lane);
+    // scores of the first tile (no softmax to overlap with yet)
+    const uint4* k0 = reinterpret_cast<const uint4*>(kb0);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sa[kb][i] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, k0[(2 * ks + c.lh) * 64 + 32 * kb + c.lc]), qreg[ks], sa[kb],
+            0, 0, 0);
+  }
+
+  // step i: V(i) in vb[i&1], K(i+1) in kb[(i+1)&1], scores of tile i in cur
+  auto step = [&](auto par, int i, v16f (&cur)[2], v16f (&nxt)[2]) {
+    constexpr int P = decltype(par)::value;
+    unsigned char* k_next = P == 0 ? kb1 : kb0;   // holds K(i+1)
+    unsigned char* k_free = P == 0 ? kb0 : kb1;   // held K(i): free for K(i+2)
+    unsigned char* v_cur = P == 0 ? vb0 : vb1;    // holds V(i)
+    unsigned char* v_free = P == 0 ? vb1 : vb0;   // held V(i-1): free for V(i+1)
+    const int kt = t.kt0 + i;
+    wait_vmem();
+    __syncthreads();  // V(i), K(i+1) landed; every wave is done with step i-1
+    if (i + 2 < n) load_tile<TB>(kbase + (size_t)(kt + 2) * TB, k_free, t.w, t.lane);
+    if (i + 1 < n) load_tile<TB>(vbase + (size_t)(kt + 1) * TB, v_free, t.w, t.lane);
+    if ((kt + 1) * kNTile > t.kend) {
+      zero_v_beyond<D, true>(reinterpret_cast<uint4*>(v_cur), kt, t.kend, t.tid);
+      __syncthreads();
+    }
+    float alpha;
+    qk_next_softmax_cur_b<D>(t, c, reinterpret_cast<const uint4*>(k_next), qreg, nxt, cur, kt,
+                             start, sl2e, m_run, l_run, alpha);
+    rescale_acc_b<D>(alpha, acc_o);
+    pv_tile_b<D>(reinterpret_cast<const uint4*>(v_cur), cur, acc_o, c);
+  };
+  for (int i = 0; i < n; i += 2) {
+    step(std::integral_constant<int, 0>(), i, sa, sb);
+    if (i + 1 < n) step(std::integral_constant<int, 1>(), i + 1, sb, sa);
+  }
+  store_result_b<D>(t, c, out, part, part_ml, acc_o, m_run, l_run, R, Hq, Hkv, m_tiles, S);
+}
+
+// Sequential prefill (one K+V stage) for shapes whose four tiles do not fit
+// in LDS: copy tile i, then compute it, then copy tile i+1.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void prefill_seq_kernel(
+    const float* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
+    float* __restrict__ part_ml, int Hq, int Hkv, int C, int start, int R, int m_tiles, int S,
+    float sl2e) {
+  using Cfg = PrefillCfg<D, BF16>;
+  constexpr int NDB = Cfg::NDB, TB = Cfg::TILE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char kb[TB];
+  __shared__ __attribute__((aligned(16))) unsigned char vb[TB];
+
+  const Tiling t = make_tiling(Hq, Hkv, start, R, S);
+  const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_cache) + slab * (BF16 ? 2 : 4);
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v_cache) + slab * (BF16 ? 2 : 4);
 
-  if (kt0 < kt1)
-    stage_tiles<Cfg::TILE_BYTES>(kbase + (size_t)kt0 * Cfg::TILE_BYTES,
-                                 vbase + (size_t)kt0 * Cfg::TILE_BYTES, stage0,
-                                 stage0 + Cfg::TILE_BYTES, w, lane);
-
-  // One key tile; ST is the stage holding it (compile-time, so every LDS access
-  // names its own object).
-  auto tile = [&](auto stc, int kt) {
-    constexpr int ST = decltype(stc)::value;
-    unsigned char* cur = ST == 0 ? stage0 : stage1;
-    unsigned char* nxt = ST == 0 ? stage1 : stage0;
+  typename Cfg::QReg qreg[2][Cfg::NQ];
+  load_q<D, BF16>(t, q, R, Hq, qreg);
+  v4f acc_o[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc_o[db][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  v4f sacc[4][2];
+  for (int kt = t.kt0; kt < t.kt1; ++kt) {
+    __syncthreads();  // every wave is done with the previous tile
+    load_tile<TB>(kbase + (size_t)kt * TB, kb, t.w, t.lane);
+    load_tile<TB>(vbase + (size_t)kt * TB, vb, t.w, t.lane);
     wait_vmem();
-    __syncthreads();  // tile kt is in LDS; every wave is done with the other stage
-    if (STAGES == 2 && kt + 1 < kt1)
-      stage_tiles<Cfg::TILE_BYTES>(kbase + (size_t)(kt + 1) * Cfg::TILE_BYTES,
-                                   vbase + (size_t)(kt + 1) * Cfg::TILE_BYTES, nxt,
-                                   nxt + Cfg::TILE_BYTES, w, lane);
-    const uint4* k_lds = reinterpret_cast<const uint4*>(cur);
-    uint4* v_lds = reinterpret_cast<uint4*>(cur + Cfg::TILE_BYTES);
-    if ((kt + 1) * kNTile > kend) {
-      // positions at or beyond start + R may hold anything: zero their values
-      for (int i = tid; i < Cfg::VVEC; i += 256) {
-        const int gi = i / D;  // vector i of the tile: group gi holds E positions
-        uint32_t keep[4];
-        if constexpr (BF16) {
-          const int blk = kt * 2 + (gi >> 2), sg = gi & 3;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            keep[e] = (vbf16_pos(blk, sg, 2 * e) < kend ? 0x0000ffffu : 0u) |
-                      (vbf16_pos(blk, sg, 2 * e + 1) < kend ? 0xffff0000u : 0u);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) keep[e] = (kt * kNTile + gi * 4 + e) < kend ? ~0u : 0u;
-        }
-        if ((keep[0] & keep[1] & keep[2] & keep[3]) != ~0u) {
-          uint4 v = v_lds[i];
-          v.x &= keep[0]; v.y &= keep[1]; v.z &= keep[2]; v.w &= keep[3];
-          v_lds[i] = v;
-        }
-      }
+    __syncthreads();
+    if ((kt + 1) * kNTile > t.kend) {
+      zero_v_beyond<D, BF16>(reinterpret_cast<uint4*>(vb), kt, t.kend, t.tid);
       __syncthreads();
     }
-
-    // ---- S^T = K . Q^T for 4 key blocks x 2 column blocks
-    v4f sacc[4][2];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) sacc[kb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
-    if constexpr (BF16) {
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const uint4 a = k_lds[(4 * ks + lg) * 64 + 16 * kb + lr];
-          const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[mb][ks], sacc[kb][mb], 0, 0, 0);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int c4 = 0; c4 < D / 16; ++c4) {
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const uint4 a = k_lds[(4 * c4 + lg) * 64 + 16 * kb + lr];
-          const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
-                               __uint_as_float(a.w)};
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], qreg[mb][c4][t], sacc[kb][mb], 0, 0, 0);
-        }
-      }
-    }
-
-    // ---- causal mask (only tiles that cross some row's limit), online softmax
-    const bool diag = kt * kNTile + kNTile - 1 > start + row_lo;
-    float tile_max[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int lim = start + row_col[mb];
-      // scores to the log2 domain first, so the row's largest term is
-      // exactly exp2(0) = 1
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sv = sacc[kb][mb][i] * sl2e;
-          if (diag) {
-            const int key = kt * kNTile + 16 * kb + 4 * lg + i;
-            if (key > lim || !valid_col[mb]) sv = -INFINITY;
-          }
-          sacc[kb][mb][i] = sv;
-          mx = fmaxf(mx, sv);
-        }
-      mx = fmaxf(mx, xor_shfl(mx, 16));
-      mx = fmaxf(mx, xor_shfl(mx, 32));
-      tile_max[mb] = mx;
-    }
-    // Lazy rescale: the reference max of a column moves only when the tile
-    // max exceeds it by more than kRescaleSlack (log2 units), so weights stay
-    // below 2^kRescaleSlack and the accumulator pass below runs only in the
-    // rare tiles where some column of the wave needs it.  acc and l always
-    // share one reference, so the result is the same softmax.
-    bool need = false;
-    float alpha[2] = {1.f, 1.f};
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      if (tile_max[mb] > m_run[mb] + kRescaleSlack) {
-        alpha[mb] = fast_exp2(m_run[mb] - tile_max[mb]);   // 0 when m_run is -inf
-        m_run[mb] = tile_max[mb];
-        l_run[mb] *= alpha[mb];
-        need = true;
-      }
-    }
-    if (__any(need)) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) acc_o[db][mb] *= alpha[mb];
-    }
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const float m_use = m_run[mb] == -INFINITY ? 0.f : m_run[mb];
-      float ls = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(sacc[kb][mb][i] - m_use);
-          sacc[kb][mb][i] = pv;
-          ls += pv;
-        }
-      l_run[mb] += ls;
-    }
-
-    // ---- O^T += V^T . P^T
-    if constexpr (BF16) {
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          float f[8];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f[i] = sacc[2 * k2][mb][i];
-            f[4 + i] = sacc[2 * k2 + 1][mb][i];
-          }
-          pb[mb][k2] = to_bf16x8(f);
-        }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const uint4 a = v_lds[(k2 * 4 + lg) * D + 16 * db + lr];
-          const bf16x8 av = __builtin_bit_cast(bf16x8, a);
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            acc_o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[mb][k2], acc_o[db][mb], 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const uint4 a = v_lds[(4 * kb + lg) * D + 16 * db + lr];
-          const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
-                               __uint_as_float(a.w)};
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-              acc_o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], sacc[kb][mb][t], acc_o[db][mb], 0, 0, 0);
-        }
-    }
-    if (STAGES == 1 && kt + 1 < kt1) {
-      __syncthreads();  // every wave is done with the only stage
-      stage_tiles<Cfg::TILE_BYTES>(kbase + (size_t)(kt + 1) * Cfg::TILE_BYTES,
-                                   vbase + (size_t)(kt + 1) * Cfg::TILE_BYTES, cur,
-                                   cur + Cfg::TILE_BYTES, w, lane);
-    }
-  };
-  for (int kt = kt0; kt < kt1; kt += 2) {
-    tile(std::integral_constant<int, 0>(), kt);
-    if (kt + 1 < kt1) tile(std::integral_constant<int, STAGES == 2 ? 1 : 0>(), kt + 1);
+    qk_tile<D, BF16>(reinterpret_cast<const uint4*>(kb), qreg, sacc, t.lr, t.lg);
+    float alpha[2];
+    softmax_tile(t, kt, start, sl2e, sacc, m_run, l_run, alpha);
+    rescale_acc<NDB>(alpha, acc_o);
+    pv_tile<D, BF16>(reinterpret_cast<const uint4*>(vb), sacc, acc_o, t.lr, t.lg);
   }
-
-  // ---- epilogue: lane holds O^T[16 db + 4 lg + i][column]
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    float lt = l_run[mb];
-    lt += xor_shfl(lt, 16);
-    lt += xor_shfl(lt, 32);
-    if (!valid_col[mb]) continue;
-    if (S == 1) {
-      const int m = m_col[mb];
-      const int row = m / G, hh = m % G;
-      float* op = out + (((size_t)b * R + row) * Hq + g * G + hh) * D;
-      const float inv = 1.f / lt;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const v4f o = acc_o[db][mb] * inv;
-        *reinterpret_cast<float4*>(op + 16 * db + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
-      }
-    } else {
-      // acc [tile][S][128 columns][D]; (m, l) [tile][128 columns][S][2]
-      const size_t tile_id = ((size_t)b * Hkv + g) * m_tiles + mt;
-      const int col = m_col[mb] - m_base;
-      float* pp = part + ((tile_id * S + split) * kMTile + col) * D;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const v4f o = acc_o[db][mb];
-        *reinterpret_cast<float4*>(pp + 16 * db + 4 * lg) = make_float4(o[0], o[1], o[2], o[3]);
-      }
-      if (lg == 0) {
-        float* ml = part_ml + ((tile_id * kMTile + col) * S + split) * 2;
-        ml[0] = m_run[mb];
-        ml[1] = lt;
-      }
-    }
-  }
+  store_result<D>(t, out, part, part_ml, acc_o, m_run, l_run, R, Hq, Hkv, m_tiles, S);
 }
 
 // Combines the S split partials of 16 columns of one M-tile.  Thread (c, v)
@@ -491,13 +979,21 @@ hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const 
                     const void* vc, float* out, int start, int R, float scale, void* ws,
                     hipStream_t st) {
   using Cfg = PrefillCfg<D, BF16>;
-  auto kern = prefill_kernel<D, BF16>;
-  dim3 grid(p.m_tiles * p.splits, s.num_kv_heads, s.batch);
   float* part = reinterpret_cast<float*>(ws);
   float* part_ml = part + (size_t)s.batch * s.num_kv_heads * p.m_tiles * p.splits * kMTile * D;
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, q, kc, vc, out, part, part_ml,
-                     s.num_q_heads, s.num_kv_heads, s.capacity, start, R, p.m_tiles, p.splits,
-                     scale * kLog2e);
+  dim3 grid(p.m_tiles * p.splits, s.num_kv_heads, s.batch);
+  if constexpr (BF16)
+    hipLaunchKernelGGL((prefill_bf16_kernel<D>), grid, dim3(256), 0, st, q, kc, vc, out, part,
+                       part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, start, R, p.m_tiles,
+                       p.splits, scale * kLog2e);
+  else if constexpr (Cfg::PIPE)
+    hipLaunchKernelGGL((prefill_pipe_kernel<D, BF16>), grid, dim3(256), 0, st, q, kc, vc, out, part,
+                       part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, start, R, p.m_tiles,
+                       p.splits, scale * kLog2e);
+  else
+    hipLaunchKernelGGL((prefill_seq_kernel<D, BF16>), grid, dim3(256), 0, st, q, kc, vc, out, part,
+                       part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, start, R, p.m_tiles,
+                       p.splits, scale * kLog2e);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.splits > 1) {

@@ -26,8 +26,8 @@ def unpack_v(raw, B, Hkv, C, D, kv_dtype):
     a = a.reshape(B, Hkv, C // 32, 4, D, 8)
     out = np.empty((B, Hkv, C // 32, 32, D), dtype=a.dtype)
     for r in range(32):
-        s = (r % 16) // 4
-        t = r % 4 + 4 * (r // 16)
+        s = 2 * (r // 16) + (r % 8) // 4
+        t = r % 4 + 4 * ((r % 16) // 8)
         out[:, :, :, r, :] = a[:, :, :, s, :, t]
     return out.reshape(B, Hkv, C, D)
 

@@ -174,7 +174,7 @@ def test_layout_reader_round_trip_k_and_v():
                             vi = (((b * Hkv + g) * (C // 4) + j // 4) * D + d) * 4 + j % 4
                         else:
                             r = j % 32
-                            s_, t = (r % 16) // 4, r % 4 + 4 * (r // 16)
+                            s_, t = 2 * (r // 16) + (r % 8) // 4, r % 4 + 4 * ((r % 16) // 8)
                             vi = ((((b * Hkv + g) * (C // 32) + j // 32) * 4 + s_) * D + d) * 8 + t
                         raw_k[ki] = val
                         raw_v[vi] = val
