@@ -42,6 +42,38 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "session16k_decode128k_hbm_traffic.md")
+
+
+def kernel_source_hash():
+    """SHA-256 over the library's kernel sources (names and contents, sorted)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "kv_cache_attention_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        h.update(f.encode())
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or {} when the
+    kernels have changed since those counters were taken."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                k, sep, v = line.partition(":")
+                if sep and k.strip() and " " not in k.strip():
+                    kv[k.strip()] = v.strip()
+        if kv.get("traffic_source_sha256") != kernel_source_hash():
+            return {}
+        return {k: int(v) for k, v in kv.items() if k.endswith("_bytes_per_launch")}
+    except (OSError, ValueError):
+        return {}
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -196,6 +228,31 @@ def bench_decode_cold_16k(s, hold, copies=64, reps=3):
     return float(np.median(times))
 
 
+def copy_calibration(mib=256, reps=5):
+    """A plain device-to-device copy of known size: its measured bandwidth is
+    printed beside the HBM peak, and under a counter profiler its FETCH_SIZE /
+    WRITE_SIZE per dispatch give the factor that turns those counters into
+    bytes (it reads and writes exactly ``mib`` MiB)."""
+    n = mib * 2**20 // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = ev_pair()
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    nbytes = 2 * n * 4
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"bytes_read": n * 4, "bytes_written": n * 4,
+            "gbs": round(nbytes / (float(np.median(times)) * 1e-3) / 1e9, 1)}
+
+
 def bench_decode_128k(hold, steps=32):
     w = WORKLOADS[5]
     c = draw_batch(w)
@@ -246,11 +303,13 @@ def bench_decode_128k(hold, steps=32):
                 bytes=decode_bytes(w, ctx_mean, w.batch), ctx_mean=ctx_mean)
 
 
-def cpu_baseline(session_w, budget_s=12.0):
-    """The oracle (as written) on a bounded sample of the 16K prefill."""
+def cpu_baseline(session_w, budget_s=15.0):
+    """The oracle (as written) on a bounded sample of the 16K prefill: 16-row
+    blocks spaced evenly over all 16384 prompt rows (so the mean context is the
+    session's), as many as fit the time budget, plus one 16K decode step."""
     import oracle
     try:
-        from threadpoolctl import threadpool_info, threadpool_limits
+        from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     cores = len(os.sched_getaffinity(0))
@@ -258,31 +317,36 @@ def cpu_baseline(session_w, budget_s=12.0):
     c = draw_batch(w)
     ks = oracle.stored_values(c.k, "bf16")[0]
     vs = oracle.stored_values(c.v, "bf16")[0]
-    start, R = w.chunks[-2]            # the last 768-row chunk, at 15360
-    qrow = sum(r for _, r in w.chunks[:-2])
+    rows = sum(R for _, R in w.chunks)           # prompt rows = positions 0..rows-1
+    q = c.q[0]
+
+    def run(nblocks):
+        starts = np.linspace(0, rows - 16, nblocks).astype(np.int64)
+        t = time.perf_counter()
+        for s0 in starts:
+            oracle.attend_rows(q[s0:s0 + 16], ks, vs, np.arange(s0, s0 + 16), w.scale)
+        return time.perf_counter() - t
+
     ctxm = threadpool_limits(limits=cores) if threadpool_limits else None
     try:
-        n = 16
-        t = time.perf_counter()
-        oracle.attend_rows(c.q[0, qrow:qrow + n], ks, vs, np.arange(start, start + n), w.scale)
-        dt = time.perf_counter() - t
-        n2 = int(min(R, max(n, n * budget_s / max(dt, 1e-3))))
-        t = time.perf_counter()
-        oracle.attend_rows(c.q[0, qrow:qrow + n2], ks, vs, np.arange(start, start + n2), w.scale)
-        dt2 = time.perf_counter() - t
-        # one 16K decode step
+        t_cal = run(8)
+        nblocks = int(min(rows // 16, max(8, 8 * budget_s / max(t_cal, 1e-3))))
+        dt = run(nblocks)
         p = w.decode_positions[0]
         t = time.perf_counter()
-        oracle.attend_rows(c.q[0, sum(r for _, r in w.chunks)][None], ks, vs, [p], w.scale)
-        dt3 = time.perf_counter() - t
+        oracle.attend_rows(q[rows][None], ks, vs, [p], w.scale)
+        dt_dec = time.perf_counter() - t
     finally:
         if ctxm is not None:
             ctxm.__exit__(None, None, None)
-    return {"value": n2 / dt2, "unit": "rows/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{n2} query rows of the 768-row chunk at positions 15360.. (16K context, "
-                       f"8 heads, head_dim 256, bf16-stored K/V), numpy float64 two-pass softmax, "
-                       f"{cores} BLAS threads; {dt2:.1f} s"),
-            "decode_16k_us_per_token": dt3 * 1e6}
+    n = nblocks * 16
+    return {"value": round(n / dt, 2), "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{n} of the 16384 prompt rows of the 16K session (16-row blocks evenly spaced "
+                       f"over positions 0..16383, each row against its full causal context; 8 heads, "
+                       f"head_dim 256, bf16-stored K/V), numpy float64 two-pass softmax with "
+                       f"{cores} BLAS threads, {dt:.1f} s; plus one decode step at 16384 "
+                       f"({dt_dec * 1e3:.1f} ms)"),
+            "decode_16k_us_per_token": round(dt_dec * 1e6, 1)}
 
 
 def main():
@@ -303,6 +367,8 @@ def main():
     ka.lib()
     torch.cuda.set_device(0)
     hold = Hold()
+    copy = copy_calibration()
+    traffic = measured_traffic()
 
     r = bench_session(args.steps, args.warmup, hold)
     w = r["w"]
@@ -330,8 +396,9 @@ def main():
                    "global_batch": 1, "seq_len": 16384, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved_tf / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None,
-                     "kernel": "prefill (prefill_kernel + prefill_merge_kernel), 22 chunks",
+                     "traffic": traffic.get("prefill_call_bytes_per_launch"),
+                     "kernel": "prefill chunk call (prefill_bf16_kernel + prefill_merge_kernel), "
+                               "average over the 22 chunks",
                      "algorithmic_flops_per_step": flops, "causal_pairs": pairs,
                      "avg_launch_ms": round(pre_kernel_ms / len(w.chunks), 5)},
         "wall_ms_per_step": round(r["wall_ms"], 3),
@@ -343,6 +410,7 @@ def main():
         "decode_us_per_token_16k_p10_p90": [round(float(np.percentile(dec16, 10)) * 1e3, 3),
                                             round(float(np.percentile(dec16, 90)) * 1e3, 3)],
     }
+    out["copy_calibration"] = copy
     b16 = decode_bytes(w, w.decode_positions[-1] + 1, 1)
     if not args.no_cold:
         cold = bench_decode_cold_16k(r["session"], hold)
@@ -359,7 +427,9 @@ def main():
         out["decode_us_per_step_128k_x4_with_append"] = round(d["step_ms"] * 1e3, 3)
         out["roofline_decode_128k"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                       "traffic": None, "kernel": "decode (split + merge), 4 x 131041..131072",
+                                       "traffic": traffic.get("decode_128k_call_bytes_per_launch"),
+                                       "kernel": "decode call (decode_split_kernel + decode_merge_kernel), "
+                                                 "4 sessions at ctx 131041..131072",
                                        "algorithmic_bytes_per_launch": d["bytes"]}
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
