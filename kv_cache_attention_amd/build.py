@@ -28,12 +28,9 @@ HIPCC_FLAGS = [
 ]
 
 
-# Per-source extra flags.  The prefill kernel wants LLVM's ILP-oriented
-# machine scheduler so that LDS operand reads are issued ahead of the MFMAs
-# that consume them (the default occupancy-oriented one serialises them).
-EXTRA_FLAGS = {
-    "prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
-}
+# Per-source extra hipcc flags (none at present: every kernel builds with the
+# default LLVM machine scheduler).
+EXTRA_FLAGS: dict = {}
 
 
 def hipcc() -> str:

@@ -34,9 +34,9 @@ namespace {
 
 constexpr int kMTile = 128;
 constexpr int kNTile = 64;
-constexpr int kTargetWgs = 512;
 constexpr int kMaxSplits = 64;
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay below 256
+constexpr float kFrameSlack = 32.f;   // log2 units (bf16 path, see fused_step_b)
 
 typedef __attribute__((ext_vector_type(4))) float v4f;
 
@@ -54,25 +54,49 @@ struct PrefillCfg {
   using QReg = typename std::conditional<BF16, bf16x8, v4f>::type;
 };
 
-// Asynchronous copy of one tile (TILE_BYTES contiguous bytes of the cache)
-// into LDS with global_load_lds: every wave instruction moves 1 KiB, lane l's
-// 16 bytes landing at the wave's LDS base + 16 l.
+// A cache slab as a buffer resource.  Tiles are copied into LDS with the
+// MUBUF LDS-DMA form (buffer_load_dwordx4 ... lds), whose completion the
+// compiler tracks on vmcnt alone: with the FLAT form (global_load_lds) it
+// must assume the copy may also count on lgkmcnt, and while one is in flight
+// every wait for an LDS read becomes a wait for all of them.  Reads past the
+// slab (num_records bytes) return zeros.
+constexpr int kBufferConfig = 0x00020000;  // gfx9 dword 3: 32-bit data format
+
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t rsrc;
+};
+
+__device__ __forceinline__ TileSrc tile_src(const void* slab, size_t bytes) {
+  TileSrc src;
+  src.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(slab), (short)0, (int)bytes,
+                                               kBufferConfig);
+  return src;
+}
+
+// Asynchronous copy of tile `tile` (TILE_BYTES contiguous bytes of the slab)
+// into LDS: every wave instruction moves 1 KiB, lane l's 16 bytes landing at
+// the wave's LDS base + 16 l.
 template <int TILE_BYTES>
-__device__ __forceinline__ void load_tile(const unsigned char* src, unsigned char* dst, int w,
+__device__ __forceinline__ void load_tile(const TileSrc& src, int tile, unsigned char* dst, int w,
                                           int lane) {
   constexpr int PER_THREAD = TILE_BYTES / (256 * 16);
 #pragma unroll
   for (int i = 0; i < PER_THREAD; ++i) {
     const int off = (i * 256 + w * 64) * 16;
-    __builtin_amdgcn_global_load_lds((const void*)(src + off + lane * 16),
-                                     (__attribute__((address_space(3))) void*)(dst + off), 16, 0,
-                                     0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsrc,
+                                             (__attribute__((address_space(3))) void*)(dst + off),
+                                             16, tile * TILE_BYTES + off + lane * 16, 0, 0, 0);
   }
 }
 
 // s_waitcnt vmcnt(0) through the builtin (not inline asm), so the compiler's
 // own wait tracking sees it.  gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt lgkmcnt(0): retires any scalar load still in flight, so that the
+// compiler can count the in-order LDS reads that follow precisely (scalar
+// loads complete out of order; while one is pending every LDS wait is a
+// wait for all).  vmcnt 63, expcnt 7, lgkmcnt 0.
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 // MFMA operands (Q, P) are rounded with the hardware converter
 // (v_cvt_pk_bf16_f32, round to nearest even).
@@ -92,19 +116,22 @@ struct Tiling {
   bool valid_col[2];
 };
 
-__device__ __forceinline__ Tiling make_tiling(int Hq, int Hkv, int start, int R, int S) {
-  Tiling t;
-  // block -> (m-tile, split), XCD-aware: blocks x, x+8, x+16, ... land on one
-  // XCD; give them the same key range so its L2 serves all of them.
+// Block -> (m-tile, split).  Work items are ordered split-major (every m-tile
+// of split 0, then of split 1, ...) and dealt to the 8 XCDs in contiguous
+// runs: consecutive workgroups go to the XCDs round-robin, so block x runs on
+// XCD x % 8 and takes item (x % 8) * per + x / 8.  An XCD then sees few
+// distinct key ranges, and its L2 serves their K / V tiles to all of its
+// m-tiles.  The grid is padded to 8 * per blocks; blocks past the last item
+// return false.
+__device__ __forceinline__ bool make_tiling(int Hq, int Hkv, int start, int R, int S,
+                                            int m_tiles, Tiling& t) {
+  const int items = m_tiles * S;
+  const int per = (items + 7) >> 3;
   const int x = blockIdx.x;
-  if (S >= 8 && S % 8 == 0) {
-    const int spx = S / 8, xcd = x & 7, j = x >> 3;
-    t.split = xcd * spx + j % spx;
-    t.mt = j / spx;
-  } else {
-    t.mt = x / S;
-    t.split = x % S;
-  }
+  const int item = (x & 7) * per + (x >> 3);
+  if (item >= items) return false;
+  t.split = item / m_tiles;
+  t.mt = item - t.split * m_tiles;
   t.g = blockIdx.y;
   t.b = blockIdx.z;
   t.G = Hq / Hkv;
@@ -127,7 +154,7 @@ __device__ __forceinline__ Tiling make_tiling(int Hq, int Hkv, int start, int R,
     t.valid_col[mb] = t.m_col[mb] < t.M_total;
     t.row_col[mb] = t.valid_col[mb] ? t.m_col[mb] / t.G : 0;
   }
-  return t;
+  return true;
 }
 
 // Stationary Q^T operand: this lane's slice of its two columns.
@@ -519,10 +546,12 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char vb0[TB];
   __shared__ __attribute__((aligned(16))) unsigned char vb1[TB];
 
-  const Tiling t = make_tiling(Hq, Hkv, start, R, S);
+  Tiling t;
+  if (!make_tiling(Hq, Hkv, start, R, S, m_tiles, t)) return;
   const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;  // elements
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_cache) + slab * (BF16 ? 2 : 4);
-  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v_cache) + slab * (BF16 ? 2 : 4);
+  constexpr int ES = BF16 ? 2 : 4;
+  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * ES, (size_t)C * D * ES);
+  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab * ES, (size_t)C * D * ES);
   const int n = t.kt1 - t.kt0;
 
   typename Cfg::QReg qreg[2][Cfg::NQ];
@@ -536,12 +565,12 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
   v4f sa[4][2], sb[4][2];
 
   if (n > 0) {
-    load_tile<TB>(kbase + (size_t)t.kt0 * TB, kb0, t.w, t.lane);
+    load_tile<TB>(ksrc, t.kt0, kb0, t.w, t.lane);
     load_q<D, BF16>(t, q, R, Hq, qreg);
     wait_vmem();
     __syncthreads();
-    load_tile<TB>(vbase + (size_t)t.kt0 * TB, vb0, t.w, t.lane);
-    if (n > 1) load_tile<TB>(kbase + (size_t)(t.kt0 + 1) * TB, kb1, t.w, t.lane);
+    load_tile<TB>(vsrc, t.kt0, vb0, t.w, t.lane);
+    if (n > 1) load_tile<TB>(ksrc, t.kt0 + 1, kb1, t.w, t.lane);
     qk_tile<D, BF16>(reinterpret_cast<const uint4*>(kb0), qreg, sa, t.lr, t.lg);
   }
 
@@ -555,8 +584,8 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
     const int kt = t.kt0 + i;
     wait_vmem();
     __syncthreads();  // V(i), K(i+1) landed; every wave is done with step i-1
-    if (i + 2 < n) load_tile<TB>(kbase + (size_t)(kt + 2) * TB, k_free, t.w, t.lane);
-    if (i + 1 < n) load_tile<TB>(vbase + (size_t)(kt + 1) * TB, v_free, t.w, t.lane);
+    if (i + 2 < n) load_tile<TB>(ksrc, kt + 2, k_free, t.w, t.lane);
+    if (i + 1 < n) load_tile<TB>(vsrc, kt + 1, v_free, t.w, t.lane);
     if ((kt + 1) * kNTile > t.kend) {
       zero_v_beyond<D, BF16>(reinterpret_cast<uint4*>(v_cur), kt, t.kend, t.tid);
       __syncthreads();
@@ -579,15 +608,32 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
 
 // ============================================================================
 // bf16 caches: 32x32x16 MFMA (v_mfma_f32_32x32x16_bf16).  A wave owns 32
-// (row, head) columns, one per lane (lane l: column l % 32, half h = l / 32).
-//   S^T = K . Q^T per 32-key block: A = K[key][16 ks + 8 h + 0..7] (16 bytes
-//     of the K layout), B = Q^T (stationary, 8 dims of the lane's column);
-//     the lane then holds keys 8 a + 4 h + 0..3 (a = 0..3) of its column.
-//   O^T += V^T . P^T per 16-key step s: A = V[group 2 s + h][dim], B = the
-//     lane's own weights for keys {16 s + 4 h + 0..3, 16 s + 8 + 4 h + 0..3},
-//     which are accumulator registers 8 s .. 8 s + 7: no data movement.
+// (row, head) columns (lane l: column l % 32, half h = l / 32).
+//   S^T = K . Q^T per 32-key block kb and 16-dim step ks: A = K[32 kb + l % 32]
+//     [16 ks + 8 h .. + 7] (16 bytes of the K layout), B = Q^T, stationary in
+//     registers and pre-multiplied by scale * log2(e), so scores arrive in the
+//     log2 domain.  Accumulator register 4 a + e of block kb then holds key
+//     32 kb + 8 a + 4 h + e of the lane's column.
+//   O^T += V^T . P^T per 16-key step (kb, s): A = V group 4 kb + 2 s + h at dim
+//     32 db + l % 32 (16 bytes of the V layout), B = the lane's own weights of
+//     keys {32 kb + 16 s + 4 h + 0..3, 32 kb + 16 s + 8 + 4 h + 0..3}, which are
+//     accumulator registers 8 s .. 8 s + 7 of block kb: no data movement.
+// Software pipeline.  Step i of a workgroup's tile range issues, on the matrix
+// pipe, the scores of tile i+1 and the value product of tile i-1 (32 + 32
+// MFMAs for D = 256) and, on the vector pipe between them, the softmax of
+// tile i.  K(i+2) and V(i) stream into LDS meanwhile; K and V each have two
+// LDS buffers.
 // ============================================================================
 typedef __attribute__((ext_vector_type(16))) float v16f;
+
+// Both lane halves' values: lane l receives (x of lane l % 32, x of lane
+// l % 32 + 32), with v_permlane32_swap (no LDS traffic).
+__device__ __forceinline__ void halves(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
 
 struct ColB {
   int m, row;
@@ -605,9 +651,10 @@ __device__ __forceinline__ ColB col_b(const Tiling& t) {
   return c;
 }
 
+// Stationary Q^T operand, scaled by sl2e in f32 and rounded once to bf16.
 template <int D>
 __device__ __forceinline__ void load_q_b(const Tiling& t, const ColB& c, const float* __restrict__ q,
-                                         int R, int Hq, bf16x8 (&qreg)[D / 16]) {
+                                         int R, int Hq, float sl2e, bf16x8 (&qreg)[D / 16]) {
   const float* qp = q + (((size_t)t.b * R + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -615,8 +662,8 @@ __device__ __forceinline__ void load_q_b(const Tiling& t, const ColB& c, const f
     if (c.valid) {
       const float4 a = *reinterpret_cast<const float4*>(qp + 16 * ks + 8 * c.lh);
       const float4 b = *reinterpret_cast<const float4*>(qp + 16 * ks + 8 * c.lh + 4);
-      f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-      f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+      f[0] = a.x * sl2e; f[1] = a.y * sl2e; f[2] = a.z * sl2e; f[3] = a.w * sl2e;
+      f[4] = b.x * sl2e; f[5] = b.y * sl2e; f[6] = b.z * sl2e; f[7] = b.w * sl2e;
     } else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) f[j] = 0.f;
@@ -625,115 +672,145 @@ __device__ __forceinline__ void load_q_b(const Tiling& t, const ColB& c, const f
   }
 }
 
-// Scores of the next tile (2 key blocks x D/16 k-steps) fused with the
-// softmax of the current tile, chunk by chunk (see qk_next_softmax_cur).
-//   phases: 0, 1 scale + mask + local max of key block 0 / 1; 2 cross-half
-//   max; 3 reference-max update; 4..7 exponentials of registers 8 p .. 8 p + 7
-//   of key block p / 2 (p = phase - 4).
+// An empty volatile asm that reads and writes x: code motion above the
+// machine scheduler cannot move the computation of x past it, so each
+// softmax slice stays in the chunk (between scheduling fences) it was
+// written in instead of sinking to its first use in the next step.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Keys past a column's causal limit get -inf (diagonal tiles only).
+__device__ __forceinline__ void mask_tile_b(v16f (&s)[2], int key0, int lim, int lh) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (key0 + 32 * kb + 8 * (i >> 2) + 4 * lh + (i & 3) > lim) s[kb][i] = -INFINITY;
+}
+
+// Operand indices (16-byte units) within a staged tile.
 template <int D>
-__device__ __forceinline__ void qk_next_softmax_cur_b(
-    const Tiling& t, const ColB& c, const uint4* __restrict__ k_lds, const bf16x8 (&qreg)[D / 16],
-    v16f (&nxt)[2], v16f (&cur)[2], int kt, int start, float sl2e, float& m_run, float& l_run,
-    float& alpha) {
-  constexpr int NKS = D / 16;
+__device__ __forceinline__ int k_op(int ks, int kb, const ColB& c) {
+  return (2 * ks + c.lh) * 64 + 32 * kb + c.lc;
+}
+template <int D>
+__device__ __forceinline__ int v_op(int db, int kb, int s, const ColB& c) {
+  return (kb * 4 + 2 * s + c.lh) * D + 32 * db + c.lc;
+}
+
+// One pipelined step (see above).  cur: scores of tile i (log2 domain, masked)
+// in, weights out; p_cur: bf16 weights of tile i out; nxt: scores of tile i+1
+// out; p_prev: bf16 weights of tile i-1, multiplied into acc_o with the V tile
+// in v_lds.
+//
+// Reference frame.  A column's weights are exp2(s - m_ref), where m_ref is the
+// largest score of the first tile in which the column sees a key.  The frame
+// never moves during a pass, so the accumulators are never rescaled.  A score
+// above m_ref + kFrameSlack (log2 units) sets ovf: the pass is then redone
+// with m_ref = m_all, the largest score of the whole range, which every
+// column tracks.  Weights stay below 2^kFrameSlack in a pass that stands.
+//
+// Chunk c (c < NC = D/16) carries the score MFMAs of k-step c (both key
+// blocks), two value MFMAs (dim block c/2, key block c%2, s = 0, 1), the LDS
+// reads of chunk c+2 and softmax phase slices; a scheduling fence closes it.
+//   phases: 0, 1 max over key block 0 / 1; 2 cross-half max and frame;
+//   3..10 exponentials (4 each); 11..14 bf16 conversion of the weights;
+//   15 running sum.
+template <int D>
+__device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
+                                             const uint4* __restrict__ v_lds,
+                                             const bf16x8 (&qreg)[D / 16], v16f (&cur)[2],
+                                             v16f (&nxt)[2], const bf16x8 (&p_prev)[2][2],
+                                             bf16x8 (&p_cur)[2][2], v16f (&acc_o)[D / 32],
+                                             const ColB& c, float& m_ref, float& m_all,
+                                             float& l_run, bool& ovf) {
+  constexpr int NC = D / 16;
+  constexpr int DIST = 2;
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) nxt[kb][i] = 0.f;
-  const bool diag = kt * kNTile + kNTile - 1 > start + t.row_lo;
-  const int lim = start + c.row;
   float lmax = -INFINITY, ls = 0.f, m_use = 0.f;
-  uint4 kbuf[2][2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) kbuf[0][kb] = k_lds[(c.lh) * 64 + 32 * kb + c.lc];
-
+  // operand ring: [slot][0..1 K (kb), 2..3 V (s)]
+  uint4 ring[DIST + 1][4];
+  auto issue = [&](int cc) {
+    uint4(&r)[4] = ring[cc % (DIST + 1)];
+    r[0] = k_lds[k_op<D>(cc, 0, c)];
+    r[1] = k_lds[k_op<D>(cc, 1, c)];
+    r[2] = v_lds[v_op<D>(cc >> 1, cc & 1, 0, c)];
+    r[3] = v_lds[v_op<D>(cc >> 1, cc & 1, 1, c)];
+  };
   auto phase = [&](int ph) {
     if (ph < 2) {
-      const int kb = ph;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        // scores to the log2 domain first, so a column's largest term is
-        // exactly exp2(0) = 1
-        float sv = cur[kb][i] * sl2e;
-        if (diag) {
-          const int key = kt * kNTile + 32 * kb + 8 * (i >> 2) + 4 * c.lh + (i & 3);
-          if (key > lim || !c.valid) sv = -INFINITY;
-        }
-        cur[kb][i] = sv;
-        lmax = fmaxf(lmax, sv);
-      }
+      for (int i = 0; i < 16; ++i) lmax = fmaxf(lmax, cur[ph][i]);
+      pin(lmax);
     } else if (ph == 2) {
-      lmax = fmaxf(lmax, xor_shfl(lmax, 32));
-    } else if (ph == 3) {
-      // Lazy rescale: the reference max moves only when the tile max exceeds
-      // it by more than kRescaleSlack (log2 units), so weights stay below
-      // 2^kRescaleSlack.  acc and l share one reference throughout.
-      alpha = 1.f;
-      if (lmax > m_run + kRescaleSlack) {
-        alpha = fast_exp2(m_run - lmax);  // 0 when m_run is -inf
-        m_run = lmax;
-        l_run *= alpha;
-      }
-      m_use = m_run == -INFINITY ? 0.f : m_run;
-    } else {
-      const int kb = (ph - 4) >> 1, i0 = ((ph - 4) & 1) * 8;
+      float lo, hi;
+      halves(lmax, lo, hi);
+      lmax = fmaxf(lo, hi);
+      m_all = fmaxf(m_all, lmax);
+      if (m_ref == -INFINITY) m_ref = lmax;  // nothing accumulated yet
+      ovf = ovf || lmax > m_ref + kFrameSlack;
+      m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      pin(m_use);
+    } else if (ph < 11) {
+      const int q = ph - 3, kb = q >> 2, i0 = (q & 3) * 4;
 #pragma unroll
-      for (int i = i0; i < i0 + 8; ++i) {
-        const float pv = fast_exp2(cur[kb][i] - m_use);
+      for (int i = i0; i < i0 + 4; ++i) {
+        float pv = fast_exp2(cur[kb][i] - m_use);
+        pin(pv);
         cur[kb][i] = pv;
         ls += pv;
       }
+      pin(ls);
+    } else if (ph < 15) {
+      const int r = ph - 11, kb = r >> 1, s = r & 1;
+      float f[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = cur[kb][8 * s + j];
+      p_cur[kb][s] = to_bf16x8(f);
+      pin(p_cur[kb][s]);
+    } else {
+      l_run += ls;
     }
   };
 
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    if (ks + 1 < NKS) {
+  for (int cc = 0; cc < DIST; ++cc) issue(cc);
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        kbuf[(ks + 1) & 1][kb] = k_lds[(2 * (ks + 1) + c.lh) * 64 + 32 * kb + c.lc];
-    }
+  for (int cc = 0; cc < NC; ++cc) {
+    if (cc + DIST < NC) issue(cc + DIST);
+    const uint4(&r)[4] = ring[cc % (DIST + 1)];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
-      nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kbuf[ks & 1][kb]),
-                                                         qreg[ks], nxt[kb], 0, 0, 0);
+      nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, r[kb]),
+                                                         qreg[cc], nxt[kb], 0, 0, 0);
 #pragma unroll
-    for (int ph = 0; ph < 8; ++ph)
-      if (ph * NKS / 8 == ks) phase(ph);
+    for (int s = 0; s < 2; ++s)
+      acc_o[cc >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, r[2 + s]), p_prev[cc & 1][s], acc_o[cc >> 1], 0, 0, 0);
+#pragma unroll
+    for (int ph = 0; ph < 16; ++ph)
+      if (ph * NC / 16 == cc) phase(ph);
     __builtin_amdgcn_sched_barrier(0);
   }
-  l_run += ls;
 }
 
+// Value product of one tile outside the pipeline (the last tile of a range).
 template <int D>
-__device__ __forceinline__ void rescale_acc_b(float alpha, v16f (&acc_o)[D / 32]) {
-  if (__any(alpha != 1.f)) {
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) acc_o[db] *= alpha;
-  }
-}
-
-// O^T += V^T . P^T for one tile; the weights are the registers of p.
-template <int D>
-__device__ __forceinline__ void pv_tile_b(const uint4* __restrict__ v_lds, const v16f (&p)[2],
+__device__ __forceinline__ void pv_tile_b(const uint4* __restrict__ v_lds, const bf16x8 (&p)[2][2],
                                           v16f (&acc_o)[D / 32], const ColB& c) {
-  bf16x8 pb[2][2];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pb[kb][s][j] = (__bf16)p[kb][8 * s + j];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const bf16x8 av =
-            __builtin_bit_cast(bf16x8, v_lds[(kb * 4 + 2 * s + c.lh) * D + 32 * db + c.lc]);
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[kb][s], acc_o[db], 0, 0, 0);
-      }
+      for (int s = 0; s < 2; ++s)
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, v_lds[v_op<D>(db, kb, s, c)]), p[kb][s], acc_o[db], 0, 0, 0);
 }
 
 template <int D>
@@ -743,7 +820,9 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c,
                                                const v16f (&acc_o)[D / 32], float m_run,
                                                float l_run, int R, int Hq, int Hkv, int m_tiles,
                                                int S) {
-  const float lt = l_run + xor_shfl(l_run, 32);
+  float lo, hi;
+  halves(l_run, lo, hi);
+  const float lt = lo + hi;
   if (!c.valid) return;
   // lane holds dims 32 db + 8 a + 4 h + 0..3
   if (S == 1) {
@@ -776,7 +855,6 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c,
   }
 }
 
-// Pipelined bf16 prefill, same schedule as prefill_pipe_kernel.
 template <int D>
 __global__ __launch_bounds__(256) void prefill_bf16_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
@@ -788,72 +866,117 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char kb1[TB];
   __shared__ __attribute__((aligned(16))) unsigned char vb0[TB];
   __shared__ __attribute__((aligned(16))) unsigned char vb1[TB];
+  __shared__ int redo;
 
-  const Tiling t = make_tiling(Hq, Hkv, start, R, S);
+  Tiling t;
+  if (!make_tiling(Hq, Hkv, start, R, S, m_tiles, t)) return;
   const ColB c = col_b(t);
   const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;  // elements
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_cache) + slab * 2;
-  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v_cache) + slab * 2;
+  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * 2, (size_t)C * D * 2);
+  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab * 2, (size_t)C * D * 2);
   const int n = t.kt1 - t.kt0;
+  const int lim = start + c.row;
 
   bf16x8 qreg[D / 16];
   v16f acc_o[D / 32];
+  float m_ref = -INFINITY, m_all = -INFINITY, l_run = 0.f;
+  v16f sa[2], sb[2];
+  bf16x8 pa[2][2], pb[2][2];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  v16f sa[2], sb[2];
+    for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;  // also the result of an empty split
+  if (n > 0) load_q_b<D>(t, c, q, R, Hq, sl2e, qreg);
 
-  if (n > 0) {
-    load_tile<TB>(kbase + (size_t)t.kt0 * TB, kb0, t.w, t.lane);
-    load_q_b<D>(t, c, q, R, Hq, qreg);
-    wait_vmem();
-    __syncthreads();
-    load_tile<TB>(vbase + (size_t)t.kt0 * TB, vb0, t.w, t.lane);
-    if (n > 1) load_tile<TB>(kbase + (size_t)(t.kt0 + 1) * TB, kb1, t.w, t.lane);
-    // scores of the first tile (no softmax to overlap with yet)
-    const uint4* k0 = reinterpret_cast<const uint4*>(kb0);
+  // At most two passes: the second only when a score left the first pass's
+  // frame (see fused_step_b); it starts from the range's largest score.
+  for (int pass = 0; pass < 2 && n > 0; ++pass) {
+    bool ovf = false;
+    if (pass == 1) {
+      m_ref = m_all;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
+      l_run = 0.f;
+    }
+    load_tile<TB>(ksrc, t.kt0, kb0, t.w, t.lane);
+    // V(-1) := 0 and P(-1) := 0: the first step's value product adds nothing.
+    {
+      uint4* z = reinterpret_cast<uint4*>(vb1);
+#pragma unroll
+      for (int i = 0; i < TB / (256 * 16); ++i) z[i * 256 + t.tid] = make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sa[kb][i] = 0.f;
+      for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+        for (int j = 0; j < 8; ++j) pb[kb][s2][j] = (__bf16)0.f;
+    wait_vmem();
+    __syncthreads();
+    if (n > 1) load_tile<TB>(ksrc, t.kt0 + 1, kb1, t.w, t.lane);
+    // scores of the first tile (no softmax to overlap with yet)
+    {
+      const uint4* k0 = reinterpret_cast<const uint4*>(kb0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, k0[(2 * ks + c.lh) * 64 + 32 * kb + c.lc]), qreg[ks], sa[kb],
-            0, 0, 0);
-  }
-
-  // step i: V(i) in vb[i&1], K(i+1) in kb[(i+1)&1], scores of tile i in cur
-  auto step = [&](auto par, int i, v16f (&cur)[2], v16f (&nxt)[2]) {
-    constexpr int P = decltype(par)::value;
-    unsigned char* k_next = P == 0 ? kb1 : kb0;   // holds K(i+1)
-    unsigned char* k_free = P == 0 ? kb0 : kb1;   // held K(i): free for K(i+2)
-    unsigned char* v_cur = P == 0 ? vb0 : vb1;    // holds V(i)
-    unsigned char* v_free = P == 0 ? vb1 : vb0;   // held V(i-1): free for V(i+1)
-    const int kt = t.kt0 + i;
-    wait_vmem();
-    __syncthreads();  // V(i), K(i+1) landed; every wave is done with step i-1
-    if (i + 2 < n) load_tile<TB>(kbase + (size_t)(kt + 2) * TB, k_free, t.w, t.lane);
-    if (i + 1 < n) load_tile<TB>(vbase + (size_t)(kt + 1) * TB, v_free, t.w, t.lane);
-    if ((kt + 1) * kNTile > t.kend) {
-      zero_v_beyond<D, true>(reinterpret_cast<uint4*>(v_cur), kt, t.kend, t.tid);
-      __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sa[kb][i] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, k0[k_op<D>(ks, kb, c)]), qreg[ks], sa[kb], 0, 0, 0);
     }
-    float alpha;
-    qk_next_softmax_cur_b<D>(t, c, reinterpret_cast<const uint4*>(k_next), qreg, nxt, cur, kt,
-                             start, sl2e, m_run, l_run, alpha);
-    rescale_acc_b<D>(alpha, acc_o);
-    pv_tile_b<D>(reinterpret_cast<const uint4*>(v_cur), cur, acc_o, c);
-  };
-  for (int i = 0; i < n; i += 2) {
-    step(std::integral_constant<int, 0>(), i, sa, sb);
-    if (i + 1 < n) step(std::integral_constant<int, 1>(), i + 1, sb, sa);
+
+    // Step i (parity P = i & 1): K(i+1) and V(i-1) are in buffers 1-P; K(i+2)
+    // and V(i) are loaded into buffers P, whose previous contents (K(i),
+    // V(i-2)) every wave finished with in step i-1.
+    auto step = [&](auto par, int i, v16f (&cur)[2], v16f (&nxt)[2], bf16x8 (&p_prev)[2][2],
+                    bf16x8 (&p_cur)[2][2]) {
+      constexpr int P = decltype(par)::value;
+      const unsigned char* k_use = P == 0 ? kb1 : kb0;
+      const unsigned char* v_use = P == 0 ? vb1 : vb0;
+      unsigned char* k_load = P == 0 ? kb0 : kb1;
+      unsigned char* v_load = P == 0 ? vb0 : vb1;
+      const int kt = t.kt0 + i;
+      wait_vmem();
+      __syncthreads();
+      wait_lgkm();
+      if (i + 2 < n) load_tile<TB>(ksrc, kt + 2, k_load, t.w, t.lane);
+      load_tile<TB>(vsrc, kt, v_load, t.w, t.lane);
+      if (kt * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(cur, kt * kNTile, lim, c.lh);
+      fused_step_b<D>(reinterpret_cast<const uint4*>(k_use), reinterpret_cast<const uint4*>(v_use),
+                      qreg, cur, nxt, p_prev, p_cur, acc_o, c, m_ref, m_all, l_run, ovf);
+    };
+    for (int i = 0; i < n; i += 2) {
+      step(std::integral_constant<int, 0>(), i, sa, sb, pb, pa);
+      if (i + 1 < n) step(std::integral_constant<int, 1>(), i + 1, sb, sa, pa, pb);
+    }
+    // value product of the last tile, V(n-1) in buffer (n-1) & 1
+    {
+      const int kt = t.kt1 - 1;
+      unsigned char* v_last = ((n - 1) & 1) ? vb1 : vb0;
+      wait_vmem();
+      if (t.tid == 0) redo = 0;
+      __syncthreads();
+      if ((kt + 1) * kNTile > t.kend) {
+        zero_v_beyond<D, true>(reinterpret_cast<uint4*>(v_last), kt, t.kend, t.tid);
+        __syncthreads();
+      }
+      if ((n - 1) & 1)
+        pv_tile_b<D>(reinterpret_cast<const uint4*>(vb1), pb, acc_o, c);
+      else
+        pv_tile_b<D>(reinterpret_cast<const uint4*>(vb0), pa, acc_o, c);
+    }
+    if (pass == 1) break;
+    if (__any(ovf) && t.lane == 0) redo = 1;
+    __syncthreads();  // also: every wave is done with the LDS tiles
+    if (!redo) break;
   }
-  store_result_b<D>(t, c, out, part, part_ml, acc_o, m_run, l_run, R, Hq, Hkv, m_tiles, S);
+  store_result_b<D>(t, c, out, part, part_ml, acc_o, m_ref, l_run, R, Hq, Hkv, m_tiles, S);
 }
 
 // Sequential prefill (one K+V stage) for shapes whose four tiles do not fit
@@ -869,10 +992,12 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char kb[TB];
   __shared__ __attribute__((aligned(16))) unsigned char vb[TB];
 
-  const Tiling t = make_tiling(Hq, Hkv, start, R, S);
+  Tiling t;
+  if (!make_tiling(Hq, Hkv, start, R, S, m_tiles, t)) return;
   const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(k_cache) + slab * (BF16 ? 2 : 4);
-  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(v_cache) + slab * (BF16 ? 2 : 4);
+  constexpr int ES = BF16 ? 2 : 4;
+  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * ES, (size_t)C * D * ES);
+  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab * ES, (size_t)C * D * ES);
 
   typename Cfg::QReg qreg[2][Cfg::NQ];
   load_q<D, BF16>(t, q, R, Hq, qreg);
@@ -886,8 +1011,8 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
   v4f sacc[4][2];
   for (int kt = t.kt0; kt < t.kt1; ++kt) {
     __syncthreads();  // every wave is done with the previous tile
-    load_tile<TB>(kbase + (size_t)kt * TB, kb, t.w, t.lane);
-    load_tile<TB>(vbase + (size_t)kt * TB, vb, t.w, t.lane);
+    load_tile<TB>(ksrc, kt, kb, t.w, t.lane);
+    load_tile<TB>(vsrc, kt, vb, t.w, t.lane);
     wait_vmem();
     __syncthreads();
     if ((kt + 1) * kNTile > t.kend) {
@@ -963,15 +1088,39 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   }
 }
 
+// Split count of a chunk: the one that minimises a model of the launch time.
+// A workgroup's LDS tiles fill most of a CU's 160 KiB, so one runs per CU:
+// ceil(workgroups / 256) rounds run back to back, each as long as its
+// longest workgroup (fixed cost + its key tiles); splitting also costs the
+// merge pass, which reads back the partials.  At most about three rounds of
+// workgroups are considered, which bounds the workspace.  Times in ns.
+constexpr int kCUs = 256;
+constexpr int kMaxWgRounds = 3;
+
+int max_splits(long long units) {
+  const long long cap = (kMaxWgRounds * (long long)kCUs + units - 1) / units;
+  return (int)(cap < kMaxSplits ? cap : kMaxSplits);
+}
+
 int choose_splits(const Shape& s, int m_tiles, int nkt) {
-  const long long wgs = (long long)s.batch * s.num_kv_heads * m_tiles;
-  long long S = (kTargetWgs + wgs / 2) / wgs;
-  if (S >= 8) S = S / 8 * 8;
-  if (S > kMaxSplits) S = kMaxSplits;
-  if (S > nkt) S = nkt;
-  if (S > 8 && S % 8) S = S / 8 * 8;
-  if (S < 1) S = 1;
-  return (int)S;
+  const long long units = (long long)s.batch * s.num_kv_heads * m_tiles;
+  const double scale_d = s.head_dim / 256.0;
+  const double tile_ns = (s.kv_dtype == 1 ? 1300.0 : 9000.0) * scale_d;
+  const double wg_ns = 3000.0, merge_ns = 4000.0, part_ns = 26.0 * scale_d;
+  const int smax = max_splits(units);
+  int best = 1;
+  double best_t = 0.0;
+  for (int S = 1; S <= smax && S <= nkt; ++S) {
+    const long long wgs = units * S;
+    const long long rounds = (wgs + kCUs - 1) / kCUs;
+    const double t = rounds * (wg_ns + tile_ns * ((nkt + S - 1) / S)) +
+                     (S > 1 ? merge_ns + part_ns * (double)wgs : 0.0);
+    if (S == 1 || t < best_t * 0.999) {
+      best_t = t;
+      best = S;
+    }
+  }
+  return best;
 }
 
 template <int D, bool BF16>
@@ -981,7 +1130,8 @@ hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const 
   using Cfg = PrefillCfg<D, BF16>;
   float* part = reinterpret_cast<float*>(ws);
   float* part_ml = part + (size_t)s.batch * s.num_kv_heads * p.m_tiles * p.splits * kMTile * D;
-  dim3 grid(p.m_tiles * p.splits, s.num_kv_heads, s.batch);
+  // padded to whole rounds of the 8 XCDs (see make_tiling)
+  dim3 grid(8 * ((p.m_tiles * p.splits + 7) / 8), s.num_kv_heads, s.batch);
   if constexpr (BF16)
     hipLaunchKernelGGL((prefill_bf16_kernel<D>), grid, dim3(256), 0, st, q, kc, vc, out, part,
                        part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, start, R, p.m_tiles,
@@ -1026,10 +1176,10 @@ size_t prefill_workspace_bound(const Shape& s, int max_rows) {
   const int mt_max = (int)(((long long)max_rows * G + kMTile - 1) / kMTile);
   size_t best = 0;
   for (int mt = 1; mt <= mt_max; ++mt) {
-    const int S = choose_splits(s, mt, 1 << 30);
-    if (S == 1) continue;
-    const size_t bytes = (size_t)s.batch * s.num_kv_heads * mt * S * kMTile *
-                         (size_t)(s.head_dim + 2) * sizeof(float);
+    const long long units = (long long)s.batch * s.num_kv_heads * mt;
+    const int S = max_splits(units);  // choose_splits never exceeds it
+    if (S <= 1) continue;
+    const size_t bytes = (size_t)units * S * kMTile * (size_t)(s.head_dim + 2) * sizeof(float);
     if (bytes > best) best = bytes;
   }
   return best;

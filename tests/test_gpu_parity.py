@@ -182,6 +182,30 @@ def test_prefill_nan_in_visible_key_poisons_later_rows_only():
     assert oracle.rel_error(got[0, :70], ref[0, :70], c.v) <= TOL[dt]
 
 
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_prefill_scores_far_above_the_first_tile(dt):
+    """Queries share one direction u and the keys at odd 64-position tiles are
+    3u, so those keys score about 40 (natural units) above every other key: a
+    split that starts on an even tile meets scores far above its first tile's
+    maximum (the bf16 kernel then redoes the split in a wider frame, the f32
+    kernel rescales).  Every row that sees such keys averages their values."""
+    B, Hq, Hkv, D, start, R = 1, 8, 1, 256, 1024, 128
+    C = start + R + 64
+    rng = np.random.default_rng(31)
+    c = random_case(31, B, Hq, Hkv, D, start + R, R)
+    u = rng.standard_normal(D).astype(np.float32)
+    c.q[:] = u + np.float32(0.1) * c.q
+    for t0 in range(64, start + R, 128):
+        c.k[0, t0 + 17, 0] = 3 * u
+    caches = DevCaches(B, Hq, Hkv, D, C, dt)
+    caches.append(c.k[:, :start], c.v[:, :start], 0)
+    caches.append(c.k[:, start:], c.v[:, start:], start)
+    got = caches.prefill(c.q, start, 1 / 16)
+    ks, vs = _stored(c.k, dt), _stored(c.v, dt)
+    ref = oracle.prefill_chunk(c.q, ks, vs, start, 1 / 16)
+    _check(got, ref, vs, dt, f"prefill far-above-first-tile {dt}")
+
+
 # ------------------------------------------------------------------ decode
 
 def _decode_case(dt, B, Hq, Hkv, D, C, ctxs, seed):
