@@ -35,6 +35,7 @@ constexpr int kWaves = 4;      // waves per workgroup
 constexpr int kTargetWgs = 512;
 constexpr int kMaxSplits = 1024;
 constexpr int kSplitWavesPerEu = 2;  // register budget: 168 VGPRs, 12 waves per CU
+constexpr float kRescaleSlack = 8.f;  // log2 units (MFMA path)
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
@@ -360,10 +361,10 @@ void decode_split_kernel(
 // one head and 32 dims.  Thread (d, r) sums splits r, r + 8, ... with all its
 // loads in flight; the eight partial sums are then added in a fixed order, so
 // the result does not depend on timing.
-template <int D, int HPW>
+template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
-    int b0, int Hq, int Hkv, int HG, int S) {
+    int b0, int Hq, int Hkv, int HG, int hpw, int S) {
   __shared__ float wgt[kMaxSplits];
   __shared__ float red[8][32];
   __shared__ float wmax[4], wsum[4];
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int G = Hq / Hkv;
   const int gq = b * (Hkv * HG) + gh;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const float* ml = part_ml + ((size_t)gq * HPW + h) * S * 2;
+  const float* ml = part_ml + ((size_t)gq * hpw + h) * S * 2;
   // M = max_s m_s over the block, then w_s = 2^(m_s - M), L = sum_s w_s l_s
   float M = -INFINITY;
   for (int s = tid; s < S; s += 256) M = fmaxf(M, ml[2 * s]);
@@ -396,8 +397,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   // weighted sum of the accumulators
   const int dl = tid & 31, r = tid >> 5;
   const int d = ds * 32 + dl;
-  const float* pa = part + ((size_t)gq * S * HPW + h) * D + d;
-  constexpr size_t PS = (size_t)HPW * D;
+  const float* pa = part + ((size_t)gq * S * hpw + h) * D + d;
+  const size_t PS = (size_t)hpw * D;
   float a = 0.f;
   int s = r;
   for (; s + 56 < S; s += 64) {
@@ -413,7 +414,254 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   if (r == 0) {
     const float t = ((red[0][dl] + red[1][dl]) + (red[2][dl] + red[3][dl])) +
                     ((red[4][dl] + red[5][dl]) + (red[6][dl] + red[7][dl]));
-    out[((size_t)b * Hq + g * G + hg * HPW + h) * D + d] = t / L;
+    out[((size_t)b * Hq + g * G + hg * hpw + h) * D + d] = t / L;
+  }
+}
+
+// ============================================================================
+// bf16 caches: the decode step on MFMA (v_mfma_f32_16x16x32_bf16).
+//
+// One query row with hpw <= 16 heads is a prefill of one row: the heads are
+// the MFMA columns.  The context is cut into 32-position tiles (one bf16 V
+// block); the S workgroups of a (session, KV head) and their four waves each
+// take every (4 S)-th tile.  A wave loads its MFMA
+// operands straight from the cache into registers -- every K / V element is
+// used by exactly one wave, so there is nothing for LDS to share -- two tiles
+// ahead (64 KiB in flight per wave for D = 256).  Per tile (lane l: column
+// l % 16, row group r = l / 16):
+//   S^T = K . Q^T per 16-position block kb and 32-dim step ks: A = K[32 t +
+//     16 kb + l % 16][32 ks + 8 r .. + 7] (16 bytes of the K layout), B = Q^T
+//     (stationary; scale * log2 e folded in, rounded once to bf16).  The lane
+//     then holds positions 32 t + 16 kb + 4 r + 0..3 of its column.
+//   O^T += V^T . P^T per 16-dim block db: A = V group r at dim 16 db + l % 16
+//     (16 bytes: 8 positions), B = the weights of those 8 positions for the
+//     lane's column.  Group r = 2 s + h holds positions {16 s + 4 h + 0..3,
+//     16 s + 8 + 4 h + 0..3}: a lane in the lower half (r < 2) owns the first
+//     four in its own block-0 scores and finds the other four in the lane 32
+//     above; a lane in the upper half owns the last four (block 1) and finds
+//     the first four 32 below -- one v_permlane32_swap per register pair.
+// The four waves merge through LDS; a workgroup writes its split's partial
+// (or, alone, the output); a second kernel combines the splits.
+// ============================================================================
+constexpr int kDecTile = 32;  // positions per wave tile
+constexpr int kDecCols = 16;  // MFMA columns = most heads per workgroup
+
+template <int D>
+struct DecTile {
+  uint4 k[2][D / 32];  // [position block kb][dim step ks]
+  uint4 v[D / 16];     // [dim block db]
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(
+    const float* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
+    float* __restrict__ part_ml, const CtxArg ctxa, int b0, int Hq, int Hkv, int HG, int hpw,
+    int C, int S, float sl2e) {
+  typedef __attribute__((ext_vector_type(4))) float v4f;
+  __shared__ float sacc[kWaves][kDecCols * D];
+  __shared__ float wm[kWaves][kDecCols], wl[kWaves][kDecCols];
+
+  const int split = blockIdx.x, gh = blockIdx.y, bl = blockIdx.z, b = b0 + bl;
+  const int g = gh / HG, hg = gh % HG;
+  const int G = Hq / Hkv;
+  const int h0 = g * G + hg * hpw;  // first query head served
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lc = lane & 15, r = lane >> 4;
+  const int ctx = ctxa.ctx[bl];
+  const int nt = (ctx + kDecTile - 1) / kDecTile;
+  // The slab's S * 4 waves take its tiles in turn (wave j: tiles j, j + NW,
+  // j + 2 NW, ...), so at any moment they read one contiguous stretch of the
+  // cache; a wave's tiles need no order (the softmax is online).
+  const int NW = S * kWaves, j0 = split * kWaves + w;
+  const int t0 = 0, t1 = j0 < nt ? (nt - 1 - j0) / NW + 1 : 0;  // local tile counts
+
+  const size_t slab_bytes = (size_t)C * D * 2;
+  const size_t slab = ((size_t)b * Hkv + g) * slab_bytes;
+  const __amdgpu_buffer_rsrc_t krs =
+      buffer_rsrc(reinterpret_cast<const unsigned char*>(k_cache) + slab, slab_bytes);
+  const __amdgpu_buffer_rsrc_t vrs =
+      buffer_rsrc(reinterpret_cast<const unsigned char*>(v_cache) + slab, slab_bytes);
+
+  // operand loads of this wave's i-th tile, tile j0 + i NW (K layout [C/64][D/8][64][8], V [C/32][4][D][8])
+  auto load = [&](DecTile<D>& x, int i) {
+    const int t = j0 + i * NW;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int pos = kDecTile * t + 16 * kb + lc;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        x.k[kb][ks] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       krs, (((pos >> 6) * (D / 8) + 4 * ks + r) * 64 + (pos & 63)) * 16, 0, 0));
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      x.v[db] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                     vrs, ((4 * t + r) * D + 16 * db + lc) * 16, 0, 0));
+  };
+
+  DecTile<D> ta_, tb_;
+  if (t0 < t1) load(ta_, t0);
+  if (t0 + 1 < t1) load(tb_, t0 + 1);
+
+  // stationary Q^T: column lc is head h0 + lc (zero past hpw)
+  bf16x8 qreg[D / 32];
+  {
+    const bool hv = lc < hpw;
+    const float* qp = q + ((size_t)b * Hq + h0 + (hv ? lc : 0)) * D + 8 * r;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      float f[8];
+      if (hv) {
+        const float4 x = *reinterpret_cast<const float4*>(qp + 32 * ks);
+        const float4 y = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
+        f[0] = x.x * sl2e; f[1] = x.y * sl2e; f[2] = x.z * sl2e; f[3] = x.w * sl2e;
+        f[4] = y.x * sl2e; f[5] = y.y * sl2e; f[6] = y.z * sl2e; f[7] = y.w * sl2e;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = 0.f;
+      }
+      qreg[ks] = to_bf16x8(f);
+    }
+  }
+
+  v4f acc[D / 16];
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) acc[db] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // One tile; x is reloaded with tile t + 2 once its operands are consumed.
+  auto tile = [&](DecTile<D>& x, int i) {
+    const int t = j0 + i * NW;
+    v4f sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sc[kb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.k[kb][ks]),
+                                                         qreg[ks], sc[kb], 0, 0, 0);
+    }
+    // positions at or past ctx (last tile only) may hold anything
+    const bool tail = kDecTile * t + kDecTile > ctx;
+    if (tail) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (kDecTile * t + 16 * kb + 4 * r + i >= ctx) sc[kb][i] = -INFINITY;
+    }
+    // column max over the tile: 8 values per lane, then the four row groups
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[kb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    // online softmax; the reference max moves only when the tile max exceeds
+    // it by more than kRescaleSlack (log2 units)
+    float alpha = 1.f;
+    if (mx > m_run + kRescaleSlack) {
+      alpha = fast_exp2(m_run - mx);  // 0 when m_run is -inf
+      m_run = mx;
+      l_run *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    uint32_t pk[2][2];  // [kb][pair]: bf16 weights of positions 16 kb + 4 r + 0..3
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = fast_exp2(sc[kb][i] - m_use);
+        l_run += p[i];
+      }
+      pk[kb][0] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)p[0], (__bf16)p[1]});
+      pk[kb][1] = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)p[2], (__bf16)p[3]});
+    }
+    // B operand: slots 0..3 from block 0 of this lane (lower half) or of the
+    // lane 32 below (upper half), slots 4..7 from block 0 of the lane 32
+    // above (lower half) or block 1 of this lane (upper half)
+    uint4 pb;
+    {
+      const auto x0 = __builtin_amdgcn_permlane32_swap(pk[0][0], pk[1][0], false, false);
+      const auto x1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
+      pb = make_uint4(x0[0], x1[0], x0[1], x1[1]);
+    }
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
+    }
+    if (tail) {
+      // zero the values of positions at or past ctx
+      uint32_t keep[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        keep[e] = (vbf16_pos(t, r, 2 * e) < ctx ? 0x0000ffffu : 0u) |
+                  (vbf16_pos(t, r, 2 * e + 1) < ctx ? 0xffff0000u : 0u);
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        x.v[db].x &= keep[0]; x.v[db].y &= keep[1]; x.v[db].z &= keep[2]; x.v[db].w &= keep[3];
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8, x.v[db]), __builtin_bit_cast(bf16x8, pb), acc[db], 0, 0, 0);
+    if (i + 2 < t1) load(x, i + 2);
+  };
+  for (int t = t0; t < t1; t += 2) {
+    tile(ta_, t);
+    if (t + 1 < t1) tile(tb_, t + 1);
+  }
+
+  // ---- merge the four waves
+  float lt = l_run;
+  lt += __shfl_xor(lt, 16, kWave);
+  lt += __shfl_xor(lt, 32, kWave);
+  if (lc < hpw) {
+    float* o = sacc[w] + lc * D;
+    // lane holds dims 16 db + 4 r + 0..3
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      *reinterpret_cast<float4*>(o + 16 * db + 4 * r) =
+          make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+    if (r == 0) {
+      wm[w][lc] = m_run;
+      wl[w][lc] = lt;
+    }
+  }
+  __syncthreads();
+  const int gq = b * (Hkv * HG) + gh;  // partial slot of (b, g, hg)
+  for (int i = tid; i < hpw * D / 4; i += 256) {
+    const int h = i / (D / 4), d = 4 * (i % (D / 4));
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, wm[ww][h]);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    float l = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float f = wm[ww][h] == -INFINITY ? 0.f : fast_exp2(wm[ww][h] - M);
+      const float4 x = *reinterpret_cast<const float4*>(sacc[ww] + h * D + d);
+      a.x += f * x.x; a.y += f * x.y; a.z += f * x.z; a.w += f * x.w;
+      l += f * wl[ww][h];
+    }
+    if (S == 1) {
+      const float inv = 1.f / l;
+      *reinterpret_cast<float4*>(out + ((size_t)b * Hq + h0 + h) * D + d) =
+          make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+    } else {
+      *reinterpret_cast<float4*>(part + (((size_t)gq * S + split) * hpw + h) * D + d) = a;
+      if (d == 0) {
+        part_ml[(((size_t)gq * hpw + h) * S + split) * 2] = M;
+        part_ml[(((size_t)gq * hpw + h) * S + split) * 2 + 1] = l;
+      }
+    }
   }
 }
 
@@ -447,18 +695,11 @@ void dispatch_hpw(int hpw, dim3 grid, hipStream_t st, const float* q, const void
 }
 
 template <int D>
-void dispatch_merge(int hpw, dim3 grid, hipStream_t st, const float* part, float* out, int b0,
-                    const Shape& s, int HG, int S) {
-  switch (hpw) {
-#define KA_MERGE(H)                                                                            \
-  case H:                                                                                      \
-    hipLaunchKernelGGL((decode_merge_kernel<D, H>), grid, dim3(256), 0, st, part,             \
-                       part + (size_t)s.batch * s.num_kv_heads * HG * S * H * D, out, b0,     \
-                       s.num_q_heads, s.num_kv_heads, HG, S);                                  \
-    break;
-    KA_MERGE(8) KA_MERGE(4) KA_MERGE(2) KA_MERGE(1)
-#undef KA_MERGE
-  }
+void launch_merge(int hpw, dim3 grid, hipStream_t st, const float* part, float* out, int b0,
+                  const Shape& s, int HG, int S) {
+  hipLaunchKernelGGL((decode_merge_kernel<D>), grid, dim3(256), 0, st, part,
+                     part + (size_t)s.batch * s.num_kv_heads * HG * S * hpw * D, out, b0,
+                     s.num_q_heads, s.num_kv_heads, HG, hpw, S);
 }
 
 }  // namespace
@@ -466,16 +707,33 @@ void dispatch_merge(int hpw, dim3 grid, hipStream_t st, const float* part, float
 DecodePlan plan_decode(const Shape& s, int max_ctx) {
   DecodePlan p;
   const int G = s.num_q_heads / s.num_kv_heads;
-  p.heads_per_wg = heads_per_wg(G);
-  p.head_groups = G / p.heads_per_wg;
-  const int units = units_for(max_ctx);
-  const long long slabs = (long long)s.batch * s.num_kv_heads * p.head_groups;
-  long long S = (kTargetWgs + slabs - 1) / slabs;
-  const long long by_units = units / kWaves;  // at least one unit per wave
-  if (S > by_units) S = by_units;
+  long long S;
+  if (s.kv_dtype == 1) {
+    // MFMA path: up to 16 heads share a workgroup's columns; one round of
+    // 256 workgroups (one per CU: a wave's operand registers fill its SIMD),
+    // at least one tile per wave
+    int hg = 1;
+    while (G / hg > kDecCols || G % hg != 0) ++hg;
+    p.head_groups = hg;
+    p.heads_per_wg = G / hg;
+    const long long slabs = (long long)s.batch * s.num_kv_heads * hg;
+    const long long tiles = (max_ctx + kDecTile - 1) / kDecTile;
+    S = (256 + slabs - 1) / slabs;
+    const long long by_tiles = (tiles + kWaves - 1) / kWaves;
+    if (S > by_tiles) S = by_tiles;
+  } else {
+    p.heads_per_wg = heads_per_wg(G);
+    p.head_groups = G / p.heads_per_wg;
+    const int units = units_for(max_ctx);
+    const long long slabs = (long long)s.batch * s.num_kv_heads * p.head_groups;
+    S = (kTargetWgs + slabs - 1) / slabs;
+    const long long by_units = units / kWaves;  // at least one unit per wave
+    if (S > by_units) S = by_units;
+  }
   if (S > kMaxSplits) S = kMaxSplits;
   if (S < 1) S = 1;
   p.splits = (int)S;
+  const long long slabs = (long long)s.batch * s.num_kv_heads * p.head_groups;
   p.workspace_bytes = p.splits == 1 ? 0
       : (size_t)slabs * p.splits * p.heads_per_wg * (s.head_dim + 2) * sizeof(float);
   // layout: acc [slab][S][HPW][D], then (m, l) [slab][HPW][S][2]
@@ -498,14 +756,17 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q,
     switch (s.head_dim) {
 #define KA_D(DD)                                                                               \
   case DD:                                                                                     \
-    if (bf16) dispatch_hpw<DD, true>(p.heads_per_wg, grid, stream, q, k_cache, v_cache, out,  \
-                                     part, ca, b0, s, HG, S, sl2e);                            \
+    if (bf16)                                                                                  \
+      hipLaunchKernelGGL((decode_mfma_kernel<DD>), grid, dim3(256), 0, stream, q, k_cache,     \
+                         v_cache, out, part,                                                   \
+                         part + (size_t)s.batch * s.num_kv_heads * HG * S * p.heads_per_wg * DD, \
+                         ca, b0, s.num_q_heads, s.num_kv_heads, HG, p.heads_per_wg,            \
+                         s.capacity, S, sl2e);                                                 \
     else dispatch_hpw<DD, false>(p.heads_per_wg, grid, stream, q, k_cache, v_cache, out, part, \
                                  ca, b0, s, HG, S, sl2e);                                      \
-    if (S > 1) dispatch_merge<DD>(p.heads_per_wg,                                             \
-                                  dim3(p.heads_per_wg * (DD / 32), s.num_kv_heads * HG, nb),   \
-                                  stream, part,                                                \
-                                  out, b0, s, HG, S);                                          \
+    if (S > 1) launch_merge<DD>(p.heads_per_wg,                                               \
+                                dim3(p.heads_per_wg * (DD / 32), s.num_kv_heads * HG, nb),     \
+                                stream, part, out, b0, s, HG, S);                              \
     break;
       KA_D(64) KA_D(128) KA_D(256)
 #undef KA_D

@@ -59,6 +59,48 @@ __device__ __forceinline__ int vbf16_pos(int blk, int g, int t) {
   return (blk << 5) + ((g >> 1) << 4) + ((g & 1) << 2) + (t & 3) + ((t >> 2) << 3);
 }
 
+// MFMA operands are rounded with the hardware converter (v_cvt_pk_bf16_f32,
+// round to nearest even).
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* f) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (__bf16)f[j];
+  return r;
+}
+
+// ------------------------------------------------- asynchronous LDS staging
+// A buffer resource over `bytes` bytes at base; reads past the end return
+// zeros.  Copies into LDS use the MUBUF LDS-DMA form (buffer_load_dwordx4 ...
+// lds), whose completion the compiler tracks on vmcnt alone: with the FLAT
+// form (global_load_lds) it must assume the copy may also count on lgkmcnt,
+// and while one is in flight every wait for an LDS read becomes a wait for
+// all of them.
+constexpr int kBufferConfig = 0x00020000;  // gfx9 dword 3: 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufferConfig);
+}
+
+// One wave instruction: lane l copies the 16 bytes at byte offset voffset
+// (its own) of the resource to LDS address lds + 16 l (lds wave-uniform).
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds, int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0) through the builtin (not inline asm), so the compiler's
+// own wait tracking sees it.  gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt lgkmcnt(0): vmcnt 63, expcnt 7, lgkmcnt 0.
+__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// s_waitcnt vmcnt(N) for a compile-time N < 64 (vmcnt bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // ------------------------------------------------------- wave reductions
 // Butterfly max / sum across the 64 lanes of a wavefront (every lane ends
 // with the result).  NaN reaching these is handled by the callers.

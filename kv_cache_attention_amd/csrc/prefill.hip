@@ -54,22 +54,14 @@ struct PrefillCfg {
   using QReg = typename std::conditional<BF16, bf16x8, v4f>::type;
 };
 
-// A cache slab as a buffer resource.  Tiles are copied into LDS with the
-// MUBUF LDS-DMA form (buffer_load_dwordx4 ... lds), whose completion the
-// compiler tracks on vmcnt alone: with the FLAT form (global_load_lds) it
-// must assume the copy may also count on lgkmcnt, and while one is in flight
-// every wait for an LDS read becomes a wait for all of them.  Reads past the
-// slab (num_records bytes) return zeros.
-constexpr int kBufferConfig = 0x00020000;  // gfx9 dword 3: 32-bit data format
-
+// A cache slab as a buffer resource (see buffer_rsrc).
 struct TileSrc {
   __amdgpu_buffer_rsrc_t rsrc;
 };
 
 __device__ __forceinline__ TileSrc tile_src(const void* slab, size_t bytes) {
   TileSrc src;
-  src.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(slab), (short)0, (int)bytes,
-                                               kBufferConfig);
+  src.rsrc = buffer_rsrc(slab, bytes);
   return src;
 }
 
@@ -83,30 +75,9 @@ __device__ __forceinline__ void load_tile(const TileSrc& src, int tile, unsigned
 #pragma unroll
   for (int i = 0; i < PER_THREAD; ++i) {
     const int off = (i * 256 + w * 64) * 16;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.rsrc,
-                                             (__attribute__((address_space(3))) void*)(dst + off),
-                                             16, tile * TILE_BYTES + off + lane * 16, 0, 0, 0);
+    dma16(src.rsrc, dst + off, tile * TILE_BYTES + off + lane * 16);
   }
 }
-
-// s_waitcnt vmcnt(0) through the builtin (not inline asm), so the compiler's
-// own wait tracking sees it.  gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// s_waitcnt lgkmcnt(0): retires any scalar load still in flight, so that the
-// compiler can count the in-order LDS reads that follow precisely (scalar
-// loads complete out of order; while one is pending every LDS wait is a
-// wait for all).  vmcnt 63, expcnt 7, lgkmcnt 0.
-__device__ __forceinline__ void wait_lgkm() { __builtin_amdgcn_s_waitcnt(0xC07F); }
-
-// MFMA operands (Q, P) are rounded with the hardware converter
-// (v_cvt_pk_bf16_f32, round to nearest even).
-__device__ __forceinline__ bf16x8 to_bf16x8(const float* f) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (__bf16)f[j];
-  return r;
-}
-
 
 // Per-block constants of the tiling.
 struct Tiling {
