@@ -170,6 +170,23 @@ ka_status ka_attn_decode(const ka_attn_shape* s, const float* q,
                          const int32_t* ctx_len, float scale,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Decode step with its append (the same passages): for each session b, the
+ * new K and V rows k_new[b], v_new[b] (f32 [B][Hkv][D]) are stored at cache
+ * position pos[b], exactly as ka_attn_append_kv would store them (same
+ * rounding, same bits), and the query row q[b] at that position attends to
+ * cache positions 0 .. pos[b].  Equivalent to one ka_attn_append_kv per
+ * session followed by ka_attn_decode with ctx_len[b] = pos[b] + 1, and bitwise
+ * equal to it, in one launch for bf16 caches (the attention kernel writes the
+ * row it uses).  pos is a HOST array of B entries, 0 <= pos[b] < C.  The
+ * workspace is ka_attn_decode's for max_b pos[b] + 1.  k_new, v_new and q may
+ * not overlap the caches or out.  Errors as ka_attn_decode.
+ */
+ka_status ka_attn_decode_step(const ka_attn_shape* s, const float* q, const float* k_new,
+                              const float* v_new, void* k_cache, void* v_cache, float* out,
+                              const int32_t* pos, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Static name of a status code ("KA_OK", ...). */
 const char* ka_attn_status_string(int32_t status);
 

@@ -19,7 +19,7 @@ import torch
 __all__ = ["Shape", "KaAttnError", "KaAttnUnavailable", "lib", "lib_path", "F32", "BF16",
            "cache_bytes", "alloc_cache", "append_kv", "prefill_workspace_bytes",
            "prefill_chunk", "decode_workspace_bytes", "decode", "status_string",
-           "last_error", "abi_version", "EXPORTED_SYMBOLS"]
+           "last_error", "abi_version", "EXPORTED_SYMBOLS", "decode_step"]
 
 F32 = 0
 BF16 = 1
@@ -30,7 +30,8 @@ _LIB_NAME = "libka_attn.so"
 EXPORTED_SYMBOLS = (
     "ka_attn_abi_version", "ka_attn_cache_bytes", "ka_attn_append_kv",
     "ka_attn_prefill_workspace_bytes", "ka_attn_prefill_chunk",
-    "ka_attn_decode_workspace_bytes", "ka_attn_decode", "ka_attn_status_string",
+    "ka_attn_decode_workspace_bytes", "ka_attn_decode", "ka_attn_decode_step",
+    "ka_attn_status_string",
     "ka_attn_last_error",
 )
 
@@ -102,6 +103,10 @@ def lib() -> ctypes.CDLL:
     L.ka_attn_decode.restype = c_int32
     L.ka_attn_decode.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p,
                                  ctypes.POINTER(c_int32), c_float, c_void_p, c_size_t, c_void_p]
+    L.ka_attn_decode_step.restype = c_int32
+    L.ka_attn_decode_step.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, ctypes.POINTER(c_int32), ctypes.c_float,
+                                      c_void_p, c_size_t, c_void_p]
     L.ka_attn_status_string.restype = ctypes.c_char_p
     L.ka_attn_status_string.argtypes = [c_int32]
     L.ka_attn_last_error.restype = ctypes.c_char_p
@@ -221,3 +226,27 @@ def decode(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.
     _check(lib().ka_attn_decode(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                 _ptr(out), arr, float(scale), _ptr(workspace), ws_bytes,
                                 _stream(stream)))
+
+
+def decode_step(shape: Shape, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                k_cache: torch.Tensor, v_cache: torch.Tensor, out: torch.Tensor,
+                pos: Sequence[int], scale: float, workspace: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    """Append one K/V row per session at pos[b] and decode the query there
+    (ka_attn_decode_step).  k_new, v_new: f32 [B][Hkv][D]; q, out: [B][Hq][D]."""
+    n = shape.batch * shape.num_q_heads * shape.head_dim
+    nk = shape.batch * shape.num_kv_heads * shape.head_dim
+    _need(q, "q", torch.float32, n)
+    _need(out, "out", torch.float32, n)
+    _need(k_new, "k_new", torch.float32, nk)
+    _need(v_new, "v_new", torch.float32, nk)
+    if len(pos) != shape.batch:
+        raise ValueError(f"pos has {len(pos)} entries, expected {shape.batch}")
+    arr = (ctypes.c_int32 * shape.batch)(*[int(p) for p in pos])
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", None)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().ka_attn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                     _ptr(k_cache), _ptr(v_cache), _ptr(out), arr, float(scale),
+                                     _ptr(workspace), ws_bytes, _stream(stream)))

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "ka_attn.h"
 #include "ka_launch.h"
@@ -162,9 +163,42 @@ ka_status ka_attn_decode(const ka_attn_shape* s, const float* q, const void* k_c
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(KA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.workspace_bytes,
                 workspace ? workspace_bytes : (size_t)0);
-  hipError_t e = ka::launch_decode(sh, plan, q, k_cache, v_cache, out, ctx_len, scale, workspace,
+  hipError_t e = ka::launch_decode(sh, plan, q, const_cast<void*>(k_cache),
+                                   const_cast<void*>(v_cache), out, ctx_len, scale, workspace,
                                    reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return ok();
+}
+
+ka_status ka_attn_decode_step(const ka_attn_shape* s, const float* q, const float* k_new,
+                              const float* v_new, void* k_cache, void* v_cache, float* out,
+                              const int32_t* pos, float scale, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  if (!pos) return fail(KA_ERR_INVALID_ARGUMENT, "pos is NULL");
+  std::vector<int32_t> ctx(sh.batch);
+  int max_ctx = 0;
+  for (int b = 0; b < sh.batch; ++b) {
+    if (pos[b] < 0 || pos[b] >= sh.capacity)
+      return fail(KA_ERR_OUT_OF_RANGE, "pos[%d] = %d outside 0..capacity-1 (%d)", b, pos[b],
+                  sh.capacity - 1);
+    ctx[b] = pos[b] + 1;
+    if (ctx[b] > max_ctx) max_ctx = ctx[b];
+  }
+  if ((st = check_scale(scale)) != KA_OK) return st;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if ((const void*)q == (const void*)out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "out must not alias q");
+  const ka::DecodePlan plan = ka::plan_decode(sh, max_ctx);
+  if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
+    return fail(KA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.workspace_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  hipError_t e = ka::launch_decode(sh, plan, q, k_cache, v_cache, out, ctx.data(), scale,
+                                   workspace, reinterpret_cast<hipStream_t>(stream), k_new, v_new);
+  if (e != hipSuccess) return hip_fail(e, "decode step launch");
   return ok();
 }
 

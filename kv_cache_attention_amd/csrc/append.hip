@@ -129,4 +129,75 @@ hipError_t launch_append(const Shape& s, void* k_cache, void* v_cache, const flo
   return hipGetLastError();
 }
 
+// One new row per session at its own position (the decode step's append):
+// k_new / v_new [B][Hkv][D] f32 -> cache position pos[b].  Thread i writes
+// one K vector or one V element (a V vector spans E positions, so only the
+// row's own element of it is stored).
+template <bool BF16>
+__global__ __launch_bounds__(256) void append_row_kernel(
+    void* __restrict__ k_cache, void* __restrict__ v_cache, const float* __restrict__ k_new,
+    const float* __restrict__ v_new, const CtxArg pos, int b0, int nb, int Hkv, int D, int C) {
+  constexpr int E = Elem<BF16>::E;
+  const int cpr = D / E;
+  const long long nk = (long long)nb * Hkv * cpr, nv = (long long)nb * Hkv * D;
+  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nk + nv;
+       i += (long long)gridDim.x * blockDim.x) {
+    if (i < nk) {
+      const int c = (int)(i % cpr);
+      const long long t = i / cpr;
+      const int g = (int)(t % Hkv), bl = (int)(t / Hkv), b = b0 + bl;
+      const int j = pos.ctx[bl];
+      const float* src = k_new + ((size_t)b * Hkv + g) * D + c * E;
+      const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;
+      const size_t vi = k_vec_index(j, c, D, E);
+      if constexpr (BF16) {
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 bq = *reinterpret_cast<const float4*>(src + 4);
+        uint4 o;
+        o.x = pack_bf16x2(a.x, a.y);
+        o.y = pack_bf16x2(a.z, a.w);
+        o.z = pack_bf16x2(bq.x, bq.y);
+        o.w = pack_bf16x2(bq.z, bq.w);
+        reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_cache) + slab)[vi] = o;
+      } else {
+        reinterpret_cast<float4*>(reinterpret_cast<float*>(k_cache) + slab)[vi] =
+            *reinterpret_cast<const float4*>(src);
+      }
+    } else {
+      const long long iv = i - nk;
+      const int d = (int)(iv % D);
+      const long long t = iv / D;
+      const int g = (int)(t % Hkv), bl = (int)(t / Hkv), b = b0 + bl;
+      const int j = pos.ctx[bl];
+      const float x = v_new[((size_t)b * Hkv + g) * D + d];
+      const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;
+      if constexpr (BF16) {
+        uint16_t* base = reinterpret_cast<uint16_t*>(v_cache) + slab;
+        base[((size_t)vbf16_group(j) * D + d) * 8 + vbf16_slot(j)] = (uint16_t)f32_to_bf16_bits(x);
+      } else {
+        float* base = reinterpret_cast<float*>(v_cache) + slab;
+        base[vf32_vec_index(j, d, D) * 4 + (j & 3)] = x;
+      }
+    }
+  }
+}
+
+hipError_t launch_append_rows(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
+                              const float* v_new, const CtxArg& pos, int b0, int nb,
+                              hipStream_t stream) {
+  const int E = s.kv_dtype == 1 ? 8 : 4;
+  const long long total = (long long)nb * s.num_kv_heads * (s.head_dim / E + s.head_dim);
+  long long blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (s.kv_dtype == 1)
+    hipLaunchKernelGGL(append_row_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       k_cache, v_cache, k_new, v_new, pos, b0, nb, s.num_kv_heads, s.head_dim,
+                       s.capacity);
+  else
+    hipLaunchKernelGGL(append_row_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       k_cache, v_cache, k_new, v_new, pos, b0, nb, s.num_kv_heads, s.head_dim,
+                       s.capacity);
+  return hipGetLastError();
+}
+
 }  // namespace ka

@@ -358,9 +358,10 @@ void decode_split_kernel(
 }
 
 // Combines the S split partials of one (session, KV head, head group) for
-// one head and 32 dims.  Thread (d, r) sums splits r, r + 8, ... with all its
-// loads in flight; the eight partial sums are then added in a fixed order, so
-// the result does not depend on timing.
+// one head and 32 dims.  Thread (d, r) sums splits r, r + 8, ...; the loads
+// of its first 16 splits go out together with the (m, l) loads, so the merge
+// waits on memory about once.  The eight partial sums are added in a fixed
+// order, so the result does not depend on timing.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
@@ -369,6 +370,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   __shared__ float red[8][32];
   __shared__ float wmax[4], wsum[4];
   constexpr int NS = D / 32;
+  constexpr int EARLY = 16;
   const int h = blockIdx.x / NS, ds = blockIdx.x % NS;
   const int gh = blockIdx.y, bl = blockIdx.z, b = b0 + bl;
   const int g = gh / HG, hg = gh % HG;
@@ -376,39 +378,54 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int gq = b * (Hkv * HG) + gh;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float* ml = part_ml + ((size_t)gq * hpw + h) * S * 2;
+  const int dl = tid & 31, r = tid >> 5;
+  const int d = ds * 32 + dl;
+  const float* pa = part + ((size_t)gq * S * hpw + h) * D + d;
+  const size_t PS = (size_t)hpw * D;
+  float av[EARLY];
+#pragma unroll
+  for (int k = 0; k < EARLY; ++k) {
+    const int s = r + 8 * k;
+    av[k] = s < S ? pa[(size_t)s * PS] : 0.f;
+  }
+  // (m, l) of splits tid, tid + 256, ... (S <= kMaxSplits = 4 * 256)
+  float mv[kMaxSplits / 256], lv[kMaxSplits / 256];
+#pragma unroll
+  for (int j = 0; j < kMaxSplits / 256; ++j) {
+    const int s = tid + 256 * j;
+    mv[j] = s < S ? ml[2 * s] : -INFINITY;
+    lv[j] = s < S ? ml[2 * s + 1] : 0.f;
+  }
   // M = max_s m_s over the block, then w_s = 2^(m_s - M), L = sum_s w_s l_s
   float M = -INFINITY;
-  for (int s = tid; s < S; s += 256) M = fmaxf(M, ml[2 * s]);
+#pragma unroll
+  for (int j = 0; j < kMaxSplits / 256; ++j) M = fmaxf(M, mv[j]);
   M = group_max<64>(M);
   if (lane == 0) wmax[w] = M;
   __syncthreads();
   M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
   float L = 0.f;
-  for (int s = tid; s < S; s += 256) {
-    const float ms = ml[2 * s];
-    const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-    wgt[s] = f;
-    L += f * ml[2 * s + 1];
+#pragma unroll
+  for (int j = 0; j < kMaxSplits / 256; ++j) {
+    const int s = tid + 256 * j;
+    if (s < S) {
+      const float f = mv[j] == -INFINITY ? 0.f : fast_exp2(mv[j] - M);
+      wgt[s] = f;
+      L += f * lv[j];
+    }
   }
   L = group_sum<64>(L);
   if (lane == 0) wsum[w] = L;
   __syncthreads();
   L = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
   // weighted sum of the accumulators
-  const int dl = tid & 31, r = tid >> 5;
-  const int d = ds * 32 + dl;
-  const float* pa = part + ((size_t)gq * S * hpw + h) * D + d;
-  const size_t PS = (size_t)hpw * D;
   float a = 0.f;
-  int s = r;
-  for (; s + 56 < S; s += 64) {
-    float v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = pa[(size_t)(s + 8 * j) * PS];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) a += wgt[s + 8 * j] * v[j];
+  for (int k = 0; k < EARLY; ++k) {
+    const int s = r + 8 * k;
+    if (s < S) a += wgt[s] * av[k];
   }
-  for (; s < S; s += 8) a += wgt[s] * pa[(size_t)s * PS];
+  for (int s = r + 8 * EARLY; s < S; s += 8) a += wgt[s] * pa[(size_t)s * PS];
   red[r][dl] = a;
   __syncthreads();
   if (r == 0) {
@@ -454,9 +471,9 @@ struct DecTile {
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(
-    const float* __restrict__ q, const void* __restrict__ k_cache,
-    const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
-    float* __restrict__ part_ml, const CtxArg ctxa, int b0, int Hq, int Hkv, int HG, int hpw,
+    const float* __restrict__ q, void* k_cache, void* v_cache, float* __restrict__ out,
+    float* __restrict__ part, float* __restrict__ part_ml, const float* __restrict__ k_new,
+    const float* __restrict__ v_new, const CtxArg ctxa, int b0, int Hq, int Hkv, int HG, int hpw,
     int C, int S, float sl2e) {
   typedef __attribute__((ext_vector_type(4))) float v4f;
   __shared__ float sacc[kWaves][kDecCols * D];
@@ -534,8 +551,74 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   // One tile; x is reloaded with tile t + 2 once its operands are consumed.
+  // The decode step's new row (position ctx - 1, given by k_new / v_new).
+  // The wave whose turn covers its tile rounds it exactly as the append
+  // kernel rounds, writes it to the cache at once (its loads overlap the
+  // first tiles) and keeps the bf16 row in its LDS merge slot, idle until the
+  // end; when it reaches that tile it uses those values in place of what its
+  // loads of the tile brought in.  No other wave touches that position.
+  const int p_new = ctx - 1, t_new = p_new / kDecTile;
+  const bool owns_new = k_new != nullptr && t_new % NW == j0;
+  uint16_t* row_lds = reinterpret_cast<uint16_t*>(sacc[w]);  // [K row D][V row D] bf16
+  if (owns_new) {
+    const size_t slab_el = ((size_t)b * Hkv + g) * (size_t)C * D;
+    const float* kn = k_new + ((size_t)b * Hkv + g) * D;
+    const float* vn = v_new + ((size_t)b * Hkv + g) * D;
+    uint4* kw = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_cache) + slab_el);
+    uint16_t* vw = reinterpret_cast<uint16_t*>(v_cache) + slab_el;
+    const int gv = vbf16_group(p_new), e = vbf16_slot(p_new);
+    for (int c = lane; c < D / 8; c += 64) {  // K: one 8-dim vector per lane
+      const float4 x0 = *reinterpret_cast<const float4*>(kn + 8 * c);
+      const float4 x1 = *reinterpret_cast<const float4*>(kn + 8 * c + 4);
+      const uint4 o = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
+                                 pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
+      kw[k_vec_index(p_new, c, D, 8)] = o;
+      reinterpret_cast<uint4*>(row_lds)[c] = o;
+    }
+    for (int d = lane; d < D; d += 64) {  // V: the row's element of each vector
+      const uint16_t h = (uint16_t)f32_to_bf16_bits(vn[d]);
+      vw[((size_t)gv * D + d) * 8 + e] = h;
+      row_lds[D + d] = h;
+    }
+  }
+  auto take_new_row = [&](DecTile<D>& x) {
+    const int kp = p_new - kDecTile * t_new;
+    if (lc == (kp & 15)) {
+      const bool hi = (kp >> 4) != 0;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const uint4 o = reinterpret_cast<const uint4*>(row_lds)[4 * ks + r];
+        // 32-bit selects: a branch on the block index would index the
+        // register arrays at run time
+        x.k[0][ks].x = hi ? x.k[0][ks].x : o.x;
+        x.k[0][ks].y = hi ? x.k[0][ks].y : o.y;
+        x.k[0][ks].z = hi ? x.k[0][ks].z : o.z;
+        x.k[0][ks].w = hi ? x.k[0][ks].w : o.w;
+        x.k[1][ks].x = hi ? o.x : x.k[1][ks].x;
+        x.k[1][ks].y = hi ? o.y : x.k[1][ks].y;
+        x.k[1][ks].z = hi ? o.z : x.k[1][ks].z;
+        x.k[1][ks].w = hi ? o.w : x.k[1][ks].w;
+      }
+    }
+    if (r == vbf16_group(p_new) - 4 * t_new) {
+      const int e = vbf16_slot(p_new);
+      // slot e of each register vector: half (e & 1) of 32-bit word e / 2
+      const uint32_t sh = (e & 1) * 16, keep = ~(0xffffu << sh);
+      const int wd = e >> 1;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        const uint32_t put = (uint32_t)row_lds[D + 16 * db + lc] << sh;
+        x.v[db].x = wd == 0 ? (x.v[db].x & keep) | put : x.v[db].x;
+        x.v[db].y = wd == 1 ? (x.v[db].y & keep) | put : x.v[db].y;
+        x.v[db].z = wd == 2 ? (x.v[db].z & keep) | put : x.v[db].z;
+        x.v[db].w = wd == 3 ? (x.v[db].w & keep) | put : x.v[db].w;
+      }
+    }
+  };
+
   auto tile = [&](DecTile<D>& x, int i) {
     const int t = j0 + i * NW;
+    if (owns_new && t == t_new) take_new_row(x);
     v4f sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -740,10 +823,10 @@ DecodePlan plan_decode(const Shape& s, int max_ctx) {
   return p;
 }
 
-hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q,
-                         const void* k_cache, const void* v_cache, float* out,
-                         const int32_t* ctx_host, float scale, void* workspace,
-                         hipStream_t stream) {
+hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, void* k_cache,
+                         void* v_cache, float* out, const int32_t* ctx_host, float scale,
+                         void* workspace, hipStream_t stream, const float* k_new,
+                         const float* v_new) {
   const bool bf16 = s.kv_dtype == 1;
   const float sl2e = scale * kLog2e;
   const int HG = p.head_groups, S = p.splits;
@@ -753,6 +836,13 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q,
     CtxArg ca;
     for (int i = 0; i < kMaxDecodeBatchPerLaunch; ++i) ca.ctx[i] = i < nb ? ctx_host[b0 + i] : 0;
     dim3 grid(S, s.num_kv_heads * HG, nb);
+    if (k_new != nullptr && !bf16) {
+      // f32 caches: the new rows go in first, by their own kernel
+      CtxArg pos;
+      for (int i = 0; i < kMaxDecodeBatchPerLaunch; ++i) pos.ctx[i] = i < nb ? ca.ctx[i] - 1 : 0;
+      const hipError_t e = launch_append_rows(s, k_cache, v_cache, k_new, v_new, pos, b0, nb, stream);
+      if (e != hipSuccess) return e;
+    }
     switch (s.head_dim) {
 #define KA_D(DD)                                                                               \
   case DD:                                                                                     \
@@ -760,7 +850,8 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q,
       hipLaunchKernelGGL((decode_mfma_kernel<DD>), grid, dim3(256), 0, stream, q, k_cache,     \
                          v_cache, out, part,                                                   \
                          part + (size_t)s.batch * s.num_kv_heads * HG * S * p.heads_per_wg * DD, \
-                         ca, b0, s.num_q_heads, s.num_kv_heads, HG, p.heads_per_wg,            \
+                         k_new, v_new, ca, b0, s.num_q_heads, s.num_kv_heads, HG,              \
+                         p.heads_per_wg,                                                       \
                          s.capacity, S, sl2e);                                                 \
     else dispatch_hpw<DD, false>(p.heads_per_wg, grid, stream, q, k_cache, v_cache, out, part, \
                                  ca, b0, s, HG, S, sl2e);                                      \

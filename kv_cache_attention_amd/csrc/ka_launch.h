@@ -22,6 +22,10 @@ struct CtxArg {
 
 hipError_t launch_append(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
                          const float* v_new, int start, int R, hipStream_t stream);
+// One row per session at position pos.ctx[b - b0], sessions b0 .. b0 + nb - 1.
+hipError_t launch_append_rows(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
+                              const float* v_new, const CtxArg& pos, int b0, int nb,
+                              hipStream_t stream);
 
 // ---- prefill
 struct PrefillPlan {
@@ -43,9 +47,12 @@ struct DecodePlan {
   size_t workspace_bytes;
 };
 DecodePlan plan_decode(const Shape& s, int max_ctx);
-hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q,
-                         const void* k_cache, const void* v_cache, float* out,
-                         const int32_t* ctx_host, float scale, void* workspace,
-                         hipStream_t stream);
+// k_new / v_new (optional, [B][Hkv][D] f32): the decode step's new rows, at
+// position ctx - 1 of each session; they are appended before they are
+// attended to (fused into the attention kernel for bf16 caches).
+hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, void* k_cache,
+                         void* v_cache, float* out, const int32_t* ctx_host, float scale,
+                         void* workspace, hipStream_t stream, const float* k_new = nullptr,
+                         const float* v_new = nullptr);
 
 }  // namespace ka

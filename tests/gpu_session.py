@@ -59,6 +59,16 @@ class DevCaches:
         torch.cuda.synchronize()
         return out.cpu().numpy()
 
+    def decode_step(self, q, k_new, v_new, pos, scale):
+        """q: [B][Hq][D], k_new / v_new: [B][Hkv][D] float32 -> out [B][Hq][D]."""
+        qt = dev(q)
+        out = torch.full_like(qt, float("nan"))
+        ws = self.workspace(ka.decode_workspace_bytes(self.shape, max(pos) + 1))
+        ka.decode_step(self.shape, qt, dev(k_new), dev(v_new), self.k, self.v, out, list(pos),
+                       scale, ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
     def raw(self):
         torch.cuda.synchronize()
         return self.k.cpu().numpy(), self.v.cpu().numpy()

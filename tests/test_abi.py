@@ -30,7 +30,7 @@ def header_functions():
 
 def test_header_declares_the_entry_points():
     names = header_functions()
-    for n in ["ka_attn_append_kv", "ka_attn_prefill_chunk", "ka_attn_decode",
+    for n in ["ka_attn_append_kv", "ka_attn_prefill_chunk", "ka_attn_decode", "ka_attn_decode_step",
               "ka_attn_decode_workspace_bytes", "ka_attn_prefill_workspace_bytes",
               "ka_attn_cache_bytes", "ka_attn_status_string", "ka_attn_last_error",
               "ka_attn_abi_version"]:
@@ -138,6 +138,29 @@ def test_decode_argument_errors():
     assert need > 0
     assert _decode(s, [4096, 10]) == 4
     assert _decode(s, [4096, 10], ws=FAKE, ws_bytes=need - 1) == 4
+
+
+def _step(shape, pos, scale=0.0625, ws=None, ws_bytes=0, q=FAKE, out=ctypes.c_void_p(0x2000)):
+    arr = (ctypes.c_int32 * len(pos))(*pos)
+    return ka.lib().ka_attn_decode_step(ctypes.byref(shape), q, FAKE, FAKE, FAKE, FAKE, out, arr,
+                                        scale, ws, ws_bytes, None)
+
+
+def test_decode_step_argument_errors():
+    _lib_or_skip()
+    s = S(batch=2)
+    assert _step(s, [0, 4096]) == 2          # pos is a position: 0 .. C - 1
+    assert _step(s, [-1, 3]) == 2
+    assert _step(s, [5, 5], scale=float("nan")) == 1
+    assert _step(s, [5, 5], q=None) == 1
+    assert _step(s, [5, 5], out=FAKE) == 1   # out aliases q
+    assert ka.lib().ka_attn_decode_step(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        ctypes.c_void_p(0x2000), None, 0.1, None, 0, None) == 1
+    need = ka.decode_workspace_bytes(s, 4096)
+    assert need > 0
+    assert _step(s, [4095, 10]) == 4
+    assert _step(s, [4095, 10], ws=FAKE, ws_bytes=need - 1) == 4
+    assert "workspace" in ka.last_error()
 
 
 def test_workspace_sizes_cover_smaller_requests():

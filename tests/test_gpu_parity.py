@@ -291,6 +291,54 @@ def test_decode_nan_value_reaches_only_its_dimension():
         assert oracle.rel_error(out[fin], ref[fin], vs[:, :200]) <= TOL[dt]
 
 
+DECODE_STEP_CASES = [
+    # dt, B, Hq, Hkv, D, C, per-session positions of the new row
+    ("bf16", 1, 8, 1, 256, 4160, [4096]),
+    ("bf16", 3, 16, 1, 128, 640, [0, 31, 600]),
+    ("bf16", 2, 3, 1, 64, 192, [32, 63]),
+    ("bf16", 2, 8, 2, 256, 1024, [64, 1000]),
+    ("f32", 2, 8, 1, 128, 512, [5, 300]),
+    ("f32", 1, 4, 2, 64, 128, [0]),
+]
+
+
+@pytest.mark.parametrize("case", DECODE_STEP_CASES,
+                         ids=lambda c: "-".join(map(str, c[:6])) + "-" + "_".join(map(str, c[6])))
+def test_decode_step_appends_then_decodes(case):
+    """ka_attn_decode_step: the new rows land in the cache bit for bit as
+    appended rows would, the output matches the oracle, and it is bitwise the
+    output of a plain decode of the cache it leaves behind."""
+    dt, B, Hq, Hkv, D, C, pos = case
+    P = max(pos) + 1
+    c = random_case(sum(pos) + D, B, Hq, Hkv, D, P, 1)
+    rng = np.random.default_rng(7 + B)
+    k_new = rng.standard_normal((B, Hkv, D), dtype=np.float32)
+    v_new = rng.standard_normal((B, Hkv, D), dtype=np.float32)
+    q = c.q[:, 0]                                      # [B][Hq][D]
+    caches = DevCaches(B, Hq, Hkv, D, C, dt)
+    caches.append(c.k, c.v, 0)                         # rows 0 .. P-1 (new rows overwrite)
+    got = caches.decode_step(q, k_new, v_new, pos, 0.0625)
+    # the cache as an append of the new rows would leave it
+    k_all, v_all = c.k.copy(), c.v.copy()
+    for b, p in enumerate(pos):
+        k_all[b, p], v_all[b, p] = k_new[b], v_new[b]
+    kb, vb = caches.bits()                             # [B][Hkv][C][D]
+    for b, p in enumerate(pos):
+        for name, got_bits, src in (("k", kb, k_all), ("v", vb, v_all)):
+            row = src[b, p]                            # [Hkv][D]
+            if dt == "bf16":
+                assert np.array_equal(got_bits[b, :, p], obf16.encode_rne(row)), (name, b)
+            else:
+                assert np.array_equal(got_bits[b, :, p].view(np.uint32), row.view(np.uint32)), (name, b)
+    # oracle: each session's row at its position, over its own context
+    ks, vs = _stored(k_all, dt), _stored(v_all, dt)
+    for b, p in enumerate(pos):
+        ref = oracle.decode(q[b:b + 1], ks[b:b + 1, :p + 1], vs[b:b + 1, :p + 1], [p + 1], 0.0625)
+        _check(got[b:b + 1], ref, vs[b:b + 1, :p + 1], dt, f"decode step {case} session {b}")
+    again = caches.decode(q, [p + 1 for p in pos], 0.0625)
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+
+
 def test_rejected_call_leaves_output_untouched():
     caches = DevCaches(1, 8, 1, 256, 4096, ka.BF16)
     q = torch.zeros(8 * 256, device="cuda")
