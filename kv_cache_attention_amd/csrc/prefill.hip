@@ -1001,62 +1001,69 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
 
 // Combines the S split partials of 16 columns of one M-tile.  Thread (c, v)
 // owns column c and the float4 dims 4 v + 64 j; splits are summed in order.
+// The accumulator loads of the first kEarly splits are issued together with
+// the (m, l) loads, so the kernel waits for one memory round trip, not two.
+constexpr int kEarly = 8;
+
 template <int D>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(
     const float* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
     int Hq, int Hkv, int R, int m_tiles, int S) {
-  __shared__ float wgt[16][kMaxSplits];
-  __shared__ float inv_l[16];
+  constexpr int J = D / 64;
   const int mt = blockIdx.x >> 3, cg = blockIdx.x & 7;
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int M_total = R * G;
   const int tid = threadIdx.x;
   const size_t tile_id = ((size_t)b * Hkv + g) * m_tiles + mt;
-  if (tid < 16) {
-    const float* ml = part_ml + (tile_id * kMTile + cg * 16 + tid) * S * 2;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
-    float L = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float f = ml[2 * s] == -INFINITY ? 0.f : fast_exp2(ml[2 * s] - M);
-      wgt[tid][s] = f;
-      L += f * ml[2 * s + 1];
-    }
-    inv_l[tid] = 1.f / L;
-  }
-  __syncthreads();
   const int c = tid >> 4, v = tid & 15;
   const int col = cg * 16 + c;
   const int m = mt * kMTile + col;
   if (m >= M_total) return;
-  const int row = m / G, hh = m % G;
-  float* op = out + (((size_t)b * R + row) * Hq + g * G + hh) * D;
-  const float* pc = part + (tile_id * S * kMTile + col) * D;
+  const float* ml = part_ml + (tile_id * kMTile + col) * S * 2;
+  const float* pc = part + (tile_id * S * kMTile + col) * D + 4 * v;
   const size_t PS = (size_t)kMTile * D;  // stride between splits
-  const float il = inv_l[c];
+  float4 early[kEarly][J];
 #pragma unroll
-  for (int j = 0; j < D / 64; ++j) {
-    const int d = 4 * v + 64 * j;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    int s = 0;
-    for (; s + 8 <= S; s += 8) {
-      float4 t[8];
+  for (int k = 0; k < kEarly; ++k)
+    if (k < S)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) t[k] = *reinterpret_cast<const float4*>(pc + (s + k) * PS + d);
+      for (int j = 0; j < J; ++j) early[k][j] = *reinterpret_cast<const float4*>(pc + k * PS + 64 * j);
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+  float4 a[J];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float f = wgt[c][s + k];
-        a.x += f * t[k].x; a.y += f * t[k].y; a.z += f * t[k].z; a.w += f * t[k].w;
-      }
+  for (int j = 0; j < J; ++j) a[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+  auto add = [&](float f, const float4 (&t)[J]) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      a[j].x += f * t[j].x; a[j].y += f * t[j].y; a[j].z += f * t[j].z; a[j].w += f * t[j].w;
     }
-    for (; s < S; ++s) {
-      const float f = wgt[c][s];
-      const float4 t = *reinterpret_cast<const float4*>(pc + s * PS + d);
-      a.x += f * t.x; a.y += f * t.y; a.z += f * t.z; a.w += f * t.w;
+  };
+#pragma unroll
+  for (int k = 0; k < kEarly; ++k) {
+    if (k < S) {
+      const float f = ml[2 * k] == -INFINITY ? 0.f : fast_exp2(ml[2 * k] - M);
+      L += f * ml[2 * k + 1];
+      add(f, early[k]);
     }
-    *reinterpret_cast<float4*>(op + d) = make_float4(a.x * il, a.y * il, a.z * il, a.w * il);
   }
+  for (int s = kEarly; s < S; ++s) {
+    float4 t[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) t[j] = *reinterpret_cast<const float4*>(pc + s * PS + 64 * j);
+    const float f = ml[2 * s] == -INFINITY ? 0.f : fast_exp2(ml[2 * s] - M);
+    L += f * ml[2 * s + 1];
+    add(f, t);
+  }
+  const float il = 1.f / L;
+  const int row = m / G, hh = m % G;
+  float* op = out + (((size_t)b * R + row) * Hq + g * G + hh) * D + 4 * v;
+#pragma unroll
+  for (int j = 0; j < J; ++j)
+    *reinterpret_cast<float4*>(op + 64 * j) =
+        make_float4(a[j].x * il, a[j].y * il, a[j].z * il, a[j].w * il);
 }
 
 // Split count of a chunk: the one that minimises a model of the launch time.
