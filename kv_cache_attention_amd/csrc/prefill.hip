@@ -23,6 +23,7 @@
 // a row's causal limit are masked; tiles above every row's limit are not
 // visited.  Positions at or beyond start + R are zeroed in LDS so that
 // whatever the cache holds there cannot reach a result.
+#include <cfloat>
 #include <type_traits>
 
 #include "ka_common.h"
@@ -596,6 +597,7 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
 // LDS buffers.
 // ============================================================================
 typedef __attribute__((ext_vector_type(16))) float v16f;
+typedef __attribute__((ext_vector_type(4))) _Float16 half4;
 
 // Both lane halves' values: lane l receives (x of lane l % 32, x of lane
 // l % 32 + 32), with v_permlane32_swap (no LDS traffic).
@@ -807,22 +809,39 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c,
             make_float4(acc_o[db][4 * a] * inv, acc_o[db][4 * a + 1] * inv,
                         acc_o[db][4 * a + 2] * inv, acc_o[db][4 * a + 3] * inv);
   } else {
-    // acc [tile][S][128 columns][D]; (m, l) [tile][128 columns][S][2]
+    // acc [tile][S][128 columns][D] as binary16, each lane's 8 D / 32 values
+    // scaled by 2^-e so that the largest finite one lies in [0.5, 1);
+    // (m, l, e of lane half 0, e of lane half 1) [tile][128 columns][S][4].
+    // Rounding adds at most 2^-12 of the lane's largest value.
     const size_t tile_id = ((size_t)t.b * Hkv + t.g) * m_tiles + t.mt;
     const int col = c.m - t.m_base;
-    float* pp = part + ((tile_id * S + t.split) * kMTile + col) * D;
+    float amax = 0.f;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<float4*>(pp + 32 * db + 8 * a + 4 * c.lh) =
-            make_float4(acc_o[db][4 * a], acc_o[db][4 * a + 1], acc_o[db][4 * a + 2],
-                        acc_o[db][4 * a + 3]);
+      for (int i = 0; i < 16; ++i) {
+        const float x = fabsf(acc_o[db][i]);
+        amax = x <= FLT_MAX ? fmaxf(amax, x) : amax;  // finite values only
+      }
+    int e = 0;
+    if (amax > 0.f) (void)frexpf(amax, &e);
+    const float sc = ldexpf(1.f, -e);
+    _Float16* pp = reinterpret_cast<_Float16*>(part) + ((tile_id * S + t.split) * kMTile + col) * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        half4 h;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) h[k] = (_Float16)(acc_o[db][4 * a + k] * sc);
+        *reinterpret_cast<half4*>(pp + 32 * db + 8 * a + 4 * c.lh) = h;
+      }
+    float* ml = part_ml + ((tile_id * kMTile + col) * S + t.split) * 4;
     if (c.lh == 0) {
-      float* ml = part_ml + ((tile_id * kMTile + col) * S + t.split) * 2;
       ml[0] = m_run;
       ml[1] = lt;
     }
+    ml[2 + c.lh] = (float)e;
   }
 }
 
@@ -1003,13 +1022,31 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
 // owns column c and the float4 dims 4 v + 64 j; splits are summed in order.
 // The accumulator loads of the first kEarly splits are issued together with
 // the (m, l) loads, so the kernel waits for one memory round trip, not two.
+// H16: binary16 partials with per-lane exponents (the bf16 kernel's format);
+// otherwise f32 partials with (m, l) pairs.
 constexpr int kEarly = 8;
 
-template <int D>
+template <bool H16>
+struct PartFmt {
+  static constexpr int ML = H16 ? 4 : 2;  // floats per (column, split) record
+};
+
+template <int D, bool H16>
+__device__ __forceinline__ float4 load_part(const void* base, size_t idx) {
+  if constexpr (H16) {
+    const half4 h = *reinterpret_cast<const half4*>(reinterpret_cast<const _Float16*>(base) + idx);
+    return make_float4((float)h[0], (float)h[1], (float)h[2], (float)h[3]);
+  } else {
+    return *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+  }
+}
+
+template <int D, bool H16>
 __global__ __launch_bounds__(256) void prefill_merge_kernel(
-    const float* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
+    const void* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
     int Hq, int Hkv, int R, int m_tiles, int S) {
   constexpr int J = D / 64;
+  constexpr int ML = PartFmt<H16>::ML;
   const int mt = blockIdx.x >> 3, cg = blockIdx.x & 7;
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
@@ -1020,21 +1057,28 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   const int col = cg * 16 + c;
   const int m = mt * kMTile + col;
   if (m >= M_total) return;
-  const float* ml = part_ml + (tile_id * kMTile + col) * S * 2;
-  const float* pc = part + (tile_id * S * kMTile + col) * D + 4 * v;
+  const float* ml = part_ml + (tile_id * kMTile + col) * S * ML;
+  const size_t pc = (tile_id * S * kMTile + col) * D + 4 * v;  // element index
   const size_t PS = (size_t)kMTile * D;  // stride between splits
   float4 early[kEarly][J];
 #pragma unroll
   for (int k = 0; k < kEarly; ++k)
     if (k < S)
 #pragma unroll
-      for (int j = 0; j < J; ++j) early[k][j] = *reinterpret_cast<const float4*>(pc + k * PS + 64 * j);
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+      for (int j = 0; j < J; ++j) early[k][j] = load_part<D, H16>(part, pc + k * PS + 64 * j);
+  float M = -INFINITY, L = 0.f;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[ML * s]);
+  // weight of split s: its frame relative to M, times its lane-half scale
+  // (dims 4 v .. 4 v + 3 were written by lane half v & 1)
+  auto weight = [&](int s) {
+    const float f = ml[ML * s] == -INFINITY ? 0.f : fast_exp2(ml[ML * s] - M);
+    L += f * ml[ML * s + 1];
+    if constexpr (H16) return ldexpf(f, (int)ml[ML * s + 2 + (v & 1)]);
+    else return f;
+  };
   float4 a[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) a[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  float L = 0.f;
   auto add = [&](float f, const float4 (&t)[J]) {
 #pragma unroll
     for (int j = 0; j < J; ++j) {
@@ -1043,19 +1087,13 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   };
 #pragma unroll
   for (int k = 0; k < kEarly; ++k) {
-    if (k < S) {
-      const float f = ml[2 * k] == -INFINITY ? 0.f : fast_exp2(ml[2 * k] - M);
-      L += f * ml[2 * k + 1];
-      add(f, early[k]);
-    }
+    if (k < S) add(weight(k), early[k]);
   }
   for (int s = kEarly; s < S; ++s) {
     float4 t[J];
 #pragma unroll
-    for (int j = 0; j < J; ++j) t[j] = *reinterpret_cast<const float4*>(pc + s * PS + 64 * j);
-    const float f = ml[2 * s] == -INFINITY ? 0.f : fast_exp2(ml[2 * s] - M);
-    L += f * ml[2 * s + 1];
-    add(f, t);
+    for (int j = 0; j < J; ++j) t[j] = load_part<D, H16>(part, pc + s * PS + 64 * j);
+    add(weight(s), t);
   }
   const float il = 1.f / L;
   const int row = m / G, hh = m % G;
@@ -1106,8 +1144,12 @@ hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const 
                     const void* vc, float* out, int start, int R, float scale, void* ws,
                     hipStream_t st) {
   using Cfg = PrefillCfg<D, BF16>;
+  // partials: binary16 accumulators for bf16 caches, f32 otherwise; then the
+  // per-(column, split) records
   float* part = reinterpret_cast<float*>(ws);
-  float* part_ml = part + (size_t)s.batch * s.num_kv_heads * p.m_tiles * p.splits * kMTile * D;
+  float* part_ml = reinterpret_cast<float*>(
+      reinterpret_cast<unsigned char*>(ws) +
+      (size_t)s.batch * s.num_kv_heads * p.m_tiles * p.splits * kMTile * D * (BF16 ? 2 : 4));
   // padded to whole rounds of the 8 XCDs (see make_tiling)
   dim3 grid(8 * ((p.m_tiles * p.splits + 7) / 8), s.num_kv_heads, s.batch);
   if constexpr (BF16)
@@ -1125,7 +1167,7 @@ hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.splits > 1) {
-    hipLaunchKernelGGL(prefill_merge_kernel<D>, dim3(p.m_tiles * 8, s.num_kv_heads, s.batch),
+    hipLaunchKernelGGL((prefill_merge_kernel<D, BF16>), dim3(p.m_tiles * 8, s.num_kv_heads, s.batch),
                        dim3(256), 0, st, part, part_ml, out, s.num_q_heads, s.num_kv_heads, R,
                        p.m_tiles, p.splits);
     e = hipGetLastError();
@@ -1135,6 +1177,13 @@ hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const 
 
 }  // namespace
 
+// Workspace bytes per (column, split): binary16 accumulators and a 4-float
+// record for bf16 caches, f32 accumulators and an (m, l) pair otherwise.
+static size_t partial_bytes(const Shape& s) {
+  return s.kv_dtype == 1 ? (size_t)s.head_dim * 2 + 4 * sizeof(float)
+                         : (size_t)(s.head_dim + 2) * sizeof(float);
+}
+
 PrefillPlan plan_prefill(const Shape& s, int start, int R) {
   PrefillPlan p;
   const int G = s.num_q_heads / s.num_kv_heads;
@@ -1143,8 +1192,7 @@ PrefillPlan plan_prefill(const Shape& s, int start, int R) {
   const int nkt = (start + R - 1) / kNTile + 1;
   p.splits = choose_splits(s, p.m_tiles, nkt);
   p.workspace_bytes = p.splits == 1 ? 0
-      : (size_t)s.batch * s.num_kv_heads * p.m_tiles * p.splits * kMTile *
-            (size_t)(s.head_dim + 2) * sizeof(float);
+      : (size_t)s.batch * s.num_kv_heads * p.m_tiles * p.splits * kMTile * partial_bytes(s);
   return p;
 }
 
@@ -1157,7 +1205,7 @@ size_t prefill_workspace_bound(const Shape& s, int max_rows) {
     const long long units = (long long)s.batch * s.num_kv_heads * mt;
     const int S = max_splits(units);  // choose_splits never exceeds it
     if (S <= 1) continue;
-    const size_t bytes = (size_t)units * S * kMTile * (size_t)(s.head_dim + 2) * sizeof(float);
+    const size_t bytes = (size_t)units * S * kMTile * partial_bytes(s);
     if (bytes > best) best = bytes;
   }
   return best;

@@ -206,6 +206,28 @@ def test_prefill_scores_far_above_the_first_tile(dt):
     _check(got, ref, vs, dt, f"prefill far-above-first-tile {dt}")
 
 
+def test_prefill_split_partials_per_dim_range():
+    """Value dims scaled by 2^-6 .. 2^6 (a different power per dim), a chunk
+    long enough to be split: every dim must keep its own relative accuracy
+    through the split partials, not only accuracy relative to the largest
+    dim (the bf16 kernel stores partials as binary16 with per-lane scales)."""
+    B, Hq, Hkv, D, start, R = 1, 8, 1, 256, 2048, 256
+    C = start + R
+    c = random_case(41, B, Hq, Hkv, D, start + R, R)
+    rng = np.random.default_rng(41)
+    dim_scale = np.ldexp(np.float32(1), rng.integers(-6, 7, size=D)).astype(np.float32)
+    c.v[:] = c.v * dim_scale
+    caches = DevCaches(B, Hq, Hkv, D, C, "bf16")
+    caches.append(c.k, c.v, 0)
+    got = caches.prefill(c.q, start, 1 / 16)
+    ks, vs = _stored(c.k, "bf16"), _stored(c.v, "bf16")
+    ref = oracle.prefill_chunk(c.q, ks, vs, start, 1 / 16)
+    _check(got, ref, vs, "bf16", "prefill per-dim range")
+    per_dim_max = np.abs(vs).max(axis=(0, 1, 2))  # [D]
+    per_dim_err = np.abs(got - ref).max(axis=(0, 1, 2)) / per_dim_max
+    assert per_dim_err.max() <= TOL["bf16"], f"worst per-dim rel err {per_dim_err.max():.3e}"
+
+
 # ------------------------------------------------------------------ decode
 
 def _decode_case(dt, B, Hq, Hkv, D, C, ctxs, seed):
