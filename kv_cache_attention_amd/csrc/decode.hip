@@ -87,7 +87,7 @@ __device__ __forceinline__ void load_unit_k(UnitRegs<D, BF16>& r, int u, int lan
   const int pos = unit_pos(u, kk);
 #pragma unroll
   for (int i = 0; i < R::NCH; ++i)
-    r.k[i] = *reinterpret_cast<const uint4*>(kc + k_vec_index(pos, qd * R::NCH + i, D, E) * E);
+    r.k[i] = load_stream16(kc + k_vec_index(pos, qd * R::NCH + i, D, E) * E);
 }
 
 template <int D, bool BF16>
@@ -102,7 +102,7 @@ __device__ __forceinline__ void load_unit_v(UnitRegs<D, BF16>& r, int u, int lan
     else grp = u * R::NG + gi;
 #pragma unroll
     for (int t = 0; t < R::ND; ++t)
-      r.v[gi][t] = *reinterpret_cast<const uint4*>(vc + ((size_t)grp * D + lane + 64 * t) * E);
+      r.v[gi][t] = load_stream16(vc + ((size_t)grp * D + lane + 64 * t) * E);
   }
 }
 
@@ -461,6 +461,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
 // (or, alone, the output); a second kernel combines the splits.
 // ============================================================================
 constexpr int kDecTile = 32;  // positions per wave tile
+// Buffer-load cache policy of the streamed K / V operands: non-temporal (NT).
+constexpr int kStreamAux = 2;
 constexpr int kDecCols = 16;  // MFMA columns = most heads per workgroup
 
 template <int D>
@@ -501,7 +503,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   const __amdgpu_buffer_rsrc_t vrs =
       buffer_rsrc(reinterpret_cast<const unsigned char*>(v_cache) + slab, slab_bytes);
 
-  // operand loads of this wave's i-th tile, tile j0 + i NW (K layout [C/64][D/8][64][8], V [C/32][4][D][8])
+  // operand loads of this wave's i-th tile, tile j0 + i NW (K layout [C/64][D/8][64][8], V [C/32][4][D][8]);
+  // every cache byte is read once per step, so the loads are marked non-temporal
   auto load = [&](DecTile<D>& x, int i) {
     const int t = j0 + i * NW;
 #pragma unroll
@@ -511,13 +514,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
       for (int ks = 0; ks < D / 32; ++ks)
         x.k[kb][ks] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       krs, (((pos >> 6) * (D / 8) + 4 * ks + r) * 64 + (pos & 63)) * 16, 0, 0));
+                       krs, (((pos >> 6) * (D / 8) + 4 * ks + r) * 64 + (pos & 63)) * 16, 0, kStreamAux));
     }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
       x.v[db] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                     vrs, ((4 * t + r) * D + 16 * db + lc) * 16, 0, 0));
+                     vrs, ((4 * t + r) * D + 16 * db + lc) * 16, 0, kStreamAux));
   };
 
   DecTile<D> ta_, tb_;

@@ -84,6 +84,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 
 // One wave instruction: lane l copies the 16 bytes at byte offset voffset
 // (its own) of the resource to LDS address lds + 16 l (lds wave-uniform).
+// 16-byte load marked non-temporal: data that is read once per call (the
+// decode's streamed cache) need not displace reusable lines.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void* lds, int voffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16,
                                            voffset, 0, 0, 0);
