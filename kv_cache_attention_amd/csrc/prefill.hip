@@ -1,28 +1,31 @@
 // Chunked prefill on MFMA: rows start .. start+R-1 attend causally to the
 // cache of their session.
 //
-// Tiling.  One workgroup (4 waves) owns an M-tile of 128 (row, query head)
-// pairs of one KV head -- for 8 heads per KV head that is 16 consecutive rows
-// x 8 heads -- and a range of 64-position key tiles (one split of the causal
-// key range).  Each K / V tile is staged once in LDS and read by all four
+// Tiling.  One workgroup owns an M-tile of 128 (row, query head) pairs of one
+// KV head -- for 8 heads per KV head that is 16 consecutive rows x 8 heads --
+// and a range of 64-position key tiles (one split of the causal key range).
+// Each K / V tile is staged once in LDS and read by all the workgroup's
 // waves, so every K / V row is fetched once per M-tile, i.e. once per 128 / G
-// chunk rows and shared by every query head of the group.  Each wave owns 32
-// of the 128 M columns.
+// chunk rows and shared by every query head of the group.  bf16 caches: 8
+// waves on v_mfma_f32_32x32x16_bf16 (Q and P rounded to bf16, f32
+// accumulation); f32 caches: 4 waves on v_mfma_f32_16x16x4_f32, each owning
+// 32 of the 128 M columns.
 //
-// Products.  Scores are computed transposed, S^T = K . Q^T (M = 16 keys,
-// N = 16 (row, head) pairs), and values as O^T = V^T . P^T (M = 16 dims).  In
-// the MFMA accumulator layout a lane then holds one (row, head) column and 4
-// keys / dims, so the running max, the running sum and the rescale of the
-// accumulator are lane-local, and the exponentiated S^T registers are
-// already the B operand of the value product: the V layout groups positions
-// {4s..4s+3, 16+4s..16+4s+3} of a 32-block exactly as a lane group holds
-// them.  bf16 caches use v_mfma_f32_16x16x32_bf16 with Q and P rounded to
-// bf16 and f32 accumulation; f32 caches use v_mfma_f32_16x16x4_f32.
+// Products.  Scores are computed transposed, S^T = K . Q^T (M = keys,
+// N = (row, head) pairs), and values as O^T = V^T . P^T (M = dims).  In the
+// MFMA accumulator layout a lane then holds one (row, head) column and a set
+// of keys / dims, so the running max, the running sum and any rescale of the
+// accumulator are lane-local, and the exponentiated S^T registers are already
+// the B operand of the value product: the V layouts group positions exactly
+// as a lane holds them.
 //
 // Softmax.  Online (flash-style) in f32, log2 domain.  Only tiles that cross
 // a row's causal limit are masked; tiles above every row's limit are not
 // visited.  Positions at or beyond start + R are zeroed in LDS so that
 // whatever the cache holds there cannot reach a result.
+//
+// Splits.  When the key range is split, each split writes a partial (m, l,
+// acc) and a second kernel combines them in fixed split order.
 #include <cfloat>
 #include <type_traits>
 
@@ -37,7 +40,7 @@ constexpr int kMTile = 128;
 constexpr int kNTile = 64;
 constexpr int kMaxSplits = 64;
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay below 256
-constexpr float kFrameSlack = 32.f;   // log2 units (bf16 path, see fused_step_b)
+constexpr float kFrameSlack = 32.f;   // log2 units (bf16 path, see prefill_bf16_kernel)
 
 typedef __attribute__((ext_vector_type(4))) float v4f;
 
@@ -69,13 +72,13 @@ __device__ __forceinline__ TileSrc tile_src(const void* slab, size_t bytes) {
 // Asynchronous copy of tile `tile` (TILE_BYTES contiguous bytes of the slab)
 // into LDS: every wave instruction moves 1 KiB, lane l's 16 bytes landing at
 // the wave's LDS base + 16 l.
-template <int TILE_BYTES>
+template <int TILE_BYTES, int NT = 256>
 __device__ __forceinline__ void load_tile(const TileSrc& src, int tile, unsigned char* dst, int w,
                                           int lane) {
-  constexpr int PER_THREAD = TILE_BYTES / (256 * 16);
+  constexpr int PER_THREAD = TILE_BYTES / (NT * 16);
 #pragma unroll
   for (int i = 0; i < PER_THREAD; ++i) {
-    const int off = (i * 256 + w * 64) * 16;
+    const int off = (i * NT + w * 64) * 16;
     dma16(src.rsrc, dst + off, tile * TILE_BYTES + off + lane * 16);
   }
 }
@@ -321,10 +324,10 @@ __device__ __forceinline__ void pv_tile(const uint4* __restrict__ v_lds, const v
 
 // Positions at or beyond kend may hold anything: zero their values in the
 // staged V tile kt (every thread of the block takes part).
-template <int D, bool BF16>
+template <int D, bool BF16, int NT = 256>
 __device__ __forceinline__ void zero_v_beyond(uint4* v_lds, int kt, int kend, int tid) {
   constexpr int VVEC = PrefillCfg<D, BF16>::VVEC;
-  for (int i = tid; i < VVEC; i += 256) {
+  for (int i = tid; i < VVEC; i += NT) {
     const int gi = i / D;  // vector i of the tile: group gi holds E positions
     uint32_t keep[4];
     if constexpr (BF16) {
@@ -579,25 +582,44 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
 }
 
 // ============================================================================
-// bf16 caches: 32x32x16 MFMA (v_mfma_f32_32x32x16_bf16).  A wave owns 32
-// (row, head) columns (lane l: column l % 32, half h = l / 32).
-//   S^T = K . Q^T per 32-key block kb and 16-dim step ks: A = K[32 kb + l % 32]
-//     [16 ks + 8 h .. + 7] (16 bytes of the K layout), B = Q^T, stationary in
-//     registers and pre-multiplied by scale * log2(e), so scores arrive in the
-//     log2 domain.  Accumulator register 4 a + e of block kb then holds key
-//     32 kb + 8 a + 4 h + e of the lane's column.
+// bf16 caches: 32x32x16 MFMA (v_mfma_f32_32x32x16_bf16), 8 waves.
+//
+// Work split.  Wave w takes column block cb = w & 3 (M columns 32 cb ..
+// 32 cb + 31 of the tile) and half kh = w >> 2: it scores keys 32 kh ..
+// 32 kh + 31 of every 64-position tile and owns output dims kh D/2 ..
+// kh D/2 + D/2 - 1.  Waves w and w ^ 4 (the pair of a column block) exchange
+// their bf16 weights through LDS (2 KiB per wave and tile) and share one
+// softmax frame.  Two waves per SIMD, at most 256 registers each, so one
+// wave's LDS and dependency waits are covered by the other's work.  Lane l
+// holds column l % 32 of the block (half h = l / 32).
+//   S^T = K . Q^T per 16-dim step ks: A = K[32 kh + l % 32][16 ks + 8 h .. + 7]
+//     (16 bytes of the K layout), B = Q^T, stationary in registers and
+//     pre-multiplied by scale * log2(e), so scores arrive in the log2 domain.
+//     Accumulator register 4 a + e holds key 32 kh + 8 a + 4 h + e.
 //   O^T += V^T . P^T per 16-key step (kb, s): A = V group 4 kb + 2 s + h at dim
-//     32 db + l % 32 (16 bytes of the V layout), B = the lane's own weights of
-//     keys {32 kb + 16 s + 4 h + 0..3, 32 kb + 16 s + 8 + 4 h + 0..3}, which are
-//     accumulator registers 8 s .. 8 s + 7 of block kb: no data movement.
-// Software pipeline.  Step i of a workgroup's tile range issues, on the matrix
-// pipe, the scores of tile i+1 and the value product of tile i-1 (32 + 32
-// MFMAs for D = 256) and, on the vector pipe between them, the softmax of
-// tile i.  K(i+2) and V(i) stream into LDS meanwhile; K and V each have two
-// LDS buffers.
+//     32 db + l % 32 (16 bytes of the V layout), B = the weights of keys
+//     {32 kb + 16 s + 4 h + 0..3, 32 kb + 16 s + 8 + 4 h + 0..3} of the lane's
+//     column: accumulator registers 8 s .. 8 s + 7 of the scores of key half
+//     kb, rounded to bf16 -- this wave's own for kb = kh, the partner's (same
+//     lane, from LDS) for kb = 1 - kh.
+// Pipeline.  Step i issues, on the matrix pipe, the scores of tile i+1 and the
+// value product of tile i-1 (16 + 16 MFMAs per wave for D = 256) and, on the
+// vector pipe between them, the softmax of tile i.  K(i+2) and V(i) stream
+// into LDS meanwhile; K, V and the weight exchange each have two buffers.
+//
+// Reference frame.  A column's weights are exp2(s - m_ref), where m_ref is the
+// largest score of the first tile of the range (both halves; a column that
+// sees any key of the range sees that tile's first key).  The frame never
+// moves during the pipelined pass, so the accumulators are never rescaled.  A
+// score above m_ref + kFrameSlack (log2 units) sets ovf: the range is then
+// redone, tile by tile without pipelining, with m_ref = the largest score of
+// the whole range, which every column tracks.  Weights stay below
+// 2^kFrameSlack in a pass that stands.
 // ============================================================================
 typedef __attribute__((ext_vector_type(16))) float v16f;
 typedef __attribute__((ext_vector_type(4))) _Float16 half4;
+
+constexpr int kBf16Threads = 512;
 
 // Both lane halves' values: lane l receives (x of lane l % 32, x of lane
 // l % 32 + 32), with v_permlane32_swap (no LDS traffic).
@@ -608,26 +630,36 @@ __device__ __forceinline__ void halves(float x, float& lo, float& hi) {
   hi = __uint_as_float(r[1]);
 }
 
+// An empty volatile asm that reads and writes x: code motion above the
+// machine scheduler cannot move the computation of x past it, so each
+// softmax slice stays in the chunk (between scheduling fences) it was
+// written in instead of sinking to its first use.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// A wave's column.
 struct ColB {
-  int m, row;
+  int lc, lh, m, lim;
   bool valid;
-  int lc, lh;
 };
 
-__device__ __forceinline__ ColB col_b(const Tiling& t) {
+__device__ __forceinline__ ColB col_b(const Tiling& t, int cb, int start) {
   ColB c;
   c.lc = t.lane & 31;
   c.lh = t.lane >> 5;
-  c.m = t.m_base + t.w * 32 + c.lc;
+  c.m = t.m_base + 32 * cb + c.lc;
   c.valid = c.m < t.M_total;
-  c.row = c.valid ? c.m / t.G : 0;
+  c.lim = start + (c.valid ? c.m / t.G : 0);
   return c;
 }
 
 // Stationary Q^T operand, scaled by sl2e in f32 and rounded once to bf16.
 template <int D>
-__device__ __forceinline__ void load_q_b(const Tiling& t, const ColB& c, const float* __restrict__ q,
-                                         int R, int Hq, float sl2e, bf16x8 (&qreg)[D / 16]) {
+__device__ __forceinline__ void load_q_b(const Tiling& t, const ColB& c,
+                                         const float* __restrict__ q, int R, int Hq, float sl2e,
+                                         bf16x8 (&qreg)[D / 16]) {
   const float* qp = q + (((size_t)t.b * R + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
@@ -645,107 +677,117 @@ __device__ __forceinline__ void load_q_b(const Tiling& t, const ColB& c, const f
   }
 }
 
-// An empty volatile asm that reads and writes x: code motion above the
-// machine scheduler cannot move the computation of x past it, so each
-// softmax slice stays in the chunk (between scheduling fences) it was
-// written in instead of sinking to its first use in the next step.
-template <typename T>
-__device__ __forceinline__ void pin(T& x) {
-  asm volatile("" : "+v"(x));
-}
-
-// Keys past a column's causal limit get -inf (diagonal tiles only).
-__device__ __forceinline__ void mask_tile_b(v16f (&s)[2], int key0, int lim, int lh) {
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (key0 + 32 * kb + 8 * (i >> 2) + 4 * lh + (i & 3) > lim) s[kb][i] = -INFINITY;
-}
-
 // Operand indices (16-byte units) within a staged tile.
-template <int D>
-__device__ __forceinline__ int k_op(int ks, int kb, const ColB& c) {
-  return (2 * ks + c.lh) * 64 + 32 * kb + c.lc;
+__device__ __forceinline__ int k_op_b(int ks, int kh, int lc, int lh) {
+  return (2 * ks + lh) * 64 + 32 * kh + lc;
 }
 template <int D>
-__device__ __forceinline__ int v_op(int db, int kb, int s, const ColB& c) {
-  return (kb * 4 + 2 * s + c.lh) * D + 32 * db + c.lc;
+__device__ __forceinline__ int v_op_b(int db, int kb, int s, int lc, int lh) {
+  return (kb * 4 + 2 * s + lh) * D + 32 * db + lc;
+}
+// Value chunk j (dim block j / 4 of this wave's half, key step j % 4; steps
+// 0, 1 in this wave's own key half, 2, 3 in the partner's).
+template <int D>
+__device__ __forceinline__ int pv_op_b(int j, int kh, int lc, int lh) {
+  const int kstep = j & 3;
+  const int kb = (kstep >> 1) ? 1 - kh : kh;
+  return v_op_b<D>(kh * (D / 64) + (j >> 2), kb, kstep & 1, lc, lh);
+}
+
+// Weight exchange slots (16-byte units): [parity][wave][s][lane].
+__device__ __forceinline__ int xp_slot(int par, int w, int s, int lane) {
+  return ((par * 8 + w) * 2 + s) * 64 + lane;
+}
+
+// Scores of one tile (this wave's key half), unpipelined.
+template <int D>
+__device__ __forceinline__ void qk_tile_b(const uint4* __restrict__ k_lds,
+                                          const bf16x8 (&qreg)[D / 16], v16f& s, int kh,
+                                          const ColB& c) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+        __builtin_bit_cast(bf16x8, k_lds[k_op_b(ks, kh, c.lc, c.lh)]), qreg[ks], s, 0, 0, 0);
+}
+
+// Keys past the column's causal limit get -inf (tiles that cross a limit only).
+__device__ __forceinline__ void mask_tile_b(v16f& s, int key0, const ColB& c) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    s[i] = key0 + 8 * (i >> 2) + 4 * c.lh + (i & 3) > c.lim ? -INFINITY : s[i];
+}
+
+template <int D>
+__device__ __forceinline__ void pv_chunk_b(int j, uint4 vop, const bf16x8 (&p_own)[2],
+                                           const bf16x8 (&p_oth)[2], v16f (&acc)[D / 64]) {
+  const int kstep = j & 3;
+  acc[j >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      __builtin_bit_cast(bf16x8, vop), kstep < 2 ? p_own[kstep & 1] : p_oth[kstep & 1],
+      acc[j >> 2], 0, 0, 0);
 }
 
 // One pipelined step (see above).  cur: scores of tile i (log2 domain, masked)
 // in, weights out; p_cur: bf16 weights of tile i out; nxt: scores of tile i+1
-// out; p_prev: bf16 weights of tile i-1, multiplied into acc_o with the V tile
-// in v_lds.
+// out; p_prev / p_oth: this wave's / the partner's bf16 weights of tile i-1,
+// multiplied into acc with the V tile in v_lds (skipped when FIRST).
 //
-// Reference frame.  A column's weights are exp2(s - m_ref), where m_ref is the
-// largest score of the first tile in which the column sees a key.  The frame
-// never moves during a pass, so the accumulators are never rescaled.  A score
-// above m_ref + kFrameSlack (log2 units) sets ovf: the pass is then redone
-// with m_ref = m_all, the largest score of the whole range, which every
-// column tracks.  Weights stay below 2^kFrameSlack in a pass that stands.
-//
-// Chunk c (c < NC = D/16) carries the score MFMAs of k-step c (both key
-// blocks), two value MFMAs (dim block c/2, key block c%2, s = 0, 1), the LDS
-// reads of chunk c+2 and softmax phase slices; a scheduling fence closes it.
-//   phases: 0, 1 max over key block 0 / 1; 2 cross-half max and frame;
-//   3..10 exponentials (4 each); 11..14 bf16 conversion of the weights;
-//   15 running sum.
-template <int D>
+// Chunk c (c < NC = D/16) carries the score MFMA of k-step c, the value MFMA
+// of chunk c, the LDS reads of chunk c+2 and softmax phase slices; a
+// scheduling fence closes it.
+//   phases: 0 max; 1 cross-half max, largest score and frame check;
+//   2..9 exponentials (2 each); 10, 11 bf16 conversion of the weights;
+//   12 running sum.
+template <int D, bool FIRST>
 __device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
                                              const uint4* __restrict__ v_lds,
-                                             const bf16x8 (&qreg)[D / 16], v16f (&cur)[2],
-                                             v16f (&nxt)[2], const bf16x8 (&p_prev)[2][2],
-                                             bf16x8 (&p_cur)[2][2], v16f (&acc_o)[D / 32],
-                                             const ColB& c, float& m_ref, float& m_all,
-                                             float& l_run, bool& ovf) {
+                                             const bf16x8 (&qreg)[D / 16], v16f& cur, v16f& nxt,
+                                             const bf16x8 (&p_prev)[2], const bf16x8 (&p_oth)[2],
+                                             bf16x8 (&p_cur)[2], v16f (&acc)[D / 64],
+                                             const ColB& c, int kh, float m_use, float m_ref,
+                                             float& m_all, float& l_run, bool& ovf) {
   constexpr int NC = D / 16;
-  constexpr int DIST = 2;
+  constexpr int DIST = 1;
+  constexpr int NPH = 13;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) nxt[kb][i] = 0.f;
-  float lmax = -INFINITY, ls = 0.f, m_use = 0.f;
-  // operand ring: [slot][0..1 K (kb), 2..3 V (s)]
-  uint4 ring[DIST + 1][4];
+  for (int i = 0; i < 16; ++i) nxt[i] = 0.f;
+  float lmax = -INFINITY, ls = 0.f;
+  // operand ring: [slot][0 K, 1 V]
+  uint4 ring[DIST + 1][2];
   auto issue = [&](int cc) {
-    uint4(&r)[4] = ring[cc % (DIST + 1)];
-    r[0] = k_lds[k_op<D>(cc, 0, c)];
-    r[1] = k_lds[k_op<D>(cc, 1, c)];
-    r[2] = v_lds[v_op<D>(cc >> 1, cc & 1, 0, c)];
-    r[3] = v_lds[v_op<D>(cc >> 1, cc & 1, 1, c)];
+    uint4(&r)[2] = ring[cc % (DIST + 1)];
+    r[0] = k_lds[k_op_b(cc, kh, c.lc, c.lh)];
+    if (!FIRST) r[1] = v_lds[pv_op_b<D>(cc, kh, c.lc, c.lh)];
   };
   auto phase = [&](int ph) {
-    if (ph < 2) {
+    if (ph == 0) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) lmax = fmaxf(lmax, cur[ph][i]);
+      for (int i = 0; i < 16; ++i) lmax = fmaxf(lmax, cur[i]);
       pin(lmax);
-    } else if (ph == 2) {
+    } else if (ph == 1) {
       float lo, hi;
       halves(lmax, lo, hi);
-      lmax = fmaxf(lo, hi);
-      m_all = fmaxf(m_all, lmax);
-      if (m_ref == -INFINITY) m_ref = lmax;  // nothing accumulated yet
-      ovf = ovf || lmax > m_ref + kFrameSlack;
-      m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      pin(m_use);
-    } else if (ph < 11) {
-      const int q = ph - 3, kb = q >> 2, i0 = (q & 3) * 4;
+      const float mx = fmaxf(lo, hi);
+      m_all = fmaxf(m_all, mx);
+      ovf = ovf || mx > m_ref + kFrameSlack;
+    } else if (ph < 10) {
+      const int i0 = (ph - 2) * 2;
 #pragma unroll
-      for (int i = i0; i < i0 + 4; ++i) {
-        float pv = fast_exp2(cur[kb][i] - m_use);
+      for (int i = i0; i < i0 + 2; ++i) {
+        float pv = fast_exp2(cur[i] - m_use);
         pin(pv);
-        cur[kb][i] = pv;
+        cur[i] = pv;
         ls += pv;
       }
       pin(ls);
-    } else if (ph < 15) {
-      const int r = ph - 11, kb = r >> 1, s = r & 1;
+    } else if (ph < 12) {
+      const int ss = ph - 10;
       float f[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = cur[kb][8 * s + j];
-      p_cur[kb][s] = to_bf16x8(f);
-      pin(p_cur[kb][s]);
+      for (int j = 0; j < 8; ++j) f[j] = cur[8 * ss + j];
+      p_cur[ss] = to_bf16x8(f);
+      pin(p_cur[ss]);
     } else {
       l_run += ls;
     }
@@ -756,177 +798,150 @@ __device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
     if (cc + DIST < NC) issue(cc + DIST);
-    const uint4(&r)[4] = ring[cc % (DIST + 1)];
+    const uint4(&r)[2] = ring[cc % (DIST + 1)];
+    nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, r[0]), qreg[cc], nxt,
+                                                  0, 0, 0);
+    if (!FIRST) pv_chunk_b<D>(cc, r[1], p_prev, p_oth, acc);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-      nxt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, r[kb]),
-                                                         qreg[cc], nxt[kb], 0, 0, 0);
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-      acc_o[cc >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-          __builtin_bit_cast(bf16x8, r[2 + s]), p_prev[cc & 1][s], acc_o[cc >> 1], 0, 0, 0);
-#pragma unroll
-    for (int ph = 0; ph < 16; ++ph)
-      if (ph * NC / 16 == cc) phase(ph);
+    for (int ph = 0; ph < NPH; ++ph)
+      if (ph * NC / NPH == cc) phase(ph);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Value product of one tile outside the pipeline (the last tile of a range).
+// Stores this wave's dims of its column: the normalised output (one split)
+// or the split's partial.  Partials: acc [tile][S][128 columns][D] as
+// binary16, each lane's D / 4 values scaled by 2^-e so that the largest finite
+// one lies in [0.5, 1) (rounding adds at most 2^-12 of it); records
+// (m, l, e of (half kh, lane half h) at 2 + 2 kh + h) [tile][128 columns][S][6].
 template <int D>
-__device__ __forceinline__ void pv_tile_b(const uint4* __restrict__ v_lds, const bf16x8 (&p)[2][2],
-                                          v16f (&acc_o)[D / 32], const ColB& c) {
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, v_lds[v_op<D>(db, kb, s, c)]), p[kb][s], acc_o[db], 0, 0, 0);
-}
-
-template <int D>
-__device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c,
-                                               float* __restrict__ out, float* __restrict__ part,
+__device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, int kh,
+                                               float* __restrict__ out, void* __restrict__ part,
                                                float* __restrict__ part_ml,
-                                               const v16f (&acc_o)[D / 32], float m_run,
-                                               float l_run, int R, int Hq, int Hkv, int m_tiles,
-                                               int S) {
-  float lo, hi;
-  halves(l_run, lo, hi);
-  const float lt = lo + hi;
+                                               const v16f (&acc)[D / 64], float m_ref, float l_tot,
+                                               int R, int Hq, int Hkv, int m_tiles, int S) {
   if (!c.valid) return;
-  // lane holds dims 32 db + 8 a + 4 h + 0..3
   if (S == 1) {
-    float* op = out + (((size_t)t.b * R + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D;
-    const float inv = 1.f / lt;
+    float* op = out + (((size_t)t.b * R + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D + kh * (D / 2);
+    const float sc = 1.f / l_tot;
+    // lane holds dims 32 db + 8 a + 4 h + 0..3 of this wave's half
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 64; ++db)
 #pragma unroll
       for (int a = 0; a < 4; ++a)
         *reinterpret_cast<float4*>(op + 32 * db + 8 * a + 4 * c.lh) =
-            make_float4(acc_o[db][4 * a] * inv, acc_o[db][4 * a + 1] * inv,
-                        acc_o[db][4 * a + 2] * inv, acc_o[db][4 * a + 3] * inv);
-  } else {
-    // acc [tile][S][128 columns][D] as binary16, each lane's 8 D / 32 values
-    // scaled by 2^-e so that the largest finite one lies in [0.5, 1);
-    // (m, l, e of lane half 0, e of lane half 1) [tile][128 columns][S][4].
-    // Rounding adds at most 2^-12 of the lane's largest value.
-    const size_t tile_id = ((size_t)t.b * Hkv + t.g) * m_tiles + t.mt;
-    const int col = c.m - t.m_base;
-    float amax = 0.f;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float x = fabsf(acc_o[db][i]);
-        amax = x <= FLT_MAX ? fmaxf(amax, x) : amax;  // finite values only
-      }
-    int e = 0;
-    if (amax > 0.f) (void)frexpf(amax, &e);
-    const float sc = ldexpf(1.f, -e);
-    _Float16* pp = reinterpret_cast<_Float16*>(part) + ((tile_id * S + t.split) * kMTile + col) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        half4 h;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) h[k] = (_Float16)(acc_o[db][4 * a + k] * sc);
-        *reinterpret_cast<half4*>(pp + 32 * db + 8 * a + 4 * c.lh) = h;
-      }
-    float* ml = part_ml + ((tile_id * kMTile + col) * S + t.split) * 4;
-    if (c.lh == 0) {
-      ml[0] = m_run;
-      ml[1] = lt;
-    }
-    ml[2 + c.lh] = (float)e;
+            make_float4(acc[db][4 * a] * sc, acc[db][4 * a + 1] * sc, acc[db][4 * a + 2] * sc,
+                        acc[db][4 * a + 3] * sc);
+    return;
   }
+  const size_t tile_id = ((size_t)t.b * Hkv + t.g) * m_tiles + t.mt;
+  const int col = c.m - t.m_base;
+  float amax = 0.f;
+#pragma unroll
+  for (int db = 0; db < D / 64; ++db)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float x = fabsf(acc[db][i]);
+      amax = x <= FLT_MAX ? fmaxf(amax, x) : amax;  // finite values only
+    }
+  int e = 0;
+  if (amax > 0.f) (void)frexpf(amax, &e);
+  const float sc = ldexpf(1.f, -e);
+  _Float16* pp = reinterpret_cast<_Float16*>(part) + ((tile_id * S + t.split) * kMTile + col) * D +
+                 kh * (D / 2);
+#pragma unroll
+  for (int db = 0; db < D / 64; ++db)
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      half4 h;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) h[k] = (_Float16)(acc[db][4 * a + k] * sc);
+      *reinterpret_cast<half4*>(pp + 32 * db + 8 * a + 4 * c.lh) = h;
+    }
+  float* ml = part_ml + ((tile_id * kMTile + col) * S + t.split) * 6;
+  if (kh == 0 && c.lh == 0) {
+    ml[0] = m_ref;
+    ml[1] = l_tot;
+  }
+  ml[2 + 2 * kh + c.lh] = (float)e;
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(
+__global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
-    const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
+    const void* __restrict__ v_cache, float* __restrict__ out, void* __restrict__ part,
     float* __restrict__ part_ml, int Hq, int Hkv, int C, int start, int R, int m_tiles, int S,
     float sl2e) {
   constexpr int TB = PrefillCfg<D, true>::TILE_BYTES;
-  __shared__ __attribute__((aligned(16))) unsigned char kb0[TB];
-  __shared__ __attribute__((aligned(16))) unsigned char kb1[TB];
-  __shared__ __attribute__((aligned(16))) unsigned char vb0[TB];
-  __shared__ __attribute__((aligned(16))) unsigned char vb1[TB];
-  __shared__ int redo;
+  constexpr int NT = kBf16Threads;
+  // K(0), K(1), V(0), V(1), then two weight-exchange buffers of 16 KiB.  The
+  // exchange buffer that holds no weights at that moment also carries the
+  // per-pass exchanges (frame, votes, sums), so no other LDS is used:
+  // 160 KiB at D = 256.
+  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * TB + 2 * 16384];
+  unsigned char* const kb0 = lds;
+  unsigned char* const kb1 = lds + TB;
+  unsigned char* const vb0 = lds + 2 * TB;
+  unsigned char* const vb1 = lds + 3 * TB;
+  uint4* const xp = reinterpret_cast<uint4*>(lds + 4 * TB);
 
   Tiling t;
   if (!make_tiling(Hq, Hkv, start, R, S, m_tiles, t)) return;
-  const ColB c = col_b(t);
+  const int kh = t.w >> 2, partner = t.w ^ 4;
+  const ColB c = col_b(t, t.w & 3, start);
   const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;  // elements
   const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * 2, (size_t)C * D * 2);
   const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab * 2, (size_t)C * D * 2);
   const int n = t.kt1 - t.kt0;
-  const int lim = start + c.row;
 
   bf16x8 qreg[D / 16];
-  v16f acc_o[D / 32];
-  float m_ref = -INFINITY, m_all = -INFINITY, l_run = 0.f;
-  v16f sa[2], sb[2];
-  bf16x8 pa[2][2], pb[2][2];
+  v16f acc[D / 64];
+  float m_ref = -INFINITY, m_all = -INFINITY, l_run = 0.f, l_tot = 0.f;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 64; ++db)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;  // also the result of an empty split
+    for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;  // also the result of an empty split
   if (n > 0) load_q_b<D>(t, c, q, R, Hq, sl2e, qreg);
+  // per-pass exchange area (floats) in the exchange buffer that holds no
+  // weights at that moment: [wave][slot][lane]
+  auto xf = [&](int par, int w, int slot) {
+    return reinterpret_cast<float*>(xp + xp_slot(par, 0, 0, 0)) + (w * 4 + slot) * 64 + t.lane;
+  };
 
-  // At most two passes: the second only when a score left the first pass's
-  // frame (see fused_step_b); it starts from the range's largest score.
-  for (int pass = 0; pass < 2 && n > 0; ++pass) {
+  v16f sa, sb;
+  bf16x8 pw[2], pc[2], po[2];
+  bool redo = false;
+
+  // Pipelined pass in the frame of the first tile (see above).
+  if (n > 0) {
     bool ovf = false;
-    if (pass == 1) {
-      m_ref = m_all;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc_o[db][i] = 0.f;
-      l_run = 0.f;
-    }
-    load_tile<TB>(ksrc, t.kt0, kb0, t.w, t.lane);
-    // V(-1) := 0 and P(-1) := 0: the first step's value product adds nothing.
-    {
-      uint4* z = reinterpret_cast<uint4*>(vb1);
-#pragma unroll
-      for (int i = 0; i < TB / (256 * 16); ++i) z[i * 256 + t.tid] = make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pb[kb][s2][j] = (__bf16)0.f;
+    load_tile<TB, NT>(ksrc, t.kt0, kb0, t.w, t.lane);
     wait_vmem();
     __syncthreads();
-    if (n > 1) load_tile<TB>(ksrc, t.kt0 + 1, kb1, t.w, t.lane);
+    if (n > 1) load_tile<TB, NT>(ksrc, t.kt0 + 1, kb1, t.w, t.lane);
     // scores of the first tile (no softmax to overlap with yet)
+    qk_tile_b<D>(reinterpret_cast<const uint4*>(kb0), qreg, sa, kh, c);
+    if (t.kt0 * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(sa, t.kt0 * kNTile + 32 * kh, c);
     {
-      const uint4* k0 = reinterpret_cast<const uint4*>(kb0);
+      // frame: the first tile's largest score over both key halves; this
+      // wave's half goes to exchange buffer 1 (first holds weights in step 1)
+      float mx = -INFINITY, lo, hi;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sa[kb][i] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          sa[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, k0[k_op<D>(ks, kb, c)]), qreg[ks], sa[kb], 0, 0, 0);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sa[i]);
+      halves(mx, lo, hi);
+      m_ref = fmaxf(lo, hi);
+      *xf(1, t.w, 0) = m_ref;
     }
+    float m_use = 0.f;
 
     // Step i (parity P = i & 1): K(i+1) and V(i-1) are in buffers 1-P; K(i+2)
     // and V(i) are loaded into buffers P, whose previous contents (K(i),
-    // V(i-2)) every wave finished with in step i-1.
-    auto step = [&](auto par, int i, v16f (&cur)[2], v16f (&nxt)[2], bf16x8 (&p_prev)[2][2],
-                    bf16x8 (&p_cur)[2][2]) {
+    // V(i-2)) every wave finished with in step i-1.  The weights of tile i go
+    // to exchange buffer P (both waves of the pair read them back in step
+    // i+1); those of tile i-1 are in buffer 1-P.
+    auto step = [&](auto par, auto first, int i, v16f& cur, v16f& nxt) {
       constexpr int P = decltype(par)::value;
+      constexpr bool FIRST = decltype(first)::value;
       const unsigned char* k_use = P == 0 ? kb1 : kb0;
       const unsigned char* v_use = P == 0 ? vb1 : vb0;
       unsigned char* k_load = P == 0 ? kb0 : kb1;
@@ -935,38 +950,124 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(
       wait_vmem();
       __syncthreads();
       wait_lgkm();
-      if (i + 2 < n) load_tile<TB>(ksrc, kt + 2, k_load, t.w, t.lane);
-      load_tile<TB>(vsrc, kt, v_load, t.w, t.lane);
-      if (kt * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(cur, kt * kNTile, lim, c.lh);
-      fused_step_b<D>(reinterpret_cast<const uint4*>(k_use), reinterpret_cast<const uint4*>(v_use),
-                      qreg, cur, nxt, p_prev, p_cur, acc_o, c, m_ref, m_all, l_run, ovf);
+      if (i + 2 < n) load_tile<TB, NT>(ksrc, kt + 2, k_load, t.w, t.lane);
+      load_tile<TB, NT>(vsrc, kt, v_load, t.w, t.lane);
+      if (FIRST) {
+        m_ref = fmaxf(m_ref, *xf(1, partner, 0));
+        m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        pin(m_use);
+      } else {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          po[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(1 - P, partner, s2, t.lane)]);
+          pw[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(1 - P, t.w, s2, t.lane)]);
+        }
+        if (kt * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(cur, kt * kNTile + 32 * kh, c);
+      }
+      fused_step_b<D, FIRST>(reinterpret_cast<const uint4*>(k_use),
+                             reinterpret_cast<const uint4*>(v_use), qreg, cur, nxt, pw, po, pc,
+                             acc, c, kh, m_use, m_ref, m_all, l_run, ovf);
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        xp[xp_slot(P, t.w, s2, t.lane)] = __builtin_bit_cast(uint4, pc[s2]);
     };
-    for (int i = 0; i < n; i += 2) {
-      step(std::integral_constant<int, 0>(), i, sa, sb, pb, pa);
-      if (i + 1 < n) step(std::integral_constant<int, 1>(), i + 1, sb, sa, pa, pb);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    step(I0(), std::true_type(), 0, sa, sb);
+    for (int i = 1; i < n; i += 2) {
+      step(I1(), std::false_type(), i, sb, sa);
+      if (i + 1 < n) step(I0(), std::false_type(), i + 1, sa, sb);
     }
-    // value product of the last tile, V(n-1) in buffer (n-1) & 1
-    {
-      const int kt = t.kt1 - 1;
-      unsigned char* v_last = ((n - 1) & 1) ? vb1 : vb0;
+    // value product of the last tile: V(n-1) in buffer (n-1) & 1, weights in
+    // exchange buffer (n-1) & 1
+    const int kt = t.kt1 - 1;
+    const int pl = (n - 1) & 1;
+    unsigned char* v_last = pl ? vb1 : vb0;
+    wait_vmem();
+    __syncthreads();
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      po[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(pl, partner, s2, t.lane)]);
+      pw[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(pl, t.w, s2, t.lane)]);
+    }
+    if ((kt + 1) * kNTile > t.kend) {
+      zero_v_beyond<D, true, NT>(reinterpret_cast<uint4*>(v_last), kt, t.kend, t.tid);
+      __syncthreads();
+    }
+    const uint4* vl = reinterpret_cast<const uint4*>(v_last);
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) pv_chunk_b<D>(j, vl[pv_op_b<D>(j, kh, c.lc, c.lh)], pw, po, acc);
+    // votes, largest scores and sums, in exchange buffer 1 - pl (free since
+    // the barrier above)
+    const int px = 1 - pl;
+    *xf(px, t.w, 1) = __any(ovf) ? 1.f : 0.f;
+    *xf(px, t.w, 2) = m_all;
+    *xf(px, t.w, 3) = l_run;
+    __syncthreads();
+#pragma unroll
+    for (int w2 = 0; w2 < 8; ++w2) redo = redo || *xf(px, w2, 1) != 0.f;
+    l_tot = l_run + *xf(px, partner, 3);
+    if (redo) m_ref = fmaxf(m_all, *xf(px, partner, 2));
+  }
+
+  // Rare: a score left the frame.  The range is redone, tile by tile without
+  // pipelining, in the frame of its largest score.
+  if (redo) {
+    l_run = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 64; ++db)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    const uint4* kl = reinterpret_cast<const uint4*>(kb0);
+    uint4* vl = reinterpret_cast<uint4*>(vb0);
+    for (int i = 0; i < n; ++i) {
+      const int kt = t.kt0 + i;
+      __syncthreads();  // every wave is done with the previous tile and weights
+      load_tile<TB, NT>(ksrc, kt, kb0, t.w, t.lane);
+      load_tile<TB, NT>(vsrc, kt, vb0, t.w, t.lane);
       wait_vmem();
-      if (t.tid == 0) redo = 0;
       __syncthreads();
       if ((kt + 1) * kNTile > t.kend) {
-        zero_v_beyond<D, true>(reinterpret_cast<uint4*>(v_last), kt, t.kend, t.tid);
+        zero_v_beyond<D, true, NT>(vl, kt, t.kend, t.tid);
         __syncthreads();
       }
-      if ((n - 1) & 1)
-        pv_tile_b<D>(reinterpret_cast<const uint4*>(vb1), pb, acc_o, c);
-      else
-        pv_tile_b<D>(reinterpret_cast<const uint4*>(vb0), pa, acc_o, c);
+      v16f s;
+      qk_tile_b<D>(kl, qreg, s, kh, c);
+      if (kt * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(s, kt * kNTile + 32 * kh, c);
+      float ls = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        s[k] = fast_exp2(s[k] - m_use);
+        ls += s[k];
+      }
+      l_run += ls;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float f[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f[j] = s[8 * s2 + j];
+        pw[s2] = to_bf16x8(f);
+        xp[xp_slot(0, t.w, s2, t.lane)] = __builtin_bit_cast(uint4, pw[s2]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+        po[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(0, partner, s2, t.lane)]);
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) pv_chunk_b<D>(j, vl[pv_op_b<D>(j, kh, c.lc, c.lh)], pw, po, acc);
     }
-    if (pass == 1) break;
-    if (__any(ovf) && t.lane == 0) redo = 1;
-    __syncthreads();  // also: every wave is done with the LDS tiles
-    if (!redo) break;
+    __syncthreads();
+    *xf(1, t.w, 3) = l_run;
+    __syncthreads();
+    l_tot = l_run + *xf(1, partner, 3);
   }
-  store_result_b<D>(t, c, out, part, part_ml, acc_o, m_ref, l_run, R, Hq, Hkv, m_tiles, S);
+  {
+    float lo, hi;
+    halves(l_tot, lo, hi);
+    l_tot = lo + hi;
+  }
+  store_result_b<D>(t, c, kh, out, part, part_ml, acc, m_ref, l_tot, R, Hq, Hkv, m_tiles, S);
 }
 
 // Sequential prefill (one K+V stage) for shapes whose four tiles do not fit
@@ -1028,7 +1129,7 @@ constexpr int kEarly = 8;
 
 template <bool H16>
 struct PartFmt {
-  static constexpr int ML = H16 ? 4 : 2;  // floats per (column, split) record
+  static constexpr int ML = H16 ? 6 : 2;  // floats per (column, split) record
 };
 
 template <int D, bool H16>
@@ -1068,32 +1169,37 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
       for (int j = 0; j < J; ++j) early[k][j] = load_part<D, H16>(part, pc + k * PS + 64 * j);
   float M = -INFINITY, L = 0.f;
   for (int s = 0; s < S; ++s) M = fmaxf(M, ml[ML * s]);
-  // weight of split s: its frame relative to M, times its lane-half scale
-  // (dims 4 v .. 4 v + 3 were written by lane half v & 1)
-  auto weight = [&](int s) {
+  // weight of split s: its frame relative to M, times the scale of the lane
+  // that wrote dims 4 v + 64 j .. + 3 (half kh = (4 v + 64 j) / (D / 2), lane
+  // half v & 1)
+  auto weight = [&](int s, int j) {
     const float f = ml[ML * s] == -INFINITY ? 0.f : fast_exp2(ml[ML * s] - M);
-    L += f * ml[ML * s + 1];
-    if constexpr (H16) return ldexpf(f, (int)ml[ML * s + 2 + (v & 1)]);
+    if constexpr (H16) return ldexpf(f, (int)ml[ML * s + 2 + 2 * ((4 * v + 64 * j) / (D / 2)) + (v & 1)]);
     else return f;
+  };
+  auto frame_sum = [&](int s) {
+    if (ml[ML * s] != -INFINITY) L += fast_exp2(ml[ML * s] - M) * ml[ML * s + 1];
   };
   float4 a[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) a[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto add = [&](float f, const float4 (&t)[J]) {
+  auto add = [&](int s, const float4 (&t)[J]) {
+    frame_sum(s);
 #pragma unroll
     for (int j = 0; j < J; ++j) {
+      const float f = weight(s, j);
       a[j].x += f * t[j].x; a[j].y += f * t[j].y; a[j].z += f * t[j].z; a[j].w += f * t[j].w;
     }
   };
 #pragma unroll
   for (int k = 0; k < kEarly; ++k) {
-    if (k < S) add(weight(k), early[k]);
+    if (k < S) add(k, early[k]);
   }
   for (int s = kEarly; s < S; ++s) {
     float4 t[J];
 #pragma unroll
     for (int j = 0; j < J; ++j) t[j] = load_part<D, H16>(part, pc + s * PS + 64 * j);
-    add(weight(s), t);
+    add(s, t);
   }
   const float il = 1.f / L;
   const int row = m / G, hh = m % G;
@@ -1153,7 +1259,7 @@ hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const 
   // padded to whole rounds of the 8 XCDs (see make_tiling)
   dim3 grid(8 * ((p.m_tiles * p.splits + 7) / 8), s.num_kv_heads, s.batch);
   if constexpr (BF16)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D>), grid, dim3(256), 0, st, q, kc, vc, out, part,
+    hipLaunchKernelGGL((prefill_bf16_kernel<D>), grid, dim3(kBf16Threads), 0, st, q, kc, vc, out, part,
                        part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, start, R, p.m_tiles,
                        p.splits, scale * kLog2e);
   else if constexpr (Cfg::PIPE)
@@ -1177,10 +1283,10 @@ hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const 
 
 }  // namespace
 
-// Workspace bytes per (column, split): binary16 accumulators and a 4-float
+// Workspace bytes per (column, split): binary16 accumulators and a 6-float
 // record for bf16 caches, f32 accumulators and an (m, l) pair otherwise.
 static size_t partial_bytes(const Shape& s) {
-  return s.kv_dtype == 1 ? (size_t)s.head_dim * 2 + 4 * sizeof(float)
+  return s.kv_dtype == 1 ? (size_t)s.head_dim * 2 + 6 * sizeof(float)
                          : (size_t)(s.head_dim + 2) * sizeof(float);
 }
 
