@@ -91,13 +91,13 @@ struct Tiling {
   bool valid_col[2];
 };
 
-// Block -> (m-tile, split).  Work items are ordered split-major (every m-tile
-// of split 0, then of split 1, ...) and dealt to the 8 XCDs in contiguous
+// Block -> (m-tile, split).  Work items are ordered m-tile-major (every split
+// of m-tile 0, then of m-tile 1, ...) and dealt to the 8 XCDs in contiguous
 // runs: consecutive workgroups go to the XCDs round-robin, so block x runs on
-// XCD x % 8 and takes item (x % 8) * per + x / 8.  An XCD then sees few
-// distinct key ranges, and its L2 serves their K / V tiles to all of its
-// m-tiles.  The grid is padded to 8 * per blocks; blocks past the last item
-// return false.
+// XCD x % 8 and takes item (x % 8) * per + x / 8.  The splits of an m-tile
+// then share one XCD, whose L2 serves their common Q rows (read once per
+// workgroup) while the key tiles stream past.  The grid is padded to 8 * per
+// blocks; blocks past the last item return false.
 __device__ __forceinline__ bool make_tiling(int Hq, int Hkv, int start, int R, int S,
                                             int m_tiles, Tiling& t) {
   const int items = m_tiles * S;
@@ -105,8 +105,8 @@ __device__ __forceinline__ bool make_tiling(int Hq, int Hkv, int start, int R, i
   const int x = blockIdx.x;
   const int item = (x & 7) * per + (x >> 3);
   if (item >= items) return false;
-  t.split = item / m_tiles;
-  t.mt = item - t.split * m_tiles;
+  t.mt = item / S;
+  t.split = item - t.mt * S;
   t.g = blockIdx.y;
   t.b = blockIdx.z;
   t.G = Hq / Hkv;
@@ -656,13 +656,20 @@ __device__ __forceinline__ ColB col_b(const Tiling& t, int cb, int start) {
 }
 
 // Stationary Q^T operand, scaled by sl2e in f32 and rounded once to bf16.
+// The two waves of a column block share it: wave half kh loads k-steps
+// kh D/32 .. kh D/32 + D/32 - 1 from memory and stores them to q_lds
+// ([column block][k-step][lane], 16 bytes each); after a barrier,
+// take_q_half reads the partner's k-steps.  Q is thus fetched once per
+// workgroup, not once per wave.
 template <int D>
-__device__ __forceinline__ void load_q_b(const Tiling& t, const ColB& c,
-                                         const float* __restrict__ q, int R, int Hq, float sl2e,
-                                         bf16x8 (&qreg)[D / 16]) {
+__device__ __forceinline__ void load_q_half(const Tiling& t, const ColB& c, int kh, int cb,
+                                            const float* __restrict__ q, int R, int Hq,
+                                            float sl2e, bf16x8 (&qreg)[D / 16],
+                                            uint4* __restrict__ q_lds) {
   const float* qp = q + (((size_t)t.b * R + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
+    if (ks / (D / 32) != kh) continue;
     float f[8];
     if (c.valid) {
       const float4 a = *reinterpret_cast<const float4*>(qp + 16 * ks + 8 * c.lh);
@@ -674,7 +681,16 @@ __device__ __forceinline__ void load_q_b(const Tiling& t, const ColB& c,
       for (int j = 0; j < 8; ++j) f[j] = 0.f;
     }
     qreg[ks] = to_bf16x8(f);
+    q_lds[(cb * (D / 16) + ks) * 64 + t.lane] = __builtin_bit_cast(uint4, qreg[ks]);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void take_q_half(int kh, int cb, int lane, bf16x8 (&qreg)[D / 16],
+                                            const uint4* __restrict__ q_lds) {
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    if (ks / (D / 32) != kh) qreg[ks] = __builtin_bit_cast(bf16x8, q_lds[(cb * (D / 16) + ks) * 64 + lane]);
 }
 
 // Operand indices (16-byte units) within a staged tile.
@@ -901,7 +917,12 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
   for (int db = 0; db < D / 64; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;  // also the result of an empty split
-  if (n > 0) load_q_b<D>(t, c, q, R, Hq, sl2e, qreg);
+  // Q staging in the V buffers, which hold nothing until step 0
+  uint4* const q_lds = reinterpret_cast<uint4*>(vb0);
+  if (n > 0) {
+    load_tile<TB, NT>(ksrc, t.kt0, kb0, t.w, t.lane);
+    load_q_half<D>(t, c, kh, t.w & 3, q, R, Hq, sl2e, qreg, q_lds);
+  }
   // per-pass exchange area (floats) in the exchange buffer that holds no
   // weights at that moment: [wave][slot][lane]
   auto xf = [&](int par, int w, int slot) {
@@ -915,9 +936,9 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
   // Pipelined pass in the frame of the first tile (see above).
   if (n > 0) {
     bool ovf = false;
-    load_tile<TB, NT>(ksrc, t.kt0, kb0, t.w, t.lane);
     wait_vmem();
-    __syncthreads();
+    __syncthreads();  // K(0) and both Q halves are in LDS
+    take_q_half<D>(kh, t.w & 3, t.lane, qreg, q_lds);
     if (n > 1) load_tile<TB, NT>(ksrc, t.kt0 + 1, kb1, t.w, t.lane);
     // scores of the first tile (no softmax to overlap with yet)
     qk_tile_b<D>(reinterpret_cast<const uint4*>(kb0), qreg, sa, kh, c);
