@@ -41,6 +41,7 @@ from synth import WORKLOADS, draw_batch  # noqa: E402
 METRIC = "prefill rows/s at 16K ctx; decode µs/token at 16K & 128K; % HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3   # MI355X dense FP32 MFMA, AMD's published figure
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "session16k_decode128k_hbm_traffic.md")
@@ -303,6 +304,37 @@ def bench_decode_128k(hold, steps=32):
                 bytes=decode_bytes(w, ctx_mean, w.batch), ctx_mean=ctx_mean)
 
 
+def bench_prefill_f32(hold, reps=10):
+    """The f32 chunk workload: a 768-row chunk at 3072 over 3072 cached rows
+    (8 query heads / 1 KV head, head_dim 256, f32 cache); median of reps."""
+    w = WORKLOADS[3]
+    c = draw_batch(w)
+    shape = ka.Shape(1, 8, 1, 256, w.capacity, "f32")
+    kc = ka.alloc_cache(shape, fill_byte=0xFF)
+    vc = ka.alloc_cache(shape, fill_byte=0xFF)
+    (s0, R), = w.chunks
+    ka.append_kv(shape, kc, vc, dev(c.k[:, :s0 + R]), dev(c.v[:, :s0 + R]), 0, s0 + R)
+    q = dev(c.q)
+    out = torch.empty(R * 8 * 256, device="cuda")
+    ws = torch.empty(max(ka.prefill_workspace_bytes(shape, R), 1), dtype=torch.uint8, device="cuda")
+    del c
+    ka.prefill_chunk(shape, q, kc, vc, out, s0, R, w.scale, ws)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = ev_pair()
+        hold(0.5)
+        a.record()
+        ka.prefill_chunk(shape, q, kc, vc, out, s0, R, w.scale, ws)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    pairs = R * s0 + R * (R + 1) // 2
+    flops = pairs * 8 * 256 * 4
+    return dict(ms=ms, rows=R, flops=flops)
+
+
 def cpu_baseline(session_w, budget_s=15.0):
     """The oracle (as written) on a bounded sample of the 16K prefill: 16-row
     blocks spaced evenly over all 16384 prompt rows (so the mean context is the
@@ -340,13 +372,51 @@ def cpu_baseline(session_w, budget_s=15.0):
         if ctxm is not None:
             ctxm.__exit__(None, None, None)
     n = nblocks * 16
+    extras = oracle_extras(oracle, threadpool_limits, cores)
     return {"value": round(n / dt, 2), "unit": "rows/s", "cores": cores, "kind": "oracle",
             "sample": (f"{n} of the 16384 prompt rows of the 16K session (16-row blocks evenly spaced "
                        f"over positions 0..16383, each row against its full causal context; 8 heads, "
                        f"head_dim 256, bf16-stored K/V), numpy float64 two-pass softmax with "
                        f"{cores} BLAS threads, {dt:.1f} s; plus one decode step at 16384 "
                        f"({dt_dec * 1e3:.1f} ms)"),
-            "decode_16k_us_per_token": round(dt_dec * 1e6, 1)}
+            "decode_16k_us_per_token": round(dt_dec * 1e6, 1),
+            "other_workloads": extras}
+
+
+def oracle_extras(oracle, threadpool_limits, cores):
+    """The oracle on samples of the other timed workloads, with all host cores
+    and with one BLAS thread: 64 of the 768 rows of the f32 chunk at 3072
+    (evenly spaced, each against its full causal context), and one decode step
+    of the first of the four 131K sessions."""
+    from synth import draw_session
+    res = {}
+    w3 = WORKLOADS[3]
+    c3 = draw_batch(w3)
+    (s0, R), = w3.chunks
+    pick = np.linspace(0, R - 1, 64).astype(np.int64)
+    w5 = WORKLOADS[5]
+    p5 = w5.decode_positions[0]
+    c5 = draw_session(w5, 0, q_positions=[p5])
+    k5, v5 = oracle.stored_values(c5.k, "bf16"), oracle.stored_values(c5.v, "bf16")
+    for threads in (cores, 1):
+        ctxm = threadpool_limits(limits=threads) if threadpool_limits else None
+        try:
+            t = time.perf_counter()
+            oracle.attend_rows(c3.q[0][pick], c3.k[0], c3.v[0], s0 + pick, w3.scale)
+            dt3 = time.perf_counter() - t
+            t = time.perf_counter()
+            oracle.attend_rows(c5.q, k5, v5, [p5], w5.scale)
+            dt5 = time.perf_counter() - t
+        finally:
+            if ctxm is not None:
+                ctxm.__exit__(None, None, None)
+        res[f"threads_{threads}"] = {
+            "f32_chunk_3072_768_rows_per_s": round(len(pick) / dt3, 2),
+            "decode_131k_us_per_session_token": round(dt5 * 1e6, 1)}
+    res["sample"] = ("64 of the 768 rows of the f32 chunk at 3072 (evenly spaced, full causal "
+                     "context each); one decode step at position 131040 of one of the four 131K "
+                     "sessions (bf16-stored K/V, 8 heads)")
+    return res
 
 
 def main():
@@ -427,6 +497,7 @@ def main():
         out["decode_us_per_step_128k_x4_back_to_back"] = round(d["step_ms"] * 1e3, 3)
         out["roofline_decode_128k"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                       "frac_of_measured_copy": round(gbs / copy["gbs"], 4),
                                        "traffic": traffic.get("decode_128k_call_bytes_per_launch"),
                                        "traffic_unit": "B/launch",
                                        "kernel": "decode step call (decode_mfma_kernel with the "
@@ -434,6 +505,16 @@ def main():
                                                  "at ctx 131041..131072",
                                        "algorithmic_bytes_per_launch": d["bytes"]}
         torch.cuda.empty_cache()
+    f = bench_prefill_f32(hold)
+    tf = f["flops"] / (f["ms"] * 1e-3) / 1e12
+    out["prefill_f32_3072_768_us"] = round(f["ms"] * 1e3, 2)
+    out["prefill_f32_3072_768_rows_per_s"] = round(f["rows"] / (f["ms"] * 1e-3), 1)
+    out["roofline_prefill_f32"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS,
+                                   "unit": "TFLOP/s", "frac": round(tf / FP32_PEAK_TFLOPS, 4),
+                                   "kernel": "f32 prefill chunk call (prefill_seq_kernel + merge), "
+                                             "768 rows at 3072",
+                                   "algorithmic_flops_per_launch": f["flops"]}
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(out), flush=True)
