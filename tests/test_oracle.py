@@ -340,3 +340,61 @@ def test_outlier_rows_are_drawn_without_replacement():
     from synth import draw_session
     c = draw_session(w, 1, positions=4096)
     assert len(np.unique(c.outlier_idx)) == c.outlier_idx.size
+
+
+# ------------------------------------------------------------------- rotary
+
+def test_rope_identity_and_quarter_turn_exact():
+    """cos 1 / sin 0 leaves rows unchanged; cos 0 / sin 1 turns each pair
+    (x[d], x[d + D/2]) by a quarter: (-x[d + D/2], x[d]).  Worked by hand for
+    D = 4, pairs (0, 2) and (1, 3): [1, 2, 3, 4] with the first pair turned
+    and the second left alone gives [-3, 2, 1, 4]."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 2, 8)).astype(np.float32)
+    one, zero = np.ones((5, 4), np.float32), np.zeros((5, 4), np.float32)
+    assert np.array_equal(oracle.rope.rotate_half_f32(x, one, zero), x)
+    turned = oracle.rope.rotate_half_f32(x, zero, one)
+    assert np.array_equal(turned[..., :4], -x[..., 4:]) and np.array_equal(turned[..., 4:], x[..., :4])
+    y = oracle.rope.rotate_half_f32(np.array([[[1, 2, 3, 4]]], np.float32),
+                                    np.array([[0, 1]], np.float32), np.array([[1, 0]], np.float32))
+    assert y.tolist() == [[[-3.0, 2.0, 1.0, 4.0]]]
+
+
+def test_rope_f32_within_rounding_of_complex_f64():
+    """The f32 evaluation (two rounded products, one rounded sum) stays within
+    1.5 units in the last place of the larger product of the complex-number
+    statement in float64."""
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((64, 3, 256)) * 10).astype(np.float32)
+    cos, sin = oracle.rope.angles_table(np.arange(1000, 1064), 256)
+    got = oracle.rope.rotate_half_f32(x, cos, sin).astype(np.float64)
+    ref = oracle.rope.rotate_half_f64(x, cos, sin)
+    h = 128
+    a, b = x[..., :h].astype(np.float64), x[..., h:].astype(np.float64)
+    c, s = cos[:, None, :].astype(np.float64), sin[:, None, :].astype(np.float64)
+    mag = np.concatenate([np.maximum(abs(a * c), abs(b * s)), np.maximum(abs(b * c), abs(a * s))], -1)
+    assert np.all(np.abs(got - ref) <= 1.5 * 2.0 ** -23 * 2 * mag + 1e-30)
+
+
+def test_rope_dot_products_depend_only_on_position_difference():
+    """With angles p * w (the usual table), <rope(q, m), rope(k, n)> depends
+    on m - n only: shifting both positions by t leaves it unchanged, and a
+    lag of zero gives the plain dot product (float64)."""
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((1, 1, 64))
+    k = rng.standard_normal((1, 1, 64))
+    def dot(m, n):
+        # float64 tables of the angles p * w
+        pm = np.asarray([m], float)[:, None] * 10000.0 ** (-np.arange(32) * 2.0 / 64)
+        pn = np.asarray([n], float)[:, None] * 10000.0 ** (-np.arange(32) * 2.0 / 64)
+        a = oracle.rope.rotate_half_f64(q, np.cos(pm), np.sin(pm))
+        b = oracle.rope.rotate_half_f64(k, np.cos(pn), np.sin(pn))
+        return float(np.sum(a * b))
+    base = dot(37, 5)
+    for t in (1, 100, 4096):
+        assert abs(dot(37 + t, 5 + t) - base) <= 1e-9 * (1 + abs(base))
+    assert abs(dot(9, 9) - float(np.sum(q * k))) <= 1e-12 * (1 + abs(base))
+    # and rotation keeps the norm of every pair
+    p = 123.0 * 10000.0 ** (-np.arange(32) * 2.0 / 64)
+    r = oracle.rope.rotate_half_f64(q, np.cos(p)[None], np.sin(p)[None])
+    assert np.allclose(r[..., :32] ** 2 + r[..., 32:] ** 2, q[..., :32] ** 2 + q[..., 32:] ** 2, rtol=1e-12)
