@@ -335,6 +335,45 @@ def bench_prefill_f32(hold, reps=10):
     return dict(ms=ms, rows=R, flops=flops)
 
 
+def bench_rope(hold, reps=20):
+    """Rotary entry points at the session's chunk shape: a 768-row append
+    whose K rows are rotated on the way into the bf16 cache, and the rotation
+    of the chunk's 768 x 8 query rows (medians of reps, event-timed)."""
+    w = WORKLOADS[4]
+    shape = ka.Shape(1, 8, 1, 256, w.capacity, "bf16")
+    kc = ka.alloc_cache(shape)
+    vc = ka.alloc_cache(shape)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    R, s0 = 768, 7680
+    k = torch.randn(R * 256, device="cuda", generator=g)
+    v = torch.randn(R * 256, device="cuda", generator=g)
+    q = torch.randn(R * 8 * 256, device="cuda", generator=g)
+    qo = torch.empty_like(q)
+    pos = torch.arange(s0, s0 + R, device="cuda", dtype=torch.float64)[:, None]
+    inv = 10000.0 ** (-torch.arange(128, device="cuda", dtype=torch.float64) * 2.0 / 256)
+    cos = torch.cos(pos * inv).float().contiguous()
+    sin = torch.sin(pos * inv).float().contiguous()
+    calls = {"append_kv_rope_768_us": lambda: ka.append_kv_rope(shape, kc, vc, k, v, cos, sin, s0, R),
+             "rope_rows_768x8_us": lambda: ka.rope_rows(shape, q, qo, cos, sin, R),
+             "append_kv_768_us": lambda: ka.append_kv(shape, kc, vc, k, v, s0, R)}
+    res = {}
+    for name, f in calls.items():
+        f()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = ev_pair()
+            hold(0.2)
+            a.record()
+            f()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b) * 1e3)
+        res[name] = round(float(np.median(ts)), 2)
+    return res
+
+
 def cpu_baseline(session_w, budget_s=15.0):
     """The oracle (as written) on a bounded sample of the 16K prefill: 16-row
     blocks spaced evenly over all 16384 prompt rows (so the mean context is the
@@ -514,6 +553,8 @@ def main():
                                    "kernel": "f32 prefill chunk call (prefill_seq_kernel + merge), "
                                              "768 rows at 3072",
                                    "algorithmic_flops_per_launch": f["flops"]}
+    torch.cuda.empty_cache()
+    out["rope"] = bench_rope(hold)
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

@@ -119,6 +119,41 @@ ka_status ka_attn_append_kv(const ka_attn_shape* s, void* k_cache, void* v_cache
                             int32_t start_pos, int32_t row_count, void* stream);
 
 /*
+ * KV append with rotary position embedding of the new K rows.  The Karume
+ * pages make the rotary tables a per-chunk host input: the host generates
+ * the cos / sin rows of each chunk from the model's rope parameters (Karume
+ * v0.8.0 release notes, "Features", the conversation-window bullet;
+ * karume-gemma4-e2b model card, the context bullet).
+ *
+ * As ka_attn_append_kv, except that each new K row is first rotated:
+ * rope_cos, rope_sin are f32 [row_count][D/2] device arrays (16-byte
+ * aligned, like every f32 array here), row i holding the values for position
+ * start_pos + i (shared by every session and KV head).  Dims d and d + D/2 form one pair (rotate-half pairing): for d < D/2
+ *   k'[d]       = k[d] * cos[d] - k[d + D/2] * sin[d]
+ *   k'[d + D/2] = k[d + D/2] * cos[d] + k[d] * sin[d]
+ * evaluated in f32 as two rounded products and one rounded sum or difference
+ * (no fused multiply-add), then stored like ka_attn_append_kv.  V rows are
+ * stored as given.  Errors: those of ka_attn_append_kv; a null rope_cos or
+ * rope_sin is KA_ERR_INVALID_ARGUMENT when row_count > 0.
+ */
+ka_status ka_attn_append_kv_rope(const ka_attn_shape* s, void* k_cache, void* v_cache,
+                                 const float* k_new, const float* v_new,
+                                 const float* rope_cos, const float* rope_sin,
+                                 int32_t start_pos, int32_t row_count, void* stream);
+
+/*
+ * Rotary embedding of query rows (the same passages): x and y are f32
+ * [B][row_count][Hq][D] device arrays (y may equal x for an in-place
+ * rotation); row i of every session and head is rotated by rope_cos[i],
+ * rope_sin[i] ([row_count][D/2]) exactly as ka_attn_append_kv_rope rotates
+ * K rows.  row_count == 0 is a no-op.  Errors: KA_ERR_INVALID_ARGUMENT (null
+ * pointer, row_count < 0), KA_ERR_UNSUPPORTED, KA_ERR_HIP.
+ */
+ka_status ka_attn_rope_rows(const ka_attn_shape* s, const float* x, float* y,
+                            const float* rope_cos, const float* rope_sin, int32_t row_count,
+                            void* stream);
+
+/*
  * Workspace bytes that ka_attn_prefill_chunk needs for any chunk of at most
  * max_rows rows at any start position of shape s (0 if none is needed).
  */

@@ -19,7 +19,8 @@ import torch
 __all__ = ["Shape", "KaAttnError", "KaAttnUnavailable", "lib", "lib_path", "F32", "BF16",
            "cache_bytes", "alloc_cache", "append_kv", "prefill_workspace_bytes",
            "prefill_chunk", "decode_workspace_bytes", "decode", "status_string",
-           "last_error", "abi_version", "EXPORTED_SYMBOLS", "decode_step"]
+           "last_error", "abi_version", "EXPORTED_SYMBOLS", "decode_step", "append_kv_rope",
+           "rope_rows"]
 
 F32 = 0
 BF16 = 1
@@ -28,7 +29,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libka_attn.so"
 
 EXPORTED_SYMBOLS = (
-    "ka_attn_abi_version", "ka_attn_cache_bytes", "ka_attn_append_kv",
+    "ka_attn_abi_version", "ka_attn_cache_bytes", "ka_attn_append_kv", "ka_attn_append_kv_rope",
+    "ka_attn_rope_rows",
     "ka_attn_prefill_workspace_bytes", "ka_attn_prefill_chunk",
     "ka_attn_decode_workspace_bytes", "ka_attn_decode", "ka_attn_decode_step",
     "ka_attn_status_string",
@@ -94,6 +96,11 @@ def lib() -> ctypes.CDLL:
     L.ka_attn_append_kv.restype = c_int32
     L.ka_attn_append_kv.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_void_p]
     L.ka_attn_prefill_workspace_bytes.restype = c_size_t
+    L.ka_attn_append_kv_rope.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                         c_void_p, c_int32, c_int32, c_void_p]
+    L.ka_attn_append_kv_rope.restype = c_int32
+    L.ka_attn_rope_rows.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
+    L.ka_attn_rope_rows.restype = c_int32
     L.ka_attn_prefill_workspace_bytes.argtypes = [P, c_int32]
     L.ka_attn_prefill_chunk.restype = c_int32
     L.ka_attn_prefill_chunk.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
@@ -185,6 +192,37 @@ def append_kv(shape: Shape, k_cache: torch.Tensor, v_cache: torch.Tensor,
     _check(lib().ka_attn_append_kv(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache),
                                    _ptr(k_new), _ptr(v_new), int(start_pos), int(row_count),
                                    _stream(stream)))
+
+
+def append_kv_rope(shape: Shape, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   k_new: torch.Tensor, v_new: torch.Tensor, rope_cos: torch.Tensor,
+                   rope_sin: torch.Tensor, start_pos: int, row_count: int, stream=None) -> None:
+    """ka_attn_append_kv_rope: rope_cos / rope_sin f32 [row_count][head_dim / 2]."""
+    n = shape.batch * row_count * shape.num_kv_heads * shape.head_dim
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, torch.float32, n)
+    for t, nm in ((rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        _need(t, nm, torch.float32, row_count * (shape.head_dim // 2))
+    cb = cache_bytes(shape)
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, None)
+        if t.numel() * t.element_size() < cb:
+            raise ValueError(f"{nm} is smaller than {cb} bytes")
+    _check(lib().ka_attn_append_kv_rope(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(k_new), _ptr(v_new), _ptr(rope_cos), _ptr(rope_sin),
+                                        int(start_pos), int(row_count), _stream(stream)))
+
+
+def rope_rows(shape: Shape, x: torch.Tensor, y: torch.Tensor, rope_cos: torch.Tensor,
+              rope_sin: torch.Tensor, row_count: int, stream=None) -> None:
+    """ka_attn_rope_rows: x, y f32 [batch][row_count][num_q_heads][head_dim] (y may be x)."""
+    n = shape.batch * row_count * shape.num_q_heads * shape.head_dim
+    _need(x, "x", torch.float32, n)
+    _need(y, "y", torch.float32, n)
+    for t, nm in ((rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+        _need(t, nm, torch.float32, row_count * (shape.head_dim // 2))
+    _check(lib().ka_attn_rope_rows(ctypes.byref(shape), _ptr(x), _ptr(y), _ptr(rope_cos),
+                                   _ptr(rope_sin), int(row_count), _stream(stream)))
 
 
 def prefill_workspace_bytes(shape: Shape, max_rows: int) -> int:

@@ -98,6 +98,43 @@ ka_status ka_attn_append_kv(const ka_attn_shape* s, void* k_cache, void* v_cache
   return ok();
 }
 
+ka_status ka_attn_append_kv_rope(const ka_attn_shape* s, void* k_cache, void* v_cache,
+                                 const float* k_new, const float* v_new, const float* rope_cos,
+                                 const float* rope_sin, int32_t start_pos, int32_t row_count,
+                                 void* stream) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  if (row_count < 0) return fail(KA_ERR_INVALID_ARGUMENT, "row_count %d < 0", row_count);
+  if (start_pos < 0) return fail(KA_ERR_INVALID_ARGUMENT, "start_pos %d < 0", start_pos);
+  if ((long long)start_pos + row_count > sh.capacity)
+    return fail(KA_ERR_OUT_OF_RANGE, "start_pos %d + row_count %d exceeds capacity %d",
+                start_pos, row_count, sh.capacity);
+  if (row_count == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new || !rope_cos || !rope_sin)
+    return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  hipError_t e = ka::launch_append(sh, k_cache, v_cache, k_new, v_new, start_pos, row_count,
+                                   reinterpret_cast<hipStream_t>(stream), rope_cos, rope_sin);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
+ka_status ka_attn_rope_rows(const ka_attn_shape* s, const float* x, float* y,
+                            const float* rope_cos, const float* rope_sin, int32_t row_count,
+                            void* stream) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  if (row_count < 0) return fail(KA_ERR_INVALID_ARGUMENT, "row_count %d < 0", row_count);
+  if (row_count == 0) return ok();
+  if (!x || !y || !rope_cos || !rope_sin) return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  hipError_t e = ka::launch_rope_rows(x, y, rope_cos, rope_sin, sh.batch, row_count,
+                                      sh.num_q_heads, sh.head_dim,
+                                      reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope launch");
+  return ok();
+}
+
 size_t ka_attn_prefill_workspace_bytes(const ka_attn_shape* s, int32_t max_rows) {
   ka::Shape sh;
   if (check_shape(s, &sh) != KA_OK) return 0;

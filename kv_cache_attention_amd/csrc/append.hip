@@ -9,10 +9,41 @@
 
 namespace ka {
 
-template <bool BF16>
+// Rotary embedding of element d of a row x (rotate-half pairing: dims d and
+// d + D/2 form one pair, turned by the angle whose cos / sin are c[d mod D/2],
+// s[d mod D/2]).  Two rounded products and one rounded sum or difference, in
+// that order: no fused multiply-add, so the result is reproducible bit for
+// bit.
+// A product held opaque to the code generator, so it cannot be fused into a
+// multiply-add with the sum that follows (the library builds with FP
+// contraction on).
+__device__ __forceinline__ float rounded_mul(float a, float b) {
+  float p = a * b;
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
+// Four pairs at once: a = x[j .. j+3], b = x[j+D/2 .. j+D/2+3], c / s the
+// row's cos / sin at j .. j+3.  lo gets the first-half outputs, hi the second.
+__device__ __forceinline__ void rope4(float4 a, float4 b, float4 c, float4 s, float4& lo,
+                                      float4& hi) {
+  lo.x = rounded_mul(a.x, c.x) - rounded_mul(b.x, s.x);
+  lo.y = rounded_mul(a.y, c.y) - rounded_mul(b.y, s.y);
+  lo.z = rounded_mul(a.z, c.z) - rounded_mul(b.z, s.z);
+  lo.w = rounded_mul(a.w, c.w) - rounded_mul(b.w, s.w);
+  hi.x = rounded_mul(b.x, c.x) + rounded_mul(a.x, s.x);
+  hi.y = rounded_mul(b.y, c.y) + rounded_mul(a.y, s.y);
+  hi.z = rounded_mul(b.z, c.z) + rounded_mul(a.z, s.z);
+  hi.w = rounded_mul(b.w, c.w) + rounded_mul(a.w, s.w);
+}
+
+// ROPE: each new K row is rotated by its position's angles (cos / sin rows
+// [R][D/2], row i for position start + i) before it is stored; V as given.
+template <bool BF16, bool ROPE>
 __global__ __launch_bounds__(256) void append_kernel(
     void* __restrict__ k_cache, void* __restrict__ v_cache,
     const float* __restrict__ k_new, const float* __restrict__ v_new,
+    const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
     int Hkv, int D, int C, int start, int R,
     long long n_k_vecs, long long n_v_vecs, int v_groups_per_slab, int v_group0) {
   constexpr int E = Elem<BF16>::E;
@@ -29,21 +60,44 @@ __global__ __launch_bounds__(256) void append_kernel(
       const int row = (int)(t % R);
       const int b = (int)(t / R);
       const int j = start + row;
-      const float* src = k_new + (((size_t)b * R + row) * Hkv + g) * D + c * E;
+      const float* rowp = k_new + (((size_t)b * R + row) * Hkv + g) * D;
+      const float* src = rowp + c * E;
       const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;  // elements
       const size_t vi = k_vec_index(j, c, D, E);
+      float f[E];
+      if constexpr (ROPE) {
+        // this vector's E dims and their partners in the other half
+        const int h = D >> 1;
+        const int d0 = c * E, j0 = d0 < h ? d0 : d0 - h;
+        const float* cr = rope_cos + (size_t)row * h + j0;
+        const float* sr = rope_sin + (size_t)row * h + j0;
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+          const float4 a = *reinterpret_cast<const float4*>(rowp + j0 + e);
+          const float4 b = *reinterpret_cast<const float4*>(rowp + j0 + h + e);
+          float4 lo, hi;
+          rope4(a, b, *reinterpret_cast<const float4*>(cr + e),
+                *reinterpret_cast<const float4*>(sr + e), lo, hi);
+          const float4 o = d0 < h ? lo : hi;
+          f[e] = o.x; f[e + 1] = o.y; f[e + 2] = o.z; f[e + 3] = o.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; e += 4) {
+          const float4 a = *reinterpret_cast<const float4*>(src + e);
+          f[e] = a.x; f[e + 1] = a.y; f[e + 2] = a.z; f[e + 3] = a.w;
+        }
+      }
       if constexpr (BF16) {
-        const float4 a = *reinterpret_cast<const float4*>(src);
-        const float4 bq = *reinterpret_cast<const float4*>(src + 4);
         uint4 o;
-        o.x = pack_bf16x2(a.x, a.y);
-        o.y = pack_bf16x2(a.z, a.w);
-        o.z = pack_bf16x2(bq.x, bq.y);
-        o.w = pack_bf16x2(bq.z, bq.w);
+        o.x = pack_bf16x2(f[0], f[1]);
+        o.y = pack_bf16x2(f[2], f[3]);
+        o.z = pack_bf16x2(f[4], f[5]);
+        o.w = pack_bf16x2(f[6], f[7]);
         reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_cache) + slab)[vi] = o;
       } else {
-        const float4 a = *reinterpret_cast<const float4*>(src);
-        reinterpret_cast<float4*>(reinterpret_cast<float*>(k_cache) + slab)[vi] = a;
+        reinterpret_cast<float4*>(reinterpret_cast<float*>(k_cache) + slab)[vi] =
+            make_float4(f[0], f[1], f[2], f[3]);
       }
     } else {
       // V vector: (b, g, group, d) with d innermost; a group spans E positions
@@ -98,7 +152,8 @@ __global__ __launch_bounds__(256) void append_kernel(
 }
 
 hipError_t launch_append(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
-                         const float* v_new, int start, int R, hipStream_t stream) {
+                         const float* v_new, int start, int R, hipStream_t stream,
+                         const float* rope_cos, const float* rope_sin) {
   const bool bf16 = s.kv_dtype == 1;
   const int E = bf16 ? 8 : 4;
   const long long n_k = (long long)s.batch * R * s.num_kv_heads * (s.head_dim / E);
@@ -118,14 +173,55 @@ hipError_t launch_append(const Shape& s, void* k_cache, void* v_cache, const flo
   const int threads = 256;
   long long blocks = (total + threads - 1) / threads;
   if (blocks > 65536) blocks = 65536;
-  if (bf16)
-    hipLaunchKernelGGL(append_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       k_cache, v_cache, k_new, v_new, s.num_kv_heads, s.head_dim, s.capacity,
+  const bool rope = rope_cos != nullptr;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, k_cache, v_cache,
+                       k_new, v_new, rope_cos, rope_sin, s.num_kv_heads, s.head_dim, s.capacity,
                        start, R, n_k, n_v, ng, g0);
-  else
-    hipLaunchKernelGGL(append_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0, stream,
-                       k_cache, v_cache, k_new, v_new, s.num_kv_heads, s.head_dim, s.capacity,
-                       start, R, n_k, n_v, ng, g0);
+  };
+  if (bf16 && rope) go(append_kernel<true, true>);
+  else if (bf16) go(append_kernel<true, false>);
+  else if (rope) go(append_kernel<false, true>);
+  else go(append_kernel<false, false>);
+  return hipGetLastError();
+}
+
+// Rotary embedding of query rows: x, y f32 [B][R][H][D] (y may be x), each
+// element rotated by its row's cos / sin ([R][D/2]) exactly as the append's
+// K rows are.  One thread per 4 output elements; all of a pair's inputs are
+// read before either output is written, so in-place use is safe.
+__global__ __launch_bounds__(256) void rope_rows_kernel(const float* __restrict__ x, float* y,
+                                                        const float* __restrict__ rope_cos,
+                                                        const float* __restrict__ rope_sin,
+                                                        long long n_pairs4, int R, int H, int D) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_pairs4) return;
+  // pair group i: 4 consecutive dims j .. j+3 of the first half of one
+  // (b, r, head) row, with their partners j + D/2 ..
+  const int h2 = D >> 1;
+  const int q4 = h2 >> 2;
+  const int j = (int)(i % q4) * 4;
+  const long long rowi = i / q4;  // (b, r, head) row index
+  const int r = (int)((rowi / H) % R);
+  const float* xr = x + rowi * D;
+  float* yr = y + rowi * D;
+  const float* cr = rope_cos + (size_t)r * h2;
+  const float* sr = rope_sin + (size_t)r * h2;
+  float4 lo, hi;
+  rope4(*reinterpret_cast<const float4*>(xr + j), *reinterpret_cast<const float4*>(xr + j + h2),
+        *reinterpret_cast<const float4*>(cr + j), *reinterpret_cast<const float4*>(sr + j), lo, hi);
+  *reinterpret_cast<float4*>(yr + j) = lo;
+  *reinterpret_cast<float4*>(yr + j + h2) = hi;
+}
+
+hipError_t launch_rope_rows(const float* x, float* y, const float* rope_cos,
+                            const float* rope_sin, int B, int R, int H, int D,
+                            hipStream_t stream) {
+  const long long n = (long long)B * R * H * (D / 8);
+  const int threads = 256;
+  const long long blocks = (n + threads - 1) / threads;
+  hipLaunchKernelGGL(rope_rows_kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, x, y,
+                     rope_cos, rope_sin, n, R, H, D);
   return hipGetLastError();
 }
 

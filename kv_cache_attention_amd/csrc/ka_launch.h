@@ -20,8 +20,15 @@ struct CtxArg {
   int32_t ctx[kMaxDecodeBatchPerLaunch];
 };
 
+// rope_cos / rope_sin: null for a plain append, else [R][D/2] rows that rotate
+// each new K row before it is stored.
 hipError_t launch_append(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
-                         const float* v_new, int start, int R, hipStream_t stream);
+                         const float* v_new, int start, int R, hipStream_t stream,
+                         const float* rope_cos = nullptr, const float* rope_sin = nullptr);
+// Rotary embedding of f32 rows x -> y ([B][R][H][D], y may be x).
+hipError_t launch_rope_rows(const float* x, float* y, const float* rope_cos,
+                            const float* rope_sin, int B, int R, int H, int D,
+                            hipStream_t stream);
 // One row per session at position pos.ctx[b - b0], sessions b0 .. b0 + nb - 1.
 hipError_t launch_append_rows(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
                               const float* v_new, const CtxArg& pos, int b0, int nb,

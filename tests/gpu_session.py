@@ -36,6 +36,12 @@ class DevCaches:
         R = k_rows.shape[1]
         ka.append_kv(self.shape, self.k, self.v, dev(k_rows), dev(v_rows), start, R)
 
+    def append_rope(self, k_rows, v_rows, cos, sin, start):
+        """As append, with K rows rotated by cos / sin ([R][D/2] float32)."""
+        R = k_rows.shape[1]
+        ka.append_kv_rope(self.shape, self.k, self.v, dev(k_rows), dev(v_rows), dev(cos), dev(sin),
+                          start, R)
+
     def append_dev(self, k_rows_t, v_rows_t, start, R):
         ka.append_kv(self.shape, self.k, self.v, k_rows_t, v_rows_t, start, R)
 

@@ -30,7 +30,8 @@ def header_functions():
 
 def test_header_declares_the_entry_points():
     names = header_functions()
-    for n in ["ka_attn_append_kv", "ka_attn_prefill_chunk", "ka_attn_decode", "ka_attn_decode_step",
+    for n in ["ka_attn_append_kv", "ka_attn_append_kv_rope", "ka_attn_rope_rows",
+              "ka_attn_prefill_chunk", "ka_attn_decode", "ka_attn_decode_step",
               "ka_attn_decode_workspace_bytes", "ka_attn_prefill_workspace_bytes",
               "ka_attn_cache_bytes", "ka_attn_status_string", "ka_attn_last_error",
               "ka_attn_abi_version"]:
@@ -105,6 +106,27 @@ def test_append_argument_errors():
     assert _append(s, 0, 1, ptr=None) == 1
     assert _append(s, 4096, 0) == 0          # an empty append is a no-op
     assert ka.last_error() == ""
+
+
+def test_rope_argument_errors():
+    _lib_or_skip()
+    L = ka.lib()
+    s = S()
+    def app(start, rows, cos=FAKE, sin=FAKE, ptr=FAKE):
+        return L.ka_attn_append_kv_rope(ctypes.byref(s), ptr, ptr, ptr, ptr, cos, sin, start, rows, None)
+    assert app(-1, 1) == 1
+    assert app(0, -1) == 1
+    assert app(4000, 97) == 2
+    assert app(0, 1, cos=None) == 1
+    assert app(0, 1, sin=None) == 1
+    assert app(0, 1, ptr=None) == 1
+    assert app(0, 0, cos=None, sin=None) == 0     # an empty append is a no-op
+    assert L.ka_attn_rope_rows(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, -1, None) == 1
+    assert L.ka_attn_rope_rows(ctypes.byref(s), None, FAKE, FAKE, FAKE, 3, None) == 1
+    assert L.ka_attn_rope_rows(ctypes.byref(s), FAKE, FAKE, FAKE, None, 3, None) == 1
+    assert L.ka_attn_rope_rows(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 0, None) == 0
+    bad = S(head_dim=96)
+    assert L.ka_attn_rope_rows(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, 3, None) == 3
 
 
 def test_prefill_argument_errors():
