@@ -16,8 +16,13 @@
  * Softmax rules (Karume v0.8.0 release notes, "Breaking Changes", the softmax
  * NaN bullet): a NaN among a row's visible scores makes that whole output row
  * NaN (the row max propagates NaN, no NaN is dropped); a NaN visible value
- * v[j][d] makes output dim d NaN; masked keys carry weight exactly 0, and
- * cache positions outside a row's visible range never reach its result.
+ * v[j][d] makes output dim d NaN; masked keys carry weight exactly 0, so no
+ * key past a row's position reaches its result, and no value at or past the
+ * end of the chunk (or past a decode row) does.  One exception: a NaN or
+ * infinite value v[j][d] at a position j inside a prefill chunk may also
+ * turn output dim d of the chunk's rows before j into NaN -- those rows give
+ * j the weight 0 in a product that the chunk's rows share, and 0 times a
+ * non-finite value is NaN.  Their other dims are unaffected.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -167,7 +172,13 @@ size_t ka_attn_prefill_workspace_bytes(const ka_attn_shape* s, int32_t max_rows)
  *
  * Row i (i < row_count) of the chunk is at absolute position start_pos + i
  * and attends to cache positions 0 .. start_pos + i, which must already hold
- * appended rows.  q and out are f32 [B][R][Hq][D]; out may not alias q.
+ * appended rows.  Which kernel serves a chunk depends on its size (Karume
+ * v0.12.0 release notes, "Docs": the plan-size geometry table for 1, 2-15
+ * and 16 or more rows): on bf16 caches a chunk of up to 15 rows may be
+ * served by the split-context decode kernel, its (row, head) pairs taken as
+ * columns with a causal limit each, when that is estimated to be faster;
+ * otherwise, and on f32 caches, by the 128-column M-tile kernel.  Results
+ * agree within the same tolerance either way.  q and out are f32 [B][R][Hq][D]; out may not alias q.
  * scale must be finite and > 0 (e.g. 1/sqrt(D)).  row_count == 0 is a no-op.
  * workspace: device scratch of at least
  * ka_attn_prefill_workspace_bytes(s, row_count) bytes (may be NULL when that

@@ -365,7 +365,7 @@ void decode_split_kernel(
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
-    int b0, int Hq, int Hkv, int HG, int hpw, int S) {
+    int b0, int Hq, int Hkv, int HG, int hpw, int S, int R) {
   __shared__ float wgt[kMaxSplits];
   __shared__ float red[8][32];
   __shared__ float wmax[4], wsum[4];
@@ -376,6 +376,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const int g = gh / HG, hg = gh % HG;
   const int G = Hq / Hkv;
   const int gq = b * (Hkv * HG) + gh;
+  const int ph = hg * hpw + h;  // (row, head) pair of the group: row ph / G, head ph % G
+  if (ph >= R * G) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float* ml = part_ml + ((size_t)gq * hpw + h) * S * 2;
   const int dl = tid & 31, r = tid >> 5;
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   if (r == 0) {
     const float t = ((red[0][dl] + red[1][dl]) + (red[2][dl] + red[3][dl])) +
                     ((red[4][dl] + red[5][dl]) + (red[6][dl] + red[7][dl]));
-    out[((size_t)b * Hq + g * G + hg * hpw + h) * D + d] = t / L;
+    out[(((size_t)b * R + ph / G) * Hq + g * G + ph % G) * D + d] = t / L;
   }
 }
 
@@ -475,16 +477,27 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const float* __restrict__ q, void* k_cache, void* v_cache, float* __restrict__ out,
     float* __restrict__ part, float* __restrict__ part_ml, const float* __restrict__ k_new,
-    const float* __restrict__ v_new, const CtxArg ctxa, int b0, int Hq, int Hkv, int HG, int hpw,
-    int C, int S, float sl2e) {
+    const float* __restrict__ v_new, const CtxArg ctxa, int b0, int nb, int Hq, int Hkv, int HG,
+    int hpw, int C, int S, float sl2e, int R) {
   typedef __attribute__((ext_vector_type(4))) float v4f;
   __shared__ float sacc[kWaves][kDecCols * D];
   __shared__ float wm[kWaves][kDecCols], wl[kWaves][kDecCols];
 
-  const int split = blockIdx.x, gh = blockIdx.y, bl = blockIdx.z, b = b0 + bl;
-  const int g = gh / HG, hg = gh % HG;
+  // Work item i = ((session bl, KV head g, split) , head group hg), hg fastest.
+  // One head group: item i is workgroup i.  Several: workgroups go to the 8
+  // XCDs in turn, so workgroup x takes item (x % 8) per + x / 8 and each XCD
+  // holds a contiguous run of items -- the head groups of a split together,
+  // reading the same K / V lines through one L2.  Items past the end exit.
+  int item = blockIdx.x;
+  if (HG > 1) {
+    const int per = (int)((gridDim.x + 7) / 8);
+    item = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (item >= nb * Hkv * S * HG) return;
+  }
+  const int hg = item % HG, split = (item / HG) % S, gb = item / (HG * S);
+  const int g = gb % Hkv, bl = gb / Hkv, b = b0 + bl;
+  const int gh = g * HG + hg;
   const int G = Hq / Hkv;
-  const int h0 = g * G + hg * hpw;  // first query head served
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lc = lane & 15, r = lane >> 4;
@@ -527,11 +540,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   if (t0 < t1) load(ta_, t0);
   if (t0 + 1 < t1) load(tb_, t0 + 1);
 
-  // stationary Q^T: column lc is head h0 + lc (zero past hpw)
+  // stationary Q^T: column lc is (row, head) pair pc = hg hpw + lc of the KV
+  // group -- query row pc / G of the session's R rows (the last of which sits
+  // at position ctx - 1), head g G + pc % G -- and zero past the pairs.  Its
+  // keys are 0 .. lim.
   bf16x8 qreg[D / 32];
+  const int pc = hg * hpw + lc;
+  const bool hv = lc < hpw && pc < R * G;
+  const int lim = ctx - R + (hv ? pc / G : 0);
   {
-    const bool hv = lc < hpw;
-    const float* qp = q + ((size_t)b * Hq + h0 + (hv ? lc : 0)) * D + 8 * r;
+    const float* qp = q + (((size_t)b * R + (hv ? pc / G : 0)) * Hq + g * G + (hv ? pc % G : 0)) * D + 8 * r;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       float f[8];
@@ -631,14 +649,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.k[kb][ks]),
                                                          qreg[ks], sc[kb], 0, 0, 0);
     }
-    // positions at or past ctx (last tile only) may hold anything
+    // keys past a column's limit get -inf (only tiles reaching past the
+    // first limit, ctx - R); positions at or past ctx may hold anything
     const bool tail = kDecTile * t + kDecTile > ctx;
-    if (tail) {
+    if (kDecTile * t + kDecTile - 1 > ctx - R) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (kDecTile * t + 16 * kb + 4 * r + i >= ctx) sc[kb][i] = -INFINITY;
+          if (kDecTile * t + 16 * kb + 4 * r + i > lim) sc[kb][i] = -INFINITY;
     }
     // column max over the tile: 8 values per lane, then the four row groups
     float mx = -INFINITY;
@@ -725,6 +744,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   const int gq = b * (Hkv * HG) + gh;  // partial slot of (b, g, hg)
   for (int i = tid; i < hpw * D / 4; i += 256) {
     const int h = i / (D / 4), d = 4 * (i % (D / 4));
+    const int ph = hg * hpw + h;  // row ph / G, head g G + ph % G
+    if (ph >= R * G) continue;
     float M = -INFINITY;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) M = fmaxf(M, wm[ww][h]);
@@ -739,7 +760,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     }
     if (S == 1) {
       const float inv = 1.f / l;
-      *reinterpret_cast<float4*>(out + ((size_t)b * Hq + h0 + h) * D + d) =
+      *reinterpret_cast<float4*>(out + (((size_t)b * R + ph / G) * Hq + g * G + ph % G) * D + d) =
           make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
     } else {
       *reinterpret_cast<float4*>(part + (((size_t)gq * S + split) * hpw + h) * D + d) = a;
@@ -780,12 +801,19 @@ void dispatch_hpw(int hpw, dim3 grid, hipStream_t st, const float* q, const void
   }
 }
 
+// 1-D grid of the MFMA kernel: one workgroup per item, padded to whole
+// rounds of the 8 XCDs when head groups are remapped
+dim3 mfma_grid(int nb, int Hkv, int HG, int S) {
+  const long long n = (long long)nb * Hkv * HG * S;
+  return dim3((unsigned)(HG > 1 ? 8 * ((n + 7) / 8) : n));
+}
+
 template <int D>
 void launch_merge(int hpw, dim3 grid, hipStream_t st, const float* part, float* out, int b0,
-                  const Shape& s, int HG, int S) {
+                  const Shape& s, int HG, int S, int R = 1) {
   hipLaunchKernelGGL((decode_merge_kernel<D>), grid, dim3(256), 0, st, part,
                      part + (size_t)s.batch * s.num_kv_heads * HG * S * hpw * D, out, b0,
-                     s.num_q_heads, s.num_kv_heads, HG, hpw, S);
+                     s.num_q_heads, s.num_kv_heads, HG, hpw, S, R);
 }
 
 }  // namespace
@@ -804,7 +832,7 @@ DecodePlan plan_decode(const Shape& s, int max_ctx) {
     p.heads_per_wg = G / hg;
     const long long slabs = (long long)s.batch * s.num_kv_heads * hg;
     const long long tiles = (max_ctx + kDecTile - 1) / kDecTile;
-    S = (256 + slabs - 1) / slabs;
+    S = 256 / slabs;  // a 257th workgroup would start a second round
     const long long by_tiles = (tiles + kWaves - 1) / kWaves;
     if (S > by_tiles) S = by_tiles;
   } else {
@@ -824,6 +852,59 @@ DecodePlan plan_decode(const Shape& s, int max_ctx) {
       : (size_t)slabs * p.splits * p.heads_per_wg * (s.head_dim + 2) * sizeof(float);
   // layout: acc [slab][S][HPW][D], then (m, l) [slab][HPW][S][2]
   return p;
+}
+
+DecodePlan plan_rows(const Shape& s, int R, int ctx) {
+  DecodePlan p;
+  const int G = s.num_q_heads / s.num_kv_heads;
+  const int pairs = R * G;
+  p.head_groups = (pairs + kDecCols - 1) / kDecCols;
+  p.heads_per_wg = (pairs + p.head_groups - 1) / p.head_groups;
+  const long long slabs = (long long)s.batch * s.num_kv_heads * p.head_groups;
+  const long long tiles = (ctx + kDecTile - 1) / kDecTile;
+  long long S = 256 / slabs;  // one round: one workgroup per CU
+  const long long by_tiles = (tiles + kWaves - 1) / kWaves;
+  if (S > by_tiles) S = by_tiles;
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (S < 1) S = 1;
+  p.splits = (int)S;
+  p.workspace_bytes = p.splits == 1 ? 0
+      : (size_t)slabs * p.splits * p.heads_per_wg * (s.head_dim + 2) * sizeof(float);
+  return p;
+}
+
+hipError_t launch_rows(const Shape& s, const DecodePlan& p, const float* q, const void* k_cache,
+                       const void* v_cache, float* out, int start, int R, float scale,
+                       void* workspace, hipStream_t stream) {
+  if (s.kv_dtype != 1) return hipErrorInvalidValue;
+  const float sl2e = scale * kLog2e;
+  const int HG = p.head_groups, S = p.splits, hpw = p.heads_per_wg;
+  float* part = reinterpret_cast<float*>(workspace);
+  void* kc = const_cast<void*>(k_cache);  // read only: the kernel writes only new rows, and none are given
+  void* vc = const_cast<void*>(v_cache);
+  for (int b0 = 0; b0 < s.batch; b0 += kMaxDecodeBatchPerLaunch) {
+    const int nb = s.batch - b0 < kMaxDecodeBatchPerLaunch ? s.batch - b0 : kMaxDecodeBatchPerLaunch;
+    CtxArg ca;
+    for (int i = 0; i < kMaxDecodeBatchPerLaunch; ++i) ca.ctx[i] = start + R;
+    switch (s.head_dim) {
+#define KA_D(DD)                                                                               \
+  case DD:                                                                                     \
+    hipLaunchKernelGGL((decode_mfma_kernel<DD>), mfma_grid(nb, s.num_kv_heads, HG, S), dim3(256), \
+                       0, stream, q, kc, vc, out,                                              \
+                       part, part + (size_t)s.batch * s.num_kv_heads * HG * S * hpw * DD,      \
+                       nullptr, nullptr, ca, b0, nb, s.num_q_heads, s.num_kv_heads, HG, hpw,   \
+                       s.capacity, S, sl2e, R);                                                \
+    if (S > 1) launch_merge<DD>(hpw, dim3(hpw * (DD / 32), s.num_kv_heads * HG, nb), stream,  \
+                                part, out, b0, s, HG, S, R);                                   \
+    break;
+      KA_D(64) KA_D(128) KA_D(256)
+#undef KA_D
+      default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, void* k_cache,
@@ -850,12 +931,12 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, vo
 #define KA_D(DD)                                                                               \
   case DD:                                                                                     \
     if (bf16)                                                                                  \
-      hipLaunchKernelGGL((decode_mfma_kernel<DD>), grid, dim3(256), 0, stream, q, k_cache,     \
-                         v_cache, out, part,                                                   \
+      hipLaunchKernelGGL((decode_mfma_kernel<DD>), mfma_grid(nb, s.num_kv_heads, HG, S),       \
+                         dim3(256), 0, stream, q, k_cache, v_cache, out, part,                 \
                          part + (size_t)s.batch * s.num_kv_heads * HG * S * p.heads_per_wg * DD, \
-                         k_new, v_new, ca, b0, s.num_q_heads, s.num_kv_heads, HG,              \
+                         k_new, v_new, ca, b0, nb, s.num_q_heads, s.num_kv_heads, HG,          \
                          p.heads_per_wg,                                                       \
-                         s.capacity, S, sl2e);                                                 \
+                         s.capacity, S, sl2e, 1);                                              \
     else dispatch_hpw<DD, false>(p.heads_per_wg, grid, stream, q, k_cache, v_cache, out, part, \
                                  ca, b0, s, HG, S, sl2e);                                      \
     if (S > 1) launch_merge<DD>(p.heads_per_wg,                                               \

@@ -34,11 +34,21 @@ hipError_t launch_append_rows(const Shape& s, void* k_cache, void* v_cache, cons
                               const float* v_new, const CtxArg& pos, int b0, int nb,
                               hipStream_t stream);
 
+// Split-context plan of the decode kernels.  On the bf16 MFMA kernel a
+// workgroup's columns are heads_per_wg (row, head) pairs -- one row: heads.
+struct DecodePlan {
+  int heads_per_wg;  // columns one workgroup serves
+  int head_groups;   // workgroups sharing a KV head's columns
+  int splits;        // context splits per (session, KV head, head group)
+  size_t workspace_bytes;
+};
+
 // ---- prefill
 struct PrefillPlan {
-  int m_tiles;   // ceil(R * G / 128)
+  int m_tiles;   // ceil(R * G / 128); 0: a few-row chunk served by the decode kernel
   int splits;    // key-range splits per m-tile (1 = no workspace)
   size_t workspace_bytes;
+  DecodePlan rows;  // the decode kernel's plan when m_tiles == 0
 };
 PrefillPlan plan_prefill(const Shape& s, int start, int R);
 size_t prefill_workspace_bound(const Shape& s, int max_rows);
@@ -47,12 +57,6 @@ hipError_t launch_prefill(const Shape& s, const PrefillPlan& p, const float* q,
                           float scale, void* workspace, hipStream_t stream);
 
 // ---- decode
-struct DecodePlan {
-  int heads_per_wg;  // query heads one workgroup serves (divides G)
-  int head_groups;   // G / heads_per_wg
-  int splits;        // context splits per (session, KV head, head group)
-  size_t workspace_bytes;
-};
 DecodePlan plan_decode(const Shape& s, int max_ctx);
 // k_new / v_new (optional, [B][Hkv][D] f32): the decode step's new rows, at
 // position ctx - 1 of each session; they are appended before they are
@@ -61,5 +65,13 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, vo
                          void* v_cache, float* out, const int32_t* ctx_host, float scale,
                          void* workspace, hipStream_t stream, const float* k_new = nullptr,
                          const float* v_new = nullptr);
+
+// ---- chunks of a few rows on bf16 caches: the decode kernel, its 16 MFMA
+// columns taken by (row, head) pairs of a KV group (row p / G, head p % G),
+// each pair with its own causal limit; R rows at positions start .. start + R - 1.
+DecodePlan plan_rows(const Shape& s, int R, int ctx);
+hipError_t launch_rows(const Shape& s, const DecodePlan& p, const float* q, const void* k_cache,
+                       const void* v_cache, float* out, int start, int R, float scale,
+                       void* workspace, hipStream_t stream);
 
 }  // namespace ka

@@ -1140,13 +1140,20 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
   store_result<D>(t, out, part, part_ml, acc_o, m_run, l_run, R, Hq, Hkv, m_tiles, S);
 }
 
-// Combines the S split partials of 16 columns of one M-tile.  Thread (c, v)
-// owns column c and the float4 dims 4 v + 64 j; splits are summed in order.
-// The accumulator loads of the first kEarly splits are issued together with
-// the (m, l) loads, so the kernel waits for one memory round trip, not two.
-// H16: binary16 partials with per-lane exponents (the bf16 kernel's format);
-// otherwise f32 partials with (m, l) pairs.
-constexpr int kEarly = 8;
+// Merge of the split partials: two forms.  With few splits (S <= kMergeFew,
+// the usual case for long chunks, whose many M-tiles fill the chip), thread
+// (c, v) of a block owns column c of 16 and the float4 dims 4 v + 64 j of
+// every split, and issues all its loads -- partials and (m, l, e) records --
+// before it uses any, so it waits for memory once.  With more splits (few
+// M-tiles over a long context), a block takes 4 columns x 64 dims and its
+// four waves take every fourth split each, kMergeBatch loads in flight per
+// lane and a running frame per wave, then combine through LDS.  Both sum in
+// a fixed order, so results do not depend on timing.  H16: binary16 partials
+// with per-lane exponents (the bf16 kernel's format); otherwise f32 partials
+// with (m, l) pairs.
+constexpr int kMergeFew = 8;     // most splits of the column form
+constexpr int kMergeGroups = 4;  // waves of the split form, each a subset of the splits
+constexpr int kMergeBatch = 8;   // split loads in flight per lane (split form)
 
 template <bool H16>
 struct PartFmt {
@@ -1164,7 +1171,7 @@ __device__ __forceinline__ float4 load_part(const void* base, size_t idx) {
 }
 
 template <int D, bool H16>
-__global__ __launch_bounds__(256) void prefill_merge_kernel(
+__global__ __launch_bounds__(256) void prefill_merge_few_kernel(
     const void* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
     int Hq, int Hkv, int R, int m_tiles, int S) {
   constexpr int J = D / 64;
@@ -1172,55 +1179,49 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   const int mt = blockIdx.x >> 3, cg = blockIdx.x & 7;
   const int g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
-  const int M_total = R * G;
   const int tid = threadIdx.x;
   const size_t tile_id = ((size_t)b * Hkv + g) * m_tiles + mt;
   const int c = tid >> 4, v = tid & 15;
   const int col = cg * 16 + c;
   const int m = mt * kMTile + col;
-  if (m >= M_total) return;
+  if (m >= R * G) return;
   const float* ml = part_ml + (tile_id * kMTile + col) * S * ML;
   const size_t pc = (tile_id * S * kMTile + col) * D + 4 * v;  // element index
-  const size_t PS = (size_t)kMTile * D;  // stride between splits
-  float4 early[kEarly][J];
+  const size_t PS = (size_t)kMTile * D;                        // stride between splits
+  float4 t[kMergeFew][J];
+  float mv[kMergeFew], lv[kMergeFew], ev[kMergeFew][J];
 #pragma unroll
-  for (int k = 0; k < kEarly; ++k)
-    if (k < S)
+  for (int k = 0; k < kMergeFew; ++k) {
+    if (k < S) {
 #pragma unroll
-      for (int j = 0; j < J; ++j) early[k][j] = load_part<D, H16>(part, pc + k * PS + 64 * j);
-  float M = -INFINITY, L = 0.f;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[ML * s]);
-  // weight of split s: its frame relative to M, times the scale of the lane
-  // that wrote dims 4 v + 64 j .. + 3 (half kh = (4 v + 64 j) / (D / 2), lane
-  // half v & 1)
-  auto weight = [&](int s, int j) {
-    const float f = ml[ML * s] == -INFINITY ? 0.f : fast_exp2(ml[ML * s] - M);
-    if constexpr (H16) return ldexpf(f, (int)ml[ML * s + 2 + 2 * ((4 * v + 64 * j) / (D / 2)) + (v & 1)]);
-    else return f;
-  };
-  auto frame_sum = [&](int s) {
-    if (ml[ML * s] != -INFINITY) L += fast_exp2(ml[ML * s] - M) * ml[ML * s + 1];
-  };
+      for (int j = 0; j < J; ++j) t[k][j] = load_part<D, H16>(part, pc + k * PS + 64 * j);
+      mv[k] = ml[ML * k];
+      lv[k] = ml[ML * k + 1];
+      // exponent of the lane that wrote dims 4 v + 64 j: half (4 v + 64 j) / (D / 2), lane half v & 1
+#pragma unroll
+      for (int j = 0; j < J; ++j)
+        ev[k][j] = H16 ? ml[ML * k + 2 + 2 * ((4 * v + 64 * j) / (D / 2)) + (v & 1)] : 0.f;
+    } else {
+      mv[k] = -INFINITY;
+    }
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMergeFew; ++k) M = fmaxf(M, mv[k]);
   float4 a[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) a[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto add = [&](int s, const float4 (&t)[J]) {
-    frame_sum(s);
+  float L = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMergeFew; ++k) {
+    if (mv[k] == -INFINITY) continue;  // past S, or a split that saw none of the column's keys
+    const float f = fast_exp2(mv[k] - M);
+    L += f * lv[k];
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const float f = weight(s, j);
-      a[j].x += f * t[j].x; a[j].y += f * t[j].y; a[j].z += f * t[j].z; a[j].w += f * t[j].w;
+      const float w = H16 ? ldexpf(f, (int)ev[k][j]) : f;
+      a[j].x += w * t[k][j].x; a[j].y += w * t[k][j].y; a[j].z += w * t[k][j].z; a[j].w += w * t[k][j].w;
     }
-  };
-#pragma unroll
-  for (int k = 0; k < kEarly; ++k) {
-    if (k < S) add(k, early[k]);
-  }
-  for (int s = kEarly; s < S; ++s) {
-    float4 t[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) t[j] = load_part<D, H16>(part, pc + s * PS + 64 * j);
-    add(s, t);
   }
   const float il = 1.f / L;
   const int row = m / G, hh = m % G;
@@ -1229,6 +1230,95 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(
   for (int j = 0; j < J; ++j)
     *reinterpret_cast<float4*>(op + 64 * j) =
         make_float4(a[j].x * il, a[j].y * il, a[j].z * il, a[j].w * il);
+}
+
+template <int D, bool H16>
+__global__ __launch_bounds__(256) void prefill_merge_split_kernel(
+    const void* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
+    int Hq, int Hkv, int R, int m_tiles, int S) {
+  constexpr int J = D / 64;
+  constexpr int ML = PartFmt<H16>::ML;
+  __shared__ float4 red[kMergeGroups][4][16];
+  __shared__ float red_m[kMergeGroups][4], red_l[kMergeGroups][4];
+  const int js = blockIdx.x % J, cq = (blockIdx.x / J) & 31, mt = (blockIdx.x / J) >> 5;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x, sg = tid >> 6, c = (tid >> 4) & 3, v = tid & 15;
+  const int col = cq * 4 + c;
+  const int m = mt * kMTile + col;
+  const bool valid = m < R * G;
+  const size_t tile_id = ((size_t)b * Hkv + g) * m_tiles + mt;
+  const int d = 64 * js + 4 * v;
+  const float* ml = part_ml + (tile_id * kMTile + col) * S * ML;
+  const size_t pc = (tile_id * S * kMTile + col) * D + d;  // element index
+  const size_t PS = (size_t)kMTile * D;                    // stride between splits
+  // exponent slot of the lane that wrote these dims: half d / (D / 2), lane half v & 1
+  const int eo = 2 + 2 * (d / (D / 2)) + (v & 1);
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  float mw = -INFINITY, lw = 0.f;
+  if (valid) {
+    for (int s0 = sg; s0 < S; s0 += kMergeGroups * kMergeBatch) {
+      float4 t[kMergeBatch];
+      float mv[kMergeBatch], lv[kMergeBatch], ev[kMergeBatch];
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const int s = s0 + kMergeGroups * k;
+        if (s < S) {
+          t[k] = load_part<D, H16>(part, pc + s * PS);
+          mv[k] = ml[ML * s];
+          lv[k] = ml[ML * s + 1];
+          ev[k] = H16 ? ml[ML * s + eo] : 0.f;
+        } else {
+          t[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+          mv[k] = -INFINITY;
+          lv[k] = 0.f;
+          ev[k] = 0.f;
+        }
+      }
+      float mb = mw;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) mb = fmaxf(mb, mv[k]);
+      if (mb > mw) {  // move the frame (mw = -inf: nothing added yet, factor 0)
+        const float r = fast_exp2(mw - mb);
+        a.x *= r; a.y *= r; a.z *= r; a.w *= r;
+        lw *= r;
+        mw = mb;
+      }
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        if (mv[k] != -INFINITY) {  // a split that saw none of the column's keys adds nothing
+          float f = fast_exp2(mv[k] - mw);
+          lw += f * lv[k];
+          if constexpr (H16) f = ldexpf(f, (int)ev[k]);
+          a.x += f * t[k].x; a.y += f * t[k].y; a.z += f * t[k].z; a.w += f * t[k].w;
+        }
+      }
+    }
+  }
+  red[sg][c][v] = a;
+  if (v == 0) {
+    red_m[sg][c] = mw;
+    red_l[sg][c] = lw;
+  }
+  __syncthreads();
+  if (sg != 0 || !valid) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kMergeGroups; ++w) M = fmaxf(M, red_m[w][c]);
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < kMergeGroups; ++w) {
+    if (red_m[w][c] == -INFINITY) continue;
+    const float f = fast_exp2(red_m[w][c] - M);
+    const float4 x = red[w][c][v];
+    o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;
+    L += f * red_l[w][c];
+  }
+  const float il = 1.f / L;
+  const int row = m / G, hh = m % G;
+  *reinterpret_cast<float4*>(out + (((size_t)b * R + row) * Hq + g * G + hh) * D + d) =
+      make_float4(o.x * il, o.y * il, o.z * il, o.w * il);
 }
 
 // Split count of a chunk: the one that minimises a model of the launch time.
@@ -1294,9 +1384,15 @@ hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.splits > 1) {
-    hipLaunchKernelGGL((prefill_merge_kernel<D, BF16>), dim3(p.m_tiles * 8, s.num_kv_heads, s.batch),
-                       dim3(256), 0, st, part, part_ml, out, s.num_q_heads, s.num_kv_heads, R,
-                       p.m_tiles, p.splits);
+    if (p.splits <= kMergeFew)
+      hipLaunchKernelGGL((prefill_merge_few_kernel<D, BF16>),
+                         dim3(p.m_tiles * (kMTile / 16), s.num_kv_heads, s.batch), dim3(256), 0, st,
+                         part, part_ml, out, s.num_q_heads, s.num_kv_heads, R, p.m_tiles, p.splits);
+    else
+      hipLaunchKernelGGL((prefill_merge_split_kernel<D, BF16>),
+                         dim3(p.m_tiles * (kMTile / 4) * (D / 64), s.num_kv_heads, s.batch),
+                         dim3(256), 0, st, part, part_ml, out, s.num_q_heads, s.num_kv_heads, R,
+                         p.m_tiles, p.splits);
     e = hipGetLastError();
   }
   return e;
@@ -1311,8 +1407,47 @@ static size_t partial_bytes(const Shape& s) {
                          : (size_t)(s.head_dim + 2) * sizeof(float);
 }
 
+// Chunks of at most kRowsMaxRows rows on bf16 caches may go to the streaming
+// decode kernel, its columns taken by the chunk's (row, head) pairs: it reads
+// each K / V row once per group of 16 pairs (the head groups of a split share
+// an XCD's L2, so the groups after the first mostly hit there), while an
+// M-tile spends the MFMA and LDS work of 128 columns whatever number of them
+// is used.  The faster one is picked on two estimates, in ns, linear in the
+// K / V positions read (sessions x KV heads x context) -- fits to measured
+// times on 8 query heads per KV head, head_dim 256, contexts 1K .. 128K,
+// batches 1 and 4: the streaming kernel's cost per position grows with its
+// head groups; the M-tile path pays about twice as much per position when
+// there is a single M-tile to split (all its parallelism then comes from
+// splitting the context) than when there are several, plus a cost per row.
+constexpr int kRowsMaxRows = 15;
+constexpr int kRowsMaxGroups = 8;
+
+static int rows_groups(const Shape& s, int R) {
+  const int G = s.num_q_heads / s.num_kv_heads;
+  return (R * G + 15) / 16;
+}
+
+static bool rows_path(const Shape& s, int R, int ctx) {
+  if (s.kv_dtype != 1 || R > kRowsMaxRows) return false;
+  const int G = s.num_q_heads / s.num_kv_heads;
+  const int hg = rows_groups(s, R);
+  if (hg > kRowsMaxGroups) return false;
+  const double pos = (double)s.batch * s.num_kv_heads * ctx * (s.head_dim / 256.0);
+  const long long units = (long long)s.batch * s.num_kv_heads * ((R * G + kMTile - 1) / kMTile);
+  const double t_rows = 10500.0 + pos * (0.17 + 0.06 * (hg - 1));
+  const double t_tile = 14000.0 + 350.0 * R + pos * (units == 1 ? 0.36 : 0.18);
+  return t_rows <= t_tile;
+}
+
 PrefillPlan plan_prefill(const Shape& s, int start, int R) {
-  PrefillPlan p;
+  PrefillPlan p{};
+  if (rows_path(s, R, start + R)) {
+    p.m_tiles = 0;
+    p.rows = plan_rows(s, R, start + R);
+    p.splits = p.rows.splits;
+    p.workspace_bytes = p.rows.workspace_bytes;
+    return p;
+  }
   const int G = s.num_q_heads / s.num_kv_heads;
   const long long M = (long long)R * G;
   p.m_tiles = (int)((M + kMTile - 1) / kMTile);
@@ -1335,12 +1470,21 @@ size_t prefill_workspace_bound(const Shape& s, int max_rows) {
     const size_t bytes = (size_t)units * S * kMTile * partial_bytes(s);
     if (bytes > best) best = bytes;
   }
+  // few-row chunks that may take the streaming kernel: its split count
+  // grows with the context, so the full capacity bounds every start
+  for (int R = 1; R <= max_rows && R <= kRowsMaxRows; ++R) {
+    if (s.kv_dtype != 1 || rows_groups(s, R) > kRowsMaxGroups) break;
+    const size_t bytes = plan_rows(s, R, s.capacity).workspace_bytes;
+    if (bytes > best) best = bytes;
+  }
   return best;
 }
 
 hipError_t launch_prefill(const Shape& s, const PrefillPlan& p, const float* q,
                           const void* k_cache, const void* v_cache, float* out, int start, int R,
                           float scale, void* workspace, hipStream_t stream) {
+  if (p.m_tiles == 0)
+    return launch_rows(s, p.rows, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
   const bool bf16 = s.kv_dtype == 1;
   switch (s.head_dim) {
     case 64: return bf16 ? launch_t<64, true>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream)
