@@ -374,6 +374,47 @@ def bench_rope(hold, reps=20):
     return res
 
 
+def bench_few_rows(hold, reps=20):
+    """Chunks of 1 .. 15 rows (the band between decode and the M-tile
+    prefill) ending at context 16384 and 131072 of one session, 8 query heads
+    on one KV head, head_dim 256, bf16 cache: event-timed medians per call."""
+    res = {}
+    for ctx in (16384, 131072):
+        shape = ka.Shape(1, 8, 1, 256, ctx, "bf16")
+        kc = ka.alloc_cache(shape)
+        vc = ka.alloc_cache(shape)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(11)
+        k = torch.randn(ctx * 256, device="cuda", generator=g)
+        v = torch.randn(ctx * 256, device="cuda", generator=g)
+        ka.append_kv(shape, kc, vc, k, v, 0, ctx)
+        del k, v
+        q = torch.randn(15 * 8 * 256, device="cuda", generator=g)
+        o = torch.empty_like(q)
+        ws = torch.zeros(max(1, ka.prefill_workspace_bytes(shape, 15)), dtype=torch.uint8,
+                         device="cuda")
+        row = {}
+        for R in (1, 2, 4, 8, 15):
+            n = R * 8 * 256
+            f = lambda: ka.prefill_chunk(shape, q[:n], kc, vc, o[:n], ctx - R, R, 1 / 16, ws)
+            f()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a, b = ev_pair()
+                hold(0.2)
+                a.record()
+                f()
+                b.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b) * 1e3)
+            row[str(R)] = round(float(np.median(ts)), 2)
+        res[f"ctx_{ctx}_us_by_rows"] = row
+        del kc, vc, q, o, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(session_w, budget_s=15.0):
     """The oracle (as written) on a bounded sample of the 16K prefill: 16-row
     blocks spaced evenly over all 16384 prompt rows (so the mean context is the
@@ -506,7 +547,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved_tf / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic.get("prefill_call_bytes_per_launch"), "traffic_unit": "B/launch",
-                     "kernel": "prefill chunk call (prefill_bf16_kernel + prefill_merge_kernel), "
+                     "kernel": "prefill chunk call (prefill_bf16_kernel + its merge kernel), "
                                "average over the 22 chunks",
                      "algorithmic_flops_per_step": flops, "causal_pairs": pairs,
                      "avg_launch_ms": round(pre_kernel_ms / len(w.chunks), 5)},
@@ -555,6 +596,7 @@ def main():
                                    "algorithmic_flops_per_launch": f["flops"]}
     torch.cuda.empty_cache()
     out["rope"] = bench_rope(hold)
+    out["few_row_chunks"] = bench_few_rows(hold)
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

@@ -359,7 +359,8 @@ void decode_split_kernel(
 
 // Combines the S split partials of one (session, KV head, head group) for
 // one head and 32 dims.  Thread (d, r) sums splits r, r + 8, ...; the loads
-// of its first 16 splits go out together with the (m, l) loads, so the merge
+// of its first 32 splits (all of them up to 256 splits, the most the MFMA
+// kernel's plans use) go out together with the (m, l) loads, so the merge
 // waits on memory about once.  The eight partial sums are added in a fixed
 // order, so the result does not depend on timing.
 template <int D>
@@ -370,7 +371,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   __shared__ float red[8][32];
   __shared__ float wmax[4], wsum[4];
   constexpr int NS = D / 32;
-  constexpr int EARLY = 16;
+  constexpr int EARLY = 32;
   const int h = blockIdx.x / NS, ds = blockIdx.x % NS;
   const int gh = blockIdx.y, bl = blockIdx.z, b = b0 + bl;
   const int g = gh / HG, hg = gh % HG;
