@@ -415,6 +415,63 @@ def bench_few_rows(hold, reps=20):
     return res
 
 
+def bench_ragged(hold, reps=20):
+    """Eight sessions of one 16K-capacity bf16 cache (8 query heads, one KV
+    head, head_dim 256), each with a chunk at its own position: one ragged
+    call against one chunk call per session (event-timed medians)."""
+    B, C = 8, 16384
+    shape = ka.Shape(B, 8, 1, 256, C, "bf16")
+    one = ka.Shape(1, 8, 1, 256, C, "bf16")
+    kc = ka.alloc_cache(shape)
+    vc = ka.alloc_cache(shape)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    k = torch.randn(B * C * 256, device="cuda", generator=g)
+    v = torch.randn(B * C * 256, device="cuda", generator=g)
+    ka.append_kv(shape, kc, vc, k, v, 0, C)
+    del k, v
+    slab = ka.cache_bytes(one)
+    res = {}
+    for name, rows in (("64_rows_each", [64] * B), ("mixed_768_to_1", [768, 16, 300, 1, 64, 128, 5, 512])):
+        starts = [C - r - 1000 * i for i, r in enumerate(rows)]
+        T = sum(rows)
+        q = torch.randn(T * 2048, device="cuda", generator=g)
+        o = torch.empty_like(q)
+        ws = torch.empty(max(ka.prefill_ragged_workspace_bytes(shape, T),
+                             ka.prefill_workspace_bytes(one, 768)), dtype=torch.uint8, device="cuda")
+
+        def ragged():
+            ka.prefill_ragged(shape, q, kc, vc, o, starts, rows, 1 / 16, ws)
+
+        def per_session():
+            r0 = 0
+            for b in range(B):
+                n = rows[b]
+                ka.prefill_chunk(one, q[r0 * 2048:(r0 + n) * 2048], kc[b * slab:(b + 1) * slab],
+                                 vc[b * slab:(b + 1) * slab], o[r0 * 2048:(r0 + n) * 2048],
+                                 starts[b], n, 1 / 16, ws)
+                r0 += n
+
+        row = {"rows": rows}
+        for nm, f in (("ragged_call_us", ragged), ("per_session_calls_us", per_session)):
+            f()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(reps):
+                a, b_ = ev_pair()
+                hold(0.2)
+                a.record()
+                f()
+                b_.record()
+                torch.cuda.synchronize()
+                ts.append(a.elapsed_time(b_) * 1e3)
+            row[nm] = round(float(np.median(ts)), 2)
+        res[name] = row
+    del kc, vc
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(session_w, budget_s=15.0):
     """The oracle (as written) on a bounded sample of the 16K prefill: 16-row
     blocks spaced evenly over all 16384 prompt rows (so the mean context is the
@@ -597,6 +654,7 @@ def main():
     torch.cuda.empty_cache()
     out["rope"] = bench_rope(hold)
     out["few_row_chunks"] = bench_few_rows(hold)
+    out["ragged_8_sessions_16k"] = bench_ragged(hold)
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)

@@ -233,6 +233,106 @@ ka_status ka_attn_decode_step(const ka_attn_shape* s, const float* q, const floa
                               const int32_t* pos, float scale, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/*
+ * Ragged batches: sessions at different positions in one call (several
+ * conversations served together, each continuing its own KV cache across
+ * turns; Karume v0.8.0 release notes, "Features": the multi-turn chat session
+ * and the per-run KV length).  start_pos and row_count are HOST arrays of B
+ * entries; session b covers positions start_pos[b] .. start_pos[b] +
+ * row_count[b] - 1 (row_count[b] == 0: the session takes no part).  Rows are
+ * packed session by session: the rows of session b start at row
+ * sum_{b' < b} row_count[b'] of every row array.  Each entry must satisfy
+ * row_count[b] >= 0, start_pos[b] >= 0 and start_pos[b] + row_count[b] <= C.
+ */
+
+/*
+ * Ragged KV append: k_new, v_new f32 [sum row_count][Hkv][D] (packed as
+ * above) are stored at each session's positions as ka_attn_append_kv stores
+ * them.  rope_cos / rope_sin: both NULL (no rotation) or f32 [sum row_count]
+ * [D/2] packed the same way, each row holding its own position's values; the
+ * K rows are then rotated as ka_attn_append_kv_rope rotates them.  All-zero
+ * row counts are a no-op.  Errors: KA_ERR_INVALID_ARGUMENT (null pointer,
+ * negative entry, only one of rope_cos / rope_sin), KA_ERR_OUT_OF_RANGE,
+ * KA_ERR_UNSUPPORTED, KA_ERR_HIP.
+ */
+ka_status ka_attn_append_kv_ragged(const ka_attn_shape* s, void* k_cache, void* v_cache,
+                                   const float* k_new, const float* v_new,
+                                   const float* rope_cos, const float* rope_sin,
+                                   const int32_t* start_pos, const int32_t* row_count,
+                                   void* stream);
+
+/*
+ * Workspace bytes that ka_attn_prefill_ragged needs for any call whose row
+ * counts add up to at most max_total_rows (0 if none is needed).
+ */
+size_t ka_attn_prefill_ragged_workspace_bytes(const ka_attn_shape* s, int64_t max_total_rows);
+
+/*
+ * Workspace bytes that one ka_attn_prefill_ragged call with these start_pos /
+ * row_count host arrays needs (never more than the bound above for their
+ * total; 0 if none is needed or the arguments are invalid).  Host only.
+ */
+size_t ka_attn_prefill_ragged_workspace_need(const ka_attn_shape* s, const int32_t* start_pos,
+                                             const int32_t* row_count);
+
+/*
+ * Ragged chunked prefill: row i of session b (i < row_count[b]) is at
+ * position start_pos[b] + i and attends to that session's cache positions
+ * 0 .. start_pos[b] + i, exactly as ka_attn_prefill_chunk with that session's
+ * start and row count.  q and out are f32 [sum row_count][Hq][D], packed as
+ * above; out may not alias q.  The sessions' tiles share each launch, so
+ * short chunks of many sessions fill the GPU together.  Every session runs
+ * on the M-tile kernel (on bf16 caches the few-row form of
+ * ka_attn_prefill_chunk is not used here).  workspace: device scratch of at
+ * least ka_attn_prefill_ragged_workspace_bytes(s, sum row_count) bytes.
+ * Errors: those of ka_attn_prefill_chunk, per entry.
+ */
+ka_status ka_attn_prefill_ragged(const ka_attn_shape* s, const float* q,
+                                 const void* k_cache, const void* v_cache, float* out,
+                                 const int32_t* start_pos, const int32_t* row_count, float scale,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Memory a session window costs before it is allocated (Karume v0.8.0
+ * release notes, "Features": the conversation-window bullet's session memory
+ * estimate for a capacity and chunk length; "Breaking Changes": the estimate
+ * counts the attention's transient buffers).  For shape s (its capacity is
+ * the window) and chunks of at most max_chunk_rows rows:
+ *   cache_bytes              K and V caches (2 x ka_attn_cache_bytes)
+ *   prefill_workspace_bytes  ka_attn_prefill_workspace_bytes(s, max_chunk_rows)
+ *   decode_workspace_bytes   ka_attn_decode_workspace_bytes(s, C)
+ *   chunk_io_bytes           one chunk's f32 q, out, k_new and v_new rows
+ *   total_bytes              cache + the larger workspace (prefill and decode
+ *                            calls can share one) + chunk_io_bytes
+ * Errors: KA_ERR_INVALID_ARGUMENT (m NULL), KA_ERR_OUT_OF_RANGE
+ * (max_chunk_rows outside 1 .. C), and the shape errors.
+ */
+typedef struct ka_attn_memory {
+  size_t cache_bytes;
+  size_t prefill_workspace_bytes;
+  size_t decode_workspace_bytes;
+  size_t chunk_io_bytes;
+  size_t total_bytes;
+} ka_attn_memory;
+ka_status ka_attn_session_memory(const ka_attn_shape* s, int32_t max_chunk_rows,
+                                 ka_attn_memory* m);
+
+/*
+ * Cache re-allocation to another window ("Gemma 4 E2B · WebGPU Kernels",
+ * "Top-bar Context Control": a context cap change re-allocates the on-device
+ * KV cache):
+ * copies cache positions 0 .. rows - 1 of every session and KV head from
+ * caches of shape src to caches of shape dst, which may differ from src in
+ * capacity only.  rows <= both capacities; positions at or past rows in dst
+ * are left undefined.  The copy is asynchronous on stream; the two cache
+ * pairs must not overlap.  Errors: KA_ERR_INVALID_ARGUMENT (shapes differ in
+ * more than capacity, rows < 0, null pointer, overlap),
+ * KA_ERR_OUT_OF_RANGE (rows above a capacity), the shape errors, KA_ERR_HIP.
+ */
+ka_status ka_attn_cache_resize(const ka_attn_shape* src, const void* src_k, const void* src_v,
+                               const ka_attn_shape* dst, void* dst_k, void* dst_v, int32_t rows,
+                               void* stream);
+
 /* Static name of a status code ("KA_OK", ...). */
 const char* ka_attn_status_string(int32_t status);
 

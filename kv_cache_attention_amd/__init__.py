@@ -20,7 +20,9 @@ __all__ = ["Shape", "KaAttnError", "KaAttnUnavailable", "lib", "lib_path", "F32"
            "cache_bytes", "alloc_cache", "append_kv", "prefill_workspace_bytes",
            "prefill_chunk", "decode_workspace_bytes", "decode", "status_string",
            "last_error", "abi_version", "EXPORTED_SYMBOLS", "decode_step", "append_kv_rope",
-           "rope_rows"]
+           "rope_rows", "append_kv_ragged", "prefill_ragged_workspace_bytes",
+           "prefill_ragged_workspace_need", "prefill_ragged",
+           "Memory", "session_memory", "cache_resize"]
 
 F32 = 0
 BF16 = 1
@@ -33,6 +35,9 @@ EXPORTED_SYMBOLS = (
     "ka_attn_rope_rows",
     "ka_attn_prefill_workspace_bytes", "ka_attn_prefill_chunk",
     "ka_attn_decode_workspace_bytes", "ka_attn_decode", "ka_attn_decode_step",
+    "ka_attn_append_kv_ragged", "ka_attn_prefill_ragged_workspace_bytes",
+    "ka_attn_prefill_ragged_workspace_need", "ka_attn_prefill_ragged",
+    "ka_attn_session_memory", "ka_attn_cache_resize",
     "ka_attn_status_string",
     "ka_attn_last_error",
 )
@@ -114,12 +119,35 @@ def lib() -> ctypes.CDLL:
     L.ka_attn_decode_step.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, ctypes.POINTER(c_int32), ctypes.c_float,
                                       c_void_p, c_size_t, c_void_p]
+    I32P = ctypes.POINTER(c_int32)
+    L.ka_attn_append_kv_ragged.restype = c_int32
+    L.ka_attn_append_kv_ragged.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                           c_void_p, I32P, I32P, c_void_p]
+    L.ka_attn_prefill_ragged_workspace_bytes.restype = c_size_t
+    L.ka_attn_prefill_ragged_workspace_bytes.argtypes = [P, ctypes.c_int64]
+    L.ka_attn_prefill_ragged_workspace_need.restype = c_size_t
+    L.ka_attn_prefill_ragged_workspace_need.argtypes = [P, I32P, I32P]
+    L.ka_attn_prefill_ragged.restype = c_int32
+    L.ka_attn_prefill_ragged.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, I32P, I32P,
+                                         ctypes.c_float, c_void_p, c_size_t, c_void_p]
+    L.ka_attn_session_memory.restype = c_int32
+    L.ka_attn_session_memory.argtypes = [P, c_int32, ctypes.POINTER(Memory)]
+    L.ka_attn_cache_resize.restype = c_int32
+    L.ka_attn_cache_resize.argtypes = [P, c_void_p, c_void_p, P, c_void_p, c_void_p, c_int32,
+                                       c_void_p]
     L.ka_attn_status_string.restype = ctypes.c_char_p
     L.ka_attn_status_string.argtypes = [c_int32]
     L.ka_attn_last_error.restype = ctypes.c_char_p
     L.ka_attn_last_error.argtypes = []
     _lib = L
     return L
+
+
+class Memory(ctypes.Structure):
+    """ka_attn_memory: what a session window costs (bytes)."""
+    _fields_ = [("cache_bytes", ctypes.c_size_t), ("prefill_workspace_bytes", ctypes.c_size_t),
+                ("decode_workspace_bytes", ctypes.c_size_t), ("chunk_io_bytes", ctypes.c_size_t),
+                ("total_bytes", ctypes.c_size_t)]
 
 
 def abi_version() -> int:
@@ -288,3 +316,83 @@ def decode_step(shape: Shape, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
     _check(lib().ka_attn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new),
                                      _ptr(k_cache), _ptr(v_cache), _ptr(out), arr, float(scale),
                                      _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def _int32_array(xs: Sequence[int], n: int, name: str):
+    if len(xs) != n:
+        raise ValueError(f"{name} has {len(xs)} entries, expected {n}")
+    return (ctypes.c_int32 * n)(*[int(x) for x in xs])
+
+
+def append_kv_ragged(shape: Shape, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                     k_new: torch.Tensor, v_new: torch.Tensor, start_pos: Sequence[int],
+                     row_count: Sequence[int], rope_cos: Optional[torch.Tensor] = None,
+                     rope_sin: Optional[torch.Tensor] = None, stream=None) -> None:
+    """ka_attn_append_kv_ragged: k_new / v_new f32 [sum row_count][Hkv][D], rows
+    packed session by session; rope_cos / rope_sin None or [sum row_count][D/2]."""
+    st = _int32_array(start_pos, shape.batch, "start_pos")
+    rc = _int32_array(row_count, shape.batch, "row_count")
+    total = sum(int(r) for r in row_count)
+    n = total * shape.num_kv_heads * shape.head_dim
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, torch.float32, n)
+    if rope_cos is not None or rope_sin is not None:
+        for t, nm in ((rope_cos, "rope_cos"), (rope_sin, "rope_sin")):
+            _need(t, nm, torch.float32, total * (shape.head_dim // 2))
+    cb = cache_bytes(shape)
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, None)
+        if t.numel() * t.element_size() < cb:
+            raise ValueError(f"{nm} is smaller than {cb} bytes")
+    _check(lib().ka_attn_append_kv_ragged(ctypes.byref(shape), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(k_new), _ptr(v_new), _ptr(rope_cos), _ptr(rope_sin),
+                                          st, rc, _stream(stream)))
+
+
+def prefill_ragged_workspace_bytes(shape: Shape, max_total_rows: int) -> int:
+    return int(lib().ka_attn_prefill_ragged_workspace_bytes(ctypes.byref(shape), int(max_total_rows)))
+
+
+def prefill_ragged_workspace_need(shape: Shape, start_pos: Sequence[int],
+                                  row_count: Sequence[int]) -> int:
+    return int(lib().ka_attn_prefill_ragged_workspace_need(
+        ctypes.byref(shape), _int32_array(start_pos, shape.batch, "start_pos"),
+        _int32_array(row_count, shape.batch, "row_count")))
+
+
+def prefill_ragged(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                   out: torch.Tensor, start_pos: Sequence[int], row_count: Sequence[int],
+                   scale: float, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """ka_attn_prefill_ragged: q / out f32 [sum row_count][Hq][D], rows packed
+    session by session."""
+    st = _int32_array(start_pos, shape.batch, "start_pos")
+    rc = _int32_array(row_count, shape.batch, "row_count")
+    n = sum(int(r) for r in row_count) * shape.num_q_heads * shape.head_dim
+    _need(q, "q", torch.float32, n)
+    _need(out, "out", torch.float32, n)
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", None)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().ka_attn_prefill_ragged(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(out), st, rc, float(scale), _ptr(workspace), ws_bytes,
+                                        _stream(stream)))
+
+
+def session_memory(shape: Shape, max_chunk_rows: int) -> Memory:
+    """ka_attn_session_memory: the bytes a window of shape.capacity costs."""
+    m = Memory()
+    _check(lib().ka_attn_session_memory(ctypes.byref(shape), int(max_chunk_rows), ctypes.byref(m)))
+    return m
+
+
+def cache_resize(src: Shape, src_k: torch.Tensor, src_v: torch.Tensor, dst: Shape,
+                 dst_k: torch.Tensor, dst_v: torch.Tensor, rows: int, stream=None) -> None:
+    """ka_attn_cache_resize: copy positions 0 .. rows - 1 into caches of another capacity."""
+    for t, nm, sh in ((src_k, "src_k", src), (src_v, "src_v", src), (dst_k, "dst_k", dst),
+                      (dst_v, "dst_v", dst)):
+        _need(t, nm, None)
+        if t.numel() * t.element_size() < cache_bytes(sh):
+            raise ValueError(f"{nm} is smaller than {cache_bytes(sh)} bytes")
+    _check(lib().ka_attn_cache_resize(ctypes.byref(src), _ptr(src_k), _ptr(src_v), ctypes.byref(dst),
+                                      _ptr(dst_k), _ptr(dst_v), int(rows), _stream(stream)))

@@ -61,6 +61,25 @@ ka_status check_scale(float scale) {
   return KA_OK;
 }
 
+// Per-session chunks of a ragged call: host arrays start / rows of B entries,
+// rows >= 0, start >= 0, start + rows <= capacity.  *total gets the row sum.
+ka_status check_ragged(const ka::Shape& sh, const int32_t* start, const int32_t* rows,
+                       long long* total) {
+  if (!start || !rows) return fail(KA_ERR_INVALID_ARGUMENT, "start_pos / row_count is NULL");
+  long long t = 0;
+  for (int b = 0; b < sh.batch; ++b) {
+    if (rows[b] < 0) return fail(KA_ERR_INVALID_ARGUMENT, "row_count[%d] = %d < 0", b, rows[b]);
+    if (start[b] < 0) return fail(KA_ERR_INVALID_ARGUMENT, "start_pos[%d] = %d < 0", b, start[b]);
+    if ((long long)start[b] + rows[b] > sh.capacity)
+      return fail(KA_ERR_OUT_OF_RANGE, "start_pos[%d] %d + row_count[%d] %d exceeds capacity %d", b,
+                  start[b], b, rows[b], sh.capacity);
+    t += rows[b];
+  }
+  if (t > 0x7fffffffLL) return fail(KA_ERR_OUT_OF_RANGE, "%lld rows in all exceed 2^31 - 1", t);
+  *total = t;
+  return KA_OK;
+}
+
 size_t cache_bytes(const ka::Shape& s) {
   return (size_t)s.batch * s.num_kv_heads * (size_t)s.capacity * s.head_dim *
          (s.kv_dtype == KA_DTYPE_BF16 ? 2 : 4);
@@ -119,6 +138,26 @@ ka_status ka_attn_append_kv_rope(const ka_attn_shape* s, void* k_cache, void* v_
   return ok();
 }
 
+ka_status ka_attn_append_kv_ragged(const ka_attn_shape* s, void* k_cache, void* v_cache,
+                                   const float* k_new, const float* v_new, const float* rope_cos,
+                                   const float* rope_sin, const int32_t* start_pos,
+                                   const int32_t* row_count, void* stream) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  long long total = 0;
+  if ((st = check_ragged(sh, start_pos, row_count, &total)) != KA_OK) return st;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr))
+    return fail(KA_ERR_INVALID_ARGUMENT, "rope_cos and rope_sin must both be given or both NULL");
+  if (total == 0) return ok();
+  if (!k_cache || !v_cache || !k_new || !v_new)
+    return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  hipError_t e = ka::launch_append_ragged(sh, k_cache, v_cache, k_new, v_new, start_pos, row_count,
+                                          reinterpret_cast<hipStream_t>(stream), rope_cos, rope_sin);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  return ok();
+}
+
 ka_status ka_attn_rope_rows(const ka_attn_shape* s, const float* x, float* y,
                             const float* rope_cos, const float* rope_sin, int32_t row_count,
                             void* stream) {
@@ -166,6 +205,117 @@ ka_status ka_attn_prefill_chunk(const ka_attn_shape* s, const float* q, const vo
   hipError_t e = ka::launch_prefill(sh, plan, q, k_cache, v_cache, out, start_pos, row_count,
                                     scale, workspace, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
+size_t ka_attn_prefill_ragged_workspace_bytes(const ka_attn_shape* s, int64_t max_total_rows) {
+  ka::Shape sh;
+  if (check_shape(s, &sh) != KA_OK) return 0;
+  return ka::prefill_ragged_workspace_bound(sh, max_total_rows);
+}
+
+size_t ka_attn_prefill_ragged_workspace_need(const ka_attn_shape* s, const int32_t* start_pos,
+                                             const int32_t* row_count) {
+  ka::Shape sh;
+  if (check_shape(s, &sh) != KA_OK) return 0;
+  long long total = 0;
+  if (check_ragged(sh, start_pos, row_count, &total) != KA_OK || total == 0) return 0;
+  return ka::prefill_ragged_workspace(sh, start_pos, row_count);
+}
+
+ka_status ka_attn_prefill_ragged(const ka_attn_shape* s, const float* q, const void* k_cache,
+                                 const void* v_cache, float* out, const int32_t* start_pos,
+                                 const int32_t* row_count, float scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  long long total = 0;
+  if ((st = check_ragged(sh, start_pos, row_count, &total)) != KA_OK) return st;
+  if ((st = check_scale(scale)) != KA_OK) return st;
+  if (total == 0) return ok();
+  if (!q || !k_cache || !v_cache || !out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if ((const void*)q == (const void*)out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "out must not alias q");
+  const size_t need = ka::prefill_ragged_workspace(sh, start_pos, row_count);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(KA_ERR_WORKSPACE, "ragged prefill needs %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  hipError_t e = ka::launch_prefill_ragged(sh, q, k_cache, v_cache, out, start_pos, row_count,
+                                           scale, workspace, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ragged prefill launch");
+  return ok();
+}
+
+ka_status ka_attn_session_memory(const ka_attn_shape* s, int32_t max_chunk_rows,
+                                 ka_attn_memory* m) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  if (!m) return fail(KA_ERR_INVALID_ARGUMENT, "memory estimate pointer is NULL");
+  if (max_chunk_rows < 1 || max_chunk_rows > sh.capacity)
+    return fail(KA_ERR_OUT_OF_RANGE, "max_chunk_rows %d outside 1..capacity (%d)", max_chunk_rows,
+                sh.capacity);
+  m->cache_bytes = 2 * cache_bytes(sh);
+  m->prefill_workspace_bytes = ka::prefill_workspace_bound(sh, max_chunk_rows);
+  m->decode_workspace_bytes = ka::plan_decode(sh, sh.capacity).workspace_bytes;
+  m->chunk_io_bytes = (size_t)sh.batch * max_chunk_rows *
+                      (2 * (size_t)sh.num_q_heads + 2 * (size_t)sh.num_kv_heads) * sh.head_dim *
+                      sizeof(float);
+  const size_t ws = m->prefill_workspace_bytes > m->decode_workspace_bytes
+                        ? m->prefill_workspace_bytes
+                        : m->decode_workspace_bytes;
+  m->total_bytes = m->cache_bytes + ws + m->chunk_io_bytes;
+  return ok();
+}
+
+ka_status ka_attn_cache_resize(const ka_attn_shape* src, const void* src_k, const void* src_v,
+                               const ka_attn_shape* dst, void* dst_k, void* dst_v, int32_t rows,
+                               void* stream) {
+  ka::Shape a, b;
+  ka_status st = check_shape(src, &a);
+  if (st != KA_OK) return st;
+  if ((st = check_shape(dst, &b)) != KA_OK) return st;
+  if (a.batch != b.batch || a.num_q_heads != b.num_q_heads || a.num_kv_heads != b.num_kv_heads ||
+      a.head_dim != b.head_dim || a.kv_dtype != b.kv_dtype)
+    return fail(KA_ERR_INVALID_ARGUMENT, "source and destination differ in more than capacity");
+  if (rows < 0) return fail(KA_ERR_INVALID_ARGUMENT, "rows %d < 0", rows);
+  if (rows > a.capacity || rows > b.capacity)
+    return fail(KA_ERR_OUT_OF_RANGE, "rows %d exceed a capacity (%d -> %d)", rows, a.capacity,
+                b.capacity);
+  if (rows == 0) return ok();
+  if (!src_k || !src_v || !dst_k || !dst_v)
+    return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  const size_t es = a.kv_dtype == KA_DTYPE_BF16 ? 2 : 4;
+  const size_t src_slab = (size_t)a.capacity * a.head_dim * es;
+  const size_t dst_slab = (size_t)b.capacity * b.head_dim * es;
+  const size_t nslab = (size_t)a.batch * a.num_kv_heads;
+  // the two caches must not overlap (a copy in place is not a resize)
+  auto apart = [&](const void* x, const void* y, size_t nx, size_t ny) {
+    const char* p = static_cast<const char*>(x);
+    const char* q = static_cast<const char*>(y);
+    return p + nx <= q || q + ny <= p;
+  };
+  if (!apart(src_k, dst_k, nslab * src_slab, nslab * dst_slab) ||
+      !apart(src_v, dst_v, nslab * src_slab, nslab * dst_slab) ||
+      !apart(src_k, dst_v, nslab * src_slab, nslab * dst_slab) ||
+      !apart(src_v, dst_k, nslab * src_slab, nslab * dst_slab))
+    return fail(KA_ERR_INVALID_ARGUMENT, "source and destination caches overlap");
+  // positions 0 .. rows - 1 of a slab are a prefix of it in both layouts:
+  // whole 64-position K blocks, whole V groups (32 positions for bf16, 4 for
+  // f32); both capacities are multiples of 64 >= rows, so the rounded
+  // prefix fits either slab
+  const size_t k_pos = ((size_t)rows + 63) / 64 * 64;
+  const size_t v_unit = a.kv_dtype == KA_DTYPE_BF16 ? 32 : 4;
+  const size_t v_pos = ((size_t)rows + v_unit - 1) / v_unit * v_unit;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpy2DAsync(dst_k, dst_slab, src_k, src_slab, k_pos * a.head_dim * es,
+                                  nslab, hipMemcpyDeviceToDevice, hs);
+  if (e == hipSuccess)
+    e = hipMemcpy2DAsync(dst_v, dst_slab, src_v, src_slab, v_pos * a.head_dim * es, nslab,
+                         hipMemcpyDeviceToDevice, hs);
+  if (e != hipSuccess) return hip_fail(e, "cache resize copy");
   return ok();
 }
 

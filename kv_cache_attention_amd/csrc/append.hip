@@ -1,9 +1,13 @@
-// KV append: new f32 rows [B][R][Hkv][D] -> cache positions start..start+R-1.
+// KV append: new f32 rows [rows][Hkv][D] of each session -> its cache
+// positions start .. start + rows - 1 (a uniform chunk: every session the
+// same start and rows, rows packed session by session as [B][R][Hkv][D]).
 //
 // One thread produces one 16-byte cache vector, so every store is a full
 // 16-byte store except where a V vector (which spans 4 or 8 positions) is
 // only partly covered by the appended range; there the covered elements are
 // stored one by one and the rest of the vector is left untouched.
+#include <vector>
+
 #include "ka_common.h"
 #include "ka_launch.h"
 
@@ -37,30 +41,59 @@ __device__ __forceinline__ void rope4(float4 a, float4 b, float4 c, float4 s, fl
   hi.w = rounded_mul(b.w, c.w) + rounded_mul(a.w, s.w);
 }
 
-// ROPE: each new K row is rotated by its position's angles (cos / sin rows
-// [R][D/2], row i for position start + i) before it is stored; V as given.
+// The sessions of one append launch, one per blockIdx.y: session i writes
+// rows[i] rows at positions start[i] .. of cache slab b[i], reading rows
+// row0[i] .. of k_new / v_new and cos / sin rows rope_row0[i] ...
+constexpr int kAppendSessions = 32;
+struct AppendArg {
+  int n;
+  int b[kAppendSessions], start[kAppendSessions], rows[kAppendSessions];
+  int row0[kAppendSessions], rope_row0[kAppendSessions];
+};
+
+// First V group and group count overlapping positions [start, start + R)
+// (a group holds E positions; bf16 groups interleave within a 32-position
+// block, so whole blocks are covered).
+__host__ __device__ __forceinline__ void v_groups(bool bf16, int start, int R, int& g0, int& ng) {
+  int g1;
+  if (bf16) {
+    g0 = (start >> 5) * 4;
+    g1 = ((start + R - 1) >> 5) * 4 + 4;
+  } else {
+    g0 = start >> 2;
+    g1 = ((start + R - 1) >> 2) + 1;
+  }
+  ng = g1 - g0;
+}
+
+// ROPE: each new K row is rotated by its position's angles (cos / sin rows of
+// D/2 values, one per appended row) before it is stored; V as given.
 template <bool BF16, bool ROPE>
 __global__ __launch_bounds__(256) void append_kernel(
     void* __restrict__ k_cache, void* __restrict__ v_cache,
     const float* __restrict__ k_new, const float* __restrict__ v_new,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
-    int Hkv, int D, int C, int start, int R,
-    long long n_k_vecs, long long n_v_vecs, int v_groups_per_slab, int v_group0) {
+    int Hkv, int D, int C, const AppendArg aa) {
   constexpr int E = Elem<BF16>::E;
   const int cpr = D / E;  // K vectors per row
+  const int si = blockIdx.y;
+  const int b = aa.b[si], start = aa.start[si], R = aa.rows[si], row0 = aa.row0[si];
+  const int rr0 = aa.rope_row0[si];
+  int v_group0, v_groups_per_slab;
+  v_groups(BF16, start, R, v_group0, v_groups_per_slab);
+  const long long n_k_vecs = (long long)R * Hkv * cpr;
+  const long long n_v_vecs = (long long)Hkv * v_groups_per_slab * D;
   long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long stride = (long long)gridDim.x * blockDim.x;
   for (long long i = tid; i < n_k_vecs + n_v_vecs; i += stride) {
     if (i < n_k_vecs) {
-      // K vector: (b, g, row, c) with c innermost
+      // K vector: (row, g, c) with c innermost
       const int c = (int)(i % cpr);
       long long t = i / cpr;
       const int g = (int)(t % Hkv);
-      t /= Hkv;
-      const int row = (int)(t % R);
-      const int b = (int)(t / R);
+      const int row = (int)(t / Hkv);
       const int j = start + row;
-      const float* rowp = k_new + (((size_t)b * R + row) * Hkv + g) * D;
+      const float* rowp = k_new + (((size_t)row0 + row) * Hkv + g) * D;
       const float* src = rowp + c * E;
       const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;  // elements
       const size_t vi = k_vec_index(j, c, D, E);
@@ -69,8 +102,8 @@ __global__ __launch_bounds__(256) void append_kernel(
         // this vector's E dims and their partners in the other half
         const int h = D >> 1;
         const int d0 = c * E, j0 = d0 < h ? d0 : d0 - h;
-        const float* cr = rope_cos + (size_t)row * h + j0;
-        const float* sr = rope_sin + (size_t)row * h + j0;
+        const float* cr = rope_cos + ((size_t)rr0 + row) * h + j0;
+        const float* sr = rope_sin + ((size_t)rr0 + row) * h + j0;
 #pragma unroll
         for (int e = 0; e < E; e += 4) {
           const float4 a = *reinterpret_cast<const float4*>(rowp + j0 + e);
@@ -100,14 +133,12 @@ __global__ __launch_bounds__(256) void append_kernel(
             make_float4(f[0], f[1], f[2], f[3]);
       }
     } else {
-      // V vector: (b, g, group, d) with d innermost; a group spans E positions
+      // V vector: (g, group, d) with d innermost; a group spans E positions
       const long long iv = i - n_k_vecs;
       const int d = (int)(iv % D);
-      long long t = iv / D;
+      const long long t = iv / D;
       const int gi = (int)(t % v_groups_per_slab) + v_group0;
-      t /= v_groups_per_slab;
-      const int g = (int)(t % Hkv);
-      const int b = (int)(t / Hkv);
+      const int g = (int)(t / v_groups_per_slab);
       const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;
       float vals[E];
       bool have[E];
@@ -120,7 +151,7 @@ __global__ __launch_bounds__(256) void append_kernel(
         const int row = j - start;
         have[s] = row >= 0 && row < R;
         all = all && have[s];
-        vals[s] = have[s] ? v_new[(((size_t)b * R + row) * Hkv + g) * D + d] : 0.f;
+        vals[s] = have[s] ? v_new[(((size_t)row0 + row) * Hkv + g) * D + d] : 0.f;
       }
       const size_t vi = (size_t)gi * D + d;
       if constexpr (BF16) {
@@ -151,39 +182,84 @@ __global__ __launch_bounds__(256) void append_kernel(
   }
 }
 
+// Launches the append for the sessions of tables L (grid: blocks x
+// sessions of a table).
+static hipError_t launch_append_tables(const Shape& s, void* k_cache, void* v_cache,
+                                       const float* k_new, const float* v_new,
+                                       const float* rope_cos, const float* rope_sin,
+                                       const std::vector<AppendArg>& L, hipStream_t stream) {
+  const bool bf16 = s.kv_dtype == 1;
+  const int E = bf16 ? 8 : 4;
+  const bool rope = rope_cos != nullptr;
+  for (const AppendArg& aa : L) {
+    long long most = 0;  // vectors of the largest session
+    for (int i = 0; i < aa.n; ++i) {
+      int g0, ng;
+      v_groups(bf16, aa.start[i], aa.rows[i], g0, ng);
+      const long long n = (long long)aa.rows[i] * s.num_kv_heads * (s.head_dim / E) +
+                          (long long)s.num_kv_heads * ng * s.head_dim;
+      if (n > most) most = n;
+    }
+    long long blocks = (most + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    const dim3 grid((unsigned)blocks, aa.n);
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, k_cache, v_cache, k_new, v_new,
+                         rope_cos, rope_sin, s.num_kv_heads, s.head_dim, s.capacity, aa);
+    };
+    if (bf16 && rope) go(append_kernel<true, true>);
+    else if (bf16) go(append_kernel<true, false>);
+    else if (rope) go(append_kernel<false, true>);
+    else go(append_kernel<false, false>);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Sessions with rows, kAppendSessions per table, packed rows in session
+// order; cos / sin rows shared by all sessions (shared_rope) or packed like
+// the rows.
+template <class Rows, class Start>
+static std::vector<AppendArg> append_tables(int batch, Rows rows_of, Start start_of,
+                                            bool shared_rope) {
+  std::vector<AppendArg> L;
+  AppendArg cur{};
+  long long row = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int R = rows_of(b);
+    if (R <= 0) continue;
+    if (cur.n == kAppendSessions) {
+      L.push_back(cur);
+      cur = AppendArg{};
+    }
+    const int i = cur.n++;
+    cur.b[i] = b;
+    cur.start[i] = start_of(b);
+    cur.rows[i] = R;
+    cur.row0[i] = (int)row;
+    cur.rope_row0[i] = shared_rope ? 0 : (int)row;
+    row += R;
+  }
+  if (cur.n > 0) L.push_back(cur);
+  return L;
+}
+
 hipError_t launch_append(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
                          const float* v_new, int start, int R, hipStream_t stream,
                          const float* rope_cos, const float* rope_sin) {
-  const bool bf16 = s.kv_dtype == 1;
-  const int E = bf16 ? 8 : 4;
-  const long long n_k = (long long)s.batch * R * s.num_kv_heads * (s.head_dim / E);
-  // V groups (of E positions) overlapping [start, start + R)
-  int g0, g1;
-  if (bf16) {
-    // groups are not contiguous in position within a 32-block: cover whole blocks
-    g0 = (start >> 5) * 4;
-    g1 = ((start + R - 1) >> 5) * 4 + 4;
-  } else {
-    g0 = start >> 2;
-    g1 = ((start + R - 1) >> 2) + 1;
-  }
-  const int ng = g1 - g0;
-  const long long n_v = (long long)s.batch * s.num_kv_heads * ng * s.head_dim;
-  const long long total = n_k + n_v;
-  const int threads = 256;
-  long long blocks = (total + threads - 1) / threads;
-  if (blocks > 65536) blocks = 65536;
-  const bool rope = rope_cos != nullptr;
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(threads), 0, stream, k_cache, v_cache,
-                       k_new, v_new, rope_cos, rope_sin, s.num_kv_heads, s.head_dim, s.capacity,
-                       start, R, n_k, n_v, ng, g0);
-  };
-  if (bf16 && rope) go(append_kernel<true, true>);
-  else if (bf16) go(append_kernel<true, false>);
-  else if (rope) go(append_kernel<false, true>);
-  else go(append_kernel<false, false>);
-  return hipGetLastError();
+  const auto L = append_tables(
+      s.batch, [&](int) { return R; }, [&](int) { return start; }, true);
+  return launch_append_tables(s, k_cache, v_cache, k_new, v_new, rope_cos, rope_sin, L, stream);
+}
+
+hipError_t launch_append_ragged(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
+                                const float* v_new, const int32_t* start, const int32_t* rows,
+                                hipStream_t stream, const float* rope_cos,
+                                const float* rope_sin) {
+  const auto L = append_tables(
+      s.batch, [&](int b) { return rows[b]; }, [&](int b) { return start[b]; }, false);
+  return launch_append_tables(s, k_cache, v_cache, k_new, v_new, rope_cos, rope_sin, L, stream);
 }
 
 // Rotary embedding of query rows: x, y f32 [B][R][H][D] (y may be x), each

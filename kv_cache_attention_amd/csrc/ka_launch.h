@@ -25,6 +25,13 @@ struct CtxArg {
 hipError_t launch_append(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
                          const float* v_new, int start, int R, hipStream_t stream,
                          const float* rope_cos = nullptr, const float* rope_sin = nullptr);
+// Ragged: session b appends rows[b] rows (0: none) at positions start[b] ..,
+// rows packed in session order in k_new / v_new ([sum rows][Hkv][D]) and in
+// rope_cos / rope_sin when given.  start / rows are host arrays [B].
+hipError_t launch_append_ragged(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
+                                const float* v_new, const int32_t* start, const int32_t* rows,
+                                hipStream_t stream, const float* rope_cos = nullptr,
+                                const float* rope_sin = nullptr);
 // Rotary embedding of f32 rows x -> y ([B][R][H][D], y may be x).
 hipError_t launch_rope_rows(const float* x, float* y, const float* rope_cos,
                             const float* rope_sin, int B, int R, int H, int D,
@@ -55,6 +62,15 @@ size_t prefill_workspace_bound(const Shape& s, int max_rows);
 hipError_t launch_prefill(const Shape& s, const PrefillPlan& p, const float* q,
                           const void* k_cache, const void* v_cache, float* out, int start, int R,
                           float scale, void* workspace, hipStream_t stream);
+// Ragged prefill: session b's rows[b] rows (0: none) at positions start[b] ..,
+// packed in session order in q / out ([sum rows][Hq][D]); all sessions' tiles
+// share each launch.  start / rows are host arrays [B].
+size_t prefill_ragged_workspace(const Shape& s, const int32_t* start, const int32_t* rows);
+size_t prefill_ragged_workspace_bound(const Shape& s, long long max_total_rows);
+hipError_t launch_prefill_ragged(const Shape& s, const float* q, const void* k_cache,
+                                 const void* v_cache, float* out, const int32_t* start,
+                                 const int32_t* rows, float scale, void* workspace,
+                                 hipStream_t stream);
 
 // ---- decode
 DecodePlan plan_decode(const Shape& s, int max_ctx);

@@ -28,6 +28,7 @@
 // acc) and a second kernel combines them in fixed split order.
 #include <cfloat>
 #include <type_traits>
+#include <vector>
 
 #include "ka_common.h"
 #include "ka_launch.h"
@@ -83,32 +84,63 @@ __device__ __forceinline__ void load_tile(const TileSrc& src, int tile, unsigned
   }
 }
 
-// Per-block constants of the tiling.
+// The sessions of one prefill launch.  Session i: rows start[i] ..
+// start[i] + rows[i] - 1, stored at packed rows row0[i] .. of q and out; cache
+// slab b[i]; m_tiles[i] M-tiles and splits[i] key-range splits per KV head;
+// partial slots from slot0[i] (KV head, m-tile, split order); work items
+// item0[i] .. item0[i + 1] - 1.  A uniform chunk over B sessions is B equal
+// entries (launched kChunkSessions at a time).
+constexpr int kChunkSessions = 32;
+struct ChunkArg {
+  int n;
+  int b[kChunkSessions], start[kChunkSessions], rows[kChunkSessions], m_tiles[kChunkSessions];
+  int splits[kChunkSessions], row0[kChunkSessions], slot0[kChunkSessions];
+  int item0[kChunkSessions + 1];
+};
+
+// Per-block constants of the tiling.  The block's session: rows start ..
+// start + R - 1 at packed rows row0 .. of q / out, m_tiles M-tiles and S
+// splits per KV head; slot is its partial slot of split 0 (one slot holds
+// one split's 128-column partial).
 struct Tiling {
   int mt, split, g, b, G, M_total, lr, lg, w, lane, tid;
   int m_base, row_lo, kt0, kt1, kend;
+  int start, R, m_tiles, S, row0;
+  long long slot;
   int m_col[2], row_col[2];
   bool valid_col[2];
 };
 
-// Block -> (m-tile, split).  Work items are ordered m-tile-major (every split
-// of m-tile 0, then of m-tile 1, ...) and dealt to the 8 XCDs in contiguous
-// runs: consecutive workgroups go to the XCDs round-robin, so block x runs on
-// XCD x % 8 and takes item (x % 8) * per + x / 8.  The splits of an m-tile
-// then share one XCD, whose L2 serves their common Q rows (read once per
-// workgroup) while the key tiles stream past.  The grid is padded to 8 * per
-// blocks; blocks past the last item return false.
-__device__ __forceinline__ bool make_tiling(int Hq, int Hkv, int start, int R, int S,
-                                            int m_tiles, Tiling& t) {
-  const int items = m_tiles * S;
+// Block -> (session, KV head, m-tile, split).  The sessions' work items are
+// numbered session by session, each (KV head, m-tile)-major with the split
+// fastest, and dealt to the 8 XCDs in contiguous runs: consecutive
+// workgroups go to the XCDs round-robin, so block x runs on XCD x % 8 and
+// takes item (x % 8) * per + x / 8.  The splits of an m-tile then share one
+// XCD, whose L2 serves their common Q rows (read once per workgroup) while
+// the key tiles stream past.  The grid is padded to 8 * per blocks; blocks
+// past the last item return false.
+__device__ __forceinline__ bool make_tiling(const ChunkArg& ca, int Hq, int Hkv, Tiling& t) {
+  const int items = ca.item0[ca.n];
   const int per = (items + 7) >> 3;
   const int x = blockIdx.x;
   const int item = (x & 7) * per + (x >> 3);
   if (item >= items) return false;
-  t.mt = item / S;
-  t.split = item - t.mt * S;
-  t.g = blockIdx.y;
-  t.b = blockIdx.z;
+  int i = 0;
+  while (item >= ca.item0[i + 1]) ++i;
+  const int S = ca.splits[i], m_tiles = ca.m_tiles[i];
+  const int local = item - ca.item0[i];
+  const int gm = local / S;  // (KV head, m-tile)
+  t.split = local - gm * S;
+  t.g = gm / m_tiles;
+  t.mt = gm - t.g * m_tiles;
+  t.b = ca.b[i];
+  t.start = ca.start[i];
+  t.R = ca.rows[i];
+  t.m_tiles = m_tiles;
+  t.S = S;
+  t.row0 = ca.row0[i];
+  t.slot = (long long)ca.slot0[i] + (long long)gm * S;
+  const int start = t.start, R = t.R;
   t.G = Hq / Hkv;
   t.M_total = R * t.G;
   t.tid = threadIdx.x;
@@ -140,7 +172,7 @@ __device__ __forceinline__ void load_q(const Tiling& t, const float* __restrict_
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int m = t.m_col[mb];
-    const float* qp = q + (((size_t)t.b * R + m / t.G) * Hq + t.g * t.G + m % t.G) * D;
+    const float* qp = q + (((size_t)t.row0 + m / t.G) * Hq + t.g * t.G + m % t.G) * D;
 #pragma unroll
     for (int ks = 0; ks < NQ; ++ks) {
       if constexpr (BF16) {
@@ -364,7 +396,7 @@ __device__ __forceinline__ void store_result(const Tiling& t, float* __restrict_
     if (!t.valid_col[mb]) continue;
     if (S == 1) {
       const int m = t.m_col[mb];
-      float* op = out + (((size_t)t.b * R + m / t.G) * Hq + t.g * t.G + m % t.G) * D;
+      float* op = out + (((size_t)t.row0 + m / t.G) * Hq + t.g * t.G + m % t.G) * D;
       const float inv = 1.f / lt;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
@@ -372,17 +404,16 @@ __device__ __forceinline__ void store_result(const Tiling& t, float* __restrict_
         *reinterpret_cast<float4*>(op + 16 * db + 4 * t.lg) = make_float4(o[0], o[1], o[2], o[3]);
       }
     } else {
-      // acc [tile][S][128 columns][D]; (m, l) [tile][128 columns][S][2]
-      const size_t tile_id = ((size_t)t.b * Hkv + t.g) * m_tiles + t.mt;
+      // acc [slot][128 columns][D]; (m, l) [tile][128 columns][S][2]
       const int col = t.m_col[mb] - t.m_base;
-      float* pp = part + ((tile_id * S + t.split) * kMTile + col) * D;
+      float* pp = part + (((size_t)t.slot + t.split) * kMTile + col) * D;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const v4f o = acc_o[db][mb];
         *reinterpret_cast<float4*>(pp + 16 * db + 4 * t.lg) = make_float4(o[0], o[1], o[2], o[3]);
       }
       if (t.lg == 0) {
-        float* ml = part_ml + ((tile_id * kMTile + col) * S + t.split) * 2;
+        float* ml = part_ml + ((size_t)t.slot * kMTile + (size_t)col * S + t.split) * 2;
         ml[0] = m_run[mb];
         ml[1] = lt;
       }
@@ -512,8 +543,7 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(256) void prefill_pipe_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
-    float* __restrict__ part_ml, int Hq, int Hkv, int C, int start, int R, int m_tiles, int S,
-    float sl2e) {
+    float* __restrict__ part_ml, int Hq, int Hkv, int C, const ChunkArg ca, float sl2e) {
   using Cfg = PrefillCfg<D, BF16>;
   constexpr int NDB = Cfg::NDB, TB = Cfg::TILE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char kb0[TB];
@@ -522,7 +552,8 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char vb1[TB];
 
   Tiling t;
-  if (!make_tiling(Hq, Hkv, start, R, S, m_tiles, t)) return;
+  if (!make_tiling(ca, Hq, Hkv, t)) return;
+  const int start = t.start, R = t.R, m_tiles = t.m_tiles, S = t.S;
   const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;  // elements
   constexpr int ES = BF16 ? 2 : 4;
   const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * ES, (size_t)C * D * ES);
@@ -666,7 +697,7 @@ __device__ __forceinline__ void load_q_half(const Tiling& t, const ColB& c, int 
                                             const float* __restrict__ q, int R, int Hq,
                                             float sl2e, bf16x8 (&qreg)[D / 16],
                                             uint4* __restrict__ q_lds) {
-  const float* qp = q + (((size_t)t.b * R + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D;
+  const float* qp = q + (((size_t)t.row0 + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     if (ks / (D / 32) != kh) continue;
@@ -838,7 +869,7 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, i
                                                int R, int Hq, int Hkv, int m_tiles, int S) {
   if (!c.valid) return;
   if (S == 1) {
-    float* op = out + (((size_t)t.b * R + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D + kh * (D / 2);
+    float* op = out + (((size_t)t.row0 + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D + kh * (D / 2);
     const float sc = 1.f / l_tot;
     // lane holds dims 32 db + 8 a + 4 h + 0..3 of this wave's half
 #pragma unroll
@@ -850,7 +881,6 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, i
                         acc[db][4 * a + 3] * sc);
     return;
   }
-  const size_t tile_id = ((size_t)t.b * Hkv + t.g) * m_tiles + t.mt;
   const int col = c.m - t.m_base;
   float amax = 0.f;
 #pragma unroll
@@ -863,7 +893,7 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, i
   int e = 0;
   if (amax > 0.f) (void)frexpf(amax, &e);
   const float sc = ldexpf(1.f, -e);
-  _Float16* pp = reinterpret_cast<_Float16*>(part) + ((tile_id * S + t.split) * kMTile + col) * D +
+  _Float16* pp = reinterpret_cast<_Float16*>(part) + (((size_t)t.slot + t.split) * kMTile + col) * D +
                  kh * (D / 2);
 #pragma unroll
   for (int db = 0; db < D / 64; ++db)
@@ -874,7 +904,7 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, i
       for (int k = 0; k < 4; ++k) h[k] = (_Float16)(acc[db][4 * a + k] * sc);
       *reinterpret_cast<half4*>(pp + 32 * db + 8 * a + 4 * c.lh) = h;
     }
-  float* ml = part_ml + ((tile_id * kMTile + col) * S + t.split) * 6;
+  float* ml = part_ml + ((size_t)t.slot * kMTile + (size_t)col * S + t.split) * 6;
   if (kh == 0 && c.lh == 0) {
     ml[0] = m_ref;
     ml[1] = l_tot;
@@ -886,8 +916,7 @@ template <int D>
 __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, float* __restrict__ out, void* __restrict__ part,
-    float* __restrict__ part_ml, int Hq, int Hkv, int C, int start, int R, int m_tiles, int S,
-    float sl2e) {
+    float* __restrict__ part_ml, int Hq, int Hkv, int C, const ChunkArg ca, float sl2e) {
   constexpr int TB = PrefillCfg<D, true>::TILE_BYTES;
   constexpr int NT = kBf16Threads;
   // K(0), K(1), V(0), V(1), then two weight-exchange buffers of 16 KiB.  The
@@ -902,7 +931,8 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
   uint4* const xp = reinterpret_cast<uint4*>(lds + 4 * TB);
 
   Tiling t;
-  if (!make_tiling(Hq, Hkv, start, R, S, m_tiles, t)) return;
+  if (!make_tiling(ca, Hq, Hkv, t)) return;
+  const int start = t.start, R = t.R, m_tiles = t.m_tiles, S = t.S;
   const int kh = t.w >> 2, partner = t.w ^ 4;
   const ColB c = col_b(t, t.w & 3, start);
   const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;  // elements
@@ -1097,15 +1127,15 @@ template <int D, bool BF16>
 __global__ __launch_bounds__(256) void prefill_seq_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
-    float* __restrict__ part_ml, int Hq, int Hkv, int C, int start, int R, int m_tiles, int S,
-    float sl2e) {
+    float* __restrict__ part_ml, int Hq, int Hkv, int C, const ChunkArg ca, float sl2e) {
   using Cfg = PrefillCfg<D, BF16>;
   constexpr int NDB = Cfg::NDB, TB = Cfg::TILE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char kb[TB];
   __shared__ __attribute__((aligned(16))) unsigned char vb[TB];
 
   Tiling t;
-  if (!make_tiling(Hq, Hkv, start, R, S, m_tiles, t)) return;
+  if (!make_tiling(ca, Hq, Hkv, t)) return;
+  const int start = t.start, R = t.R, m_tiles = t.m_tiles, S = t.S;
   const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;
   constexpr int ES = BF16 ? 2 : 4;
   const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * ES, (size_t)C * D * ES);
@@ -1173,20 +1203,22 @@ __device__ __forceinline__ float4 load_part(const void* base, size_t idx) {
 template <int D, bool H16>
 __global__ __launch_bounds__(256) void prefill_merge_few_kernel(
     const void* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
-    int Hq, int Hkv, int R, int m_tiles, int S) {
+    int Hq, int Hkv, const ChunkArg ca) {
   constexpr int J = D / 64;
   constexpr int ML = PartFmt<H16>::ML;
   const int mt = blockIdx.x >> 3, cg = blockIdx.x & 7;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.y, i = blockIdx.z;  // KV head, session of the launch
+  const int R = ca.rows[i], m_tiles = ca.m_tiles[i], S = ca.splits[i];
+  if (mt >= m_tiles || S == 1) return;  // a single split wrote its output itself
+  const size_t slot = (size_t)ca.slot0[i] + ((size_t)g * m_tiles + mt) * S;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x;
-  const size_t tile_id = ((size_t)b * Hkv + g) * m_tiles + mt;
   const int c = tid >> 4, v = tid & 15;
   const int col = cg * 16 + c;
   const int m = mt * kMTile + col;
   if (m >= R * G) return;
-  const float* ml = part_ml + (tile_id * kMTile + col) * S * ML;
-  const size_t pc = (tile_id * S * kMTile + col) * D + 4 * v;  // element index
+  const float* ml = part_ml + (slot * kMTile + (size_t)col * S) * ML;
+  const size_t pc = (slot * kMTile + col) * D + 4 * v;  // element index
   const size_t PS = (size_t)kMTile * D;                        // stride between splits
   float4 t[kMergeFew][J];
   float mv[kMergeFew], lv[kMergeFew], ev[kMergeFew][J];
@@ -1225,7 +1257,7 @@ __global__ __launch_bounds__(256) void prefill_merge_few_kernel(
   }
   const float il = 1.f / L;
   const int row = m / G, hh = m % G;
-  float* op = out + (((size_t)b * R + row) * Hq + g * G + hh) * D + 4 * v;
+  float* op = out + (((size_t)ca.row0[i] + row) * Hq + g * G + hh) * D + 4 * v;
 #pragma unroll
   for (int j = 0; j < J; ++j)
     *reinterpret_cast<float4*>(op + 64 * j) =
@@ -1235,22 +1267,24 @@ __global__ __launch_bounds__(256) void prefill_merge_few_kernel(
 template <int D, bool H16>
 __global__ __launch_bounds__(256) void prefill_merge_split_kernel(
     const void* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
-    int Hq, int Hkv, int R, int m_tiles, int S) {
+    int Hq, int Hkv, const ChunkArg ca) {
   constexpr int J = D / 64;
   constexpr int ML = PartFmt<H16>::ML;
   __shared__ float4 red[kMergeGroups][4][16];
   __shared__ float red_m[kMergeGroups][4], red_l[kMergeGroups][4];
   const int js = blockIdx.x % J, cq = (blockIdx.x / J) & 31, mt = (blockIdx.x / J) >> 5;
-  const int g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.y, i = blockIdx.z;  // KV head, session of the launch
+  const int R = ca.rows[i], m_tiles = ca.m_tiles[i], S = ca.splits[i];
+  if (mt >= m_tiles || S == 1) return;  // block-uniform: before any barrier
+  const size_t slot = (size_t)ca.slot0[i] + ((size_t)g * m_tiles + mt) * S;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, sg = tid >> 6, c = (tid >> 4) & 3, v = tid & 15;
   const int col = cq * 4 + c;
   const int m = mt * kMTile + col;
   const bool valid = m < R * G;
-  const size_t tile_id = ((size_t)b * Hkv + g) * m_tiles + mt;
   const int d = 64 * js + 4 * v;
-  const float* ml = part_ml + (tile_id * kMTile + col) * S * ML;
-  const size_t pc = (tile_id * S * kMTile + col) * D + d;  // element index
+  const float* ml = part_ml + (slot * kMTile + (size_t)col * S) * ML;
+  const size_t pc = (slot * kMTile + col) * D + d;  // element index
   const size_t PS = (size_t)kMTile * D;                    // stride between splits
   // exponent slot of the lane that wrote these dims: half d / (D / 2), lane half v & 1
   const int eo = 2 + 2 * (d / (D / 2)) + (v & 1);
@@ -1317,7 +1351,7 @@ __global__ __launch_bounds__(256) void prefill_merge_split_kernel(
   }
   const float il = 1.f / L;
   const int row = m / G, hh = m % G;
-  *reinterpret_cast<float4*>(out + (((size_t)b * R + row) * Hq + g * G + hh) * D + d) =
+  *reinterpret_cast<float4*>(out + (((size_t)ca.row0[i] + row) * Hq + g * G + hh) * D + d) =
       make_float4(o.x * il, o.y * il, o.z * il, o.w * il);
 }
 
@@ -1335,8 +1369,9 @@ int max_splits(long long units) {
   return (int)(cap < kMaxSplits ? cap : kMaxSplits);
 }
 
-int choose_splits(const Shape& s, int m_tiles, int nkt) {
-  const long long units = (long long)s.batch * s.num_kv_heads * m_tiles;
+// units: the (KV head, m-tile) pairs of every session in the launch; nkt:
+// this session's key tiles.
+int choose_splits(const Shape& s, long long units, int nkt) {
   const double scale_d = s.head_dim / 256.0;
   const double tile_ns = (s.kv_dtype == 1 ? 1300.0 : 9000.0) * scale_d;
   const double wg_ns = 3000.0, merge_ns = 4000.0, part_ns = 26.0 * scale_d;
@@ -1356,46 +1391,114 @@ int choose_splits(const Shape& s, int m_tiles, int nkt) {
   return best;
 }
 
+// One launch: its session table, and the largest m-tile and split counts
+// among its sessions (the merge grid's extent and form).
+struct ChunkLaunch {
+  ChunkArg ca;
+  int max_m, max_s;
+};
+
+template <int D, bool BF16>
+hipError_t launch_chunks(const Shape& s, const ChunkLaunch* L, int nl, long long total_slots,
+                         const float* q, const void* kc, const void* vc, float* out, float scale,
+                         void* ws, hipStream_t st) {
+  using Cfg = PrefillCfg<D, BF16>;
+  // partials: binary16 accumulators for bf16 caches, f32 otherwise, one
+  // 128-column slot per (session, KV head, m-tile, split); then the
+  // per-(column, split) records
+  float* part = reinterpret_cast<float*>(ws);
+  float* part_ml = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) +
+                                            (size_t)total_slots * kMTile * D * (BF16 ? 2 : 4));
+  for (int l = 0; l < nl; ++l) {
+    const ChunkArg& ca = L[l].ca;
+    const int items = ca.item0[ca.n];
+    if (items == 0) continue;
+    // padded to whole rounds of the 8 XCDs (see make_tiling)
+    const dim3 grid(8 * ((items + 7) / 8));
+    if constexpr (BF16)
+      hipLaunchKernelGGL((prefill_bf16_kernel<D>), grid, dim3(kBf16Threads), 0, st, q, kc, vc, out,
+                         part, part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, ca,
+                         scale * kLog2e);
+    else if constexpr (Cfg::PIPE)
+      hipLaunchKernelGGL((prefill_pipe_kernel<D, BF16>), grid, dim3(256), 0, st, q, kc, vc, out,
+                         part, part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, ca,
+                         scale * kLog2e);
+    else
+      hipLaunchKernelGGL((prefill_seq_kernel<D, BF16>), grid, dim3(256), 0, st, q, kc, vc, out,
+                         part, part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, ca,
+                         scale * kLog2e);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (L[l].max_s > 1) {
+      if (L[l].max_s <= kMergeFew)
+        hipLaunchKernelGGL((prefill_merge_few_kernel<D, BF16>),
+                           dim3(L[l].max_m * (kMTile / 16), s.num_kv_heads, ca.n), dim3(256), 0, st,
+                           part, part_ml, out, s.num_q_heads, s.num_kv_heads, ca);
+      else
+        hipLaunchKernelGGL((prefill_merge_split_kernel<D, BF16>),
+                           dim3(L[l].max_m * (kMTile / 4) * (D / 64), s.num_kv_heads, ca.n),
+                           dim3(256), 0, st, part, part_ml, out, s.num_q_heads, s.num_kv_heads, ca);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+// Session tables of a call: the sessions with rows, kChunkSessions per
+// launch, packed rows in session order, partial slots numbered across the
+// whole call.  rows_of(b) / start_of(b): session b's chunk; splits_of(b, m):
+// its split count given its m-tile count.  Returns the call's slot count.
+template <class Rows, class Start, class Splits>
+long long build_launches(const Shape& s, Rows rows_of, Start start_of, Splits splits_of,
+                         std::vector<ChunkLaunch>& out) {
+  const int G = s.num_q_heads / s.num_kv_heads;
+  long long slot = 0, row = 0;
+  ChunkLaunch cur{};
+  for (int b = 0; b < s.batch; ++b) {
+    const int R = rows_of(b);
+    if (R <= 0) continue;
+    if (cur.ca.n == kChunkSessions) {
+      out.push_back(cur);
+      cur = ChunkLaunch{};
+    }
+    ChunkArg& ca = cur.ca;
+    const int i = ca.n;
+    const int m = (int)(((long long)R * G + kMTile - 1) / kMTile);
+    const int S = splits_of(b, m);
+    ca.b[i] = b;
+    ca.start[i] = start_of(b);
+    ca.rows[i] = R;
+    ca.m_tiles[i] = m;
+    ca.splits[i] = S;
+    ca.row0[i] = (int)row;
+    ca.slot0[i] = (int)slot;
+    ca.item0[i + 1] = ca.item0[i] + s.num_kv_heads * m * S;
+    ca.n = i + 1;
+    if (m > cur.max_m) cur.max_m = m;
+    if (S > cur.max_s) cur.max_s = S;
+    row += R;
+    slot += (long long)s.num_kv_heads * m * S;
+  }
+  if (cur.ca.n > 0) out.push_back(cur);
+  return slot;
+}
+
 template <int D, bool BF16>
 hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const void* kc,
                     const void* vc, float* out, int start, int R, float scale, void* ws,
                     hipStream_t st) {
-  using Cfg = PrefillCfg<D, BF16>;
-  // partials: binary16 accumulators for bf16 caches, f32 otherwise; then the
-  // per-(column, split) records
-  float* part = reinterpret_cast<float*>(ws);
-  float* part_ml = reinterpret_cast<float*>(
-      reinterpret_cast<unsigned char*>(ws) +
-      (size_t)s.batch * s.num_kv_heads * p.m_tiles * p.splits * kMTile * D * (BF16 ? 2 : 4));
-  // padded to whole rounds of the 8 XCDs (see make_tiling)
-  dim3 grid(8 * ((p.m_tiles * p.splits + 7) / 8), s.num_kv_heads, s.batch);
-  if constexpr (BF16)
-    hipLaunchKernelGGL((prefill_bf16_kernel<D>), grid, dim3(kBf16Threads), 0, st, q, kc, vc, out, part,
-                       part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, start, R, p.m_tiles,
-                       p.splits, scale * kLog2e);
-  else if constexpr (Cfg::PIPE)
-    hipLaunchKernelGGL((prefill_pipe_kernel<D, BF16>), grid, dim3(256), 0, st, q, kc, vc, out, part,
-                       part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, start, R, p.m_tiles,
-                       p.splits, scale * kLog2e);
-  else
-    hipLaunchKernelGGL((prefill_seq_kernel<D, BF16>), grid, dim3(256), 0, st, q, kc, vc, out, part,
-                       part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, start, R, p.m_tiles,
-                       p.splits, scale * kLog2e);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (p.splits > 1) {
-    if (p.splits <= kMergeFew)
-      hipLaunchKernelGGL((prefill_merge_few_kernel<D, BF16>),
-                         dim3(p.m_tiles * (kMTile / 16), s.num_kv_heads, s.batch), dim3(256), 0, st,
-                         part, part_ml, out, s.num_q_heads, s.num_kv_heads, R, p.m_tiles, p.splits);
-    else
-      hipLaunchKernelGGL((prefill_merge_split_kernel<D, BF16>),
-                         dim3(p.m_tiles * (kMTile / 4) * (D / 64), s.num_kv_heads, s.batch),
-                         dim3(256), 0, st, part, part_ml, out, s.num_q_heads, s.num_kv_heads, R,
-                         p.m_tiles, p.splits);
-    e = hipGetLastError();
-  }
-  return e;
+  std::vector<ChunkLaunch> L;
+  const long long slots = build_launches(
+      s, [&](int) { return R; }, [&](int) { return start; }, [&](int, int) { return p.splits; }, L);
+  return launch_chunks<D, BF16>(s, L.data(), (int)L.size(), slots, q, kc, vc, out, scale, ws, st);
+}
+
+template <int D, bool BF16>
+hipError_t launch_ragged_t(const Shape& s, const std::vector<ChunkLaunch>& L, long long slots,
+                           const float* q, const void* kc, const void* vc, float* out,
+                           float scale, void* ws, hipStream_t st) {
+  return launch_chunks<D, BF16>(s, L.data(), (int)L.size(), slots, q, kc, vc, out, scale, ws, st);
 }
 
 }  // namespace
@@ -1452,7 +1555,7 @@ PrefillPlan plan_prefill(const Shape& s, int start, int R) {
   const long long M = (long long)R * G;
   p.m_tiles = (int)((M + kMTile - 1) / kMTile);
   const int nkt = (start + R - 1) / kNTile + 1;
-  p.splits = choose_splits(s, p.m_tiles, nkt);
+  p.splits = choose_splits(s, (long long)s.batch * s.num_kv_heads * p.m_tiles, nkt);
   p.workspace_bytes = p.splits == 1 ? 0
       : (size_t)s.batch * s.num_kv_heads * p.m_tiles * p.splits * kMTile * partial_bytes(s);
   return p;
@@ -1478,6 +1581,62 @@ size_t prefill_workspace_bound(const Shape& s, int max_rows) {
     if (bytes > best) best = bytes;
   }
   return best;
+}
+
+// Ragged calls: each session's split count is the one a uniform chunk of its
+// own length would get with the call's total m-tile count.
+static long long ragged_launches(const Shape& s, const int32_t* start, const int32_t* rows,
+                                 std::vector<ChunkLaunch>& L) {
+  const int G = s.num_q_heads / s.num_kv_heads;
+  long long units = 0;
+  for (int b = 0; b < s.batch; ++b)
+    if (rows[b] > 0) units += (long long)s.num_kv_heads * (((long long)rows[b] * G + kMTile - 1) / kMTile);
+  return build_launches(
+      s, [&](int b) { return rows[b]; }, [&](int b) { return start[b]; },
+      [&](int b, int) { return choose_splits(s, units, (start[b] + rows[b] - 1) / kNTile + 1); }, L);
+}
+
+size_t prefill_ragged_workspace(const Shape& s, const int32_t* start, const int32_t* rows) {
+  std::vector<ChunkLaunch> L;
+  const long long slots = ragged_launches(s, start, rows, L);
+  bool split = false;
+  for (const ChunkLaunch& l : L) split = split || l.max_s > 1;
+  return split ? (size_t)slots * kMTile * partial_bytes(s) : 0;
+}
+
+// Every session's split count is at most max_splits(U) for the call's total
+// m-tile count U, so the slots number at most U max_splits(U); U is at most
+// Hkv (ceil(T G / 128) + min(B, T)) for T rows in all.
+size_t prefill_ragged_workspace_bound(const Shape& s, long long max_total_rows) {
+  if (max_total_rows <= 0) return 0;
+  const int G = s.num_q_heads / s.num_kv_heads;
+  const long long sessions = max_total_rows < s.batch ? max_total_rows : s.batch;
+  const long long u_max = (long long)s.num_kv_heads * ((max_total_rows * G + kMTile - 1) / kMTile + sessions);
+  long long most = 0;
+  // past kMaxWgRounds * kCUs units no session splits and nothing is stored
+  for (long long u = 1; u <= u_max && u <= (long long)kMaxWgRounds * kCUs; ++u) {
+    const int S = max_splits(u);
+    if (S > 1 && u * S > most) most = u * S;
+  }
+  return (size_t)most * kMTile * partial_bytes(s);
+}
+
+hipError_t launch_prefill_ragged(const Shape& s, const float* q, const void* k_cache,
+                                 const void* v_cache, float* out, const int32_t* start,
+                                 const int32_t* rows, float scale, void* workspace,
+                                 hipStream_t stream) {
+  std::vector<ChunkLaunch> L;
+  const long long slots = ragged_launches(s, start, rows, L);
+  const bool bf16 = s.kv_dtype == 1;
+  switch (s.head_dim) {
+#define KA_R(DD)                                                                                  \
+  case DD:                                                                                        \
+    return bf16 ? launch_ragged_t<DD, true>(s, L, slots, q, k_cache, v_cache, out, scale, workspace, stream) \
+                : launch_ragged_t<DD, false>(s, L, slots, q, k_cache, v_cache, out, scale, workspace, stream);
+    KA_R(64) KA_R(128) KA_R(256)
+#undef KA_R
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_prefill(const Shape& s, const PrefillPlan& p, const float* q,

@@ -6,7 +6,7 @@ nothing from the library and no code is shared with the GPU path.
 """
 from . import bf16, rope
 from .attention import (attend_rows, attend_rows_scalar, decode, kv_group,
-                        prefill_chunk, rel_error, stored_values)
+                        prefill_chunk, prefill_ragged, rel_error, stored_values)
 
 __all__ = ["bf16", "rope", "attend_rows", "attend_rows_scalar", "decode", "kv_group",
-           "prefill_chunk", "rel_error", "stored_values"]
+           "prefill_chunk", "prefill_ragged", "rel_error", "stored_values"]

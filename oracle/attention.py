@@ -47,7 +47,7 @@ import numpy as np
 from . import bf16 as _bf16
 
 __all__ = ["kv_group", "stored_values", "attend_rows_scalar", "attend_rows",
-           "prefill_chunk", "decode", "rel_error"]
+           "prefill_chunk", "prefill_ragged", "decode", "rel_error"]
 
 
 def kv_group(h: int, num_q_heads: int, num_kv_heads: int) -> int:
@@ -177,6 +177,31 @@ def prefill_chunk(q, k_store, v_store, start: int, scale: float,
     pos = np.arange(start, start + R)
     return np.stack([attend_rows(q[b], k_store[b], v_store[b], pos, scale, row_block)
                      for b in range(B)]) if B else np.zeros(q.shape)
+
+
+def prefill_ragged(q, k_store, v_store, starts: Sequence[int], rows: Sequence[int],
+                   scale: float) -> np.ndarray:
+    """Sessions at different positions in one call (several conversations,
+    each continuing its own cache; Karume v0.8.0 release notes, "Features":
+    the multi-turn chat session).  Session b's rows[b] rows sit at positions
+    starts[b] .. starts[b] + rows[b] - 1 and attend to its own keys, exactly as
+    a chunk of that session alone.
+
+    q: [sum rows][Hq][D] f32, rows packed session by session; k_store /
+    v_store: [B][P][Hkv][D] stored values.  Returns float64 [sum rows][Hq][D].
+    """
+    q = np.asarray(q)
+    parts, r0 = [], 0
+    for b, (s0, n) in enumerate(zip(starts, rows)):
+        n = int(n)
+        if n == 0:
+            continue
+        parts.append(attend_rows(q[r0:r0 + n], k_store[b], v_store[b],
+                                 np.arange(int(s0), int(s0) + n), scale))
+        r0 += n
+    if not parts:
+        return np.zeros((0,) + q.shape[1:])
+    return np.concatenate(parts, axis=0)
 
 
 def decode(q, k_store, v_store, ctx_len: Iterable[int], scale: float) -> np.ndarray:

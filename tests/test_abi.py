@@ -34,7 +34,10 @@ def test_header_declares_the_entry_points():
               "ka_attn_prefill_chunk", "ka_attn_decode", "ka_attn_decode_step",
               "ka_attn_decode_workspace_bytes", "ka_attn_prefill_workspace_bytes",
               "ka_attn_cache_bytes", "ka_attn_status_string", "ka_attn_last_error",
-              "ka_attn_abi_version"]:
+              "ka_attn_abi_version", "ka_attn_append_kv_ragged", "ka_attn_prefill_ragged",
+              "ka_attn_prefill_ragged_workspace_bytes", "ka_attn_prefill_ragged_workspace_need",
+              "ka_attn_session_memory",
+              "ka_attn_cache_resize"]:
         assert n in names
     assert set(names) == set(ka.EXPORTED_SYMBOLS)
 
@@ -194,6 +197,106 @@ def test_workspace_sizes_cover_smaller_requests():
     p = ka.prefill_workspace_bytes(s, 768)
     for r in [1, 16, 100, 767]:
         assert ka.prefill_workspace_bytes(s, r) <= p
+
+
+def _i32(xs):
+    return (ctypes.c_int32 * len(xs))(*xs)
+
+
+def test_ragged_argument_errors():
+    _lib_or_skip()
+    L = ka.lib()
+    s = S(batch=3)
+    def pre(starts, rows, scale=0.0625, ws=None, ws_bytes=0, q=FAKE, out=ctypes.c_void_p(0x2000)):
+        return L.ka_attn_prefill_ragged(ctypes.byref(s), q, FAKE, FAKE, out, _i32(starts),
+                                        _i32(rows), scale, ws, ws_bytes, None)
+    def app(starts, rows, cos=None, sin=None):
+        return L.ka_attn_append_kv_ragged(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, cos, sin,
+                                          _i32(starts), _i32(rows), None)
+    assert pre([0, 0, 0], [1, -1, 1]) == 1
+    assert pre([0, -2, 0], [1, 1, 1]) == 1
+    assert pre([0, 4000, 0], [1, 97, 1]) == 2
+    assert "start_pos[1]" in ka.last_error()
+    assert pre([0, 0, 0], [0, 0, 0]) == 0             # nothing to do
+    assert pre([0, 0, 0], [1, 1, 1], scale=float("nan")) == 1
+    assert pre([0, 0, 0], [1, 1, 1], out=FAKE) == 1   # out aliases q
+    assert L.ka_attn_prefill_ragged(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.c_void_p(0x2000),
+                                    None, _i32([1, 1, 1]), 0.1, None, 0, None) == 1
+    # long chunks need a workspace: the bound for their total covers them
+    starts, rows = [3000, 0, 1000], [768, 0, 500]
+    need = ka.prefill_ragged_workspace_bytes(s, sum(rows))
+    assert need > 0
+    assert pre(starts, rows) == 4
+    assert pre(starts, rows, ws=FAKE, ws_bytes=16) == 4
+    assert app([0, 0, 0], [1, 0, -1]) == 1
+    assert app([0, 4090, 0], [1, 7, 1]) == 2
+    assert app([0, 0, 0], [1, 1, 1], cos=FAKE) == 1   # only one rotary table
+    assert app([5, 5, 5], [0, 0, 0]) == 0
+
+
+def test_ragged_workspace_bound_covers_every_split_of_the_rows():
+    """The bound for T rows covers the exact need of any split of T rows over
+    the sessions at any starts (host-side queries only)."""
+    _lib_or_skip()
+    s = S(batch=4, capacity=16384)
+    g = np.random.default_rng(3)
+    needed = 0
+    for _ in range(200):
+        total = int(g.integers(1, 4000))
+        cuts = np.sort(g.integers(0, total + 1, size=3))
+        rows = np.diff(np.concatenate([[0], cuts, [total]])).astype(int).tolist()
+        if max(rows) > 16384:
+            continue
+        starts = [int(g.integers(0, 16384 - r + 1)) for r in rows]
+        need = ka.prefill_ragged_workspace_need(s, starts, rows)
+        assert need <= ka.prefill_ragged_workspace_bytes(s, total), (rows, starts)
+        needed += need > 0
+    assert needed > 50
+    assert ka.prefill_ragged_workspace_need(s, [0] * 4, [0] * 4) == 0
+    assert ka.prefill_ragged_workspace_need(s, [0, 0, 0, 16384], [1, 1, 1, 1]) == 0  # invalid
+
+
+def test_session_memory_closed_forms():
+    _lib_or_skip()
+    for sh, rows in [(S(batch=1, num_q_heads=8, num_kv_heads=1, head_dim=256, capacity=16384), 768),
+                     (S(batch=4, num_q_heads=8, num_kv_heads=1, head_dim=256, capacity=131072), 768),
+                     (S(batch=2, num_q_heads=16, num_kv_heads=2, head_dim=128, capacity=4096,
+                        kv_dtype=ka.F32), 100)]:
+        m = ka.session_memory(sh, rows)
+        es = 2 if sh.kv_dtype == ka.BF16 else 4
+        assert m.cache_bytes == 2 * sh.batch * sh.num_kv_heads * sh.capacity * sh.head_dim * es
+        assert m.cache_bytes == 2 * ka.cache_bytes(sh)
+        assert m.prefill_workspace_bytes == ka.prefill_workspace_bytes(sh, rows)
+        assert m.decode_workspace_bytes == ka.decode_workspace_bytes(sh, sh.capacity)
+        assert m.chunk_io_bytes == sh.batch * rows * (2 * sh.num_q_heads + 2 * sh.num_kv_heads) * sh.head_dim * 4
+        assert m.total_bytes == (m.cache_bytes + max(m.prefill_workspace_bytes, m.decode_workspace_bytes)
+                                 + m.chunk_io_bytes)
+    # 4 sessions x 131072 positions of bf16 K and V, head_dim 256: exactly 512 MiB
+    assert ka.session_memory(S(batch=4, capacity=131072), 768).cache_bytes == 512 * 2**20
+    with pytest.raises(ka.KaAttnError):
+        ka.session_memory(S(), 0)
+    with pytest.raises(ka.KaAttnError):
+        ka.session_memory(S(), 4097)
+
+
+def test_cache_resize_argument_errors():
+    _lib_or_skip()
+    L = ka.lib()
+    a, b = S(capacity=1024), S(capacity=2048)
+    A, Bp = ctypes.c_void_p(0x100000), ctypes.c_void_p(0x200000)
+    Av, Bv = ctypes.c_void_p(0x300000), ctypes.c_void_p(0x400000)
+    def rs(src, dst, rows, sk=A, sv=Av, dk=Bp, dv=Bv):
+        return L.ka_attn_cache_resize(ctypes.byref(src), sk, sv, ctypes.byref(dst), dk, dv, rows, None)
+    assert rs(a, S(capacity=2048, head_dim=128), 10) == 1     # more than capacity differs
+    assert rs(a, S(capacity=2048, kv_dtype=ka.F32), 10) == 1
+    assert rs(a, b, -1) == 1
+    assert rs(a, b, 1025) == 2
+    assert rs(b, a, 1500) == 2
+    assert rs(a, b, 0) == 0
+    assert rs(a, b, 10, dk=None) == 1
+    # overlapping caches: K of the destination inside K of the source
+    assert rs(a, b, 10, dk=ctypes.c_void_p(0x100000 + 64)) == 1
+    assert "overlap" in ka.last_error()
 
 
 # ------------------------------------------- the test-side layout readers

@@ -398,3 +398,32 @@ def test_rope_dot_products_depend_only_on_position_difference():
     p = 123.0 * 10000.0 ** (-np.arange(32) * 2.0 / 64)
     r = oracle.rope.rotate_half_f64(q, np.cos(p)[None], np.sin(p)[None])
     assert np.allclose(r[..., :32] ** 2 + r[..., 32:] ** 2, q[..., :32] ** 2 + q[..., 32:] ** 2, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- ragged batches
+
+def test_ragged_matches_scalar_brute_force_per_session():
+    """Three sessions at different positions, one of them empty, packed rows:
+    each session's rows equal the scalar brute force on that session's own
+    cache (a slip in the row packing or the session-to-cache map fails)."""
+    B, Hq, Hkv, D, P = 3, 4, 2, 8, 12
+    g = np.random.default_rng(5)
+    k = g.standard_normal((B, P, Hkv, D)).astype(np.float32)
+    v = g.standard_normal((B, P, Hkv, D)).astype(np.float32)
+    starts, rows = [4, 0, 7], [3, 0, 5]
+    q = g.standard_normal((sum(rows), Hq, D)).astype(np.float32)
+    got = oracle.prefill_ragged(q, k, v, starts, rows, 0.4)
+    assert got.shape == (8, Hq, D)
+    want0 = oracle.attend_rows_scalar(q[:3], k[0], v[0], [4, 5, 6], 0.4)
+    want2 = oracle.attend_rows_scalar(q[3:], k[2], v[2], [7, 8, 9, 10, 11], 0.4)
+    np.testing.assert_allclose(got[:3], np.array(want0), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(got[3:], np.array(want2), rtol=1e-12, atol=1e-13)
+
+
+def test_ragged_with_equal_sessions_is_the_uniform_chunk():
+    B, Hq, Hkv, D, start, R = 2, 4, 1, 16, 6, 5
+    c = random_case(21, B, Hq, Hkv, D, start + R, R)
+    uni = oracle.prefill_chunk(c.q, c.k, c.v, start, 0.25)
+    rag = oracle.prefill_ragged(c.q.reshape(B * R, Hq, D), c.k, c.v, [start] * B, [R] * B, 0.25)
+    np.testing.assert_array_equal(rag, uni.reshape(B * R, Hq, D))
+    assert oracle.prefill_ragged(c.q[0, :0], c.k, c.v, [0, 0], [0, 0], 0.25).shape == (0, Hq, D)
