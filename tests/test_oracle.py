@@ -427,3 +427,85 @@ def test_ragged_with_equal_sessions_is_the_uniform_chunk():
     rag = oracle.prefill_ragged(c.q.reshape(B * R, Hq, D), c.k, c.v, [start] * B, [R] * B, 0.25)
     np.testing.assert_array_equal(rag, uni.reshape(B * R, Hq, D))
     assert oracle.prefill_ragged(c.q[0, :0], c.k, c.v, [0, 0], [0, 0], 0.25).shape == (0, Hq, D)
+
+
+# ---------------------------------------------------------------- int8 scores
+
+from oracle import int8 as oi8  # noqa: E402
+
+
+def test_int8_quantisation_hand_cases():
+    """Worked by hand: amax 1 gives s = f32(1/127) (bits 0x3C010204); 0.5 / s
+    is 63.50000024 exactly, which is 63.5 in f32, a tie that goes to the even
+    code 64; 0.25 / s is 31.75 -> 32; amax maps to 127.  A zero row keeps s = 0
+    and codes 0; a row with NaN gets s = NaN, one with an infinity s = inf,
+    both with codes 0 (their scores then come out NaN)."""
+    x = np.array([[1.0, -0.5, 0.25, 0.0], [0, 0, 0, 0], [1, np.nan, 2, 3], [1, np.inf, 0, 0]],
+                 np.float32)
+    c, s = oi8.quantize_rows(x)
+    assert c.dtype == np.int8
+    assert c[0].tolist() == [127, -64, 32, 0]
+    assert s[0].view(np.uint32) == 0x3C010204
+    assert c[1].tolist() == [0, 0, 0, 0] and s[1] == 0
+    assert c[2].tolist() == [0, 0, 0, 0] and np.isnan(s[2])
+    assert c[3].tolist() == [0, 0, 0, 0] and np.isinf(s[3])
+
+
+def test_int8_quantisation_bounds():
+    """Random rows: codes in -127 .. 127, the largest |x| maps to +-127 with
+    its sign, and every value is within half a step of code * s (plus the
+    f32 rounding of x / s)."""
+    g = np.random.default_rng(11)
+    x = (g.standard_normal((64, 256)) * np.exp(g.uniform(-8, 8, size=(64, 1)))).astype(np.float32)
+    c, s = oi8.quantize_rows(x)
+    assert np.abs(c.astype(int)).max() <= 127
+    i = np.abs(x).argmax(axis=1)
+    assert (c[np.arange(64), i].astype(int) == 127 * np.sign(x[np.arange(64), i])).all()
+    err = np.abs(x.astype(np.float64) - oi8.dequantize(c, s))
+    assert (err <= s[:, None].astype(np.float64) * (0.5 + 2 ** -16)).all()
+
+
+def test_int8_attention_is_exact_attention_when_quantisation_is_lossless():
+    """Rows that are integer codes (largest |code| 127) times a power of two
+    quantise back to exactly those codes with s = that power of two (127 *
+    f32(1/127) rounds to 1 in f32), so the int8 scores are the exact scores
+    and the int8 attention equals the float64 attention: a dropped or doubled
+    scale factor, or a transposed code matrix, fails here."""
+    g = np.random.default_rng(12)
+    Hq, Hkv, D, P, n = 4, 2, 64, 40, 6
+
+    def rows(shape, e):
+        c = g.integers(-127, 128, size=shape + (D,)).astype(np.float32)
+        c[..., 0] = 127 * np.where(g.random(shape) < 0.5, -1, 1)
+        return (c * np.float32(2.0 ** e)).astype(np.float32)
+
+    q = rows((n, Hq), -9)
+    k = rows((P, Hkv), -7)
+    v = g.standard_normal((P, Hkv, D)).astype(np.float32)
+    qc, qs = oi8.quantize_rows(q)
+    kc, ks = oi8.quantize_rows(k)
+    assert (qs == np.float32(2.0 ** -9)).all() and (ks == np.float32(2.0 ** -7)).all()
+    np.testing.assert_array_equal(oi8.dequantize(qc, qs), q.astype(np.float64))
+    pos = np.arange(P - n, P)
+    want = oracle.attend_rows(q, k, v, pos, 0.5)
+    got = oi8.attend_rows_i8(qc, qs, kc, ks, v, pos, 0.5)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_int8_scores_match_integer_brute_force():
+    """One row, tiny sizes: the scores from Python integers and the scales
+    (the scale enters as its f32 value, as everywhere in the oracle)."""
+    g = np.random.default_rng(13)
+    q = g.standard_normal((1, 2, 8)).astype(np.float32)
+    k = g.standard_normal((5, 1, 8)).astype(np.float32)
+    v = np.eye(5, 8, dtype=np.float32)[:, None, :]            # value row j = e_j
+    qc, qs = oi8.quantize_rows(q)
+    kc, ks = oi8.quantize_rows(k)
+    out = oi8.attend_rows_i8(qc, qs, kc, ks, v, [4], 0.3)
+    for h in range(2):
+        s = [float(np.float32(0.3)) * sum(int(a) * int(b) for a, b in zip(qc[0, h], kc[j, 0])) *
+             float(qs[0, h]) *
+             float(ks[j, 0]) for j in range(5)]
+        m = max(s)
+        w = [math.exp(t - m) for t in s]
+        np.testing.assert_allclose(out[0, h, :5], np.array(w) / sum(w), rtol=1e-12)
