@@ -60,30 +60,43 @@ def dequantize(codes, s):
     return np.asarray(codes, dtype=np.float64) * np.asarray(s, dtype=np.float64)[..., None]
 
 
-def attend_rows_i8(qc, qs, kc, ks, v, q_pos: Sequence[int], scale: float) -> np.ndarray:
+def attend_rows_i8(qc, qs, kc, ks, v, q_pos: Sequence[int], scale: float,
+                   row_block: int = 256) -> np.ndarray:
     """One session: qc [n][Hq][D] int8 and qs [n][Hq] f32 (query codes and
     scales), kc [P][Hkv][D] int8 and ks [P][Hkv] f32, v [P][Hkv][D] stored
     values; row i at absolute position q_pos[i] sees keys 0 .. q_pos[i].
-    Returns float64 [n][Hq][D]."""
-    qc = np.asarray(qc, dtype=np.int64)
-    kc = np.asarray(kc, dtype=np.int64)
+    Returns float64 [n][Hq][D].
+
+    The integer dot is formed by a float64 matrix product, which is exact
+    here: every product and partial sum is an integer of magnitude at most
+    D * 127^2 < 2^53."""
+    qc = np.asarray(qc)
+    kc = np.asarray(kc)
     qs = np.asarray(qs, dtype=np.float64)
     ks = np.asarray(ks, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
+    q_pos = np.asarray(q_pos, dtype=np.int64)
     n, Hq, D = qc.shape
     Hkv = kc.shape[1]
     G = Hq // Hkv
     sc = float(np.float32(scale))
     out = np.zeros((n, Hq, D))
     with np.errstate(invalid="ignore", over="ignore"):
-        for i in range(n):
-            p = int(q_pos[i]) + 1
+        for r0 in range(0, n, row_block):
+            r1 = min(n, r0 + row_block)
+            pos = q_pos[r0:r1]
+            nk = int(pos.max()) + 1
+            visible = np.arange(nk)[None, :] <= pos[:, None]             # [r][nk]
             for g in range(Hkv):
-                dot = qc[i, g * G:(g + 1) * G] @ kc[:p, g].T            # exact integers [G][p]
-                s = sc * dot * qs[i, g * G:(g + 1) * G, None] * ks[None, :p, g]
-                m = np.max(s, axis=1, keepdims=True)                     # NaN propagates
-                w = np.exp(s - m)
-                out[i, g * G:(g + 1) * G] = (w @ v[:p, g]) / w.sum(axis=1, keepdims=True)
+                qb = qc[r0:r1, g * G:(g + 1) * G].reshape(-1, D).astype(np.float64)
+                kb = kc[:nk, g].astype(np.float64)
+                dot = (qb @ kb.T).reshape(r1 - r0, G, nk)                # exact integers
+                s = sc * dot * qs[r0:r1, g * G:(g + 1) * G, None] * ks[None, None, :nk, g]
+                s = np.where(visible[:, None, :], s, -np.inf)
+                m = np.max(s, axis=2, keepdims=True)                      # NaN propagates
+                w = np.where(visible[:, None, :], np.exp(s - m), 0.0)
+                vb = np.asarray(v[:nk, g], dtype=np.float64)
+                o = (w.reshape(-1, nk) @ vb).reshape(r1 - r0, G, D)
+                out[r0:r1, g * G:(g + 1) * G] = o / w.sum(axis=2, keepdims=True)
     return out
 
 
