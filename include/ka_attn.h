@@ -62,6 +62,25 @@
  *                     four groups of 8 positions {16u+4h..16u+4h+3,
  *                     16u+8+4h..16u+8+4h+3}, group s = 2u + h.
  *
+ *   int8-K caches (kv_dtype 2, KA_DTYPE_I8K): V as bf16 above; K as int8
+ *   codes with one f32 scale per row (session, KV head, position), both in
+ *   the K buffer: code (b, g, j, d) at BYTE index
+ *                     (((b*Hkv + g)*(C/64) + j/64)*(D/16) + d/16)*64*16 + (j%64)*16 + d%16
+ *   (the K layout above with E = 16), and the scale of row (b, g, j) as the
+ *   f32 at byte B*Hkv*C*D + 4*((b*Hkv + g)*C + j).  Both buffers are
+ *   ka_attn_cache_bytes() long (the V size; the K data use C*(D + 4) bytes per
+ *   slab of it).  The append quantises each K row symmetrically (Karume
+ *   v0.8.0 release notes, "Fixes": the activation-quantisation scale is amax
+ *   times the f32 value of 1/127): s = f32(amax * f32(1/127)), code =
+ *   round-half-even(x / s) limited to +-127 (IEEE f32 division); a row with
+ *   a NaN gets s = NaN, one with an infinity s = inf, and rows whose s is 0
+ *   or not finite get codes 0.  Attention quantises each query row (one
+ *   head's D values) the same way and scores with the exact integer dot:
+ *   score = scale * s_q * s_k * sum_d code_q[d] * code_k[d] (the pages' int8
+ *   dot with i32 accumulation and an f32 epilogue, "Fixes": the dp4a bullet);
+ *   V stays bf16.  The first int8 call on a device runs
+ *   ka_attn_int8_self_test.
+ *
  *   Cache contents beyond the rows appended so far are never read into a
  *   result (they may hold anything, NaN included).
  *
@@ -90,7 +109,7 @@ typedef enum ka_status {
   KA_ERR_HIP = 5               /* a HIP runtime error; text in ka_attn_last_error */
 } ka_status;
 
-typedef enum ka_dtype { KA_DTYPE_F32 = 0, KA_DTYPE_BF16 = 1 } ka_dtype;
+typedef enum ka_dtype { KA_DTYPE_F32 = 0, KA_DTYPE_BF16 = 1, KA_DTYPE_I8K = 2 } ka_dtype;
 
 typedef struct ka_attn_shape {
   int32_t batch;        /* B: independent sessions, each with its own cache rows */
@@ -104,7 +123,8 @@ typedef struct ka_attn_shape {
 /* Version of this ABI (KA_ATTN_ABI_VERSION of the built library). */
 int32_t ka_attn_abi_version(void);
 
-/* Bytes of ONE cache buffer (K or V) for shape s; 0 if s is invalid. */
+/* Bytes of ONE cache buffer (K or V) for shape s; 0 if s is invalid.  For
+ * int8-K caches both buffers take the V size. */
 size_t ka_attn_cache_bytes(const ka_attn_shape* s);
 
 /*
@@ -332,6 +352,21 @@ ka_status ka_attn_session_memory(const ka_attn_shape* s, int32_t max_chunk_rows,
 ka_status ka_attn_cache_resize(const ka_attn_shape* src, const void* src_k, const void* src_v,
                                const ka_attn_shape* dst, void* dst_k, void* dst_v, int32_t rows,
                                void* stream);
+
+/*
+ * Device self-test of the int8 scores (Karume v0.8.0 release notes, "Fixes":
+ * the int8 dot is not taken on faith; a canary checks the instruction and its
+ * emulation against a known answer at first use, and the library fails
+ * loudly when they are not sane).  On the current device, one wave
+ * multiplies a fixed 16 x 64 by 64 x 16 int8 pattern with the int8 MFMA
+ * instruction the int8-K kernels use, in their lane layout, and with plain
+ * integer arithmetic; both must equal the exact product.  It runs once per
+ * device (synchronising the device that once; call it before capturing a
+ * graph) and the outcome is kept.  Every int8-K attention call runs it first.
+ * Returns KA_OK, or KA_ERR_UNSUPPORTED (int8-K attention calls then fail the
+ * same way; the text names what disagreed), or KA_ERR_HIP.
+ */
+ka_status ka_attn_int8_self_test(void);
 
 /* Static name of a status code ("KA_OK", ...). */
 const char* ka_attn_status_string(int32_t status);

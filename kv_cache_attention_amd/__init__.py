@@ -22,10 +22,11 @@ __all__ = ["Shape", "KaAttnError", "KaAttnUnavailable", "lib", "lib_path", "F32"
            "last_error", "abi_version", "EXPORTED_SYMBOLS", "decode_step", "append_kv_rope",
            "rope_rows", "append_kv_ragged", "prefill_ragged_workspace_bytes",
            "prefill_ragged_workspace_need", "prefill_ragged",
-           "Memory", "session_memory", "cache_resize"]
+           "Memory", "session_memory", "cache_resize", "I8K", "int8_self_test"]
 
 F32 = 0
 BF16 = 1
+I8K = 2
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libka_attn.so"
@@ -37,7 +38,7 @@ EXPORTED_SYMBOLS = (
     "ka_attn_decode_workspace_bytes", "ka_attn_decode", "ka_attn_decode_step",
     "ka_attn_append_kv_ragged", "ka_attn_prefill_ragged_workspace_bytes",
     "ka_attn_prefill_ragged_workspace_need", "ka_attn_prefill_ragged",
-    "ka_attn_session_memory", "ka_attn_cache_resize",
+    "ka_attn_session_memory", "ka_attn_cache_resize", "ka_attn_int8_self_test",
     "ka_attn_status_string",
     "ka_attn_last_error",
 )
@@ -65,14 +66,14 @@ class Shape(ctypes.Structure):
 
     def __init__(self, batch, num_q_heads, num_kv_heads, head_dim, capacity, kv_dtype):
         if isinstance(kv_dtype, str):
-            kv_dtype = {"f32": F32, "bf16": BF16}[kv_dtype]
+            kv_dtype = {"f32": F32, "bf16": BF16, "i8k": I8K}[kv_dtype]
         super().__init__(int(batch), int(num_q_heads), int(num_kv_heads), int(head_dim),
                          int(capacity), int(kv_dtype))
 
     def __repr__(self):
         return (f"Shape(batch={self.batch}, Hq={self.num_q_heads}, Hkv={self.num_kv_heads}, "
                 f"D={self.head_dim}, C={self.capacity}, "
-                f"kv={'bf16' if self.kv_dtype == BF16 else 'f32'})")
+                f"kv={ {F32: 'f32', BF16: 'bf16', I8K: 'i8k'}.get(self.kv_dtype, self.kv_dtype)})")
 
 
 _lib = None
@@ -135,6 +136,8 @@ def lib() -> ctypes.CDLL:
     L.ka_attn_cache_resize.restype = c_int32
     L.ka_attn_cache_resize.argtypes = [P, c_void_p, c_void_p, P, c_void_p, c_void_p, c_int32,
                                        c_void_p]
+    L.ka_attn_int8_self_test.restype = c_int32
+    L.ka_attn_int8_self_test.argtypes = []
     L.ka_attn_status_string.restype = ctypes.c_char_p
     L.ka_attn_status_string.argtypes = [c_int32]
     L.ka_attn_last_error.restype = ctypes.c_char_p
@@ -396,3 +399,9 @@ def cache_resize(src: Shape, src_k: torch.Tensor, src_v: torch.Tensor, dst: Shap
             raise ValueError(f"{nm} is smaller than {cache_bytes(sh)} bytes")
     _check(lib().ka_attn_cache_resize(ctypes.byref(src), _ptr(src_k), _ptr(src_v), ctypes.byref(dst),
                                       _ptr(dst_k), _ptr(dst_v), int(rows), _stream(stream)))
+
+
+def int8_self_test() -> None:
+    """ka_attn_int8_self_test: raises KaAttnError if the device's int8 scores
+    are not sane."""
+    _check(lib().ka_attn_int8_self_test())

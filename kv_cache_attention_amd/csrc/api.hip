@@ -43,8 +43,9 @@ ka_status check_shape(const ka_attn_shape* s, ka::Shape* out) {
                 s->num_q_heads, s->num_kv_heads);
   if (s->head_dim != 64 && s->head_dim != 128 && s->head_dim != 256)
     return fail(KA_ERR_UNSUPPORTED, "head_dim %d not supported (64, 128 or 256)", s->head_dim);
-  if (s->kv_dtype != KA_DTYPE_F32 && s->kv_dtype != KA_DTYPE_BF16)
-    return fail(KA_ERR_UNSUPPORTED, "kv_dtype %d not supported (0 = f32, 1 = bf16)", s->kv_dtype);
+  if (s->kv_dtype != KA_DTYPE_F32 && s->kv_dtype != KA_DTYPE_BF16 && s->kv_dtype != KA_DTYPE_I8K)
+    return fail(KA_ERR_UNSUPPORTED, "kv_dtype %d not supported (0 = f32, 1 = bf16, 2 = int8 K)",
+                s->kv_dtype);
   if (s->capacity > KA_ATTN_MAX_CAPACITY)
     return fail(KA_ERR_OUT_OF_RANGE, "capacity %d exceeds %d", s->capacity, KA_ATTN_MAX_CAPACITY);
   if (s->capacity < 64 || s->capacity % 64 != 0)
@@ -80,9 +81,24 @@ ka_status check_ragged(const ka::Shape& sh, const int32_t* start, const int32_t*
   return KA_OK;
 }
 
+// One buffer: f32 4 bytes per element, bf16 2; int8-K caches size both
+// buffers as the bf16 V buffer, which also holds the K codes (1 byte per
+// element) and their row scales (4 bytes per row).
 size_t cache_bytes(const ka::Shape& s) {
   return (size_t)s.batch * s.num_kv_heads * (size_t)s.capacity * s.head_dim *
-         (s.kv_dtype == KA_DTYPE_BF16 ? 2 : 4);
+         (s.kv_dtype == KA_DTYPE_F32 ? 4 : 2);
+}
+
+// Calls that compute int8 scores first make sure the device passed the
+// self-test (run at the first such call on each device).
+ka_status check_int8(const ka::Shape& sh) {
+  if (sh.kv_dtype != KA_DTYPE_I8K) return KA_OK;
+  bool passed = false;
+  const char* why = "";
+  const hipError_t e = ka::int8_self_test(&passed, &why);
+  if (e != hipSuccess) return hip_fail(e, "int8 self-test");
+  if (!passed) return fail(KA_ERR_UNSUPPORTED, "%s", why);
+  return KA_OK;
 }
 
 }  // namespace
@@ -202,6 +218,7 @@ ka_status ka_attn_prefill_chunk(const ka_attn_shape* s, const float* q, const vo
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(KA_ERR_WORKSPACE, "prefill needs %zu workspace bytes, got %zu", plan.workspace_bytes,
                 workspace ? workspace_bytes : (size_t)0);
+  if ((st = check_int8(sh)) != KA_OK) return st;
   hipError_t e = ka::launch_prefill(sh, plan, q, k_cache, v_cache, out, start_pos, row_count,
                                     scale, workspace, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "prefill launch");
@@ -242,6 +259,7 @@ ka_status ka_attn_prefill_ragged(const ka_attn_shape* s, const float* q, const v
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(KA_ERR_WORKSPACE, "ragged prefill needs %zu workspace bytes, got %zu", need,
                 workspace ? workspace_bytes : (size_t)0);
+  if ((st = check_int8(sh)) != KA_OK) return st;
   hipError_t e = ka::launch_prefill_ragged(sh, q, k_cache, v_cache, out, start_pos, row_count,
                                            scale, workspace, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ragged prefill launch");
@@ -287,7 +305,8 @@ ka_status ka_attn_cache_resize(const ka_attn_shape* src, const void* src_k, cons
   if (rows == 0) return ok();
   if (!src_k || !src_v || !dst_k || !dst_v)
     return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
-  const size_t es = a.kv_dtype == KA_DTYPE_BF16 ? 2 : 4;
+  const size_t es = a.kv_dtype == KA_DTYPE_F32 ? 4 : 2;               // V (and f32 / bf16 K)
+  const size_t ek = a.kv_dtype == KA_DTYPE_I8K ? 1 : es;               // K codes
   const size_t src_slab = (size_t)a.capacity * a.head_dim * es;
   const size_t dst_slab = (size_t)b.capacity * b.head_dim * es;
   const size_t nslab = (size_t)a.batch * a.num_kv_heads;
@@ -307,15 +326,29 @@ ka_status ka_attn_cache_resize(const ka_attn_shape* src, const void* src_k, cons
   // f32); both capacities are multiples of 64 >= rows, so the rounded
   // prefix fits either slab
   const size_t k_pos = ((size_t)rows + 63) / 64 * 64;
-  const size_t v_unit = a.kv_dtype == KA_DTYPE_BF16 ? 32 : 4;
+  const size_t v_unit = a.kv_dtype == KA_DTYPE_F32 ? 4 : 32;  // V in the bf16 layout unless f32
   const size_t v_pos = ((size_t)rows + v_unit - 1) / v_unit * v_unit;
   const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = hipMemcpy2DAsync(dst_k, dst_slab, src_k, src_slab, k_pos * a.head_dim * es,
+  hipError_t e = hipMemcpy2DAsync(dst_k, (size_t)b.capacity * b.head_dim * ek, src_k,
+                                  (size_t)a.capacity * a.head_dim * ek, k_pos * a.head_dim * ek,
                                   nslab, hipMemcpyDeviceToDevice, hs);
+  if (e == hipSuccess && a.kv_dtype == KA_DTYPE_I8K)  // the row scales: [B][Hkv][C] f32
+    e = hipMemcpy2DAsync(ka::k_scale_array(b, dst_k), (size_t)b.capacity * 4,
+                         ka::k_scale_array(a, src_k), (size_t)a.capacity * 4, (size_t)rows * 4,
+                         nslab, hipMemcpyDeviceToDevice, hs);
   if (e == hipSuccess)
     e = hipMemcpy2DAsync(dst_v, dst_slab, src_v, src_slab, v_pos * a.head_dim * es, nslab,
                          hipMemcpyDeviceToDevice, hs);
   if (e != hipSuccess) return hip_fail(e, "cache resize copy");
+  return ok();
+}
+
+ka_status ka_attn_int8_self_test(void) {
+  bool passed = false;
+  const char* why = "";
+  const hipError_t e = ka::int8_self_test(&passed, &why);
+  if (e != hipSuccess) return hip_fail(e, "int8 self-test");
+  if (!passed) return fail(KA_ERR_UNSUPPORTED, "%s", why);
   return ok();
 }
 
@@ -350,6 +383,7 @@ ka_status ka_attn_decode(const ka_attn_shape* s, const float* q, const void* k_c
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(KA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.workspace_bytes,
                 workspace ? workspace_bytes : (size_t)0);
+  if ((st = check_int8(sh)) != KA_OK) return st;
   hipError_t e = ka::launch_decode(sh, plan, q, const_cast<void*>(k_cache),
                                    const_cast<void*>(v_cache), out, ctx_len, scale, workspace,
                                    reinterpret_cast<hipStream_t>(stream));
@@ -383,6 +417,7 @@ ka_status ka_attn_decode_step(const ka_attn_shape* s, const float* q, const floa
   if (plan.workspace_bytes > 0 && (!workspace || workspace_bytes < plan.workspace_bytes))
     return fail(KA_ERR_WORKSPACE, "decode needs %zu workspace bytes, got %zu", plan.workspace_bytes,
                 workspace ? workspace_bytes : (size_t)0);
+  if ((st = check_int8(sh)) != KA_OK) return st;
   hipError_t e = ka::launch_decode(sh, plan, q, k_cache, v_cache, out, ctx.data(), scale,
                                    workspace, reinterpret_cast<hipStream_t>(stream), k_new, v_new);
   if (e != hipSuccess) return hip_fail(e, "decode step launch");

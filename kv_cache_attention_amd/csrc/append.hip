@@ -66,16 +66,56 @@ __host__ __device__ __forceinline__ void v_groups(bool bf16, int start, int R, i
   ng = g1 - g0;
 }
 
+// Dims d .. d + 3 (d a multiple of 4) of a K row as stored: as given, or
+// rotated (rotate-half pairs) with the row's cos / sin rows cr / sr.
+template <bool ROPE>
+__device__ __forceinline__ float4 k_dims4(const float* rowp, const float* cr, const float* sr,
+                                          int d, int D) {
+  if constexpr (!ROPE) {
+    return *reinterpret_cast<const float4*>(rowp + d);
+  } else {
+    const int h = D >> 1, j = d < h ? d : d - h;
+    float4 lo, hi;
+    rope4(*reinterpret_cast<const float4*>(rowp + j), *reinterpret_cast<const float4*>(rowp + j + h),
+          *reinterpret_cast<const float4*>(cr + j), *reinterpret_cast<const float4*>(sr + j), lo, hi);
+    return d < h ? lo : hi;
+  }
+}
+
+// int8 K: the 16 codes of dims 16 c .. 16 c + 15 of one row, and the row's
+// scale (every thread of the row finds the same amax over all D dims).
+template <bool ROPE>
+__device__ __forceinline__ uint4 k_codes16(const float* rowp, const float* cr, const float* sr,
+                                           int c, int D, float& s) {
+  AbsMax am;
+  for (int d = 0; d < D; d += 4) {
+    const float4 x = k_dims4<ROPE>(rowp, cr, sr, d, D);
+    am.add(x.x); am.add(x.y); am.add(x.z); am.add(x.w);
+  }
+  s = am.scale();
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float4 x = k_dims4<ROPE>(rowp, cr, sr, 16 * c + 4 * e, D);
+    w[e] = pack_codes4(x.x, x.y, x.z, x.w, s);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // ROPE: each new K row is rotated by its position's angles (cos / sin rows of
-// D/2 values, one per appended row) before it is stored; V as given.
-template <bool BF16, bool ROPE>
+// D/2 values, one per appended row) before it is stored; V as given.  MODE
+// (KvMode): f32 K / V; bf16 K / V; int8 K codes with their row scales in
+// k_scales ([B][Hkv][C] f32) and bf16 V.
+template <int MODE, bool ROPE>
 __global__ __launch_bounds__(256) void append_kernel(
     void* __restrict__ k_cache, void* __restrict__ v_cache,
     const float* __restrict__ k_new, const float* __restrict__ v_new,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
-    int Hkv, int D, int C, const AppendArg aa) {
-  constexpr int E = Elem<BF16>::E;
-  const int cpr = D / E;  // K vectors per row
+    float* __restrict__ k_scales, int Hkv, int D, int C, const AppendArg aa) {
+  constexpr bool BF16 = MODE != kF32;             // V (and bf16 K) in the bf16 layouts
+  constexpr int E = BF16 ? 8 : 4;                 // V elements per 16-byte vector
+  constexpr int EK = MODE == kI8K ? 16 : E;       // K elements per 16-byte vector
+  const int cpr = D / EK;  // K vectors per row
   const int si = blockIdx.y;
   const int b = aa.b[si], start = aa.start[si], R = aa.rows[si], row0 = aa.row0[si];
   const int rr0 = aa.rope_row0[si];
@@ -94,9 +134,18 @@ __global__ __launch_bounds__(256) void append_kernel(
       const int row = (int)(t / Hkv);
       const int j = start + row;
       const float* rowp = k_new + (((size_t)row0 + row) * Hkv + g) * D;
-      const float* src = rowp + c * E;
+      const float* src = rowp + c * EK;
       const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;  // elements
-      const size_t vi = k_vec_index(j, c, D, E);
+      const size_t vi = k_vec_index(j, c, D, EK);
+      if constexpr (MODE == kI8K) {
+        const float* cr = ROPE ? rope_cos + ((size_t)rr0 + row) * (D >> 1) : nullptr;
+        const float* sr = ROPE ? rope_sin + ((size_t)rr0 + row) * (D >> 1) : nullptr;
+        float sc;
+        const uint4 o = k_codes16<ROPE>(rowp, cr, sr, c, D, sc);
+        reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(k_cache) + slab)[vi] = o;
+        if (c == 0) k_scales[((size_t)b * Hkv + g) * C + j] = sc;
+        continue;
+      }
       float f[E];
       if constexpr (ROPE) {
         // this vector's E dims and their partners in the other half
@@ -188,9 +237,11 @@ static hipError_t launch_append_tables(const Shape& s, void* k_cache, void* v_ca
                                        const float* k_new, const float* v_new,
                                        const float* rope_cos, const float* rope_sin,
                                        const std::vector<AppendArg>& L, hipStream_t stream) {
-  const bool bf16 = s.kv_dtype == 1;
-  const int E = bf16 ? 8 : 4;
+  const int mode = s.kv_dtype;
+  const bool bf16 = mode != kF32;                      // V layout
+  const int E = mode == kF32 ? 4 : mode == kBF16 ? 8 : 16;   // K elements per vector
   const bool rope = rope_cos != nullptr;
+  float* k_scales = k_scale_array(s, k_cache);
   for (const AppendArg& aa : L) {
     long long most = 0;  // vectors of the largest session
     for (int i = 0; i < aa.n; ++i) {
@@ -205,12 +256,11 @@ static hipError_t launch_append_tables(const Shape& s, void* k_cache, void* v_ca
     const dim3 grid((unsigned)blocks, aa.n);
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, k_cache, v_cache, k_new, v_new,
-                         rope_cos, rope_sin, s.num_kv_heads, s.head_dim, s.capacity, aa);
+                         rope_cos, rope_sin, k_scales, s.num_kv_heads, s.head_dim, s.capacity, aa);
     };
-    if (bf16 && rope) go(append_kernel<true, true>);
-    else if (bf16) go(append_kernel<true, false>);
-    else if (rope) go(append_kernel<false, true>);
-    else go(append_kernel<false, false>);
+    if (mode == kI8K) rope ? go(append_kernel<kI8K, true>) : go(append_kernel<kI8K, false>);
+    else if (mode == kBF16) rope ? go(append_kernel<kBF16, true>) : go(append_kernel<kBF16, false>);
+    else rope ? go(append_kernel<kF32, true>) : go(append_kernel<kF32, false>);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -305,11 +355,13 @@ hipError_t launch_rope_rows(const float* x, float* y, const float* rope_cos,
 // k_new / v_new [B][Hkv][D] f32 -> cache position pos[b].  Thread i writes
 // one K vector or one V element (a V vector spans E positions, so only the
 // row's own element of it is stored).
-template <bool BF16>
+template <int MODE>
 __global__ __launch_bounds__(256) void append_row_kernel(
     void* __restrict__ k_cache, void* __restrict__ v_cache, const float* __restrict__ k_new,
-    const float* __restrict__ v_new, const CtxArg pos, int b0, int nb, int Hkv, int D, int C) {
-  constexpr int E = Elem<BF16>::E;
+    const float* __restrict__ v_new, float* __restrict__ k_scales, const CtxArg pos, int b0,
+    int nb, int Hkv, int D, int C) {
+  constexpr bool BF16 = MODE != kF32;
+  constexpr int E = MODE == kI8K ? 16 : MODE == kBF16 ? 8 : 4;  // K elements per vector
   const int cpr = D / E;
   const long long nk = (long long)nb * Hkv * cpr, nv = (long long)nb * Hkv * D;
   for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nk + nv;
@@ -322,7 +374,12 @@ __global__ __launch_bounds__(256) void append_row_kernel(
       const float* src = k_new + ((size_t)b * Hkv + g) * D + c * E;
       const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;
       const size_t vi = k_vec_index(j, c, D, E);
-      if constexpr (BF16) {
+      if constexpr (MODE == kI8K) {
+        float sc;
+        const uint4 o = k_codes16<false>(k_new + ((size_t)b * Hkv + g) * D, nullptr, nullptr, c, D, sc);
+        reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(k_cache) + slab)[vi] = o;
+        if (c == 0) k_scales[((size_t)b * Hkv + g) * C + j] = sc;
+      } else if constexpr (BF16) {
         const float4 a = *reinterpret_cast<const float4*>(src);
         const float4 bq = *reinterpret_cast<const float4*>(src + 4);
         uint4 o;
@@ -357,18 +414,18 @@ __global__ __launch_bounds__(256) void append_row_kernel(
 hipError_t launch_append_rows(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
                               const float* v_new, const CtxArg& pos, int b0, int nb,
                               hipStream_t stream) {
-  const int E = s.kv_dtype == 1 ? 8 : 4;
+  const int E = s.kv_dtype == kI8K ? 16 : s.kv_dtype == kBF16 ? 8 : 4;
   const long long total = (long long)nb * s.num_kv_heads * (s.head_dim / E + s.head_dim);
   long long blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  if (s.kv_dtype == 1)
-    hipLaunchKernelGGL(append_row_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       k_cache, v_cache, k_new, v_new, pos, b0, nb, s.num_kv_heads, s.head_dim,
-                       s.capacity);
-  else
-    hipLaunchKernelGGL(append_row_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       k_cache, v_cache, k_new, v_new, pos, b0, nb, s.num_kv_heads, s.head_dim,
-                       s.capacity);
+  float* k_scales = k_scale_array(s, k_cache);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k_cache, v_cache,
+                       k_new, v_new, k_scales, pos, b0, nb, s.num_kv_heads, s.head_dim, s.capacity);
+  };
+  if (s.kv_dtype == kI8K) go(append_row_kernel<kI8K>);
+  else if (s.kv_dtype == kBF16) go(append_row_kernel<kBF16>);
+  else go(append_row_kernel<kF32>);
   return hipGetLastError();
 }
 

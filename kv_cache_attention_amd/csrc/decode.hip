@@ -468,19 +468,26 @@ constexpr int kDecTile = 32;  // positions per wave tile
 constexpr int kStreamAux = 2;
 constexpr int kDecCols = 16;  // MFMA columns = most heads per workgroup
 
-template <int D>
+// I8: int8 K codes (16 per 16-byte vector, so a score step covers 64 dims)
+// with one f32 scale per position, scores on v_mfma_i32_16x16x64_i8.
+template <int D, bool I8>
 struct DecTile {
-  uint4 k[2][D / 32];  // [position block kb][dim step ks]
+  static constexpr int NKS = I8 ? D / 64 : D / 32;  // score k-steps
+  uint4 k[2][NKS];     // [position block kb][dim step ks]
   uint4 v[D / 16];     // [dim block db]
+  float4 sk[I8 ? 2 : 1];  // I8: scales of positions 16 kb + 4 r + 0..3
 };
 
-template <int D>
+template <int D, bool I8>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const float* __restrict__ q, void* k_cache, void* v_cache, float* __restrict__ out,
     float* __restrict__ part, float* __restrict__ part_ml, const float* __restrict__ k_new,
-    const float* __restrict__ v_new, const CtxArg ctxa, int b0, int nb, int Hq, int Hkv, int HG,
-    int hpw, int C, int S, float sl2e, int R) {
+    const float* __restrict__ v_new, const float* __restrict__ k_scales, const CtxArg ctxa,
+    int b0, int nb, int Hq, int Hkv, int HG, int hpw, int C, int S, float sl2e, int R) {
   typedef __attribute__((ext_vector_type(4))) float v4f;
+  typedef __attribute__((ext_vector_type(4))) int i32x4;
+  constexpr int NKS = DecTile<D, I8>::NKS;
+  constexpr int KE = I8 ? 16 : 8;  // K elements per 16-byte vector
   __shared__ float sacc[kWaves][kDecCols * D];
   __shared__ float wm[kWaves][kDecCols], wl[kWaves][kDecCols];
 
@@ -510,25 +517,30 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   const int NW = S * kWaves, j0 = split * kWaves + w;
   const int t0 = 0, t1 = j0 < nt ? (nt - 1 - j0) / NW + 1 : 0;  // local tile counts
 
-  const size_t slab_bytes = (size_t)C * D * 2;
-  const size_t slab = ((size_t)b * Hkv + g) * slab_bytes;
-  const __amdgpu_buffer_rsrc_t krs =
-      buffer_rsrc(reinterpret_cast<const unsigned char*>(k_cache) + slab, slab_bytes);
-  const __amdgpu_buffer_rsrc_t vrs =
-      buffer_rsrc(reinterpret_cast<const unsigned char*>(v_cache) + slab, slab_bytes);
+  const size_t slab_bytes = (size_t)C * D * 2;                 // V (and bf16 K)
+  const size_t k_slab_bytes = (size_t)C * D * (I8 ? 1 : 2);
+  const size_t slab_i = (size_t)b * Hkv + g;
+  const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(
+      reinterpret_cast<const unsigned char*>(k_cache) + slab_i * k_slab_bytes, k_slab_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(
+      reinterpret_cast<const unsigned char*>(v_cache) + slab_i * slab_bytes, slab_bytes);
+  const float* __restrict__ sk_row = I8 ? k_scales + slab_i * C : nullptr;
 
-  // operand loads of this wave's i-th tile, tile j0 + i NW (K layout [C/64][D/8][64][8], V [C/32][4][D][8]);
-  // every cache byte is read once per step, so the loads are marked non-temporal
-  auto load = [&](DecTile<D>& x, int i) {
+  // operand loads of this wave's i-th tile, tile j0 + i NW (K layout
+  // [C/64][D/KE][64][KE], V [C/32][4][D][8]); every cache byte is read once per
+  // step, so the loads are marked non-temporal
+  auto load = [&](DecTile<D, I8>& x, int i) {
     const int t = j0 + i * NW;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int pos = kDecTile * t + 16 * kb + lc;
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
+      for (int ks = 0; ks < NKS; ++ks)
         x.k[kb][ks] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       krs, (((pos >> 6) * (D / 8) + 4 * ks + r) * 64 + (pos & 63)) * 16, 0, kStreamAux));
+                       krs, (((pos >> 6) * (D / KE) + 4 * ks + r) * 64 + (pos & 63)) * 16, 0, kStreamAux));
+      if constexpr (I8)
+        x.sk[kb] = *reinterpret_cast<const float4*>(sk_row + kDecTile * t + 16 * kb + 4 * r);
     }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
@@ -537,7 +549,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
                      vrs, ((4 * t + r) * D + 16 * db + lc) * 16, 0, kStreamAux));
   };
 
-  DecTile<D> ta_, tb_;
+  DecTile<D, I8> ta_, tb_;
   if (t0 < t1) load(ta_, t0);
   if (t0 + 1 < t1) load(tb_, t0 + 1);
 
@@ -545,11 +557,42 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // group -- query row pc / G of the session's R rows (the last of which sits
   // at position ctx - 1), head g G + pc % G -- and zero past the pairs.  Its
   // keys are 0 .. lim.
-  bf16x8 qreg[D / 32];
+  bf16x8 qreg[I8 ? 1 : D / 32];
+  i32x4 qcode[I8 ? D / 64 : 1];  // I8: the column's codes, dims 64 ks + 16 r .. + 15
+  float sq = 0.f;                // I8: the column's scale times scale * log2 e
   const int pc = hg * hpw + lc;
   const bool hv = lc < hpw && pc < R * G;
   const int lim = ctx - R + (hv ? pc / G : 0);
-  {
+  if constexpr (I8) {
+    // symmetric int8 codes of the column's query row: amax over its D dims
+    // (this lane's D / 4 and the three lanes 16 and 32 apart), then codes
+    const float* qp = q + (((size_t)b * R + (hv ? pc / G : 0)) * Hq + g * G + (hv ? pc % G : 0)) * D + 16 * r;
+    float4 xq[D / 64][4];
+    AbsMax am;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xq[ks][e] = hv ? *reinterpret_cast<const float4*>(qp + 64 * ks + 4 * e)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        am.add(xq[ks][e].x); am.add(xq[ks][e].y); am.add(xq[ks][e].z); am.add(xq[ks][e].w);
+      }
+    float m = am.m, nf = am.nan ? 1.f : 0.f;
+    m = fmaxf(m, __shfl_xor(m, 16, kWave));
+    m = fmaxf(m, __shfl_xor(m, 32, kWave));
+    nf = fmaxf(nf, __shfl_xor(nf, 16, kWave));
+    nf = fmaxf(nf, __shfl_xor(nf, 32, kWave));
+    AbsMax col;
+    col.m = m;
+    col.nan = nf != 0.f;
+    const float s = col.scale();
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qcode[ks][e] = (int)pack_codes4(xq[ks][e].x, xq[ks][e].y, xq[ks][e].z, xq[ks][e].w, s);
+    sq = s * sl2e;
+  } else {
     const float* qp = q + (((size_t)b * R + (hv ? pc / G : 0)) * Hq + g * G + (hv ? pc % G : 0)) * D + 8 * r;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
@@ -580,7 +623,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // end; when it reaches that tile it uses those values in place of what its
   // loads of the tile brought in.  No other wave touches that position.
   const int p_new = ctx - 1, t_new = p_new / kDecTile;
-  const bool owns_new = k_new != nullptr && t_new % NW == j0;
+  // (int8-K caches get their new rows from the append kernel beforehand)
+  const bool owns_new = !I8 && k_new != nullptr && t_new % NW == j0;
   uint16_t* row_lds = reinterpret_cast<uint16_t*>(sacc[w]);  // [K row D][V row D] bf16
   if (owns_new) {
     const size_t slab_el = ((size_t)b * Hkv + g) * (size_t)C * D;
@@ -603,12 +647,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
       row_lds[D + d] = h;
     }
   }
-  auto take_new_row = [&](DecTile<D>& x) {
+  auto take_new_row = [&](DecTile<D, I8>& x) {
+    if constexpr (I8) return;
     const int kp = p_new - kDecTile * t_new;
     if (lc == (kp & 15)) {
       const bool hi = (kp >> 4) != 0;
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
+      for (int ks = 0; ks < NKS; ++ks) {
         const uint4 o = reinterpret_cast<const uint4*>(row_lds)[4 * ks + r];
         // 32-bit selects: a branch on the block index would index the
         // register arrays at run time
@@ -638,17 +683,30 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     }
   };
 
-  auto tile = [&](DecTile<D>& x, int i) {
+  auto tile = [&](DecTile<D, I8>& x, int i) {
     const int t = j0 + i * NW;
     if (owns_new && t == t_new) take_new_row(x);
     v4f sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      sc[kb] = v4f{0.f, 0.f, 0.f, 0.f};
+      if constexpr (I8) {
+        // integer scores, then times the column's and the key's scales
+        i32x4 si = {0, 0, 0, 0};
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-        sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.k[kb][ks]),
-                                                         qreg[ks], sc[kb], 0, 0, 0);
+        for (int ks = 0; ks < NKS; ++ks)
+          si = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, x.k[kb][ks]),
+                                                     qcode[ks], si, 0, 0, 0);
+        sc[kb][0] = (float)si[0] * (sq * x.sk[kb].x);
+        sc[kb][1] = (float)si[1] * (sq * x.sk[kb].y);
+        sc[kb][2] = (float)si[2] * (sq * x.sk[kb].z);
+        sc[kb][3] = (float)si[3] * (sq * x.sk[kb].w);
+      } else {
+        sc[kb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks)
+          sc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x.k[kb][ks]),
+                                                           qreg[ks], sc[kb], 0, 0, 0);
+      }
     }
     // keys past a column's limit get -inf (only tiles reaching past the
     // first limit, ctx - R); positions at or past ctx may hold anything
@@ -823,8 +881,8 @@ DecodePlan plan_decode(const Shape& s, int max_ctx) {
   DecodePlan p;
   const int G = s.num_q_heads / s.num_kv_heads;
   long long S;
-  if (s.kv_dtype == 1) {
-    // MFMA path: up to 16 heads share a workgroup's columns; one round of
+  if (s.kv_dtype != kF32) {
+    // MFMA path (bf16 and int8-K caches): up to 16 heads share a workgroup's columns; one round of
     // 256 workgroups (one per CU: a wave's operand registers fill its SIMD),
     // at least one tile per wave
     int hg = 1;
@@ -877,7 +935,7 @@ DecodePlan plan_rows(const Shape& s, int R, int ctx) {
 hipError_t launch_rows(const Shape& s, const DecodePlan& p, const float* q, const void* k_cache,
                        const void* v_cache, float* out, int start, int R, float scale,
                        void* workspace, hipStream_t stream) {
-  if (s.kv_dtype != 1) return hipErrorInvalidValue;
+  if (s.kv_dtype == kF32) return hipErrorInvalidValue;
   const float sl2e = scale * kLog2e;
   const int HG = p.head_groups, S = p.splits, hpw = p.heads_per_wg;
   float* part = reinterpret_cast<float*>(workspace);
@@ -890,11 +948,18 @@ hipError_t launch_rows(const Shape& s, const DecodePlan& p, const float* q, cons
     switch (s.head_dim) {
 #define KA_D(DD)                                                                               \
   case DD:                                                                                     \
-    hipLaunchKernelGGL((decode_mfma_kernel<DD>), mfma_grid(nb, s.num_kv_heads, HG, S), dim3(256), \
-                       0, stream, q, kc, vc, out,                                              \
-                       part, part + (size_t)s.batch * s.num_kv_heads * HG * S * hpw * DD,      \
-                       nullptr, nullptr, ca, b0, nb, s.num_q_heads, s.num_kv_heads, HG, hpw,   \
-                       s.capacity, S, sl2e, R);                                                \
+    if (s.kv_dtype == kI8K)                                                                    \
+      hipLaunchKernelGGL((decode_mfma_kernel<DD, true>), mfma_grid(nb, s.num_kv_heads, HG, S), \
+                         dim3(256), 0, stream, q, kc, vc, out, part,                           \
+                         part + (size_t)s.batch * s.num_kv_heads * HG * S * hpw * DD, nullptr, \
+                         nullptr, k_scale_array(s, kc), ca, b0, nb, s.num_q_heads,             \
+                         s.num_kv_heads, HG, hpw, s.capacity, S, sl2e, R);                     \
+    else                                                                                       \
+      hipLaunchKernelGGL((decode_mfma_kernel<DD, false>), mfma_grid(nb, s.num_kv_heads, HG, S),\
+                         dim3(256), 0, stream, q, kc, vc, out, part,                           \
+                         part + (size_t)s.batch * s.num_kv_heads * HG * S * hpw * DD, nullptr, \
+                         nullptr, nullptr, ca, b0, nb, s.num_q_heads, s.num_kv_heads, HG, hpw, \
+                         s.capacity, S, sl2e, R);                                              \
     if (S > 1) launch_merge<DD>(hpw, dim3(hpw * (DD / 32), s.num_kv_heads * HG, nb), stream,  \
                                 part, out, b0, s, HG, S, R);                                   \
     break;
@@ -912,7 +977,7 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, vo
                          void* v_cache, float* out, const int32_t* ctx_host, float scale,
                          void* workspace, hipStream_t stream, const float* k_new,
                          const float* v_new) {
-  const bool bf16 = s.kv_dtype == 1;
+  const bool bf16 = s.kv_dtype == kBF16, i8 = s.kv_dtype == kI8K;
   const float sl2e = scale * kLog2e;
   const int HG = p.head_groups, S = p.splits;
   float* part = reinterpret_cast<float*>(workspace);
@@ -922,7 +987,7 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, vo
     for (int i = 0; i < kMaxDecodeBatchPerLaunch; ++i) ca.ctx[i] = i < nb ? ctx_host[b0 + i] : 0;
     dim3 grid(S, s.num_kv_heads * HG, nb);
     if (k_new != nullptr && !bf16) {
-      // f32 caches: the new rows go in first, by their own kernel
+      // f32 and int8-K caches: the new rows go in first, by their own kernel
       CtxArg pos;
       for (int i = 0; i < kMaxDecodeBatchPerLaunch; ++i) pos.ctx[i] = i < nb ? ca.ctx[i] - 1 : 0;
       const hipError_t e = launch_append_rows(s, k_cache, v_cache, k_new, v_new, pos, b0, nb, stream);
@@ -932,12 +997,19 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, vo
 #define KA_D(DD)                                                                               \
   case DD:                                                                                     \
     if (bf16)                                                                                  \
-      hipLaunchKernelGGL((decode_mfma_kernel<DD>), mfma_grid(nb, s.num_kv_heads, HG, S),       \
+      hipLaunchKernelGGL((decode_mfma_kernel<DD, false>), mfma_grid(nb, s.num_kv_heads, HG, S),\
                          dim3(256), 0, stream, q, k_cache, v_cache, out, part,                 \
                          part + (size_t)s.batch * s.num_kv_heads * HG * S * p.heads_per_wg * DD, \
-                         k_new, v_new, ca, b0, nb, s.num_q_heads, s.num_kv_heads, HG,          \
+                         k_new, v_new, nullptr, ca, b0, nb, s.num_q_heads, s.num_kv_heads, HG, \
                          p.heads_per_wg,                                                       \
                          s.capacity, S, sl2e, 1);                                              \
+    else if (i8)                                                                               \
+      hipLaunchKernelGGL((decode_mfma_kernel<DD, true>), mfma_grid(nb, s.num_kv_heads, HG, S), \
+                         dim3(256), 0, stream, q, k_cache, v_cache, out, part,                 \
+                         part + (size_t)s.batch * s.num_kv_heads * HG * S * p.heads_per_wg * DD, \
+                         nullptr, nullptr, k_scale_array(s, k_cache), ca, b0, nb,              \
+                         s.num_q_heads, s.num_kv_heads, HG, p.heads_per_wg, s.capacity, S,     \
+                         sl2e, 1);                                                             \
     else dispatch_hpw<DD, false>(p.heads_per_wg, grid, stream, q, k_cache, v_cache, out, part, \
                                  ca, b0, s, HG, S, sl2e);                                      \
     if (S > 1) launch_merge<DD>(p.heads_per_wg,                                               \

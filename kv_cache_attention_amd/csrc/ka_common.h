@@ -31,6 +31,10 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // --------------------------------------------------------- cache layouts
 // Element counts per 16-byte vector: 8 bf16 or 4 f32.
+// Cache element formats: kv_dtype 0 = f32, 1 = bf16, 2 = int8 K codes (with
+// one f32 scale per row) and bf16 V.
+enum KvMode { kF32 = 0, kBF16 = 1, kI8K = 2 };
+
 template <bool BF16> struct Elem;
 template <> struct Elem<true> { typedef uint16_t T; static constexpr int E = 8; };
 template <> struct Elem<false> { typedef float T; static constexpr int E = 4; };
@@ -128,5 +132,37 @@ __device__ __forceinline__ float group_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------- int8 K rows
+// Symmetric int8 quantisation of one row (Karume v0.8.0 release notes,
+// "Fixes": the activation-quantisation scale is amax times the f32 value of
+// 1/127, in f32): s = amax * f32(1/127); code = round-half-even(x / s) (IEEE
+// division), limited to +-127.  A row with a NaN gets s = NaN, an infinite
+// one s = inf; rows whose s is 0 or not finite get codes 0 (their scores are
+// then 0 * s).
+constexpr float kInv127 = 1.0f / 127.0f;
+
+// max |x| of the values seen so far, NaN once any of them was NaN
+struct AbsMax {
+  float m = 0.f;
+  bool nan = false;
+  __device__ __forceinline__ void add(float x) {
+    nan = nan || (x != x);
+    m = fmaxf(m, fabsf(x));
+  }
+  __device__ __forceinline__ float scale() const { return nan ? __builtin_nanf("") : m * kInv127; }
+};
+
+__device__ __forceinline__ int quant_code(float x, float s) {
+  if (!(s > 0.f) || !(s <= 3.402823466e38f)) return 0;  // 0, NaN or inf
+  const float r = rintf(__fdiv_rn(x, s));
+  return (int)fminf(fmaxf(r, -127.f), 127.f);
+}
+
+// Four codes packed little-endian into one 32-bit word.
+__device__ __forceinline__ uint32_t pack_codes4(float a, float b, float c, float d, float s) {
+  return (uint32_t)(quant_code(a, s) & 0xff) | ((uint32_t)(quant_code(b, s) & 0xff) << 8) |
+         ((uint32_t)(quant_code(c, s) & 0xff) << 16) | ((uint32_t)(quant_code(d, s) & 0xff) << 24);
+}
 
 }  // namespace ka

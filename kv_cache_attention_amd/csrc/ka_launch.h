@@ -20,6 +20,14 @@ struct CtxArg {
   int32_t ctx[kMaxDecodeBatchPerLaunch];
 };
 
+// int8-K caches: the row scales follow the codes of every slab in the K
+// buffer, [B][Hkv][C] f32 from byte B * Hkv * C * D (null for other dtypes).
+inline float* k_scale_array(const Shape& s, const void* k_cache) {
+  if (s.kv_dtype != 2) return nullptr;
+  return reinterpret_cast<float*>(const_cast<unsigned char*>(static_cast<const unsigned char*>(k_cache)) +
+                                  (size_t)s.batch * s.num_kv_heads * s.capacity * s.head_dim);
+}
+
 // rope_cos / rope_sin: null for a plain append, else [R][D/2] rows that rotate
 // each new K row before it is stored.
 hipError_t launch_append(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
@@ -89,5 +97,10 @@ DecodePlan plan_rows(const Shape& s, int R, int ctx);
 hipError_t launch_rows(const Shape& s, const DecodePlan& p, const float* q, const void* k_cache,
                        const void* v_cache, float* out, int start, int R, float scale,
                        void* workspace, hipStream_t stream);
+
+// ---- int8 scores: the device self-test (run once per device, then cached).
+// *passed tells whether the int8 MFMA and its emulation both gave the known
+// answer; *why is a static description of the outcome.
+hipError_t int8_self_test(bool* passed, const char** why);
 
 }  // namespace ka

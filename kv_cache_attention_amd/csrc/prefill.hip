@@ -315,18 +315,28 @@ __device__ __forceinline__ void pv_tile(const uint4* __restrict__ v_lds, const v
                                         v4f (&acc_o)[D / 16][2], int lr, int lg) {
   constexpr int NDB = D / 16;
   if constexpr (BF16) {
+    // B operand of 32-key half k2 for the lane's V group g = 2 u + h (this
+    // lane's l / 16), which holds keys {16 u + 4 h + 0..3, 16 u + 8 + 4 h +
+    // 0..3} of the half.  The lane has the weights of keys 16 kb + 4 (l / 16)
+    // + 0..3: a lane of the lower half (g < 2: u = 0, h = g) owns the first
+    // four in its block 2 k2 and finds the other four in the lane 32 above;
+    // a lane of the upper half (u = 1, h = g - 2) owns the last four (block
+    // 2 k2 + 1) and finds the first four 32 below -- one v_permlane32_swap
+    // per pair of packed words.
     bf16x8 pb[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        float f[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          f[i] = p[2 * k2][mb][i];
-          f[4 + i] = p[2 * k2 + 1][mb][i];
-        }
-        pb[mb][k2] = to_bf16x8(f);
+        const v4f& lo = p[2 * k2][mb];
+        const v4f& hi = p[2 * k2 + 1][mb];
+        const uint32_t a0 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo[0], (__bf16)lo[1]});
+        const uint32_t a1 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo[2], (__bf16)lo[3]});
+        const uint32_t b0 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)hi[0], (__bf16)hi[1]});
+        const uint32_t b1 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)hi[2], (__bf16)hi[3]});
+        const auto x0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+        const auto x1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+        pb[mb][k2] = __builtin_bit_cast(bf16x8, make_uint4(x0[0], x1[0], x0[1], x1[1]));
       }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -608,6 +618,300 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
   for (int i = 0; i < n; i += 2) {
     step(std::integral_constant<int, 0>(), i, sa, sb);
     if (i + 1 < n) step(std::integral_constant<int, 1>(), i + 1, sb, sa);
+  }
+  store_result<D>(t, out, part, part_ml, acc_o, m_run, l_run, R, Hq, Hkv, m_tiles, S);
+}
+
+// ============================================================================
+// int8-K caches: the pipelined 4-wave kernel with integer scores.
+//
+// K tiles hold int8 codes (64 D bytes: vector (dim group c, key) at c 64 +
+// key, 16 codes each) followed in LDS by the tile's 64 row scales (staged by
+// 16 lanes of wave 0); V tiles are bf16.  Q is quantised per (row, head)
+// column as K is (amax over the column's D values, shared by the four lanes
+// that hold them), its codes stationary in registers.  S^T = K . Q^T on
+// v_mfma_i32_16x16x64_i8: A = 16 codes of key 16 kb + l % 16, dims 64 ks +
+// 16 (l / 16) ..; B = 16 codes of the lane's column at the same dims; lane l
+// gets keys 16 kb + 4 (l / 16) + 0..3.  The integer scores stay in the score
+// registers until the softmax of their tile turns them into
+// (float) dot * (s_q * scale * log2 e) * s_k.  A tile's key scales are read
+// from LDS while the tile is the next one (its buffer is refilled before its
+// softmax runs) and carried in registers with its scores.  Partials are f32.
+// ============================================================================
+template <int D>
+struct I8Cfg {
+  static constexpr int KTB = 64 * D;             // K tile: int8 codes
+  static constexpr int KTB_LDS = KTB + 256;      // + the tile's 64 scales
+  static constexpr int VTB = 64 * D * 2;         // V tile: bf16
+  static constexpr int NKS = D / 64;             // score k-steps
+  static constexpr int NDB = D / 16;
+};
+
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+// Codes and scale of this lane's two columns: lane (lr, lg) holds dims
+// 64 ks + 16 lg .. + 15; sq = s_q * scale * log2 e.
+template <int D>
+__device__ __forceinline__ void load_q_i8(const Tiling& t, const float* __restrict__ q, int Hq,
+                                          float sl2e, i32x4 (&qc)[2][D / 64], float (&sq)[2]) {
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int m = t.m_col[mb];
+    const bool ok = t.valid_col[mb];
+    const float* qp = q + (((size_t)t.row0 + (ok ? m / t.G : 0)) * Hq + t.g * t.G + (ok ? m % t.G : 0)) * D +
+                      16 * t.lg;
+    float4 x[D / 64][4];
+    AbsMax am;
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[ks][e] = ok ? *reinterpret_cast<const float4*>(qp + 64 * ks + 4 * e)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        am.add(x[ks][e].x); am.add(x[ks][e].y); am.add(x[ks][e].z); am.add(x[ks][e].w);
+      }
+    float mx = am.m, nf = am.nan ? 1.f : 0.f;
+    mx = fmaxf(mx, xor_shfl(mx, 16));
+    mx = fmaxf(mx, xor_shfl(mx, 32));
+    nf = fmaxf(nf, xor_shfl(nf, 16));
+    nf = fmaxf(nf, xor_shfl(nf, 32));
+    AbsMax col;
+    col.m = mx;
+    col.nan = nf != 0.f;
+    const float sc = col.scale();
+#pragma unroll
+    for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qc[mb][ks][e] = (int)pack_codes4(x[ks][e].x, x[ks][e].y, x[ks][e].z, x[ks][e].w, sc);
+    sq[mb] = sc * sl2e;
+  }
+}
+
+// This lane's key scales of a staged K tile: keys 16 kb + 4 lg + 0..3.
+template <int D>
+__device__ __forceinline__ void tile_scales(const unsigned char* k_lds, int lg, float4 (&sk)[4]) {
+  const float4* p = reinterpret_cast<const float4*>(k_lds + I8Cfg<D>::KTB);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) sk[kb] = p[4 * kb + lg];
+}
+
+// Integer scores of one staged K tile (into the score registers, as bits).
+template <int D>
+__device__ __forceinline__ void qk_tile_i8(const uint4* __restrict__ k_lds,
+                                           const i32x4 (&qc)[2][D / 64], v4f (&sacc)[4][2], int lr,
+                                           int lg) {
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) sacc[kb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const i32x4 a = __builtin_bit_cast(i32x4, k_lds[(4 * ks + lg) * 64 + 16 * kb + lr]);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        sacc[kb][mb] = __builtin_bit_cast(
+            v4f, __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qc[mb][ks],
+                                                       __builtin_bit_cast(i32x4, sacc[kb][mb]), 0, 0, 0));
+    }
+}
+
+// As qk_next_softmax_cur, with integer scores: the next tile's MFMAs
+// interleaved with the current tile's softmax, whose phases 0 and 1 first
+// scale the integer scores (sk_cur: the current tile's key scales); the next
+// tile's key scales are read from its LDS buffer into sk_nxt.
+template <int D>
+__device__ __forceinline__ void qk_next_softmax_cur_i8(
+    const Tiling& t, const unsigned char* __restrict__ k_next_lds, const i32x4 (&qc)[2][D / 64],
+    const float (&sq)[2], v4f (&nxt)[4][2], v4f (&cur)[4][2], const float4 (&sk_cur)[4],
+    float4 (&sk_nxt)[4], int kt, int start, float (&m_run)[2], float (&l_run)[2],
+    float (&alpha)[2]) {
+  constexpr int NKS = D / 64;
+  const int lr = t.lr, lg = t.lg;
+  const uint4* k_lds = reinterpret_cast<const uint4*>(k_next_lds);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) nxt[kb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  const bool diag = kt * kNTile + kNTile - 1 > start + t.row_lo;
+  float lmax[2] = {-INFINITY, -INFINITY};
+  float ls[2] = {0.f, 0.f};
+  float m_use[2];
+  uint4 kbuf[2][4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) kbuf[0][kb] = k_lds[(4 * 0 + lg) * 64 + 16 * kb + lr];
+  tile_scales<D>(k_next_lds, lg, sk_nxt);
+
+  auto phase = [&](int ph) {
+    if (ph == 0 || ph == 1) {
+      const int mb = ph;
+      const int lim = start + t.row_col[mb];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float skv[4] = {sk_cur[kb].x, sk_cur[kb].y, sk_cur[kb].z, sk_cur[kb].w};
+        // the four integer scores, read as one vector before any is
+        // overwritten (a bit cast of one element of the float vector does
+        // not reliably read that element)
+        const i32x4 ci = __builtin_bit_cast(i32x4, cur[kb][mb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // integer score -> log2 domain: dot * (s_q scale log2 e) * s_k
+          float sv = (float)ci[i] * (sq[mb] * skv[i]);
+          if (diag) {
+            const int key = kt * kNTile + 16 * kb + 4 * lg + i;
+            if (key > lim || !t.valid_col[mb]) sv = -INFINITY;
+          }
+          cur[kb][mb][i] = sv;
+          lmax[mb] = fmaxf(lmax[mb], sv);
+        }
+      }
+    } else if (ph == 2) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        lmax[mb] = fmaxf(lmax[mb], xor_shfl(lmax[mb], 16));
+        lmax[mb] = fmaxf(lmax[mb], xor_shfl(lmax[mb], 32));
+      }
+    } else if (ph == 3) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        alpha[mb] = 1.f;
+        if (lmax[mb] > m_run[mb] + kRescaleSlack) {
+          alpha[mb] = fast_exp2(m_run[mb] - lmax[mb]);  // 0 when m_run is -inf
+          m_run[mb] = lmax[mb];
+          l_run[mb] *= alpha[mb];
+        }
+        m_use[mb] = m_run[mb] == -INFINITY ? 0.f : m_run[mb];
+      }
+    } else {
+      const int kb = ph - 4;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pv = fast_exp2(cur[kb][mb][i] - m_use[mb]);
+          cur[kb][mb][i] = pv;
+          ls[mb] += pv;
+        }
+    }
+  };
+
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    if (ks + 1 < NKS) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        kbuf[(ks + 1) & 1][kb] = k_lds[(4 * (ks + 1) + lg) * 64 + 16 * kb + lr];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const i32x4 a = __builtin_bit_cast(i32x4, kbuf[ks & 1][kb]);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+        nxt[kb][mb] = __builtin_bit_cast(
+            v4f, __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qc[mb][ks],
+                                                       __builtin_bit_cast(i32x4, nxt[kb][mb]), 0, 0, 0));
+    }
+    // softmax phases assigned to this chunk (all 8 spread over NKS chunks)
+#pragma unroll
+    for (int ph = 0; ph < 8; ++ph)
+      if (ph * NKS / 8 == ks) phase(ph);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) l_run[mb] += ls[mb];
+}
+
+// Copies the row scales of K tile `tile` (256 bytes) behind its codes in LDS:
+// lanes 0..15 of wave 0, 16 bytes each.
+template <int D>
+__device__ __forceinline__ void load_tile_scales(const TileSrc& src, int tile, unsigned char* dst,
+                                                 int w, int lane) {
+  if (w == 0 && lane < 16) dma16(src.rsrc, dst + I8Cfg<D>::KTB, tile * 256 + lane * 16);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void prefill_i8_kernel(
+    const float* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
+    float* __restrict__ part_ml, const float* __restrict__ k_scales, int Hq, int Hkv, int C,
+    const ChunkArg ca, float sl2e) {
+  using Cfg = I8Cfg<D>;
+  constexpr int NDB = Cfg::NDB, KTB = Cfg::KTB, VTB = Cfg::VTB;
+  __shared__ __attribute__((aligned(16))) unsigned char kb0[Cfg::KTB_LDS];
+  __shared__ __attribute__((aligned(16))) unsigned char kb1[Cfg::KTB_LDS];
+  __shared__ __attribute__((aligned(16))) unsigned char vb0[VTB];
+  __shared__ __attribute__((aligned(16))) unsigned char vb1[VTB];
+
+  Tiling t;
+  if (!make_tiling(ca, Hq, Hkv, t)) return;
+  const int start = t.start, R = t.R, m_tiles = t.m_tiles, S = t.S;
+  const size_t slab_i = (size_t)t.b * Hkv + t.g;
+  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab_i * C * D, (size_t)C * D);
+  const TileSrc ssrc = tile_src(k_scales + slab_i * C, (size_t)C * 4);
+  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab_i * C * D * 2, (size_t)C * D * 2);
+  const int n = t.kt1 - t.kt0;
+
+  i32x4 qc[2][D / 64];
+  float sq[2];
+  v4f acc_o[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc_o[db][mb] = v4f{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+  v4f sa[4][2], sb[4][2];
+  float4 ska[4], skb[4];
+
+  if (n > 0) {
+    load_tile<KTB>(ksrc, t.kt0, kb0, t.w, t.lane);
+    load_tile_scales<D>(ssrc, t.kt0, kb0, t.w, t.lane);
+    load_q_i8<D>(t, q, Hq, sl2e, qc, sq);
+    wait_vmem();
+    __syncthreads();
+    load_tile<VTB>(vsrc, t.kt0, vb0, t.w, t.lane);
+    if (n > 1) {
+      load_tile<KTB>(ksrc, t.kt0 + 1, kb1, t.w, t.lane);
+      load_tile_scales<D>(ssrc, t.kt0 + 1, kb1, t.w, t.lane);
+    }
+    qk_tile_i8<D>(reinterpret_cast<const uint4*>(kb0), qc, sa, t.lr, t.lg);
+    tile_scales<D>(kb0, t.lg, ska);
+  }
+
+  // step i: V(i) in vb[i&1], K(i+1) in kb[(i+1)&1], integer scores of tile i
+  // in cur and its key scales in sk_cur
+  auto step = [&](auto par, int i, v4f (&cur)[4][2], v4f (&nxt)[4][2], float4 (&sk_cur)[4],
+                  float4 (&sk_nxt)[4]) {
+    constexpr int P = decltype(par)::value;
+    unsigned char* k_next = P == 0 ? kb1 : kb0;   // holds K(i+1)
+    unsigned char* k_free = P == 0 ? kb0 : kb1;   // held K(i): free for K(i+2)
+    unsigned char* v_cur = P == 0 ? vb0 : vb1;    // holds V(i)
+    unsigned char* v_free = P == 0 ? vb1 : vb0;   // held V(i-1): free for V(i+1)
+    const int kt = t.kt0 + i;
+    wait_vmem();
+    __syncthreads();  // V(i), K(i+1) landed; every wave is done with step i-1
+    if (i + 2 < n) {
+      load_tile<KTB>(ksrc, kt + 2, k_free, t.w, t.lane);
+      load_tile_scales<D>(ssrc, kt + 2, k_free, t.w, t.lane);
+    }
+    if (i + 1 < n) load_tile<VTB>(vsrc, kt + 1, v_free, t.w, t.lane);
+    if ((kt + 1) * kNTile > t.kend) {
+      zero_v_beyond<D, true>(reinterpret_cast<uint4*>(v_cur), kt, t.kend, t.tid);
+      __syncthreads();
+    }
+    // (the last step computes one spare tile of scores from a stale buffer,
+    // which is never used)
+    float alpha[2];
+    qk_next_softmax_cur_i8<D>(t, k_next, qc, sq, nxt, cur, sk_cur, sk_nxt, kt, start, m_run, l_run,
+                              alpha);
+    rescale_acc<NDB>(alpha, acc_o);
+    pv_tile<D, true>(reinterpret_cast<const uint4*>(v_cur), cur, acc_o, t.lr, t.lg);
+  };
+  for (int i = 0; i < n; i += 2) {
+    step(std::integral_constant<int, 0>(), i, sa, sb, ska, skb);
+    if (i + 1 < n) step(std::integral_constant<int, 1>(), i + 1, sb, sa, skb, ska);
   }
   store_result<D>(t, out, part, part_ml, acc_o, m_run, l_run, R, Hq, Hkv, m_tiles, S);
 }
@@ -1373,7 +1677,7 @@ int max_splits(long long units) {
 // this session's key tiles.
 int choose_splits(const Shape& s, long long units, int nkt) {
   const double scale_d = s.head_dim / 256.0;
-  const double tile_ns = (s.kv_dtype == 1 ? 1300.0 : 9000.0) * scale_d;
+  const double tile_ns = (s.kv_dtype == kBF16 ? 1300.0 : s.kv_dtype == kI8K ? 2000.0 : 9000.0) * scale_d;
   const double wg_ns = 3000.0, merge_ns = 4000.0, part_ns = 26.0 * scale_d;
   const int smax = max_splits(units);
   int best = 1;
@@ -1398,11 +1702,12 @@ struct ChunkLaunch {
   int max_m, max_s;
 };
 
-template <int D, bool BF16>
+template <int D, int MODE>
 hipError_t launch_chunks(const Shape& s, const ChunkLaunch* L, int nl, long long total_slots,
                          const float* q, const void* kc, const void* vc, float* out, float scale,
                          void* ws, hipStream_t st) {
-  using Cfg = PrefillCfg<D, BF16>;
+  constexpr bool BF16 = MODE == kBF16;  // binary16 partials (the 8-wave kernel)
+  using Cfg = PrefillCfg<D, false>;
   // partials: binary16 accumulators for bf16 caches, f32 otherwise, one
   // 128-column slot per (session, KV head, m-tile, split); then the
   // per-(column, split) records
@@ -1415,16 +1720,20 @@ hipError_t launch_chunks(const Shape& s, const ChunkLaunch* L, int nl, long long
     if (items == 0) continue;
     // padded to whole rounds of the 8 XCDs (see make_tiling)
     const dim3 grid(8 * ((items + 7) / 8));
-    if constexpr (BF16)
+    if constexpr (MODE == kBF16)
       hipLaunchKernelGGL((prefill_bf16_kernel<D>), grid, dim3(kBf16Threads), 0, st, q, kc, vc, out,
                          part, part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, ca,
                          scale * kLog2e);
+    else if constexpr (MODE == kI8K)
+      hipLaunchKernelGGL((prefill_i8_kernel<D>), grid, dim3(256), 0, st, q, kc, vc, out, part,
+                         part_ml, k_scale_array(s, kc), s.num_q_heads, s.num_kv_heads, s.capacity,
+                         ca, scale * kLog2e);
     else if constexpr (Cfg::PIPE)
-      hipLaunchKernelGGL((prefill_pipe_kernel<D, BF16>), grid, dim3(256), 0, st, q, kc, vc, out,
+      hipLaunchKernelGGL((prefill_pipe_kernel<D, false>), grid, dim3(256), 0, st, q, kc, vc, out,
                          part, part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, ca,
                          scale * kLog2e);
     else
-      hipLaunchKernelGGL((prefill_seq_kernel<D, BF16>), grid, dim3(256), 0, st, q, kc, vc, out,
+      hipLaunchKernelGGL((prefill_seq_kernel<D, false>), grid, dim3(256), 0, st, q, kc, vc, out,
                          part, part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, ca,
                          scale * kLog2e);
     hipError_t e = hipGetLastError();
@@ -1484,21 +1793,26 @@ long long build_launches(const Shape& s, Rows rows_of, Start start_of, Splits sp
   return slot;
 }
 
-template <int D, bool BF16>
+template <int D>
+hipError_t launch_mode(const Shape& s, const std::vector<ChunkLaunch>& L, long long slots,
+                       const float* q, const void* kc, const void* vc, float* out, float scale,
+                       void* ws, hipStream_t st) {
+  const int n = (int)L.size();
+  switch (s.kv_dtype) {
+    case kBF16: return launch_chunks<D, kBF16>(s, L.data(), n, slots, q, kc, vc, out, scale, ws, st);
+    case kI8K: return launch_chunks<D, kI8K>(s, L.data(), n, slots, q, kc, vc, out, scale, ws, st);
+    default: return launch_chunks<D, kF32>(s, L.data(), n, slots, q, kc, vc, out, scale, ws, st);
+  }
+}
+
+template <int D>
 hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const void* kc,
                     const void* vc, float* out, int start, int R, float scale, void* ws,
                     hipStream_t st) {
   std::vector<ChunkLaunch> L;
   const long long slots = build_launches(
       s, [&](int) { return R; }, [&](int) { return start; }, [&](int, int) { return p.splits; }, L);
-  return launch_chunks<D, BF16>(s, L.data(), (int)L.size(), slots, q, kc, vc, out, scale, ws, st);
-}
-
-template <int D, bool BF16>
-hipError_t launch_ragged_t(const Shape& s, const std::vector<ChunkLaunch>& L, long long slots,
-                           const float* q, const void* kc, const void* vc, float* out,
-                           float scale, void* ws, hipStream_t st) {
-  return launch_chunks<D, BF16>(s, L.data(), (int)L.size(), slots, q, kc, vc, out, scale, ws, st);
+  return launch_mode<D>(s, L, slots, q, kc, vc, out, scale, ws, st);
 }
 
 }  // namespace
@@ -1506,7 +1820,7 @@ hipError_t launch_ragged_t(const Shape& s, const std::vector<ChunkLaunch>& L, lo
 // Workspace bytes per (column, split): binary16 accumulators and a 6-float
 // record for bf16 caches, f32 accumulators and an (m, l) pair otherwise.
 static size_t partial_bytes(const Shape& s) {
-  return s.kv_dtype == 1 ? (size_t)s.head_dim * 2 + 6 * sizeof(float)
+  return s.kv_dtype == kBF16 ? (size_t)s.head_dim * 2 + 6 * sizeof(float)
                          : (size_t)(s.head_dim + 2) * sizeof(float);
 }
 
@@ -1531,7 +1845,7 @@ static int rows_groups(const Shape& s, int R) {
 }
 
 static bool rows_path(const Shape& s, int R, int ctx) {
-  if (s.kv_dtype != 1 || R > kRowsMaxRows) return false;
+  if (s.kv_dtype == kF32 || R > kRowsMaxRows) return false;
   const int G = s.num_q_heads / s.num_kv_heads;
   const int hg = rows_groups(s, R);
   if (hg > kRowsMaxGroups) return false;
@@ -1576,7 +1890,7 @@ size_t prefill_workspace_bound(const Shape& s, int max_rows) {
   // few-row chunks that may take the streaming kernel: its split count
   // grows with the context, so the full capacity bounds every start
   for (int R = 1; R <= max_rows && R <= kRowsMaxRows; ++R) {
-    if (s.kv_dtype != 1 || rows_groups(s, R) > kRowsMaxGroups) break;
+    if (s.kv_dtype == kF32 || rows_groups(s, R) > kRowsMaxGroups) break;
     const size_t bytes = plan_rows(s, R, s.capacity).workspace_bytes;
     if (bytes > best) best = bytes;
   }
@@ -1627,14 +1941,10 @@ hipError_t launch_prefill_ragged(const Shape& s, const float* q, const void* k_c
                                  hipStream_t stream) {
   std::vector<ChunkLaunch> L;
   const long long slots = ragged_launches(s, start, rows, L);
-  const bool bf16 = s.kv_dtype == 1;
   switch (s.head_dim) {
-#define KA_R(DD)                                                                                  \
-  case DD:                                                                                        \
-    return bf16 ? launch_ragged_t<DD, true>(s, L, slots, q, k_cache, v_cache, out, scale, workspace, stream) \
-                : launch_ragged_t<DD, false>(s, L, slots, q, k_cache, v_cache, out, scale, workspace, stream);
-    KA_R(64) KA_R(128) KA_R(256)
-#undef KA_R
+    case 64: return launch_mode<64>(s, L, slots, q, k_cache, v_cache, out, scale, workspace, stream);
+    case 128: return launch_mode<128>(s, L, slots, q, k_cache, v_cache, out, scale, workspace, stream);
+    case 256: return launch_mode<256>(s, L, slots, q, k_cache, v_cache, out, scale, workspace, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1644,14 +1954,10 @@ hipError_t launch_prefill(const Shape& s, const PrefillPlan& p, const float* q,
                           float scale, void* workspace, hipStream_t stream) {
   if (p.m_tiles == 0)
     return launch_rows(s, p.rows, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
-  const bool bf16 = s.kv_dtype == 1;
   switch (s.head_dim) {
-    case 64: return bf16 ? launch_t<64, true>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream)
-                         : launch_t<64, false>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
-    case 128: return bf16 ? launch_t<128, true>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream)
-                          : launch_t<128, false>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
-    case 256: return bf16 ? launch_t<256, true>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream)
-                          : launch_t<256, false>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
+    case 64: return launch_t<64>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
+    case 128: return launch_t<128>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
+    case 256: return launch_t<256>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -41,3 +41,14 @@ def logical_values(raw, B, Hkv, C, D, kv_dtype, which):
     un = (unpack_k if which == "k" else unpack_v)(raw, B, Hkv, C, D, kv_dtype)
     vals = bits_to_f32(un) if kv_dtype == "bf16" else un
     return np.ascontiguousarray(vals.transpose(0, 2, 1, 3))
+
+
+def unpack_k_i8(raw, B, Hkv, C, D):
+    """int8-K caches: codes [B][Hkv][C][D] (int8) and row scales [B][Hkv][C]
+    (f32) from the raw K buffer, by the header's byte index formulas."""
+    a = np.ascontiguousarray(raw).view(np.uint8)
+    n = B * Hkv * C * D
+    codes = a[:n].view(np.int8).reshape(B, Hkv, C // 64, D // 16, 64, 16)
+    codes = codes.transpose(0, 1, 2, 4, 3, 5).reshape(B, Hkv, C, D)
+    scales = a[n:n + B * Hkv * C * 4].view(np.float32).reshape(B, Hkv, C)
+    return codes, scales

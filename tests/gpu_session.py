@@ -4,7 +4,7 @@ import numpy as np
 import torch
 
 import kv_cache_attention_amd as ka
-from tests.cache_layout import logical_values, unpack_k, unpack_v
+from tests.cache_layout import logical_values, unpack_k, unpack_k_i8, unpack_v
 
 POISON = 0xFF   # every byte 0xFF: a NaN in both f32 and bf16
 
@@ -16,7 +16,7 @@ def dev(x: np.ndarray) -> torch.Tensor:
 class DevCaches:
     def __init__(self, B, Hq, Hkv, D, C, kv_dtype, poison=True):
         if isinstance(kv_dtype, str):
-            kv_dtype = {"f32": ka.F32, "bf16": ka.BF16}[kv_dtype]
+            kv_dtype = {"f32": ka.F32, "bf16": ka.BF16, "i8k": ka.I8K}[kv_dtype]
         self.B, self.Hq, self.Hkv, self.D, self.C, self.dt = B, Hq, Hkv, D, C, kv_dtype
         self.shape = ka.Shape(B, Hq, Hkv, D, C, kv_dtype)
         fill = POISON if poison else 0
@@ -91,6 +91,16 @@ class DevCaches:
         a = (self.B, self.Hkv, self.C, self.D, self.dt_name)
         return unpack_k(rk, *a), unpack_v(rv, *a)
 
+    def k_i8(self):
+        """int8-K caches: K codes [B][Hkv][C][D] and row scales [B][Hkv][C]."""
+        rk, _ = self.raw()
+        return unpack_k_i8(rk, self.B, self.Hkv, self.C, self.D)
+
+    def v_bits(self):
+        """V element bit patterns [B][Hkv][C][D] (bf16 layout for int8-K caches)."""
+        _, rv = self.raw()
+        return unpack_v(rv, self.B, self.Hkv, self.C, self.D, "f32" if self.dt == ka.F32 else "bf16")
+
     @property
     def dt_name(self):
-        return "bf16" if self.dt == ka.BF16 else "f32"
+        return {ka.BF16: "bf16", ka.F32: "f32", ka.I8K: "i8k"}[self.dt]

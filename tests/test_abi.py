@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import kv_cache_attention_amd as ka
-from tests.cache_layout import unpack_k, unpack_v
+from tests.cache_layout import unpack_k, unpack_k_i8, unpack_v
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ka_attn.h")
@@ -65,6 +65,9 @@ def S(**kw):
 def test_cache_bytes():
     _lib_or_skip()
     assert ka.cache_bytes(S()) == 4096 * 256 * 2
+    # int8 K: both buffers the bf16 V size, which holds the codes and the row scales
+    assert ka.cache_bytes(S(kv_dtype=ka.I8K, batch=2)) == 2 * 4096 * 256 * 2
+    assert ka.cache_bytes(S(kv_dtype=ka.I8K, head_dim=64)) >= 4096 * (64 + 4)
     assert ka.cache_bytes(S(kv_dtype=ka.F32, batch=3, num_kv_heads=2)) == 3 * 2 * 4096 * 256 * 4
     assert ka.cache_bytes(S(head_dim=96)) == 0
     assert ka.cache_bytes(S(capacity=100)) == 0
@@ -328,3 +331,24 @@ def test_layout_reader_round_trip_k_and_v():
                         raw_v[vi] = val
         assert np.array_equal(unpack_k(raw_k, B, Hkv, C, D, dt).astype(np.float64), want)
         assert np.array_equal(unpack_v(raw_v, B, Hkv, C, D, dt).astype(np.float64), want)
+
+
+def test_int8_k_layout_reader():
+    """The int8-K reader inverts the header's byte formulas (a marked buffer:
+    every code byte holds its (j + d) mod 251 - 125, every scale its row)."""
+    B, Hkv, C, D = 2, 2, 128, 32
+    raw = np.zeros(B * Hkv * C * D + B * Hkv * C * 4, np.uint8)
+    want_c = np.zeros((B, Hkv, C, D), np.int8)
+    for b in range(B):
+        for g in range(Hkv):
+            for j in range(C):
+                for d in range(D):
+                    v = (j + d + 7 * b + 3 * g) % 251 - 125
+                    want_c[b, g, j, d] = v
+                    i = (((b * Hkv + g) * (C // 64) + j // 64) * (D // 16) + d // 16) * 64 * 16 + (j % 64) * 16 + d % 16
+                    raw[i] = np.uint8(v & 0xFF)
+    sc = np.arange(B * Hkv * C, dtype=np.float32) * 0.5
+    raw[B * Hkv * C * D:] = sc.view(np.uint8)
+    codes, scales = unpack_k_i8(raw, B, Hkv, C, D)
+    assert np.array_equal(codes, want_c)
+    assert np.array_equal(scales.reshape(-1), sc)
