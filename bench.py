@@ -112,9 +112,15 @@ def prefill_flops(w):
     return pairs * w.num_q_heads * w.head_dim * 4 * w.batch, pairs
 
 
-def decode_bytes(w, ctx, batch):
-    """Algorithmic HBM bytes of one decode call: K and V rows once, q and out."""
-    el = 2 if w.kv_dtype == "bf16" else 4
+def decode_bytes(w, ctx, batch, kv_dtype=None):
+    """Algorithmic HBM bytes of one decode call: K and V rows once, q and out.
+    int8-K caches: per row D code bytes and a 4-byte scale for K, 2 D for V."""
+    kv_dtype = kv_dtype or w.kv_dtype
+    if kv_dtype == "i8k":
+        kv = batch * w.num_kv_heads * ctx * (3 * w.head_dim + 4)
+        qo = 2 * batch * w.num_q_heads * w.head_dim * 4
+        return kv + qo
+    el = 2 if kv_dtype == "bf16" else 4
     kv = 2 * batch * w.num_kv_heads * ctx * w.head_dim * el
     qo = 2 * batch * w.num_q_heads * w.head_dim * 4
     return kv + qo
@@ -123,13 +129,13 @@ def decode_bytes(w, ctx, batch):
 class Session16K:
     """Device state of the 16K session workload."""
 
-    def __init__(self):
+    def __init__(self, kv_dtype="bf16"):
         self.w = w = WORKLOADS[4]
         c = draw_batch(w)
         self.k = dev(c.k)          # [1][P][1][256]
         self.v = dev(c.v)
         self.q = dev(c.q)          # [1][16448][8][256]
-        self.shape = ka.Shape(1, 8, 1, 256, w.capacity, "bf16")
+        self.shape = ka.Shape(1, 8, 1, 256, w.capacity, kv_dtype)
         self.kc = ka.alloc_cache(self.shape, fill_byte=0xFF)
         self.vc = ka.alloc_cache(self.shape, fill_byte=0xFF)
         self.out_p = torch.empty(768 * 8 * 256, device="cuda")
@@ -255,11 +261,11 @@ def copy_calibration(mib=256, reps=5):
             "gbs": round(nbytes / (float(np.median(times)) * 1e-3) / 1e9, 1)}
 
 
-def bench_decode_128k(hold, steps=32):
+def bench_decode_128k(hold, steps=32, kv_dtype="bf16"):
     w = WORKLOADS[5]
     c = draw_batch(w)
     log("128K: drawn")
-    shape = ka.Shape(w.batch, 8, 1, 256, w.capacity, "bf16")
+    shape = ka.Shape(w.batch, 8, 1, 256, w.capacity, kv_dtype)
     kc = ka.alloc_cache(shape, fill_byte=0xFF)
     vc = ka.alloc_cache(shape, fill_byte=0xFF)
     for s0 in range(0, w.positions, 16384):
@@ -301,7 +307,7 @@ def bench_decode_128k(hold, steps=32):
     dec = np.array(reps)
     ctx_mean = int(np.mean([p + 1 for p in w.decode_positions[:steps]]))
     return dict(w=w, decode_ms=float(np.median(dec)), step_ms=float(np.median(step_ms)),
-                bytes=decode_bytes(w, ctx_mean, w.batch), ctx_mean=ctx_mean)
+                bytes=decode_bytes(w, ctx_mean, w.batch, kv_dtype), ctx_mean=ctx_mean)
 
 
 def bench_prefill_f32(hold, reps=10):
@@ -371,6 +377,42 @@ def bench_rope(hold, reps=20):
             torch.cuda.synchronize()
             ts.append(a.elapsed_time(b) * 1e3)
         res[name] = round(float(np.median(ts)), 2)
+    return res
+
+
+def bench_int8(hold):
+    """The 16K session and the 4 x 131K decode steps on int8-K caches (int8 K
+    codes with row scales, bf16 V, integer scores): the session's 22 chunk
+    calls and 64 decode steps, and the 128K steps with their HBM rate."""
+    ka.int8_self_test()
+    s = Session16K("i8k")
+    s.prefill_phase()
+    s.decode_phase()
+    torch.cuda.synchronize()
+    pre, dec = [], []
+    for _ in range(3):
+        pe = [ev_pair() for _ in s.chunk_views]
+        de = [ev_pair() for _ in s.dec_views]
+        hold(3.0)
+        s.prefill_phase(pe)
+        hold(3.0)
+        s.decode_phase(de)
+        torch.cuda.synchronize()
+        pre.append(sum(a.elapsed_time(b) for a, b in pe))
+        dec.append([a.elapsed_time(b) * 1e3 for a, b in de])
+    rows = sum(R for _, R in s.w.chunks)
+    pm = float(np.median(pre))
+    res = {"prefill_16k_ms": round(pm, 4), "prefill_16k_rows_per_s": round(rows / (pm * 1e-3), 1),
+           "decode_us_per_token_16k_kernel_median": round(float(np.median(dec)), 3)}
+    del s
+    torch.cuda.empty_cache()
+    d = bench_decode_128k(hold, kv_dtype="i8k")
+    gbs = d["bytes"] / (d["decode_ms"] * 1e-3) / 1e9
+    res["decode_us_per_step_128k_x4"] = round(d["decode_ms"] * 1e3, 3)
+    res["roofline_decode_128k"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                   "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                   "algorithmic_bytes_per_launch": d["bytes"]}
+    torch.cuda.empty_cache()
     return res
 
 
@@ -655,6 +697,7 @@ def main():
     out["rope"] = bench_rope(hold)
     out["few_row_chunks"] = bench_few_rows(hold)
     out["ragged_8_sessions_16k"] = bench_ragged(hold)
+    out["int8_k"] = bench_int8(hold)
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w)
