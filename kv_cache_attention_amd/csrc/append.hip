@@ -82,24 +82,36 @@ __device__ __forceinline__ float4 k_dims4(const float* rowp, const float* cr, co
   }
 }
 
-// int8 K: the 16 codes of dims 16 c .. 16 c + 15 of one row, and the row's
-// scale (every thread of the row finds the same amax over all D dims).
+// int8 K: one wave quantises one row.  Lane l takes dims 4 l .. 4 l + 3
+// (lanes past D / 4 take none), the amax and the NaN flag are reduced across
+// the wave, and every lane stores its four codes as one 32-bit word of the
+// row's 16-byte code vectors; lane 0 stores the scale.  codes: the slab's
+// code bytes; vec_base(c): the byte offset of the row's code vector c.
 template <bool ROPE>
-__device__ __forceinline__ uint4 k_codes16(const float* rowp, const float* cr, const float* sr,
-                                           int c, int D, float& s) {
+__device__ __forceinline__ void quantise_row_wave(const float* rowp, const float* cr,
+                                                  const float* sr, int D, int lane,
+                                                  int8_t* codes, size_t row_vec0, float* scale_out) {
+  const bool mine = 4 * lane < D;
+  const float4 x = mine ? k_dims4<ROPE>(rowp, cr, sr, 4 * lane, D) : make_float4(0.f, 0.f, 0.f, 0.f);
   AbsMax am;
-  for (int d = 0; d < D; d += 4) {
-    const float4 x = k_dims4<ROPE>(rowp, cr, sr, d, D);
-    am.add(x.x); am.add(x.y); am.add(x.z); am.add(x.w);
-  }
-  s = am.scale();
-  uint32_t w[4];
+  am.add(x.x); am.add(x.y); am.add(x.z); am.add(x.w);
+  float m = am.m, nf = am.nan ? 1.f : 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float4 x = k_dims4<ROPE>(rowp, cr, sr, 16 * c + 4 * e, D);
-    w[e] = pack_codes4(x.x, x.y, x.z, x.w, s);
+  for (int k = 1; k < kWave; k <<= 1) {
+    m = fmaxf(m, __shfl_xor(m, k, kWave));
+    nf = fmaxf(nf, __shfl_xor(nf, k, kWave));
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  AbsMax row;
+  row.m = m;
+  row.nan = nf != 0.f;
+  const float s = row.scale();
+  if (mine) {
+    // dims 4 l .. 4 l + 3 sit in code vector l / 4, bytes 4 (l % 4) .. + 3; vectors
+    // of one row are 64 vectors (1 KiB) apart in the [D/16][64][16] block layout
+    const size_t off = (row_vec0 + (size_t)(lane >> 2) * 64) * 16 + 4 * (lane & 3);
+    *reinterpret_cast<uint32_t*>(codes + off) = pack_codes4(x.x, x.y, x.z, x.w, s);
+  }
+  if (lane == 0) *scale_out = s;
 }
 
 // ROPE: each new K row is rotated by its position's angles (cos / sin rows of
@@ -125,7 +137,24 @@ __global__ __launch_bounds__(256) void append_kernel(
   const long long n_v_vecs = (long long)Hkv * v_groups_per_slab * D;
   long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long stride = (long long)gridDim.x * blockDim.x;
-  for (long long i = tid; i < n_k_vecs + n_v_vecs; i += stride) {
+  long long first = tid;
+  if constexpr (MODE == kI8K) {
+    // K rows one per wave, then the V vectors
+    const int lane = threadIdx.x & (kWave - 1);
+    const long long wv = tid / kWave, nw = stride / kWave;
+    for (long long rt = wv; rt < (long long)R * Hkv; rt += nw) {
+      const int g = (int)(rt % Hkv), row = (int)(rt / Hkv);
+      const int j = start + row;
+      const float* rowp = k_new + (((size_t)row0 + row) * Hkv + g) * D;
+      const float* cr = ROPE ? rope_cos + ((size_t)rr0 + row) * (D >> 1) : nullptr;
+      const float* sr = ROPE ? rope_sin + ((size_t)rr0 + row) * (D >> 1) : nullptr;
+      const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;  // bytes
+      quantise_row_wave<ROPE>(rowp, cr, sr, D, lane, reinterpret_cast<int8_t*>(k_cache) + slab,
+                              k_vec_index(j, 0, D, 16), k_scales + ((size_t)b * Hkv + g) * C + j);
+    }
+    first = tid + n_k_vecs;  // the vector loop below does V only
+  }
+  for (long long i = first; i < n_k_vecs + n_v_vecs; i += stride) {
     if (i < n_k_vecs) {
       // K vector: (row, g, c) with c innermost
       const int c = (int)(i % cpr);
@@ -137,15 +166,6 @@ __global__ __launch_bounds__(256) void append_kernel(
       const float* src = rowp + c * EK;
       const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;  // elements
       const size_t vi = k_vec_index(j, c, D, EK);
-      if constexpr (MODE == kI8K) {
-        const float* cr = ROPE ? rope_cos + ((size_t)rr0 + row) * (D >> 1) : nullptr;
-        const float* sr = ROPE ? rope_sin + ((size_t)rr0 + row) * (D >> 1) : nullptr;
-        float sc;
-        const uint4 o = k_codes16<ROPE>(rowp, cr, sr, c, D, sc);
-        reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(k_cache) + slab)[vi] = o;
-        if (c == 0) k_scales[((size_t)b * Hkv + g) * C + j] = sc;
-        continue;
-      }
       float f[E];
       if constexpr (ROPE) {
         // this vector's E dims and their partners in the other half
@@ -247,8 +267,10 @@ static hipError_t launch_append_tables(const Shape& s, void* k_cache, void* v_ca
     for (int i = 0; i < aa.n; ++i) {
       int g0, ng;
       v_groups(bf16, aa.start[i], aa.rows[i], g0, ng);
-      const long long n = (long long)aa.rows[i] * s.num_kv_heads * (s.head_dim / E) +
-                          (long long)s.num_kv_heads * ng * s.head_dim;
+      // threads: one per K vector (int8 K: one wave per row) and per V vector
+      const long long nk = mode == kI8K ? (long long)aa.rows[i] * s.num_kv_heads * kWave
+                                        : (long long)aa.rows[i] * s.num_kv_heads * (s.head_dim / E);
+      const long long n = nk + (long long)s.num_kv_heads * ng * s.head_dim;
       if (n > most) most = n;
     }
     long long blocks = (most + 255) / 256;
@@ -364,8 +386,23 @@ __global__ __launch_bounds__(256) void append_row_kernel(
   constexpr int E = MODE == kI8K ? 16 : MODE == kBF16 ? 8 : 4;  // K elements per vector
   const int cpr = D / E;
   const long long nk = (long long)nb * Hkv * cpr, nv = (long long)nb * Hkv * D;
-  for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < nk + nv;
-       i += (long long)gridDim.x * blockDim.x) {
+  const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long stride = (long long)gridDim.x * blockDim.x;
+  long long first = tid;
+  if constexpr (MODE == kI8K) {
+    // K rows one per wave, then the V elements
+    const int lane = threadIdx.x & (kWave - 1);
+    for (long long rt = tid / kWave; rt < (long long)nb * Hkv; rt += stride / kWave) {
+      const int g = (int)(rt % Hkv), bl = (int)(rt / Hkv), b = b0 + bl;
+      const int j = pos.ctx[bl];
+      const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;  // bytes
+      quantise_row_wave<false>(k_new + ((size_t)b * Hkv + g) * D, nullptr, nullptr, D, lane,
+                               reinterpret_cast<int8_t*>(k_cache) + slab, k_vec_index(j, 0, D, 16),
+                               k_scales + ((size_t)b * Hkv + g) * C + j);
+    }
+    first = tid + nk;
+  }
+  for (long long i = first; i < nk + nv; i += stride) {
     if (i < nk) {
       const int c = (int)(i % cpr);
       const long long t = i / cpr;
@@ -374,12 +411,7 @@ __global__ __launch_bounds__(256) void append_row_kernel(
       const float* src = k_new + ((size_t)b * Hkv + g) * D + c * E;
       const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;
       const size_t vi = k_vec_index(j, c, D, E);
-      if constexpr (MODE == kI8K) {
-        float sc;
-        const uint4 o = k_codes16<false>(k_new + ((size_t)b * Hkv + g) * D, nullptr, nullptr, c, D, sc);
-        reinterpret_cast<uint4*>(reinterpret_cast<int8_t*>(k_cache) + slab)[vi] = o;
-        if (c == 0) k_scales[((size_t)b * Hkv + g) * C + j] = sc;
-      } else if constexpr (BF16) {
+      if constexpr (BF16) {
         const float4 a = *reinterpret_cast<const float4*>(src);
         const float4 bq = *reinterpret_cast<const float4*>(src + 4);
         uint4 o;
@@ -415,7 +447,8 @@ hipError_t launch_append_rows(const Shape& s, void* k_cache, void* v_cache, cons
                               const float* v_new, const CtxArg& pos, int b0, int nb,
                               hipStream_t stream) {
   const int E = s.kv_dtype == kI8K ? 16 : s.kv_dtype == kBF16 ? 8 : 4;
-  const long long total = (long long)nb * s.num_kv_heads * (s.head_dim / E + s.head_dim);
+  const long long total = (long long)nb * s.num_kv_heads *
+                          ((s.kv_dtype == kI8K ? kWave : s.head_dim / E) + s.head_dim);
   long long blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   float* k_scales = k_scale_array(s, k_cache);
