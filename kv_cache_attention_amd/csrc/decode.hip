@@ -482,7 +482,7 @@ template <int D, bool I8>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const float* __restrict__ q, void* k_cache, void* v_cache, float* __restrict__ out,
     float* __restrict__ part, float* __restrict__ part_ml, const float* __restrict__ k_new,
-    const float* __restrict__ v_new, const float* __restrict__ k_scales, const CtxArg ctxa,
+    const float* __restrict__ v_new, float* __restrict__ k_scales, const CtxArg ctxa,
     int b0, int nb, int Hq, int Hkv, int HG, int hpw, int C, int S, float sl2e, int R) {
   typedef __attribute__((ext_vector_type(4))) float v4f;
   typedef __attribute__((ext_vector_type(4))) int i32x4;
@@ -623,23 +623,54 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // end; when it reaches that tile it uses those values in place of what its
   // loads of the tile brought in.  No other wave touches that position.
   const int p_new = ctx - 1, t_new = p_new / kDecTile;
-  // (int8-K caches get their new rows from the append kernel beforehand)
-  const bool owns_new = !I8 && k_new != nullptr && t_new % NW == j0;
-  uint16_t* row_lds = reinterpret_cast<uint16_t*>(sacc[w]);  // [K row D][V row D] bf16
+  // int8-K: the wave quantises the row as the append kernel does and keeps
+  // its codes (as bf16 keeps its rounded row) and its scale s_new.
+  const bool owns_new = k_new != nullptr && t_new % NW == j0;
+  uint16_t* row_lds = reinterpret_cast<uint16_t*>(sacc[w]);  // [K row][V row D bf16]
+  float s_new = 0.f;
   if (owns_new) {
     const size_t slab_el = ((size_t)b * Hkv + g) * (size_t)C * D;
     const float* kn = k_new + ((size_t)b * Hkv + g) * D;
     const float* vn = v_new + ((size_t)b * Hkv + g) * D;
-    uint4* kw = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_cache) + slab_el);
     uint16_t* vw = reinterpret_cast<uint16_t*>(v_cache) + slab_el;
     const int gv = vbf16_group(p_new), e = vbf16_slot(p_new);
-    for (int c = lane; c < D / 8; c += 64) {  // K: one 8-dim vector per lane
-      const float4 x0 = *reinterpret_cast<const float4*>(kn + 8 * c);
-      const float4 x1 = *reinterpret_cast<const float4*>(kn + 8 * c + 4);
-      const uint4 o = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
-                                 pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
-      kw[k_vec_index(p_new, c, D, 8)] = o;
-      reinterpret_cast<uint4*>(row_lds)[c] = o;
+    if constexpr (I8) {
+      // lane l: dims 4 l .. 4 l + 3; amax and NaN flag across the wave
+      const bool mine = 4 * lane < D;
+      const float4 x = mine ? *reinterpret_cast<const float4*>(kn + 4 * lane)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+      AbsMax am;
+      am.add(x.x); am.add(x.y); am.add(x.z); am.add(x.w);
+      float m = am.m, nf = am.nan ? 1.f : 0.f;
+#pragma unroll
+      for (int k = 1; k < kWave; k <<= 1) {
+        m = fmaxf(m, __shfl_xor(m, k, kWave));
+        nf = fmaxf(nf, __shfl_xor(nf, k, kWave));
+      }
+      AbsMax row;
+      row.m = m;
+      row.nan = nf != 0.f;
+      s_new = row.scale();
+      if (mine) {
+        // codes of dims 4 l .. + 3: word l % 4 of code vector l / 4 (vectors of a
+        // row are 64 vectors apart); the same word index in LDS
+        const uint32_t wc = pack_codes4(x.x, x.y, x.z, x.w, s_new);
+        int8_t* kb8 = reinterpret_cast<int8_t*>(k_cache) + slab_el;  // one byte per code
+        *reinterpret_cast<uint32_t*>(
+            kb8 + (k_vec_index(p_new, 0, D, 16) + (size_t)(lane >> 2) * 64) * 16 + 4 * (lane & 3)) = wc;
+        reinterpret_cast<uint32_t*>(row_lds)[lane] = wc;
+      }
+      if (lane == 0) k_scales[slab_i * C + p_new] = s_new;
+    } else {
+      uint4* kw = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_cache) + slab_el);
+      for (int c = lane; c < D / 8; c += 64) {  // K: one 8-dim vector per lane
+        const float4 x0 = *reinterpret_cast<const float4*>(kn + 8 * c);
+        const float4 x1 = *reinterpret_cast<const float4*>(kn + 8 * c + 4);
+        const uint4 o = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
+                                   pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
+        kw[k_vec_index(p_new, c, D, 8)] = o;
+        reinterpret_cast<uint4*>(row_lds)[c] = o;
+      }
     }
     for (int d = lane; d < D; d += 64) {  // V: the row's element of each vector
       const uint16_t h = (uint16_t)f32_to_bf16_bits(vn[d]);
@@ -648,8 +679,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     }
   }
   auto take_new_row = [&](DecTile<D, I8>& x) {
-    if constexpr (I8) return;
     const int kp = p_new - kDecTile * t_new;
+    // K operand of the new key: 16-byte vector 4 ks + r of the row in LDS (8
+    // bf16 values, or 16 int8 codes)
     if (lc == (kp & 15)) {
       const bool hi = (kp >> 4) != 0;
 #pragma unroll
@@ -665,6 +697,21 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         x.k[1][ks].y = hi ? o.y : x.k[1][ks].y;
         x.k[1][ks].z = hi ? o.z : x.k[1][ks].z;
         x.k[1][ks].w = hi ? o.w : x.k[1][ks].w;
+      }
+    }
+    if constexpr (I8) {
+      // its scale, in the lanes that hold key kp's scores (keys 16 kb + 4 r + i)
+      if (r == ((kp & 15) >> 2)) {
+        const bool hi = (kp >> 4) != 0;
+        const int i = kp & 3;
+        x.sk[0].x = (!hi && i == 0) ? s_new : x.sk[0].x;
+        x.sk[0].y = (!hi && i == 1) ? s_new : x.sk[0].y;
+        x.sk[0].z = (!hi && i == 2) ? s_new : x.sk[0].z;
+        x.sk[0].w = (!hi && i == 3) ? s_new : x.sk[0].w;
+        x.sk[1].x = (hi && i == 0) ? s_new : x.sk[1].x;
+        x.sk[1].y = (hi && i == 1) ? s_new : x.sk[1].y;
+        x.sk[1].z = (hi && i == 2) ? s_new : x.sk[1].z;
+        x.sk[1].w = (hi && i == 3) ? s_new : x.sk[1].w;
       }
     }
     if (r == vbf16_group(p_new) - 4 * t_new) {
@@ -986,8 +1033,8 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, vo
     CtxArg ca;
     for (int i = 0; i < kMaxDecodeBatchPerLaunch; ++i) ca.ctx[i] = i < nb ? ctx_host[b0 + i] : 0;
     dim3 grid(S, s.num_kv_heads * HG, nb);
-    if (k_new != nullptr && !bf16) {
-      // f32 and int8-K caches: the new rows go in first, by their own kernel
+    if (k_new != nullptr && s.kv_dtype == kF32) {
+      // f32 caches: the new rows go in first, by their own kernel
       CtxArg pos;
       for (int i = 0; i < kMaxDecodeBatchPerLaunch; ++i) pos.ctx[i] = i < nb ? ca.ctx[i] - 1 : 0;
       const hipError_t e = launch_append_rows(s, k_cache, v_cache, k_new, v_new, pos, b0, nb, stream);
@@ -1007,7 +1054,7 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, vo
       hipLaunchKernelGGL((decode_mfma_kernel<DD, true>), mfma_grid(nb, s.num_kv_heads, HG, S), \
                          dim3(256), 0, stream, q, k_cache, v_cache, out, part,                 \
                          part + (size_t)s.batch * s.num_kv_heads * HG * S * p.heads_per_wg * DD, \
-                         nullptr, nullptr, k_scale_array(s, k_cache), ca, b0, nb,              \
+                         k_new, v_new, k_scale_array(s, k_cache), ca, b0, nb,                  \
                          s.num_q_heads, s.num_kv_heads, HG, p.heads_per_wg, s.capacity, S,     \
                          sl2e, 1);                                                             \
     else dispatch_hpw<DD, false>(p.heads_per_wg, grid, stream, q, k_cache, v_cache, out, part, \
