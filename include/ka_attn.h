@@ -51,7 +51,7 @@
  *   that every kernel reads whole 16-byte vectors.  Element (b, g, j, d) --
  *   session b, KV head g, position j, dimension d -- lives at element index
  *
- *   K (both dtypes):  ((((b*Hkv + g)*(C/64) + j/64)*(D/E) + d/E)*64 + j%64)*E + d%E
+ *   K (f32, bf16):    ((((b*Hkv + g)*(C/64) + j/64)*(D/E) + d/E)*64 + j%64)*E + d%E
  *                     i.e. [B][Hkv][C/64][D/E][64][E]: per 64-position block,
  *                     E consecutive dims of 64 consecutive positions.
  *   V, f32:           (((b*Hkv + g)*(C/4) + j/4)*D + d)*4 + j%4
@@ -134,7 +134,9 @@ size_t ka_attn_cache_bytes(const ka_attn_shape* s);
  *
  * Writes rows k_new[b][i], v_new[b][i] (f32 [B][R][Hkv][D]) into cache
  * positions start_pos + i, i < row_count, of every session b: an exact copy
- * for f32 caches, round-to-nearest-even to bf16 for bf16 caches.
+ * for f32 caches, round-to-nearest-even to bf16 for bf16 caches; on int8-K
+ * caches K rows are quantised (see the int8-K layout above) and V rows
+ * rounded to bf16.
  * row_count == 0 is a no-op.  Errors: KA_ERR_INVALID_ARGUMENT (null pointer,
  * row_count < 0, start_pos < 0), KA_ERR_OUT_OF_RANGE (start_pos + row_count
  * > C), KA_ERR_UNSUPPORTED, KA_ERR_HIP.
@@ -194,7 +196,7 @@ size_t ka_attn_prefill_workspace_bytes(const ka_attn_shape* s, int32_t max_rows)
  * and attends to cache positions 0 .. start_pos + i, which must already hold
  * appended rows.  Which kernel serves a chunk depends on its size (Karume
  * v0.12.0 release notes, "Docs": the plan-size geometry table for 1, 2-15
- * and 16 or more rows): on bf16 caches a chunk of up to 15 rows may be
+ * and 16 or more rows): on bf16 and int8-K caches a chunk of up to 15 rows may be
  * served by the split-context decode kernel, its (row, head) pairs taken as
  * columns with a causal limit each, when that is estimated to be faster;
  * otherwise, and on f32 caches, by the 128-column M-tile kernel.  Results
@@ -243,7 +245,7 @@ ka_status ka_attn_decode(const ka_attn_shape* s, const float* q,
  * rounding, same bits), and the query row q[b] at that position attends to
  * cache positions 0 .. pos[b].  Equivalent to one ka_attn_append_kv per
  * session followed by ka_attn_decode with ctx_len[b] = pos[b] + 1, and bitwise
- * equal to it, in one launch for bf16 caches (the attention kernel writes the
+ * equal to it, in one launch for bf16 and int8-K caches (the attention kernel writes the
  * row it uses).  pos is a HOST array of B entries, 0 <= pos[b] < C.  The
  * workspace is ka_attn_decode's for max_b pos[b] + 1.  k_new, v_new and q may
  * not overlap the caches or out.  Errors as ka_attn_decode.
@@ -302,7 +304,7 @@ size_t ka_attn_prefill_ragged_workspace_need(const ka_attn_shape* s, const int32
  * start and row count.  q and out are f32 [sum row_count][Hq][D], packed as
  * above; out may not alias q.  The sessions' tiles share each launch, so
  * short chunks of many sessions fill the GPU together.  Every session runs
- * on the M-tile kernel (on bf16 caches the few-row form of
+ * on the M-tile kernel (on bf16 and int8-K caches the few-row form of
  * ka_attn_prefill_chunk is not used here).  workspace: device scratch of at
  * least ka_attn_prefill_ragged_workspace_bytes(s, sum row_count) bytes.
  * Errors: those of ka_attn_prefill_chunk, per entry.
