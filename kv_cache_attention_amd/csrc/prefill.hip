@@ -991,41 +991,50 @@ __device__ __forceinline__ ColB col_b(const Tiling& t, int cb, int start) {
 }
 
 // Stationary Q^T operand, scaled by sl2e in f32 and rounded once to bf16.
-// The two waves of a column block share it: wave half kh loads k-steps
-// kh D/32 .. kh D/32 + D/32 - 1 from memory and stores them to q_lds
-// ([column block][k-step][lane], 16 bytes each); after a barrier,
-// take_q_half reads the partner's k-steps.  Q is thus fetched once per
-// workgroup, not once per wave.
+// The workgroup's 128 columns of Q (f32, D values each) are first copied
+// into LDS by the buffer-to-LDS DMA, every wave instruction moving one
+// column's contiguous D * 4 bytes (D = 256) or several columns: column col's
+// 16-byte chunk j (dims 4 j .. 4 j + 3) lands at granule
+// col * D/4 + (j ^ (col mod D/4)).  The permutation costs nothing on the
+// global side (a lane may fetch any address) and makes the operand reads of
+// one k-step (32 columns, the same chunk of each) hit every LDS bank
+// equally.  Columns past the chunk's end read the last valid column (their
+// results are never stored).
 template <int D>
-__device__ __forceinline__ void load_q_half(const Tiling& t, const ColB& c, int kh, int cb,
-                                            const float* __restrict__ q, int R, int Hq,
-                                            float sl2e, bf16x8 (&qreg)[D / 16],
-                                            uint4* __restrict__ q_lds) {
-  const float* qp = q + (((size_t)t.row0 + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D;
+__device__ __forceinline__ void dma_q(const Tiling& t, const float* __restrict__ q, int Hq,
+                                      unsigned char* dst) {
+  constexpr int NT = kBf16Threads, GR = D / 4;
+  const int row_hi = min(t.R - 1, (t.m_base + kMTile - 1) / t.G);
+  const float* base = q + ((size_t)t.row0 + t.row_lo) * Hq * D;
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, (size_t)(row_hi - t.row_lo + 1) * Hq * D * 4);
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    if (ks / (D / 32) != kh) continue;
-    float f[8];
-    if (c.valid) {
-      const float4 a = *reinterpret_cast<const float4*>(qp + 16 * ks + 8 * c.lh);
-      const float4 b = *reinterpret_cast<const float4*>(qp + 16 * ks + 8 * c.lh + 4);
-      f[0] = a.x * sl2e; f[1] = a.y * sl2e; f[2] = a.z * sl2e; f[3] = a.w * sl2e;
-      f[4] = b.x * sl2e; f[5] = b.y * sl2e; f[6] = b.z * sl2e; f[7] = b.w * sl2e;
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) f[j] = 0.f;
-    }
-    qreg[ks] = to_bf16x8(f);
-    q_lds[(cb * (D / 16) + ks) * 64 + t.lane] = __builtin_bit_cast(uint4, qreg[ks]);
+  for (int i = 0; i < kMTile * GR / NT; ++i) {
+    const int p = i * NT + t.w * 64 + t.lane;  // LDS granule this lane fills
+    const int col = p / GR, j = (p % GR) ^ (col & (GR - 1));
+    const int m = min(t.m_base + col, t.M_total - 1);
+    const int off = (((m / t.G - t.row_lo) * Hq + t.g * t.G + m % t.G) * D + 4 * j) * 4;
+    dma16(rs, dst + (size_t)(i * NT + t.w * 64) * 16, off);
   }
 }
 
+// This lane's operand registers from the staged Q: k-step ks holds dims
+// 16 ks + 8 h .. 16 ks + 8 h + 7 of column 32 cb + lane % 32 (h = lane / 32).
 template <int D>
-__device__ __forceinline__ void take_q_half(int kh, int cb, int lane, bf16x8 (&qreg)[D / 16],
-                                            const uint4* __restrict__ q_lds) {
+__device__ __forceinline__ void take_q(const ColB& c, int cb, float sl2e,
+                                       const float4* __restrict__ q_lds, bf16x8 (&qreg)[D / 16]) {
+  constexpr int GR = D / 4;
+  const int col = 32 * cb + c.lc, sw = col & (GR - 1);
+  const float4* qc = q_lds + col * GR;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    if (ks / (D / 32) != kh) qreg[ks] = __builtin_bit_cast(bf16x8, q_lds[(cb * (D / 16) + ks) * 64 + lane]);
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int j = 4 * ks + 2 * c.lh;
+    const float4 a = qc[j ^ sw];
+    const float4 b = qc[(j + 1) ^ sw];
+    float f[8];
+    f[0] = a.x * sl2e; f[1] = a.y * sl2e; f[2] = a.z * sl2e; f[3] = a.w * sl2e;
+    f[4] = b.x * sl2e; f[5] = b.y * sl2e; f[6] = b.z * sl2e; f[7] = b.w * sl2e;
+    qreg[ks] = to_bf16x8(f);
+  }
 }
 
 // Operand indices (16-byte units) within a staged tile.
@@ -1160,32 +1169,54 @@ __device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
   }
 }
 
-// Stores this wave's dims of its column: the normalised output (one split)
-// or the split's partial.  Partials: acc [tile][S][128 columns][D] as
-// binary16, each lane's D / 4 values scaled by 2^-e so that the largest finite
-// one lies in [0.5, 1) (rounding adds at most 2^-12 of it); records
-// (m, l, e of (half kh, lane half h) at 2 + 2 kh + h) [tile][128 columns][S][6].
+// Stores the workgroup's 128 columns: the normalised output (one split) or
+// the split's partial.  Partials: acc [tile][S][128 columns][D] as binary16,
+// each lane's D / 4 values scaled by 2^-e so that the largest finite one lies
+// in [0.5, 1) (rounding adds at most 2^-12 of it); records (m, l, e of (half
+// kh, lane half h) at 2 + 2 kh + h) [tile][128 columns][S][6].
+//
+// A lane holds 4-value pieces of its column spread over the column's dims, so
+// the values go through LDS first: each wave writes its pieces into a
+// [128 columns][D] staging array (the K / V buffers, free by now) whose
+// 16-byte granules are permuted within each column row (granule k of column
+// col at position k ^ (col mod granules per row), which spreads the 32
+// columns of one write over the LDS banks), and after a barrier every thread
+// stores whole granules, so each wave instruction writes 1 KiB of
+// consecutive bytes.  Every thread of the block calls this (it holds
+// barriers); lanes of columns past the chunk's end store nothing.
 template <int D>
 __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, int kh,
                                                float* __restrict__ out, void* __restrict__ part,
                                                float* __restrict__ part_ml,
                                                const v16f (&acc)[D / 64], float m_ref, float l_tot,
-                                               int R, int Hq, int Hkv, int m_tiles, int S) {
-  if (!c.valid) return;
+                                               int Hq, int S, unsigned char* __restrict__ stage) {
+  constexpr int NT = kBf16Threads;
+  const int col = c.m - t.m_base;  // 0 .. 127
+  __syncthreads();                 // every wave is done with the K / V buffers
   if (S == 1) {
-    float* op = out + (((size_t)t.row0 + c.m / t.G) * Hq + t.g * t.G + c.m % t.G) * D + kh * (D / 2);
+    // f32 granules of 4 dims, D / 4 per column
+    constexpr int GR = D / 4;
+    float4* st = reinterpret_cast<float4*>(stage);
     const float sc = 1.f / l_tot;
     // lane holds dims 32 db + 8 a + 4 h + 0..3 of this wave's half
 #pragma unroll
     for (int db = 0; db < D / 64; ++db)
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<float4*>(op + 32 * db + 8 * a + 4 * c.lh) =
+      for (int a = 0; a < 4; ++a) {
+        const int k = kh * (D / 8) + 8 * db + 2 * a + c.lh;
+        st[col * GR + (k ^ (col & (GR - 1)))] =
             make_float4(acc[db][4 * a] * sc, acc[db][4 * a + 1] * sc, acc[db][4 * a + 2] * sc,
                         acc[db][4 * a + 3] * sc);
+      }
+    __syncthreads();
+    for (int gi = t.tid; gi < kMTile * GR; gi += NT) {
+      const int cc = gi / GR, k = gi - cc * GR, m = t.m_base + cc;
+      if (m >= t.M_total) continue;
+      float* op = out + (((size_t)t.row0 + m / t.G) * Hq + t.g * t.G + m % t.G) * D;
+      reinterpret_cast<float4*>(op)[k] = st[cc * GR + (k ^ (cc & (GR - 1)))];
+    }
     return;
   }
-  const int col = c.m - t.m_base;
   float amax = 0.f;
 #pragma unroll
   for (int db = 0; db < D / 64; ++db)
@@ -1197,8 +1228,10 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, i
   int e = 0;
   if (amax > 0.f) (void)frexpf(amax, &e);
   const float sc = ldexpf(1.f, -e);
-  _Float16* pp = reinterpret_cast<_Float16*>(part) + (((size_t)t.slot + t.split) * kMTile + col) * D +
-                 kh * (D / 2);
+  // binary16 granules of 8 dims, D / 8 per column; a lane's 4 values are
+  // half a granule
+  constexpr int GR = D / 8;
+  half4* st = reinterpret_cast<half4*>(stage);
 #pragma unroll
   for (int db = 0; db < D / 64; ++db)
 #pragma unroll
@@ -1206,14 +1239,26 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, i
       half4 h;
 #pragma unroll
       for (int k = 0; k < 4; ++k) h[k] = (_Float16)(acc[db][4 * a + k] * sc);
-      *reinterpret_cast<half4*>(pp + 32 * db + 8 * a + 4 * c.lh) = h;
+      const int k = kh * (D / 16) + 4 * db + a;
+      st[2 * (col * GR + (k ^ (col & (GR - 1)))) + c.lh] = h;
     }
-  float* ml = part_ml + ((size_t)t.slot * kMTile + (size_t)col * S + t.split) * 6;
-  if (kh == 0 && c.lh == 0) {
-    ml[0] = m_ref;
-    ml[1] = l_tot;
+  if (c.valid) {
+    float* ml = part_ml + ((size_t)t.slot * kMTile + (size_t)col * S + t.split) * 6;
+    if (kh == 0 && c.lh == 0) {
+      ml[0] = m_ref;
+      ml[1] = l_tot;
+    }
+    ml[2 + 2 * kh + c.lh] = (float)e;
   }
-  ml[2 + 2 * kh + c.lh] = (float)e;
+  __syncthreads();
+  const uint4* sg = reinterpret_cast<const uint4*>(stage);
+  uint4* pp = reinterpret_cast<uint4*>(reinterpret_cast<_Float16*>(part) +
+                                       ((size_t)t.slot + t.split) * kMTile * D);
+  for (int gi = t.tid; gi < kMTile * GR; gi += NT) {
+    const int cc = gi / GR, k = gi - cc * GR;
+    if (t.m_base + cc >= t.M_total) continue;
+    pp[gi] = sg[cc * GR + (k ^ (cc & (GR - 1)))];
+  }
 }
 
 template <int D>
@@ -1236,7 +1281,7 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
 
   Tiling t;
   if (!make_tiling(ca, Hq, Hkv, t)) return;
-  const int start = t.start, R = t.R, m_tiles = t.m_tiles, S = t.S;
+  const int start = t.start, R = t.R, S = t.S;
   const int kh = t.w >> 2, partner = t.w ^ 4;
   const ColB c = col_b(t, t.w & 3, start);
   const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;  // elements
@@ -1251,11 +1296,14 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
   for (int db = 0; db < D / 64; ++db)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;  // also the result of an empty split
-  // Q staging in the V buffers, which hold nothing until step 0
-  uint4* const q_lds = reinterpret_cast<uint4*>(vb0);
+  // Q (f32) is staged behind K(0): kb1 onwards, up to the end of the
+  // exchange buffers (512 D bytes), which hold nothing until every wave has
+  // taken its operands
+  unsigned char* const q_lds = kb1;
+  static_assert(kMTile * D * 4 <= 3 * TB + 2 * 16384, "Q staging fits behind K(0)");
   if (n > 0) {
     load_tile<TB, NT>(ksrc, t.kt0, kb0, t.w, t.lane);
-    load_q_half<D>(t, c, kh, t.w & 3, q, R, Hq, sl2e, qreg, q_lds);
+    dma_q<D>(t, q, Hq, q_lds);
   }
   // per-pass exchange area (floats) in the exchange buffer that holds no
   // weights at that moment: [wave][slot][lane]
@@ -1271,8 +1319,9 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
   if (n > 0) {
     bool ovf = false;
     wait_vmem();
-    __syncthreads();  // K(0) and both Q halves are in LDS
-    take_q_half<D>(kh, t.w & 3, t.lane, qreg, q_lds);
+    __syncthreads();  // K(0) and Q are in LDS
+    take_q<D>(c, t.w & 3, sl2e, reinterpret_cast<const float4*>(q_lds), qreg);
+    __syncthreads();  // every wave holds its Q: kb1 and the exchange buffers are free
     if (n > 1) load_tile<TB, NT>(ksrc, t.kt0 + 1, kb1, t.w, t.lane);
     // scores of the first tile (no softmax to overlap with yet)
     qk_tile_b<D>(reinterpret_cast<const uint4*>(kb0), qreg, sa, kh, c);
@@ -1422,7 +1471,7 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
     halves(l_tot, lo, hi);
     l_tot = lo + hi;
   }
-  store_result_b<D>(t, c, kh, out, part, part_ml, acc, m_ref, l_tot, R, Hq, Hkv, m_tiles, S);
+  store_result_b<D>(t, c, kh, out, part, part_ml, acc, m_ref, l_tot, Hq, S, lds);
 }
 
 // Sequential prefill (one K+V stage) for shapes whose four tiles do not fit
