@@ -1362,18 +1362,18 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
         pin(m_use);
       } else {
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
+        for (int s2 = 0; s2 < 2; ++s2)
           po[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(1 - P, partner, s2, t.lane)]);
-          pw[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(1 - P, t.w, s2, t.lane)]);
-        }
         if (kt * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(cur, kt * kNTile + 32 * kh, c);
       }
       fused_step_b<D, FIRST>(reinterpret_cast<const uint4*>(k_use),
                              reinterpret_cast<const uint4*>(v_use), qreg, cur, nxt, pw, po, pc,
                              acc, c, kh, m_use, m_ref, m_all, l_run, ovf);
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+      for (int s2 = 0; s2 < 2; ++s2) {
         xp[xp_slot(P, t.w, s2, t.lane)] = __builtin_bit_cast(uint4, pc[s2]);
+        pw[s2] = pc[s2];  // this wave's own weights stay in registers
+      }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -1390,10 +1390,8 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
     wait_vmem();
     __syncthreads();
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int s2 = 0; s2 < 2; ++s2)
       po[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(pl, partner, s2, t.lane)]);
-      pw[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(pl, t.w, s2, t.lane)]);
-    }
     if ((kt + 1) * kNTile > t.kend) {
       zero_v_beyond<D, true, NT>(reinterpret_cast<uint4*>(v_last), kt, t.kend, t.tid);
       __syncthreads();
