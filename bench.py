@@ -646,7 +646,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved_tf / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic.get("prefill_call_bytes_per_launch"), "traffic_unit": "B/launch",
-                     "kernel": "prefill chunk call (prefill_bf16_kernel + its merge kernel), "
+                     "kernel": "prefill chunk call (prefill_mtile_kernel<256, false> + its merge kernel), "
                                "average over the 22 chunks",
                      "algorithmic_flops_per_step": flops, "causal_pairs": pairs,
                      "avg_launch_ms": round(pre_kernel_ms / len(w.chunks), 5)},

@@ -623,301 +623,7 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
 }
 
 // ============================================================================
-// int8-K caches: the pipelined 4-wave kernel with integer scores.
-//
-// K tiles hold int8 codes (64 D bytes: vector (dim group c, key) at c 64 +
-// key, 16 codes each) followed in LDS by the tile's 64 row scales (staged by
-// 16 lanes of wave 0); V tiles are bf16.  Q is quantised per (row, head)
-// column as K is (amax over the column's D values, shared by the four lanes
-// that hold them), its codes stationary in registers.  S^T = K . Q^T on
-// v_mfma_i32_16x16x64_i8: A = 16 codes of key 16 kb + l % 16, dims 64 ks +
-// 16 (l / 16) ..; B = 16 codes of the lane's column at the same dims; lane l
-// gets keys 16 kb + 4 (l / 16) + 0..3.  The integer scores stay in the score
-// registers until the softmax of their tile turns them into
-// (float) dot * (s_q * scale * log2 e) * s_k.  A tile's key scales are read
-// from LDS while the tile is the next one (its buffer is refilled before its
-// softmax runs) and carried in registers with its scores.  Partials are f32.
-// ============================================================================
-template <int D>
-struct I8Cfg {
-  static constexpr int KTB = 64 * D;             // K tile: int8 codes
-  static constexpr int KTB_LDS = KTB + 256;      // + the tile's 64 scales
-  static constexpr int VTB = 64 * D * 2;         // V tile: bf16
-  static constexpr int NKS = D / 64;             // score k-steps
-  static constexpr int NDB = D / 16;
-};
-
-typedef __attribute__((ext_vector_type(4))) int i32x4;
-
-// Codes and scale of this lane's two columns: lane (lr, lg) holds dims
-// 64 ks + 16 lg .. + 15; sq = s_q * scale * log2 e.
-template <int D>
-__device__ __forceinline__ void load_q_i8(const Tiling& t, const float* __restrict__ q, int Hq,
-                                          float sl2e, i32x4 (&qc)[2][D / 64], float (&sq)[2]) {
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int m = t.m_col[mb];
-    const bool ok = t.valid_col[mb];
-    const float* qp = q + (((size_t)t.row0 + (ok ? m / t.G : 0)) * Hq + t.g * t.G + (ok ? m % t.G : 0)) * D +
-                      16 * t.lg;
-    float4 x[D / 64][4];
-    AbsMax am;
-#pragma unroll
-    for (int ks = 0; ks < D / 64; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[ks][e] = ok ? *reinterpret_cast<const float4*>(qp + 64 * ks + 4 * e)
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
-        am.add(x[ks][e].x); am.add(x[ks][e].y); am.add(x[ks][e].z); am.add(x[ks][e].w);
-      }
-    float mx = am.m, nf = am.nan ? 1.f : 0.f;
-    mx = fmaxf(mx, xor_shfl(mx, 16));
-    mx = fmaxf(mx, xor_shfl(mx, 32));
-    nf = fmaxf(nf, xor_shfl(nf, 16));
-    nf = fmaxf(nf, xor_shfl(nf, 32));
-    AbsMax col;
-    col.m = mx;
-    col.nan = nf != 0.f;
-    const float sc = col.scale();
-#pragma unroll
-    for (int ks = 0; ks < D / 64; ++ks)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qc[mb][ks][e] = (int)pack_codes4(x[ks][e].x, x[ks][e].y, x[ks][e].z, x[ks][e].w, sc);
-    sq[mb] = sc * sl2e;
-  }
-}
-
-// This lane's key scales of a staged K tile: keys 16 kb + 4 lg + 0..3.
-template <int D>
-__device__ __forceinline__ void tile_scales(const unsigned char* k_lds, int lg, float4 (&sk)[4]) {
-  const float4* p = reinterpret_cast<const float4*>(k_lds + I8Cfg<D>::KTB);
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) sk[kb] = p[4 * kb + lg];
-}
-
-// Integer scores of one staged K tile (into the score registers, as bits).
-template <int D>
-__device__ __forceinline__ void qk_tile_i8(const uint4* __restrict__ k_lds,
-                                           const i32x4 (&qc)[2][D / 64], v4f (&sacc)[4][2], int lr,
-                                           int lg) {
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) sacc[kb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < D / 64; ++ks)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const i32x4 a = __builtin_bit_cast(i32x4, k_lds[(4 * ks + lg) * 64 + 16 * kb + lr]);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        sacc[kb][mb] = __builtin_bit_cast(
-            v4f, __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qc[mb][ks],
-                                                       __builtin_bit_cast(i32x4, sacc[kb][mb]), 0, 0, 0));
-    }
-}
-
-// As qk_next_softmax_cur, with integer scores: the next tile's MFMAs
-// interleaved with the current tile's softmax, whose phases 0 and 1 first
-// scale the integer scores (sk_cur: the current tile's key scales); the next
-// tile's key scales are read from its LDS buffer into sk_nxt.
-template <int D>
-__device__ __forceinline__ void qk_next_softmax_cur_i8(
-    const Tiling& t, const unsigned char* __restrict__ k_next_lds, const i32x4 (&qc)[2][D / 64],
-    const float (&sq)[2], v4f (&nxt)[4][2], v4f (&cur)[4][2], const float4 (&sk_cur)[4],
-    float4 (&sk_nxt)[4], int kt, int start, float (&m_run)[2], float (&l_run)[2],
-    float (&alpha)[2]) {
-  constexpr int NKS = D / 64;
-  const int lr = t.lr, lg = t.lg;
-  const uint4* k_lds = reinterpret_cast<const uint4*>(k_next_lds);
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) nxt[kb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
-  const bool diag = kt * kNTile + kNTile - 1 > start + t.row_lo;
-  float lmax[2] = {-INFINITY, -INFINITY};
-  float ls[2] = {0.f, 0.f};
-  float m_use[2];
-  uint4 kbuf[2][4];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) kbuf[0][kb] = k_lds[(4 * 0 + lg) * 64 + 16 * kb + lr];
-  tile_scales<D>(k_next_lds, lg, sk_nxt);
-
-  auto phase = [&](int ph) {
-    if (ph == 0 || ph == 1) {
-      const int mb = ph;
-      const int lim = start + t.row_col[mb];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const float skv[4] = {sk_cur[kb].x, sk_cur[kb].y, sk_cur[kb].z, sk_cur[kb].w};
-        // the four integer scores, read as one vector before any is
-        // overwritten (a bit cast of one element of the float vector does
-        // not reliably read that element)
-        const i32x4 ci = __builtin_bit_cast(i32x4, cur[kb][mb]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          // integer score -> log2 domain: dot * (s_q scale log2 e) * s_k
-          float sv = (float)ci[i] * (sq[mb] * skv[i]);
-          if (diag) {
-            const int key = kt * kNTile + 16 * kb + 4 * lg + i;
-            if (key > lim || !t.valid_col[mb]) sv = -INFINITY;
-          }
-          cur[kb][mb][i] = sv;
-          lmax[mb] = fmaxf(lmax[mb], sv);
-        }
-      }
-    } else if (ph == 2) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        lmax[mb] = fmaxf(lmax[mb], xor_shfl(lmax[mb], 16));
-        lmax[mb] = fmaxf(lmax[mb], xor_shfl(lmax[mb], 32));
-      }
-    } else if (ph == 3) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        alpha[mb] = 1.f;
-        if (lmax[mb] > m_run[mb] + kRescaleSlack) {
-          alpha[mb] = fast_exp2(m_run[mb] - lmax[mb]);  // 0 when m_run is -inf
-          m_run[mb] = lmax[mb];
-          l_run[mb] *= alpha[mb];
-        }
-        m_use[mb] = m_run[mb] == -INFINITY ? 0.f : m_run[mb];
-      }
-    } else {
-      const int kb = ph - 4;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pv = fast_exp2(cur[kb][mb][i] - m_use[mb]);
-          cur[kb][mb][i] = pv;
-          ls[mb] += pv;
-        }
-    }
-  };
-
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    if (ks + 1 < NKS) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        kbuf[(ks + 1) & 1][kb] = k_lds[(4 * (ks + 1) + lg) * 64 + 16 * kb + lr];
-    }
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const i32x4 a = __builtin_bit_cast(i32x4, kbuf[ks & 1][kb]);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        nxt[kb][mb] = __builtin_bit_cast(
-            v4f, __builtin_amdgcn_mfma_i32_16x16x64_i8(a, qc[mb][ks],
-                                                       __builtin_bit_cast(i32x4, nxt[kb][mb]), 0, 0, 0));
-    }
-    // softmax phases assigned to this chunk (all 8 spread over NKS chunks)
-#pragma unroll
-    for (int ph = 0; ph < 8; ++ph)
-      if (ph * NKS / 8 == ks) phase(ph);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) l_run[mb] += ls[mb];
-}
-
-// Copies the row scales of K tile `tile` (256 bytes) behind its codes in LDS:
-// lanes 0..15 of wave 0, 16 bytes each.
-template <int D>
-__device__ __forceinline__ void load_tile_scales(const TileSrc& src, int tile, unsigned char* dst,
-                                                 int w, int lane) {
-  if (w == 0 && lane < 16) dma16(src.rsrc, dst + I8Cfg<D>::KTB, tile * 256 + lane * 16);
-}
-
-template <int D>
-__global__ __launch_bounds__(256) void prefill_i8_kernel(
-    const float* __restrict__ q, const void* __restrict__ k_cache,
-    const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
-    float* __restrict__ part_ml, const float* __restrict__ k_scales, int Hq, int Hkv, int C,
-    const ChunkArg ca, float sl2e) {
-  using Cfg = I8Cfg<D>;
-  constexpr int NDB = Cfg::NDB, KTB = Cfg::KTB, VTB = Cfg::VTB;
-  __shared__ __attribute__((aligned(16))) unsigned char kb0[Cfg::KTB_LDS];
-  __shared__ __attribute__((aligned(16))) unsigned char kb1[Cfg::KTB_LDS];
-  __shared__ __attribute__((aligned(16))) unsigned char vb0[VTB];
-  __shared__ __attribute__((aligned(16))) unsigned char vb1[VTB];
-
-  Tiling t;
-  if (!make_tiling(ca, Hq, Hkv, t)) return;
-  const int start = t.start, R = t.R, m_tiles = t.m_tiles, S = t.S;
-  const size_t slab_i = (size_t)t.b * Hkv + t.g;
-  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab_i * C * D, (size_t)C * D);
-  const TileSrc ssrc = tile_src(k_scales + slab_i * C, (size_t)C * 4);
-  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab_i * C * D * 2, (size_t)C * D * 2);
-  const int n = t.kt1 - t.kt0;
-
-  i32x4 qc[2][D / 64];
-  float sq[2];
-  v4f acc_o[NDB][2];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) acc_o[db][mb] = v4f{0.f, 0.f, 0.f, 0.f};
-  float m_run[2] = {-INFINITY, -INFINITY};
-  float l_run[2] = {0.f, 0.f};
-  v4f sa[4][2], sb[4][2];
-  float4 ska[4], skb[4];
-
-  if (n > 0) {
-    load_tile<KTB>(ksrc, t.kt0, kb0, t.w, t.lane);
-    load_tile_scales<D>(ssrc, t.kt0, kb0, t.w, t.lane);
-    load_q_i8<D>(t, q, Hq, sl2e, qc, sq);
-    wait_vmem();
-    __syncthreads();
-    load_tile<VTB>(vsrc, t.kt0, vb0, t.w, t.lane);
-    if (n > 1) {
-      load_tile<KTB>(ksrc, t.kt0 + 1, kb1, t.w, t.lane);
-      load_tile_scales<D>(ssrc, t.kt0 + 1, kb1, t.w, t.lane);
-    }
-    qk_tile_i8<D>(reinterpret_cast<const uint4*>(kb0), qc, sa, t.lr, t.lg);
-    tile_scales<D>(kb0, t.lg, ska);
-  }
-
-  // step i: V(i) in vb[i&1], K(i+1) in kb[(i+1)&1], integer scores of tile i
-  // in cur and its key scales in sk_cur
-  auto step = [&](auto par, int i, v4f (&cur)[4][2], v4f (&nxt)[4][2], float4 (&sk_cur)[4],
-                  float4 (&sk_nxt)[4]) {
-    constexpr int P = decltype(par)::value;
-    unsigned char* k_next = P == 0 ? kb1 : kb0;   // holds K(i+1)
-    unsigned char* k_free = P == 0 ? kb0 : kb1;   // held K(i): free for K(i+2)
-    unsigned char* v_cur = P == 0 ? vb0 : vb1;    // holds V(i)
-    unsigned char* v_free = P == 0 ? vb1 : vb0;   // held V(i-1): free for V(i+1)
-    const int kt = t.kt0 + i;
-    wait_vmem();
-    __syncthreads();  // V(i), K(i+1) landed; every wave is done with step i-1
-    if (i + 2 < n) {
-      load_tile<KTB>(ksrc, kt + 2, k_free, t.w, t.lane);
-      load_tile_scales<D>(ssrc, kt + 2, k_free, t.w, t.lane);
-    }
-    if (i + 1 < n) load_tile<VTB>(vsrc, kt + 1, v_free, t.w, t.lane);
-    if ((kt + 1) * kNTile > t.kend) {
-      zero_v_beyond<D, true>(reinterpret_cast<uint4*>(v_cur), kt, t.kend, t.tid);
-      __syncthreads();
-    }
-    // (the last step computes one spare tile of scores from a stale buffer,
-    // which is never used)
-    float alpha[2];
-    qk_next_softmax_cur_i8<D>(t, k_next, qc, sq, nxt, cur, sk_cur, sk_nxt, kt, start, m_run, l_run,
-                              alpha);
-    rescale_acc<NDB>(alpha, acc_o);
-    pv_tile<D, true>(reinterpret_cast<const uint4*>(v_cur), cur, acc_o, t.lr, t.lg);
-  };
-  for (int i = 0; i < n; i += 2) {
-    step(std::integral_constant<int, 0>(), i, sa, sb, ska, skb);
-    if (i + 1 < n) step(std::integral_constant<int, 1>(), i + 1, sb, sa, skb, ska);
-  }
-  store_result<D>(t, out, part, part_ml, acc_o, m_run, l_run, R, Hq, Hkv, m_tiles, S);
-}
-
-// ============================================================================
-// bf16 caches: 32x32x16 MFMA (v_mfma_f32_32x32x16_bf16), 8 waves.
+// bf16 and int8-K caches: 32x32 MFMAs, 8 waves (prefill_mtile_kernel).
 //
 // Work split.  Wave w takes column block cb = w & 3 (M columns 32 cb ..
 // 32 cb + 31 of the tile) and half kh = w >> 2: it scores keys 32 kh ..
@@ -942,6 +648,19 @@ __global__ __launch_bounds__(256) void prefill_i8_kernel(
 // vector pipe between them, the softmax of tile i.  K(i+2) and V(i) stream
 // into LDS meanwhile; K, V and the weight exchange each have two buffers.
 //
+// int8-K caches (I8).  K tiles hold int8 codes (64 D bytes, the K layout with
+// 16 codes per vector) followed in LDS by the tile's 64 row scales (256
+// bytes, staged by 16 lanes of wave 0).  Q is quantised per column as K is
+// (amax over the column's D values: this lane's half and lane l ^ 32's), its
+// codes stationary in registers.  Scores use v_mfma_i32_32x32x32_i8 per
+// 32-dim step: A = the 16 codes of key 32 kh + l % 32 at dims 32 ks + 16 h ..
+// (one 16-byte vector of the K layout, at the same LDS index as a bf16 step's
+// operand), B = the column's 16 codes at those dims; the accumulator layout is
+// the bf16 one.  Half as many score MFMAs (on even chunks of a step), and
+// half the K bytes in LDS reads and DMA.  After a tile's last score MFMA the
+// integer dots become (float) dot * (s_q * scale * log2 e) * s_key, so the
+// softmax and the value product are the bf16 path's.
+//
 // Reference frame.  A column's weights are exp2(s - m_ref), where m_ref is the
 // largest score of the first tile of the range (both halves; a column that
 // sees any key of the range sees that tile's first key).  The frame never
@@ -955,6 +674,38 @@ typedef __attribute__((ext_vector_type(16))) float v16f;
 typedef __attribute__((ext_vector_type(4))) _Float16 half4;
 
 constexpr int kBf16Threads = 512;
+
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(16))) int i32x16;
+
+// Tile sizes and operand types of the 8-wave kernel.
+template <int D, bool I8>
+struct MtCfg {
+  static constexpr int KTB = I8 ? 64 * D : 128 * D;     // K tile bytes in the cache
+  static constexpr int KTB_LDS = I8 ? KTB + 256 : KTB;  // + the tile's 64 key scales
+  static constexpr int VTB = 128 * D;                    // V tile bytes (bf16)
+  static constexpr int NQS = I8 ? D / 32 : D / 16;       // score k-steps
+  using QOp = typename std::conditional<I8, i32x4, bf16x8>::type;
+  // K(0), K(1), V(0), V(1), two 16 KiB weight-exchange buffers; Q staging
+  // (f32, 512 D bytes) from K(1) on may need more
+  static constexpr int LAYOUT = 2 * KTB_LDS + 2 * VTB + 2 * 16384;
+  static constexpr int LDS = LAYOUT > KTB_LDS + 512 * D ? LAYOUT : KTB_LDS + 512 * D;
+};
+
+// Asynchronous copy of K tile kt into LDS: codes (and, I8, the tile's 64
+// scales behind them) or bf16 values.
+template <int D, bool I8>
+__device__ __forceinline__ void load_k(const TileSrc& ksrc, const TileSrc& ssrc, int kt,
+                                       unsigned char* dst, int w, int lane) {
+  constexpr int KTB = MtCfg<D, I8>::KTB, NT = kBf16Threads;
+#pragma unroll
+  for (int i = 0; i < (KTB + NT * 16 - 1) / (NT * 16); ++i) {
+    const int off = (i * NT + w * 64) * 16;
+    if (off < KTB) dma16(ksrc.rsrc, dst + off, kt * KTB + off + lane * 16);
+  }
+  if constexpr (I8)
+    if (w == 0 && lane < 16) dma16(ssrc.rsrc, dst + KTB, kt * 256 + lane * 16);
+}
 
 // Both lane halves' values: lane l receives (x of lane l % 32, x of lane
 // l % 32 + 32), with v_permlane32_swap (no LDS traffic).
@@ -1037,6 +788,42 @@ __device__ __forceinline__ void take_q(const ColB& c, int cb, float sl2e,
   }
 }
 
+// int8 form: the column's symmetric codes (as the append quantises K rows)
+// and sq = s_q * scale * log2 e.  Lane (l % 32, h) holds the 16 codes of dims
+// 32 ks + 16 h .. 32 ks + 16 h + 15 for each k-step; the amax and the NaN flag
+// cover the other half of the column through lane l ^ 32.
+template <int D>
+__device__ __forceinline__ void take_q_i8(const ColB& c, int cb, float sl2e,
+                                          const float4* __restrict__ q_lds, i32x4 (&qc)[D / 32],
+                                          float& sq) {
+  constexpr int GR = D / 4;
+  const int col = 32 * cb + c.lc, sw = col & (GR - 1);
+  const float4* qcol = q_lds + col * GR;
+  AbsMax am;
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 x = qcol[(8 * ks + 4 * c.lh + e) ^ sw];
+      am.add(x.x); am.add(x.y); am.add(x.z); am.add(x.w);
+    }
+  float m = am.m, nf = am.nan ? 1.f : 0.f;
+  m = fmaxf(m, __shfl_xor(m, 32, kWave));
+  nf = fmaxf(nf, __shfl_xor(nf, 32, kWave));
+  AbsMax colm;
+  colm.m = m;
+  colm.nan = nf != 0.f;
+  const float s = colm.scale();
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 x = qcol[(8 * ks + 4 * c.lh + e) ^ sw];
+      qc[ks][e] = (int)pack_codes4(x.x, x.y, x.z, x.w, s);
+    }
+  sq = s * sl2e;
+}
+
 // Operand indices (16-byte units) within a staged tile.
 __device__ __forceinline__ int k_op_b(int ks, int kh, int lc, int lh) {
   return (2 * ks + lh) * 64 + 32 * kh + lc;
@@ -1059,17 +846,47 @@ __device__ __forceinline__ int xp_slot(int par, int w, int s, int lane) {
   return ((par * 8 + w) * 2 + s) * 64 + lane;
 }
 
-// Scores of one tile (this wave's key half), unpipelined.
+// One score k-step: s += K operand . Q operand (integer dots kept as bits).
+template <bool I8, typename QOp>
+__device__ __forceinline__ void score_mfma(v16f& s, uint4 kop, const QOp& qop) {
+  if constexpr (I8)
+    s = __builtin_bit_cast(v16f, __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                                     __builtin_bit_cast(i32x4, kop), qop,
+                                     __builtin_bit_cast(i32x16, s), 0, 0, 0));
+  else
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kop), qop, s, 0, 0, 0);
+}
+
+// int8: integer dots (bits in s) -> log2-domain scores dot * (sq * s_key), for
+// the keys this lane holds (32 kh + 8 a + 4 h + e at register 4 a + e); the
+// key scales follow the codes of the staged tile.
 template <int D>
+__device__ __forceinline__ void scale_scores(v16f& s, const uint4* __restrict__ k_lds, int kh,
+                                             const ColB& c, float sq) {
+  const float4* ks4 = reinterpret_cast<const float4*>(
+      reinterpret_cast<const unsigned char*>(k_lds) + MtCfg<D, true>::KTB);
+  const i32x16 si = __builtin_bit_cast(i32x16, s);
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const float4 k4 = ks4[8 * kh + 2 * a + c.lh];
+    s[4 * a] = (float)si[4 * a] * (sq * k4.x);
+    s[4 * a + 1] = (float)si[4 * a + 1] * (sq * k4.y);
+    s[4 * a + 2] = (float)si[4 * a + 2] * (sq * k4.z);
+    s[4 * a + 3] = (float)si[4 * a + 3] * (sq * k4.w);
+  }
+}
+
+// Scores of one tile (this wave's key half), unpipelined.
+template <int D, bool I8>
 __device__ __forceinline__ void qk_tile_b(const uint4* __restrict__ k_lds,
-                                          const bf16x8 (&qreg)[D / 16], v16f& s, int kh,
-                                          const ColB& c) {
+                                          const typename MtCfg<D, I8>::QOp (&qreg)[MtCfg<D, I8>::NQS],
+                                          v16f& s, int kh, const ColB& c, float sq) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) s[i] = 0.f;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks)
-    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-        __builtin_bit_cast(bf16x8, k_lds[k_op_b(ks, kh, c.lc, c.lh)]), qreg[ks], s, 0, 0, 0);
+  for (int ks = 0; ks < MtCfg<D, I8>::NQS; ++ks)
+    score_mfma<I8>(s, k_lds[k_op_b(ks, kh, c.lc, c.lh)], qreg[ks]);
+  if constexpr (I8) scale_scores<D>(s, k_lds, kh, c, sq);
 }
 
 // Keys past the column's causal limit get -inf (tiles that cross a limit only).
@@ -1099,10 +916,11 @@ __device__ __forceinline__ void pv_chunk_b(int j, uint4 vop, const bf16x8 (&p_ow
 //   phases: 0 max; 1 cross-half max, largest score and frame check;
 //   2..9 exponentials (2 each); 10, 11 bf16 conversion of the weights;
 //   12 running sum.
-template <int D, bool FIRST>
+template <int D, bool FIRST, bool I8>
 __device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
                                              const uint4* __restrict__ v_lds,
-                                             const bf16x8 (&qreg)[D / 16], v16f& cur, v16f& nxt,
+                                             const typename MtCfg<D, I8>::QOp (&qreg)[MtCfg<D, I8>::NQS],
+                                             float sq, v16f& cur, v16f& nxt,
                                              const bf16x8 (&p_prev)[2], const bf16x8 (&p_oth)[2],
                                              bf16x8 (&p_cur)[2], v16f (&acc)[D / 64],
                                              const ColB& c, int kh, float m_use, float m_ref,
@@ -1115,9 +933,10 @@ __device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
   float lmax = -INFINITY, ls = 0.f;
   // operand ring: [slot][0 K, 1 V]
   uint4 ring[DIST + 1][2];
+  // I8: a score k-step covers two chunks (32 dims); it runs on even chunks
   auto issue = [&](int cc) {
     uint4(&r)[2] = ring[cc % (DIST + 1)];
-    r[0] = k_lds[k_op_b(cc, kh, c.lc, c.lh)];
+    if (!I8 || (cc & 1) == 0) r[0] = k_lds[k_op_b(I8 ? cc / 2 : cc, kh, c.lc, c.lh)];
     if (!FIRST) r[1] = v_lds[pv_op_b<D>(cc, kh, c.lc, c.lh)];
   };
   auto phase = [&](int ph) {
@@ -1159,14 +978,14 @@ __device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
   for (int cc = 0; cc < NC; ++cc) {
     if (cc + DIST < NC) issue(cc + DIST);
     const uint4(&r)[2] = ring[cc % (DIST + 1)];
-    nxt = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, r[0]), qreg[cc], nxt,
-                                                  0, 0, 0);
+    if (!I8 || (cc & 1) == 0) score_mfma<I8>(nxt, r[0], qreg[I8 ? cc / 2 : cc]);
     if (!FIRST) pv_chunk_b<D>(cc, r[1], p_prev, p_oth, acc);
 #pragma unroll
     for (int ph = 0; ph < NPH; ++ph)
       if (ph * NC / NPH == cc) phase(ph);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if constexpr (I8) scale_scores<D>(nxt, k_lds, kh, c, sq);
 }
 
 // Stores the workgroup's 128 columns: the normalised output (one split) or
@@ -1177,7 +996,7 @@ __device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
 //
 // A lane holds 4-value pieces of its column spread over the column's dims, so
 // the values go through LDS first: each wave writes its pieces into a
-// [128 columns][D] staging array (the K / V buffers, free by now) whose
+// [128 columns][D] staging array (from the start of the LDS, free by now) whose
 // 16-byte granules are permuted within each column row (granule k of column
 // col at position k ^ (col mod granules per row), which spreads the 32
 // columns of one write over the LDS banks), and after a barrier every thread
@@ -1192,7 +1011,7 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, i
                                                int Hq, int S, unsigned char* __restrict__ stage) {
   constexpr int NT = kBf16Threads;
   const int col = c.m - t.m_base;  // 0 .. 127
-  __syncthreads();                 // every wave is done with the K / V buffers
+  __syncthreads();                 // every wave is done with the tiles and exchanges
   if (S == 1) {
     // f32 granules of 4 dims, D / 4 per column
     constexpr int GR = D / 4;
@@ -1261,35 +1080,42 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, i
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
+template <int D, bool I8>
+__global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, float* __restrict__ out, void* __restrict__ part,
-    float* __restrict__ part_ml, int Hq, int Hkv, int C, const ChunkArg ca, float sl2e) {
-  constexpr int TB = PrefillCfg<D, true>::TILE_BYTES;
+    float* __restrict__ part_ml, const float* __restrict__ k_scales, int Hq, int Hkv, int C,
+    const ChunkArg ca, float sl2e) {
+  using Cfg = MtCfg<D, I8>;
+  constexpr int KTB = Cfg::KTB, KTB_LDS = Cfg::KTB_LDS, VTB = Cfg::VTB;
   constexpr int NT = kBf16Threads;
   // K(0), K(1), V(0), V(1), then two weight-exchange buffers of 16 KiB.  The
   // exchange buffer that holds no weights at that moment also carries the
   // per-pass exchanges (frame, votes, sums), so no other LDS is used:
-  // 160 KiB at D = 256.
-  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * TB + 2 * 16384];
+  // 160 KiB at D = 256 for bf16 caches, 144.25 KiB for int8-K (whose Q
+  // staging is larger than its tiles).
+  __shared__ __attribute__((aligned(16))) unsigned char lds[Cfg::LDS];
   unsigned char* const kb0 = lds;
-  unsigned char* const kb1 = lds + TB;
-  unsigned char* const vb0 = lds + 2 * TB;
-  unsigned char* const vb1 = lds + 3 * TB;
-  uint4* const xp = reinterpret_cast<uint4*>(lds + 4 * TB);
+  unsigned char* const kb1 = lds + KTB_LDS;
+  unsigned char* const vb0 = lds + 2 * KTB_LDS;
+  unsigned char* const vb1 = vb0 + VTB;
+  uint4* const xp = reinterpret_cast<uint4*>(vb1 + VTB);
 
   Tiling t;
   if (!make_tiling(ca, Hq, Hkv, t)) return;
   const int start = t.start, R = t.R, S = t.S;
   const int kh = t.w >> 2, partner = t.w ^ 4;
   const ColB c = col_b(t, t.w & 3, start);
-  const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;  // elements
-  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * 2, (size_t)C * D * 2);
-  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab * 2, (size_t)C * D * 2);
+  const size_t slab_i = (size_t)t.b * Hkv + t.g;
+  const size_t k_slab = (size_t)C * D * (I8 ? 1 : 2);  // bytes
+  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab_i * k_slab, k_slab);
+  const TileSrc ssrc = tile_src(I8 ? k_scales + slab_i * C : nullptr, I8 ? (size_t)C * 4 : 0);
+  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab_i * C * D * 2,
+                                (size_t)C * D * 2);
   const int n = t.kt1 - t.kt0;
 
-  bf16x8 qreg[D / 16];
+  typename Cfg::QOp qreg[Cfg::NQS];
+  float sq = 0.f;  // I8: s_q * scale * log2 e of this lane's column
   v16f acc[D / 64];
   float m_ref = -INFINITY, m_all = -INFINITY, l_run = 0.f, l_tot = 0.f;
 #pragma unroll
@@ -1300,9 +1126,9 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
   // exchange buffers (512 D bytes), which hold nothing until every wave has
   // taken its operands
   unsigned char* const q_lds = kb1;
-  static_assert(kMTile * D * 4 <= 3 * TB + 2 * 16384, "Q staging fits behind K(0)");
+  static_assert(KTB_LDS + kMTile * D * 4 <= Cfg::LDS, "Q staging fits behind K(0)");
   if (n > 0) {
-    load_tile<TB, NT>(ksrc, t.kt0, kb0, t.w, t.lane);
+    load_k<D, I8>(ksrc, ssrc, t.kt0, kb0, t.w, t.lane);
     dma_q<D>(t, q, Hq, q_lds);
   }
   // per-pass exchange area (floats) in the exchange buffer that holds no
@@ -1320,11 +1146,14 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
     bool ovf = false;
     wait_vmem();
     __syncthreads();  // K(0) and Q are in LDS
-    take_q<D>(c, t.w & 3, sl2e, reinterpret_cast<const float4*>(q_lds), qreg);
+    if constexpr (I8)
+      take_q_i8<D>(c, t.w & 3, sl2e, reinterpret_cast<const float4*>(q_lds), qreg, sq);
+    else
+      take_q<D>(c, t.w & 3, sl2e, reinterpret_cast<const float4*>(q_lds), qreg);
     __syncthreads();  // every wave holds its Q: kb1 and the exchange buffers are free
-    if (n > 1) load_tile<TB, NT>(ksrc, t.kt0 + 1, kb1, t.w, t.lane);
+    if (n > 1) load_k<D, I8>(ksrc, ssrc, t.kt0 + 1, kb1, t.w, t.lane);
     // scores of the first tile (no softmax to overlap with yet)
-    qk_tile_b<D>(reinterpret_cast<const uint4*>(kb0), qreg, sa, kh, c);
+    qk_tile_b<D, I8>(reinterpret_cast<const uint4*>(kb0), qreg, sa, kh, c, sq);
     if (t.kt0 * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(sa, t.kt0 * kNTile + 32 * kh, c);
     {
       // frame: the first tile's largest score over both key halves; this
@@ -1354,8 +1183,8 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
       wait_vmem();
       __syncthreads();
       wait_lgkm();
-      if (i + 2 < n) load_tile<TB, NT>(ksrc, kt + 2, k_load, t.w, t.lane);
-      load_tile<TB, NT>(vsrc, kt, v_load, t.w, t.lane);
+      if (i + 2 < n) load_k<D, I8>(ksrc, ssrc, kt + 2, k_load, t.w, t.lane);
+      load_tile<VTB, NT>(vsrc, kt, v_load, t.w, t.lane);
       if (FIRST) {
         m_ref = fmaxf(m_ref, *xf(1, partner, 0));
         m_use = m_ref == -INFINITY ? 0.f : m_ref;
@@ -1366,9 +1195,9 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
           po[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(1 - P, partner, s2, t.lane)]);
         if (kt * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(cur, kt * kNTile + 32 * kh, c);
       }
-      fused_step_b<D, FIRST>(reinterpret_cast<const uint4*>(k_use),
-                             reinterpret_cast<const uint4*>(v_use), qreg, cur, nxt, pw, po, pc,
-                             acc, c, kh, m_use, m_ref, m_all, l_run, ovf);
+      fused_step_b<D, FIRST, I8>(reinterpret_cast<const uint4*>(k_use),
+                                 reinterpret_cast<const uint4*>(v_use), qreg, sq, cur, nxt, pw, po,
+                                 pc, acc, c, kh, m_use, m_ref, m_all, l_run, ovf);
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         xp[xp_slot(P, t.w, s2, t.lane)] = __builtin_bit_cast(uint4, pc[s2]);
@@ -1426,8 +1255,8 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
     for (int i = 0; i < n; ++i) {
       const int kt = t.kt0 + i;
       __syncthreads();  // every wave is done with the previous tile and weights
-      load_tile<TB, NT>(ksrc, kt, kb0, t.w, t.lane);
-      load_tile<TB, NT>(vsrc, kt, vb0, t.w, t.lane);
+      load_k<D, I8>(ksrc, ssrc, kt, kb0, t.w, t.lane);
+      load_tile<VTB, NT>(vsrc, kt, vb0, t.w, t.lane);
       wait_vmem();
       __syncthreads();
       if ((kt + 1) * kNTile > t.kend) {
@@ -1435,7 +1264,7 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_bf16_kernel(
         __syncthreads();
       }
       v16f s;
-      qk_tile_b<D>(kl, qreg, s, kh, c);
+      qk_tile_b<D, I8>(kl, qreg, s, kh, c, sq);
       if (kt * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(s, kt * kNTile + 32 * kh, c);
       float ls = 0.f;
 #pragma unroll
@@ -1724,7 +1553,7 @@ int max_splits(long long units) {
 // this session's key tiles.
 int choose_splits(const Shape& s, long long units, int nkt) {
   const double scale_d = s.head_dim / 256.0;
-  const double tile_ns = (s.kv_dtype == kBF16 ? 1300.0 : s.kv_dtype == kI8K ? 2000.0 : 9000.0) * scale_d;
+  const double tile_ns = (s.kv_dtype == kF32 ? 9000.0 : 1300.0) * scale_d;
   const double wg_ns = 3000.0, merge_ns = 4000.0, part_ns = 26.0 * scale_d;
   const int smax = max_splits(units);
   int best = 1;
@@ -1753,9 +1582,9 @@ template <int D, int MODE>
 hipError_t launch_chunks(const Shape& s, const ChunkLaunch* L, int nl, long long total_slots,
                          const float* q, const void* kc, const void* vc, float* out, float scale,
                          void* ws, hipStream_t st) {
-  constexpr bool BF16 = MODE == kBF16;  // binary16 partials (the 8-wave kernel)
+  constexpr bool BF16 = MODE != kF32;  // binary16 partials (the 8-wave kernel)
   using Cfg = PrefillCfg<D, false>;
-  // partials: binary16 accumulators for bf16 caches, f32 otherwise, one
+  // partials: binary16 accumulators for bf16 and int8-K caches, f32 otherwise, one
   // 128-column slot per (session, KV head, m-tile, split); then the
   // per-(column, split) records
   float* part = reinterpret_cast<float*>(ws);
@@ -1768,13 +1597,13 @@ hipError_t launch_chunks(const Shape& s, const ChunkLaunch* L, int nl, long long
     // padded to whole rounds of the 8 XCDs (see make_tiling)
     const dim3 grid(8 * ((items + 7) / 8));
     if constexpr (MODE == kBF16)
-      hipLaunchKernelGGL((prefill_bf16_kernel<D>), grid, dim3(kBf16Threads), 0, st, q, kc, vc, out,
-                         part, part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, ca,
-                         scale * kLog2e);
+      hipLaunchKernelGGL((prefill_mtile_kernel<D, false>), grid, dim3(kBf16Threads), 0, st, q, kc,
+                         vc, out, part, part_ml, nullptr, s.num_q_heads, s.num_kv_heads,
+                         s.capacity, ca, scale * kLog2e);
     else if constexpr (MODE == kI8K)
-      hipLaunchKernelGGL((prefill_i8_kernel<D>), grid, dim3(256), 0, st, q, kc, vc, out, part,
-                         part_ml, k_scale_array(s, kc), s.num_q_heads, s.num_kv_heads, s.capacity,
-                         ca, scale * kLog2e);
+      hipLaunchKernelGGL((prefill_mtile_kernel<D, true>), grid, dim3(kBf16Threads), 0, st, q, kc,
+                         vc, out, part, part_ml, k_scale_array(s, kc), s.num_q_heads,
+                         s.num_kv_heads, s.capacity, ca, scale * kLog2e);
     else if constexpr (Cfg::PIPE)
       hipLaunchKernelGGL((prefill_pipe_kernel<D, false>), grid, dim3(256), 0, st, q, kc, vc, out,
                          part, part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, ca,
@@ -1865,10 +1694,11 @@ hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const 
 }  // namespace
 
 // Workspace bytes per (column, split): binary16 accumulators and a 6-float
-// record for bf16 caches, f32 accumulators and an (m, l) pair otherwise.
+// record for bf16 and int8-K caches, f32 accumulators and an (m, l) pair
+// otherwise.
 static size_t partial_bytes(const Shape& s) {
-  return s.kv_dtype == kBF16 ? (size_t)s.head_dim * 2 + 6 * sizeof(float)
-                         : (size_t)(s.head_dim + 2) * sizeof(float);
+  return s.kv_dtype != kF32 ? (size_t)s.head_dim * 2 + 6 * sizeof(float)
+                            : (size_t)(s.head_dim + 2) * sizeof(float);
 }
 
 // Chunks of at most kRowsMaxRows rows on bf16 caches may go to the streaming
