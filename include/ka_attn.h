@@ -360,9 +360,10 @@ ka_status ka_attn_cache_resize(const ka_attn_shape* src, const void* src_k, cons
  * the int8 dot is not taken on faith; a canary checks the instruction and its
  * emulation against a known answer at first use, and the library fails
  * loudly when they are not sane).  On the current device, one wave
- * multiplies a fixed 16 x 64 by 64 x 16 int8 pattern with the int8 MFMA
- * instruction the int8-K kernels use, in their lane layout, and with plain
- * integer arithmetic; both must equal the exact product.  It runs once per
+ * multiplies fixed int8 patterns (16 x 64 by 64 x 16, and 32 x 32 by
+ * 32 x 32) with each int8 MFMA instruction the int8-K kernels use, in their
+ * lane layouts, and with plain integer arithmetic; all must equal the exact
+ * products.  It runs once per
  * device (synchronising the device that once; call it before capturing a
  * graph) and the outcome is kept.  Every int8-K attention call runs it first.
  * Returns KA_OK, or KA_ERR_UNSUPPORTED (int8-K attention calls then fail the

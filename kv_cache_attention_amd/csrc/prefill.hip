@@ -41,10 +41,11 @@ constexpr int kMTile = 128;
 constexpr int kNTile = 64;
 constexpr int kMaxSplits = 64;
 constexpr float kRescaleSlack = 8.f;  // log2 units: weights stay below 256
-constexpr float kFrameSlack = 32.f;   // log2 units (bf16 path, see prefill_bf16_kernel)
+constexpr float kFrameSlack = 32.f;   // log2 units (8-wave kernel, see prefill_mtile_kernel)
 
 typedef __attribute__((ext_vector_type(4))) float v4f;
 
+// Tiles of f32 (BF16 false) or bf16 values: 16-byte vectors of E elements.
 template <int D, bool BF16>
 struct PrefillCfg {
   static constexpr int E = Elem<BF16>::E;
@@ -52,11 +53,10 @@ struct PrefillCfg {
   static constexpr int VVEC = kNTile / E * D;            // 16-byte vectors per V tile
   static constexpr int TILE_BYTES = KVEC * 16;           // same for V
   static constexpr int NDB = D / 16;                     // 16-dim output blocks
-  static constexpr int NQ = BF16 ? D / 32 : D / 16;      // Q^T operand registers per column block
-  // Pipelined form: K and V tiles double-buffered separately (4 tiles) when
-  // that fits the 160 KiB of LDS; otherwise one K+V stage.
+  // f32 kernels: K and V tiles double-buffered separately (4 tiles, the
+  // pipelined kernel) when that fits the 160 KiB of LDS; otherwise one K+V
+  // stage (the sequential kernel).
   static constexpr bool PIPE = 4 * TILE_BYTES <= 160 * 1024;
-  using QReg = typename std::conditional<BF16, bf16x8, v4f>::type;
 };
 
 // A cache slab as a buffer resource (see buffer_rsrc).
@@ -164,75 +164,50 @@ __device__ __forceinline__ bool make_tiling(const ChunkArg& ca, int Hq, int Hkv,
   return true;
 }
 
+// The 4-wave kernels below (f32 caches, v_mfma_f32_16x16x4f32): wave w owns
+// columns 32 w .. 32 w + 31 of the M-tile as two 16-column blocks mb; lane
+// (lr, lg) = (l % 16, l / 16).
+
 // Stationary Q^T operand: this lane's slice of its two columns.
-template <int D, bool BF16>
+template <int D>
 __device__ __forceinline__ void load_q(const Tiling& t, const float* __restrict__ q, int R, int Hq,
-                                       typename PrefillCfg<D, BF16>::QReg (&qreg)[2][PrefillCfg<D, BF16>::NQ]) {
-  constexpr int NQ = PrefillCfg<D, BF16>::NQ;
+                                       v4f (&qreg)[2][D / 16]) {
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     const int m = t.m_col[mb];
     const float* qp = q + (((size_t)t.row0 + m / t.G) * Hq + t.g * t.G + m % t.G) * D;
 #pragma unroll
-    for (int ks = 0; ks < NQ; ++ks) {
-      if constexpr (BF16) {
-        float f[8];
-        if (t.valid_col[mb]) {
-          const float4 a = *reinterpret_cast<const float4*>(qp + 32 * ks + 8 * t.lg);
-          const float4 c = *reinterpret_cast<const float4*>(qp + 32 * ks + 8 * t.lg + 4);
-          f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-          f[4] = c.x; f[5] = c.y; f[6] = c.z; f[7] = c.w;
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) f[j] = 0.f;
-        }
-        qreg[mb][ks] = to_bf16x8(f);
-      } else {
-        v4f a = {0.f, 0.f, 0.f, 0.f};
-        if (t.valid_col[mb]) {
-          const float4 v = *reinterpret_cast<const float4*>(qp + 16 * ks + 4 * t.lg);
-          a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
-        }
-        qreg[mb][ks] = a;
+    for (int ks = 0; ks < D / 16; ++ks) {
+      v4f a = {0.f, 0.f, 0.f, 0.f};
+      if (t.valid_col[mb]) {
+        const float4 v = *reinterpret_cast<const float4*>(qp + 16 * ks + 4 * t.lg);
+        a[0] = v.x; a[1] = v.y; a[2] = v.z; a[3] = v.w;
       }
+      qreg[mb][ks] = a;
     }
   }
 }
 
 // S^T = K . Q^T for one 64-position tile: 4 key blocks x 2 column blocks.
-template <int D, bool BF16>
-__device__ __forceinline__ void qk_tile(const uint4* __restrict__ k_lds,
-                                        const typename PrefillCfg<D, BF16>::QReg (&qreg)[2][PrefillCfg<D, BF16>::NQ],
+template <int D>
+__device__ __forceinline__ void qk_tile(const uint4* __restrict__ k_lds, const v4f (&qreg)[2][D / 16],
                                         v4f (&sacc)[4][2], int lr, int lg) {
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) sacc[kb][mb] = v4f{0.f, 0.f, 0.f, 0.f};
-  if constexpr (BF16) {
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
+  for (int c4 = 0; c4 < D / 16; ++c4) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, k_lds[(4 * ks + lg) * 64 + 16 * kb + lr]);
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint4 a = k_lds[(4 * c4 + lg) * 64 + 16 * kb + lr];
+      const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                           __uint_as_float(a.w)};
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[mb][ks], sacc[kb][mb], 0, 0, 0);
-      }
-    }
-  } else {
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int c4 = 0; c4 < D / 16; ++c4) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint4 a = k_lds[(4 * c4 + lg) * 64 + 16 * kb + lr];
-        const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
-                             __uint_as_float(a.w)};
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qreg[mb][c4][u], sacc[kb][mb], 0, 0, 0);
-      }
+        for (int u = 0; u < 4; ++u)
+          sacc[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qreg[mb][c4][u], sacc[kb][mb], 0, 0, 0);
     }
   }
 }
@@ -310,58 +285,22 @@ __device__ __forceinline__ void rescale_acc(const float (&alpha)[2], v4f (&acc_o
 }
 
 // O^T += V^T . P^T for one tile (P = the weights left in sacc).
-template <int D, bool BF16>
+template <int D>
 __device__ __forceinline__ void pv_tile(const uint4* __restrict__ v_lds, const v4f (&p)[4][2],
                                         v4f (&acc_o)[D / 16][2], int lr, int lg) {
-  constexpr int NDB = D / 16;
-  if constexpr (BF16) {
-    // B operand of 32-key half k2 for the lane's V group g = 2 u + h (this
-    // lane's l / 16), which holds keys {16 u + 4 h + 0..3, 16 u + 8 + 4 h +
-    // 0..3} of the half.  The lane has the weights of keys 16 kb + 4 (l / 16)
-    // + 0..3: a lane of the lower half (g < 2: u = 0, h = g) owns the first
-    // four in its block 2 k2 and finds the other four in the lane 32 above;
-    // a lane of the upper half (u = 1, h = g - 2) owns the last four (block
-    // 2 k2 + 1) and finds the first four 32 below -- one v_permlane32_swap
-    // per pair of packed words.
-    bf16x8 pb[2][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+  for (int db = 0; db < D / 16; ++db)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const v4f& lo = p[2 * k2][mb];
-        const v4f& hi = p[2 * k2 + 1][mb];
-        const uint32_t a0 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo[0], (__bf16)lo[1]});
-        const uint32_t a1 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)lo[2], (__bf16)lo[3]});
-        const uint32_t b0 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)hi[0], (__bf16)hi[1]});
-        const uint32_t b1 = __builtin_bit_cast(uint32_t, bf16x2{(__bf16)hi[2], (__bf16)hi[3]});
-        const auto x0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-        const auto x1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-        pb[mb][k2] = __builtin_bit_cast(bf16x8, make_uint4(x0[0], x1[0], x0[1], x1[1]));
-      }
+    for (int kb = 0; kb < 4; ++kb) {
+      const uint4 a = v_lds[(4 * kb + lg) * D + 16 * db + lr];
+      const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                           __uint_as_float(a.w)};
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int k2 = 0; k2 < 2; ++k2) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, v_lds[(k2 * 4 + lg) * D + 16 * db + lr]);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          acc_o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[mb][k2], acc_o[db][mb], 0, 0, 0);
-      }
-  } else {
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const uint4 a = v_lds[(4 * kb + lg) * D + 16 * db + lr];
-        const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
-                             __uint_as_float(a.w)};
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            acc_o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], p[kb][mb][u], acc_o[db][mb], 0, 0, 0);
-      }
-  }
+        for (int u = 0; u < 4; ++u)
+          acc_o[db][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], p[kb][mb][u], acc_o[db][mb], 0, 0, 0);
+    }
 }
 
 // Positions at or beyond kend may hold anything: zero their values in the
@@ -439,13 +378,12 @@ __device__ __forceinline__ void store_result(const Tiling& t, float* __restrict_
 //   softmax phases: 0, 1 scale + mask + local max of column block 0 / 1;
 //   2 cross-lane max; 3 reference-max update; 4..7 exponentials of key
 //   block 0..3.
-template <int D, bool BF16>
+template <int D>
 __device__ __forceinline__ void qk_next_softmax_cur(
-    const Tiling& t, const uint4* __restrict__ k_lds,
-    const typename PrefillCfg<D, BF16>::QReg (&qreg)[2][PrefillCfg<D, BF16>::NQ],
+    const Tiling& t, const uint4* __restrict__ k_lds, const v4f (&qreg)[2][D / 16],
     v4f (&nxt)[4][2], v4f (&cur)[4][2], int kt, int start, float sl2e, float (&m_run)[2],
     float (&l_run)[2], float (&alpha)[2]) {
-  constexpr int NKS = BF16 ? D / 32 : D / 16;  // k-steps of the score product
+  constexpr int NKS = D / 16;  // k-steps of the score product
   const int lr = t.lr, lg = t.lg;
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
@@ -519,21 +457,14 @@ __device__ __forceinline__ void qk_next_softmax_cur(
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      if constexpr (BF16) {
-        const bf16x8 av = __builtin_bit_cast(bf16x8, kbuf[ks & 1][kb]);
+      const uint4 a = kbuf[ks & 1][kb];
+      const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
+                           __uint_as_float(a.w)};
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-          nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qreg[mb][ks], nxt[kb][mb], 0, 0, 0);
-      } else {
-        const uint4 a = kbuf[ks & 1][kb];
-        const float av[4] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z),
-                             __uint_as_float(a.w)};
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qreg[mb][ks][u], nxt[kb][mb], 0, 0, 0);
-      }
+        for (int u = 0; u < 4; ++u)
+          nxt[kb][mb] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u], qreg[mb][ks][u], nxt[kb][mb], 0, 0, 0);
     }
     // softmax phases assigned to this chunk (all 8 spread over NKS chunks)
 #pragma unroll
@@ -549,12 +480,12 @@ __device__ __forceinline__ void qk_next_softmax_cur(
 // are formed (VALU), the score MFMAs of tile i+1 are already issued, and the
 // copies of K(i+2) and V(i+1) are in flight.  K and V each have two LDS
 // buffers; the loop is unrolled by two so every access names its buffer.
-template <int D, bool BF16>
+template <int D>
 __global__ __launch_bounds__(256) void prefill_pipe_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
     float* __restrict__ part_ml, int Hq, int Hkv, int C, const ChunkArg ca, float sl2e) {
-  using Cfg = PrefillCfg<D, BF16>;
+  using Cfg = PrefillCfg<D, false>;
   constexpr int NDB = Cfg::NDB, TB = Cfg::TILE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char kb0[TB];
   __shared__ __attribute__((aligned(16))) unsigned char kb1[TB];
@@ -565,12 +496,11 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
   if (!make_tiling(ca, Hq, Hkv, t)) return;
   const int start = t.start, R = t.R, m_tiles = t.m_tiles, S = t.S;
   const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;  // elements
-  constexpr int ES = BF16 ? 2 : 4;
-  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * ES, (size_t)C * D * ES);
-  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab * ES, (size_t)C * D * ES);
+  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * 4, (size_t)C * D * 4);
+  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab * 4, (size_t)C * D * 4);
   const int n = t.kt1 - t.kt0;
 
-  typename Cfg::QReg qreg[2][Cfg::NQ];
+  v4f qreg[2][D / 16];
   v4f acc_o[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -582,12 +512,12 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
 
   if (n > 0) {
     load_tile<TB>(ksrc, t.kt0, kb0, t.w, t.lane);
-    load_q<D, BF16>(t, q, R, Hq, qreg);
+    load_q<D>(t, q, R, Hq, qreg);
     wait_vmem();
     __syncthreads();
     load_tile<TB>(vsrc, t.kt0, vb0, t.w, t.lane);
     if (n > 1) load_tile<TB>(ksrc, t.kt0 + 1, kb1, t.w, t.lane);
-    qk_tile<D, BF16>(reinterpret_cast<const uint4*>(kb0), qreg, sa, t.lr, t.lg);
+    qk_tile<D>(reinterpret_cast<const uint4*>(kb0), qreg, sa, t.lr, t.lg);
   }
 
   // step i: V(i) in vb[i&1], K(i+1) in kb[(i+1)&1], scores of tile i in cur
@@ -603,17 +533,17 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
     if (i + 2 < n) load_tile<TB>(ksrc, kt + 2, k_free, t.w, t.lane);
     if (i + 1 < n) load_tile<TB>(vsrc, kt + 1, v_free, t.w, t.lane);
     if ((kt + 1) * kNTile > t.kend) {
-      zero_v_beyond<D, BF16>(reinterpret_cast<uint4*>(v_cur), kt, t.kend, t.tid);
+      zero_v_beyond<D, false>(reinterpret_cast<uint4*>(v_cur), kt, t.kend, t.tid);
       __syncthreads();
     }
     // The next tile's score MFMAs and this tile's softmax are independent
     // and run interleaved (the last step computes one spare tile of scores
     // from a stale buffer, which is never used).
     float alpha[2];
-    qk_next_softmax_cur<D, BF16>(t, reinterpret_cast<const uint4*>(k_next), qreg, nxt, cur, kt,
+    qk_next_softmax_cur<D>(t, reinterpret_cast<const uint4*>(k_next), qreg, nxt, cur, kt,
                                  start, sl2e, m_run, l_run, alpha);
     rescale_acc<NDB>(alpha, acc_o);
-    pv_tile<D, BF16>(reinterpret_cast<const uint4*>(v_cur), cur, acc_o, t.lr, t.lg);
+    pv_tile<D>(reinterpret_cast<const uint4*>(v_cur), cur, acc_o, t.lr, t.lg);
   };
   for (int i = 0; i < n; i += 2) {
     step(std::integral_constant<int, 0>(), i, sa, sb);
@@ -1303,12 +1233,12 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
 
 // Sequential prefill (one K+V stage) for shapes whose four tiles do not fit
 // in LDS: copy tile i, then compute it, then copy tile i+1.
-template <int D, bool BF16>
+template <int D>
 __global__ __launch_bounds__(256) void prefill_seq_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
     float* __restrict__ part_ml, int Hq, int Hkv, int C, const ChunkArg ca, float sl2e) {
-  using Cfg = PrefillCfg<D, BF16>;
+  using Cfg = PrefillCfg<D, false>;
   constexpr int NDB = Cfg::NDB, TB = Cfg::TILE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char kb[TB];
   __shared__ __attribute__((aligned(16))) unsigned char vb[TB];
@@ -1317,12 +1247,11 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
   if (!make_tiling(ca, Hq, Hkv, t)) return;
   const int start = t.start, R = t.R, m_tiles = t.m_tiles, S = t.S;
   const size_t slab = ((size_t)t.b * Hkv + t.g) * (size_t)C * D;
-  constexpr int ES = BF16 ? 2 : 4;
-  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * ES, (size_t)C * D * ES);
-  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab * ES, (size_t)C * D * ES);
+  const TileSrc ksrc = tile_src(reinterpret_cast<const unsigned char*>(k_cache) + slab * 4, (size_t)C * D * 4);
+  const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab * 4, (size_t)C * D * 4);
 
-  typename Cfg::QReg qreg[2][Cfg::NQ];
-  load_q<D, BF16>(t, q, R, Hq, qreg);
+  v4f qreg[2][D / 16];
+  load_q<D>(t, q, R, Hq, qreg);
   v4f acc_o[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db)
@@ -1338,14 +1267,14 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
     wait_vmem();
     __syncthreads();
     if ((kt + 1) * kNTile > t.kend) {
-      zero_v_beyond<D, BF16>(reinterpret_cast<uint4*>(vb), kt, t.kend, t.tid);
+      zero_v_beyond<D, false>(reinterpret_cast<uint4*>(vb), kt, t.kend, t.tid);
       __syncthreads();
     }
-    qk_tile<D, BF16>(reinterpret_cast<const uint4*>(kb), qreg, sacc, t.lr, t.lg);
+    qk_tile<D>(reinterpret_cast<const uint4*>(kb), qreg, sacc, t.lr, t.lg);
     float alpha[2];
     softmax_tile(t, kt, start, sl2e, sacc, m_run, l_run, alpha);
     rescale_acc<NDB>(alpha, acc_o);
-    pv_tile<D, BF16>(reinterpret_cast<const uint4*>(vb), sacc, acc_o, t.lr, t.lg);
+    pv_tile<D>(reinterpret_cast<const uint4*>(vb), sacc, acc_o, t.lr, t.lg);
   }
   store_result<D>(t, out, part, part_ml, acc_o, m_run, l_run, R, Hq, Hkv, m_tiles, S);
 }
@@ -1605,11 +1534,11 @@ hipError_t launch_chunks(const Shape& s, const ChunkLaunch* L, int nl, long long
                          vc, out, part, part_ml, k_scale_array(s, kc), s.num_q_heads,
                          s.num_kv_heads, s.capacity, ca, scale * kLog2e);
     else if constexpr (Cfg::PIPE)
-      hipLaunchKernelGGL((prefill_pipe_kernel<D, false>), grid, dim3(256), 0, st, q, kc, vc, out,
+      hipLaunchKernelGGL((prefill_pipe_kernel<D>), grid, dim3(256), 0, st, q, kc, vc, out,
                          part, part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, ca,
                          scale * kLog2e);
     else
-      hipLaunchKernelGGL((prefill_seq_kernel<D, false>), grid, dim3(256), 0, st, q, kc, vc, out,
+      hipLaunchKernelGGL((prefill_seq_kernel<D>), grid, dim3(256), 0, st, q, kc, vc, out,
                          part, part_ml, s.num_q_heads, s.num_kv_heads, s.capacity, ca,
                          scale * kLog2e);
     hipError_t e = hipGetLastError();
