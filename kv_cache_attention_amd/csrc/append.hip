@@ -109,7 +109,11 @@ __device__ __forceinline__ void quantise_row_wave(const float* rowp, const float
     // dims 4 l .. 4 l + 3 sit in code vector l / 4, bytes 4 (l % 4) .. + 3; vectors
     // of one row are 64 vectors (1 KiB) apart in the [D/16][64][16] block layout
     const size_t off = (row_vec0 + (size_t)(lane >> 2) * 64) * 16 + 4 * (lane & 3);
-    *reinterpret_cast<uint32_t*>(codes + off) = pack_codes4(x.x, x.y, x.z, x.w, s);
+    const RowQuant rq(s);
+    bool ok = rq.fast;
+    uint32_t wc = pack_codes4_fast(x.x, x.y, x.z, x.w, rq, ok);
+    if (__any(!ok)) wc = pack_codes4(x.x, x.y, x.z, x.w, rq);
+    *reinterpret_cast<uint32_t*>(codes + off) = wc;
   }
   if (lane == 0) *scale_out = s;
 }

@@ -586,11 +586,20 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     col.m = m;
     col.nan = nf != 0.f;
     const float s = col.scale();
+    const RowQuant rq(s);
+    bool ok = rq.fast;
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        qcode[ks][e] = (int)pack_codes4(xq[ks][e].x, xq[ks][e].y, xq[ks][e].z, xq[ks][e].w, s);
+        qcode[ks][e] = (int)pack_codes4_fast(xq[ks][e].x, xq[ks][e].y, xq[ks][e].z, xq[ks][e].w, rq, ok);
+    if (__any(!ok)) {
+#pragma unroll
+      for (int ks = 0; ks < D / 64; ++ks)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          qcode[ks][e] = (int)pack_codes4(xq[ks][e].x, xq[ks][e].y, xq[ks][e].z, xq[ks][e].w, rq);
+    }
     sq = s * sl2e;
   } else {
     const float* qp = q + (((size_t)b * R + (hv ? pc / G : 0)) * Hq + g * G + (hv ? pc % G : 0)) * D + 8 * r;
@@ -654,7 +663,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
       if (mine) {
         // codes of dims 4 l .. + 3: word l % 4 of code vector l / 4 (vectors of a
         // row are 64 vectors apart); the same word index in LDS
-        const uint32_t wc = pack_codes4(x.x, x.y, x.z, x.w, s_new);
+        const RowQuant rq(s_new);
+        bool ok = rq.fast;
+        uint32_t wc = pack_codes4_fast(x.x, x.y, x.z, x.w, rq, ok);
+        if (__any(!ok)) wc = pack_codes4(x.x, x.y, x.z, x.w, rq);
         int8_t* kb8 = reinterpret_cast<int8_t*>(k_cache) + slab_el;  // one byte per code
         *reinterpret_cast<uint32_t*>(
             kb8 + (k_vec_index(p_new, 0, D, 16) + (size_t)(lane >> 2) * 64) * 16 + 4 * (lane & 3)) = wc;

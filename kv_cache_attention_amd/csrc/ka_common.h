@@ -153,16 +153,61 @@ struct AbsMax {
   __device__ __forceinline__ float scale() const { return nan ? __builtin_nanf("") : m * kInv127; }
 };
 
-__device__ __forceinline__ int quant_code(float x, float s) {
-  if (!(s > 0.f) || !(s <= 3.402823466e38f)) return 0;  // 0, NaN or inf
-  const float r = rintf(__fdiv_rn(x, s));
-  return (int)fminf(fmaxf(r, -127.f), 127.f);
+// A row's quantiser: its scale s and, when s and 1 / s are normal numbers,
+// the correctly rounded reciprocal r = 1 / s (one division per row).  fast
+// says whether quant_code_fast applies: for those scales, and for scales that
+// are 0, NaN or infinite, whose codes are all 0 (r = 0 gives 0 for every
+// finite value; a NaN or infinite value clears ok).  Only finite nonzero
+// scales outside [2^-125, 2^125] need the division throughout.
+struct RowQuant {
+  float s, r;
+  bool fast;
+  __device__ __forceinline__ explicit RowQuant(float s_) : s(s_) {
+    const bool normal = s_ >= 0x1p-125f && s_ <= 0x1p125f;
+    fast = normal || !(s_ > 0.f) || !(s_ <= 3.402823466e38f);
+    r = normal ? __fdiv_rn(1.f, s_) : 0.f;
+  }
+};
+
+// rint of the IEEE f32 quotient x / s, limited to +-127.
+__device__ __forceinline__ int quant_code(float x, const RowQuant& q) {
+  if (!(q.s > 0.f) || !(q.s <= 3.402823466e38f)) return 0;  // 0, NaN or inf
+  const float c = rintf(__fdiv_rn(x, q.s));
+  return (int)fminf(fmaxf(c, -127.f), 127.f);
+}
+
+// Four codes (one little-endian word) without the division, valid while ok
+// stays true.  The quotient's rounding can only change rint near a
+// half-integer, so the product t = x * r (relative error below 2^-23: r's
+// rounding and the product's) decides wherever it lies farther than
+// |t| 2^-20 + 2^-22 from every half-integer h: then x / s, its f32 rounding
+// and t all lie on t's side of h and round to the same integer (the absolute
+// 2^-22 covers the rounding of fract(t) - 1/2).  About one value in 10^4
+// clears ok; callers then redo the codes with pack_codes4 for the whole wave
+// (one uniform branch), so the result is the division's bit for bit.  ok must
+// start as q.fast (false for finite nonzero scales outside [2^-125, 2^125]).
+__device__ __forceinline__ uint32_t pack_codes4_fast(float a, float b, float c, float d,
+                                                     const RowQuant& q, bool& ok) {
+  const float x[4] = {a, b, c, d};
+  int k[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = x[i] * q.r;
+    const float f = __builtin_amdgcn_fractf(t) - 0.5f;
+    ok = ok && fabsf(f) > fmaf(fabsf(t), 0x1p-20f, 0x1p-22f);
+    k[i] = (int)__builtin_amdgcn_fmed3f(rintf(t), -127.f, 127.f);
+  }
+  // low bytes of k0, k1 and of k2, k3, then the two halves
+  const uint32_t lo = __builtin_amdgcn_perm((uint32_t)k[1], (uint32_t)k[0], 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm((uint32_t)k[3], (uint32_t)k[2], 0x0c0c0400u);
+  return lo | (hi << 16);
 }
 
 // Four codes packed little-endian into one 32-bit word.
-__device__ __forceinline__ uint32_t pack_codes4(float a, float b, float c, float d, float s) {
-  return (uint32_t)(quant_code(a, s) & 0xff) | ((uint32_t)(quant_code(b, s) & 0xff) << 8) |
-         ((uint32_t)(quant_code(c, s) & 0xff) << 16) | ((uint32_t)(quant_code(d, s) & 0xff) << 24);
+__device__ __forceinline__ uint32_t pack_codes4(float a, float b, float c, float d,
+                                                const RowQuant& q) {
+  return (uint32_t)(quant_code(a, q) & 0xff) | ((uint32_t)(quant_code(b, q) & 0xff) << 8) |
+         ((uint32_t)(quant_code(c, q) & 0xff) << 16) | ((uint32_t)(quant_code(d, q) & 0xff) << 24);
 }
 
 }  // namespace ka

@@ -720,37 +720,62 @@ __device__ __forceinline__ void take_q(const ColB& c, int cb, float sl2e,
 
 // int8 form: the column's symmetric codes (as the append quantises K rows)
 // and sq = s_q * scale * log2 e.  Lane (l % 32, h) holds the 16 codes of dims
-// 32 ks + 16 h .. 32 ks + 16 h + 15 for each k-step; the amax and the NaN flag
-// cover the other half of the column through lane l ^ 32.
+// 32 ks + 16 h .. 32 ks + 16 h + 15 for each k-step.  The amax covers the
+// other half of the column through lane l ^ 32; a NaN or an infinity anywhere
+// in the column makes its scale NaN (an infinity would give inf: either way
+// the codes are 0 and every score of the column is NaN).  The two waves of a
+// column block (kh = 0, 1) hold the same columns: each computes the codes of
+// half the k-steps and they swap them through LDS, once every wave has read
+// the f32 staging (two barriers; every thread of the block calls this).
 template <int D>
-__device__ __forceinline__ void take_q_i8(const ColB& c, int cb, float sl2e,
-                                          const float4* __restrict__ q_lds, i32x4 (&qc)[D / 32],
-                                          float& sq) {
-  constexpr int GR = D / 4;
+__device__ __forceinline__ void take_q_i8(const ColB& c, int cb, int kh, int w, int lane,
+                                          float sl2e, float4* __restrict__ q_lds,
+                                          i32x4 (&qc)[D / 32], float& sq) {
+  constexpr int GR = D / 4, NQS = D / 32, HALF = NQS / 2;
   const int col = 32 * cb + c.lc, sw = col & (GR - 1);
   const float4* qcol = q_lds + col * GR;
-  AbsMax am;
+  float am = 0.f, nz = 0.f;  // max |x|; x * 0 summed (NaN once any x is NaN or infinite)
 #pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float4 x = qcol[(8 * ks + 4 * c.lh + e) ^ sw];
-      am.add(x.x); am.add(x.y); am.add(x.z); am.add(x.w);
-    }
-  float m = am.m, nf = am.nan ? 1.f : 0.f;
-  m = fmaxf(m, __shfl_xor(m, 32, kWave));
-  nf = fmaxf(nf, __shfl_xor(nf, 32, kWave));
-  AbsMax colm;
-  colm.m = m;
-  colm.nan = nf != 0.f;
-  const float s = colm.scale();
-#pragma unroll
-  for (int ks = 0; ks < D / 32; ++ks)
+  for (int ks = 0; ks < NQS; ++ks)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float4 x = qcol[(8 * ks + 4 * c.lh + e) ^ sw];
-      qc[ks][e] = (int)pack_codes4(x.x, x.y, x.z, x.w, s);
+      am = fmaxf(fmaxf(am, fabsf(x.x)), fmaxf(fabsf(x.y), fmaxf(fabsf(x.z), fabsf(x.w))));
+      nz = fmaf(x.x, 0.f, fmaf(x.y, 0.f, fmaf(x.z, 0.f, fmaf(x.w, 0.f, nz))));
     }
+  am = fmaxf(am, __shfl_xor(am, 32, kWave));
+  nz += __shfl_xor(nz, 32, kWave);
+  const float s = nz == nz ? am * kInv127 : __builtin_nanf("");
+  const RowQuant rq(s);
+  i32x4 own[HALF];
+  bool ok = rq.fast;
+#pragma unroll
+  for (int j = 0; j < HALF; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 x = qcol[(8 * (kh * HALF + j) + 4 * c.lh + e) ^ sw];
+      own[j][e] = (int)pack_codes4_fast(x.x, x.y, x.z, x.w, rq, ok);
+    }
+  if (__any(!ok)) {
+#pragma unroll
+    for (int j = 0; j < HALF; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float4 x = qcol[(8 * (kh * HALF + j) + 4 * c.lh + e) ^ sw];
+        own[j][e] = (int)pack_codes4(x.x, x.y, x.z, x.w, rq);
+      }
+  }
+  __syncthreads();  // the f32 staging is no longer read: it takes the codes
+  i32x4* xc = reinterpret_cast<i32x4*>(q_lds);  // [wave][j][lane]
+#pragma unroll
+  for (int j = 0; j < HALF; ++j) xc[(w * HALF + j) * 64 + lane] = own[j];
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < HALF; ++j) {
+    const i32x4 other = xc[((w ^ 4) * HALF + j) * 64 + lane];
+    qc[j] = kh == 0 ? own[j] : other;
+    qc[HALF + j] = kh == 0 ? other : own[j];
+  }
   sq = s * sl2e;
 }
 
@@ -1077,7 +1102,7 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
     wait_vmem();
     __syncthreads();  // K(0) and Q are in LDS
     if constexpr (I8)
-      take_q_i8<D>(c, t.w & 3, sl2e, reinterpret_cast<const float4*>(q_lds), qreg, sq);
+      take_q_i8<D>(c, t.w & 3, kh, t.w, t.lane, sl2e, reinterpret_cast<float4*>(q_lds), qreg, sq);
     else
       take_q<D>(c, t.w & 3, sl2e, reinterpret_cast<const float4*>(q_lds), qreg);
     __syncthreads();  // every wave holds its Q: kb1 and the exchange buffers are free
