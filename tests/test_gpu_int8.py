@@ -72,6 +72,33 @@ def test_append_quantises_rows_exactly():
     assert np.array_equal(vb[:, :, :200], obf16.encode_rne(np.ascontiguousarray(c.v.transpose(0, 2, 1, 3))))
 
 
+def test_append_codes_at_rounding_boundaries():
+    """Values whose quotient x / s lies at, or one f32 step beside, a
+    half-integer k + 1/2: the codes there depend on the exact rounding of the
+    division, which the kernels' product form hands to the division.  Row
+    magnitudes span the f32 range, including scales outside [2^-125, 2^125]."""
+    B, Hq, Hkv, D, C = 1, 4, 2, 128, 128
+    g = np.random.default_rng(12)
+    rows = 100
+    k = np.zeros((B, rows, Hkv, D), np.float32)
+    for r in range(rows):
+        for h in range(Hkv):
+            mag = np.float32(10.0) ** np.float32(g.uniform(-40, 36))
+            amax = np.float32(127) * mag
+            s = np.float32(amax * oi8.INV127)
+            half = ((g.integers(-127, 127, size=D).astype(np.float32) + np.float32(0.5)) * s).astype(np.float32)
+            step = g.integers(-1, 2, size=D)
+            x = np.where(step > 0, np.nextafter(half, np.float32(np.inf)),
+                         np.where(step < 0, np.nextafter(half, np.float32(-np.inf)), half)).astype(np.float32)
+            x = np.clip(x, -amax, amax)
+            x[0] = amax  # fixes the row's amax, so its scale is s
+            k[0, r, h] = x
+    v = g.standard_normal((B, rows, Hkv, D)).astype(np.float32)
+    caches = DevCaches(B, Hq, Hkv, D, C, "i8k")
+    caches.append(k, v, 0)
+    _codes_match(caches, k, rows)
+
+
 def test_append_rope_then_quantise():
     B, Hq, Hkv, D, C, start, R = 1, 8, 1, 256, 640, 300, 77
     c = random_case(4, B, Hq, Hkv, D, start + R, 1)
