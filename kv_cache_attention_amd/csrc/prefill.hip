@@ -1313,7 +1313,7 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
 // four waves take every fourth split each, kMergeBatch loads in flight per
 // lane and a running frame per wave, then combine through LDS.  Both sum in
 // a fixed order, so results do not depend on timing.  H16: binary16 partials
-// with per-lane exponents (the bf16 kernel's format); otherwise f32 partials
+// with per-lane exponents (the 8-wave kernel's format); otherwise f32 partials
 // with (m, l) pairs.
 constexpr int kMergeFew = 8;     // most splits of the column form
 constexpr int kMergeGroups = 4;  // waves of the split form, each a subset of the splits
@@ -1536,14 +1536,14 @@ template <int D, int MODE>
 hipError_t launch_chunks(const Shape& s, const ChunkLaunch* L, int nl, long long total_slots,
                          const float* q, const void* kc, const void* vc, float* out, float scale,
                          void* ws, hipStream_t st) {
-  constexpr bool BF16 = MODE != kF32;  // binary16 partials (the 8-wave kernel)
+  constexpr bool H16 = MODE != kF32;  // binary16 partials (the 8-wave kernel)
   using Cfg = PrefillCfg<D, false>;
   // partials: binary16 accumulators for bf16 and int8-K caches, f32 otherwise, one
   // 128-column slot per (session, KV head, m-tile, split); then the
   // per-(column, split) records
   float* part = reinterpret_cast<float*>(ws);
   float* part_ml = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(ws) +
-                                            (size_t)total_slots * kMTile * D * (BF16 ? 2 : 4));
+                                            (size_t)total_slots * kMTile * D * (H16 ? 2 : 4));
   for (int l = 0; l < nl; ++l) {
     const ChunkArg& ca = L[l].ca;
     const int items = ca.item0[ca.n];
@@ -1570,11 +1570,11 @@ hipError_t launch_chunks(const Shape& s, const ChunkLaunch* L, int nl, long long
     if (e != hipSuccess) return e;
     if (L[l].max_s > 1) {
       if (L[l].max_s <= kMergeFew)
-        hipLaunchKernelGGL((prefill_merge_few_kernel<D, BF16>),
+        hipLaunchKernelGGL((prefill_merge_few_kernel<D, H16>),
                            dim3(L[l].max_m * (kMTile / 16), s.num_kv_heads, ca.n), dim3(256), 0, st,
                            part, part_ml, out, s.num_q_heads, s.num_kv_heads, ca);
       else
-        hipLaunchKernelGGL((prefill_merge_split_kernel<D, BF16>),
+        hipLaunchKernelGGL((prefill_merge_split_kernel<D, H16>),
                            dim3(L[l].max_m * (kMTile / 4) * (D / 64), s.num_kv_heads, ca.n),
                            dim3(256), 0, st, part, part_ml, out, s.num_q_heads, s.num_kv_heads, ca);
       e = hipGetLastError();
