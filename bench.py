@@ -610,7 +610,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE {world}) is not "
-              f"supported by this build", file=sys.stderr)
+              f"supported: the library has no multi-GPU path", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     ka.lib()
