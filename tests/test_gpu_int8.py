@@ -198,6 +198,25 @@ def test_prefill(case):
     _check(got, ref, vs, f"int8 prefill {case}")
 
 
+def test_prefill_split_partials_per_dim_range():
+    """Value dims scaled by 2^-6 .. 2^6 (a different power per dim), a chunk
+    long enough to be split: every dim keeps its own relative accuracy through
+    the binary16 split partials (per-lane scales), as on bf16 caches."""
+    B, Hq, Hkv, D, start, R = 1, 8, 1, 256, 2048, 256
+    C = start + R
+    c = random_case(42, B, Hq, Hkv, D, C, R)
+    rng = np.random.default_rng(42)
+    c.v[:] = c.v * np.ldexp(np.float32(1), rng.integers(-6, 7, size=D)).astype(np.float32)
+    caches = DevCaches(B, Hq, Hkv, D, C, "i8k")
+    caches.append(c.k, c.v, 0)
+    got = caches.prefill(c.q, start, 1 / 16)
+    vs = oracle.stored_values(c.v, "bf16")
+    ref = oi8.prefill_chunk_i8(c.q, c.k, vs, start, 1 / 16)
+    _check(got, ref, vs, "int8 prefill per-dim range")
+    per_dim = np.abs(got - ref).max(axis=(0, 1, 2)) / np.abs(vs).max(axis=(0, 1, 2))
+    assert per_dim.max() <= TOL, f"worst per-dim rel err {per_dim.max():.3e}"
+
+
 def test_ragged_prefill():
     B, Hq, Hkv, D, C = 4, 8, 1, 256, 2048
     starts, rows = [0, 100, 1500, 7], [1, 0, 500, 64]
