@@ -94,9 +94,19 @@ def attend_rows_i8(qc, qs, kc, ks, v, q_pos: Sequence[int], scale: float,
                 s = np.where(visible[:, None, :], s, -np.inf)
                 m = np.max(s, axis=2, keepdims=True)                      # NaN propagates
                 w = np.where(visible[:, None, :], np.exp(s - m), 0.0)
+                Z = w.sum(axis=2, keepdims=True)
                 vb = np.asarray(v[:nk, g], dtype=np.float64)
-                o = (w.reshape(-1, nk) @ vb).reshape(r1 - r0, G, D)
-                out[r0:r1, g * G:(g + 1) * G] = o / w.sum(axis=2, keepdims=True)
+                if np.isfinite(vb).all():
+                    o = (w.reshape(-1, nk) @ vb).reshape(r1 - r0, G, D)
+                else:
+                    # A non-finite V row reaches only the rows that see it:
+                    # each row sums over its own visible keys, since a zero
+                    # weight times NaN or infinity is NaN.
+                    o = np.empty((r1 - r0, G, D))
+                    for i in range(r1 - r0):
+                        nv = int(pos[i]) + 1
+                        o[i] = w[i, :, :nv] @ vb[:nv]
+                out[r0:r1, g * G:(g + 1) * G] = o / Z
     return out
 
 

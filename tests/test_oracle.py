@@ -509,3 +509,84 @@ def test_int8_scores_match_integer_brute_force():
         m = max(s)
         w = [math.exp(t - m) for t in s]
         np.testing.assert_allclose(out[0, h, :5], np.array(w) / sum(w), rtol=1e-12)
+
+
+def _lossless_rows(g, shape, D, e):
+    """Rows of integer codes (largest |code| exactly 127) times 2**e: they
+    quantise back to themselves with s = 2**e."""
+    c = g.integers(-127, 128, size=shape + (D,)).astype(np.float32)
+    c[..., 0] = 127 * np.where(g.random(shape) < 0.5, -1, 1)
+    return (c * np.float32(2.0 ** e)).astype(np.float32)
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_int8_nonfinite_value_reaches_only_rows_that_see_it(bad):
+    """Causality (an output row does not change with keys after its
+    position) with a non-finite V value inside a row block: the rows before
+    the bad position equal those computed without it, and
+    blocking the rows one at a time gives the default block's result (to
+    rounding: the products may sum in another order).  A block product with
+    zero weights (0 * NaN = NaN) fails here."""
+    g = np.random.default_rng(14)
+    Hq, Hkv, D, n = 4, 2, 32, 24
+    q = g.standard_normal((n, Hq, D)).astype(np.float32)
+    k = g.standard_normal((n, Hkv, D)).astype(np.float32)
+    v = g.standard_normal((n, Hkv, D)).astype(np.float32)
+    qc, qs = oi8.quantize_rows(q)
+    kc, ks = oi8.quantize_rows(k)
+    j = 15
+    vb = v.copy()
+    vb[j, 1, 9] = bad
+    pos = np.arange(n)
+    clean = oi8.attend_rows_i8(qc, qs, kc, ks, v, pos, 0.2)
+    got = oi8.attend_rows_i8(qc, qs, kc, ks, vb, pos, 0.2)
+    one = oi8.attend_rows_i8(qc, qs, kc, ks, vb, pos, 0.2, row_block=1)
+    # (the matrix products may sum in another order: equal to rounding)
+    np.testing.assert_allclose(got, one, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(got[:j], clean[:j], rtol=1e-13, atol=1e-13)
+    assert np.isfinite(got[:j]).all()
+    # rows at j and after see the bad value in exactly that dim of the heads of KV head 1
+    assert (~np.isfinite(got[j:, 2:, 9])).all()
+    other = np.ones(got.shape, bool)
+    other[j:, 2:, 9] = False
+    assert np.isfinite(got[other]).all()
+
+
+def test_int8_chunk_and_decode_wrappers_on_lossless_inputs():
+    """prefill_chunk_i8 and decode_i8 quantise their own inputs and place the
+    rows.  On losslessly quantisable inputs their results are plain
+    attention's, which is pinned above against torch's float64 attention:
+    an error in the chunk's start offset, or in decode's ctx - 1 position,
+    fails here."""
+    g = np.random.default_rng(15)
+    B, Hq, Hkv, D, start, R = 2, 4, 2, 64, 37, 9
+    P = start + R
+    q = np.stack([_lossless_rows(g, (R, Hq), D, -8) for _ in range(B)])
+    k = np.stack([_lossless_rows(g, (P, Hkv), D, -6) for _ in range(B)])
+    v = g.standard_normal((B, P, Hkv, D)).astype(np.float32)
+    want = oracle.prefill_chunk(q, k, v, start, 0.5)
+    got = oi8.prefill_chunk_i8(q, k, v, start, 0.5)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+    ctx = [P, 11]
+    qd = q[:, 3]
+    np.testing.assert_allclose(oi8.decode_i8(qd, k, v, ctx, 0.5),
+                               oracle.decode(qd, k, v, ctx, 0.5), rtol=1e-12, atol=1e-12)
+
+
+def test_int8_chunk_rows_are_decode_rows():
+    """Row t of a chunk at start s is the decode of that row with context
+    s + t + 1, and the chunk's rows are attend_rows_i8 at s .. s + R - 1."""
+    g = np.random.default_rng(16)
+    Hq, Hkv, D, start, R = 4, 1, 32, 20, 6
+    P = start + R
+    q = g.standard_normal((1, R, Hq, D)).astype(np.float32)
+    k = g.standard_normal((1, P, Hkv, D)).astype(np.float32)
+    v = g.standard_normal((1, P, Hkv, D)).astype(np.float32)
+    chunk = oi8.prefill_chunk_i8(q, k, v, start, 0.3)
+    qc, qs = oi8.quantize_rows(q[0])
+    kc, ks = oi8.quantize_rows(k[0])
+    np.testing.assert_array_equal(
+        chunk[0], oi8.attend_rows_i8(qc, qs, kc, ks, v[0], np.arange(start, P), 0.3))
+    for t in range(R):
+        d = oi8.decode_i8(q[:, t], k, v, [start + t + 1], 0.3)
+        np.testing.assert_allclose(d[0], chunk[0, t], rtol=1e-13, atol=1e-13)
