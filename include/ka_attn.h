@@ -16,13 +16,12 @@
  * Softmax rules (Karume v0.8.0 release notes, "Breaking Changes", the softmax
  * NaN bullet): a NaN among a row's visible scores makes that whole output row
  * NaN (the row max propagates NaN, no NaN is dropped); a NaN visible value
- * v[j][d] makes output dim d NaN; masked keys carry weight exactly 0, so no
- * key past a row's position reaches its result, and no value at or past the
- * end of the chunk (or past a decode row) does.  One exception: a NaN or
- * infinite value v[j][d] at a position j inside a prefill chunk may also
- * turn output dim d of the chunk's rows before j into NaN -- those rows give
- * j the weight 0 in a product that the chunk's rows share, and 0 times a
- * non-finite value is NaN.  Their other dims are unaffected.
+ * v[j][d] makes output dim d NaN, and an infinite one makes it infinite (NaN
+ * with the other infinity, or when its weight is 0), as the row's own sum
+ * gives it; masked keys carry weight exactly 0, so no key or value past a
+ * row's position reaches its result -- a non-finite value at position j
+ * inside a chunk reaches only the rows at j and after -- and no value at or
+ * past the end of the chunk (or past a decode row) does.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -185,6 +184,14 @@ ka_status ka_attn_rope_rows(const ka_attn_shape* s, const float* x, float* y,
  * max_rows rows at any start position of shape s (0 if none is needed).
  */
 size_t ka_attn_prefill_workspace_bytes(const ka_attn_shape* s, int32_t max_rows);
+
+/*
+ * Workspace bytes one ka_attn_prefill_chunk call with these arguments needs
+ * (at most ka_attn_prefill_workspace_bytes(s, row_count); 0 if none is
+ * needed or the arguments are invalid).  Host only.
+ */
+size_t ka_attn_prefill_workspace_need(const ka_attn_shape* s, int32_t start_pos,
+                                      int32_t row_count);
 
 /*
  * Chunked prefill (Karume v0.12.0 release notes, "Performance": the

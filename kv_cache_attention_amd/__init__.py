@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["Shape", "KaAttnError", "KaAttnUnavailable", "lib", "lib_path", "F32", "BF16",
            "cache_bytes", "alloc_cache", "append_kv", "prefill_workspace_bytes",
-           "prefill_chunk", "decode_workspace_bytes", "decode", "status_string",
+           "prefill_workspace_need", "prefill_chunk", "decode_workspace_bytes", "decode", "status_string",
            "last_error", "abi_version", "EXPORTED_SYMBOLS", "decode_step", "append_kv_rope",
            "rope_rows", "append_kv_ragged", "prefill_ragged_workspace_bytes",
            "prefill_ragged_workspace_need", "prefill_ragged",
@@ -34,7 +34,7 @@ _LIB_NAME = "libka_attn.so"
 EXPORTED_SYMBOLS = (
     "ka_attn_abi_version", "ka_attn_cache_bytes", "ka_attn_append_kv", "ka_attn_append_kv_rope",
     "ka_attn_rope_rows",
-    "ka_attn_prefill_workspace_bytes", "ka_attn_prefill_chunk",
+    "ka_attn_prefill_workspace_bytes", "ka_attn_prefill_workspace_need", "ka_attn_prefill_chunk",
     "ka_attn_decode_workspace_bytes", "ka_attn_decode", "ka_attn_decode_step",
     "ka_attn_append_kv_ragged", "ka_attn_prefill_ragged_workspace_bytes",
     "ka_attn_prefill_ragged_workspace_need", "ka_attn_prefill_ragged",
@@ -108,6 +108,8 @@ def lib() -> ctypes.CDLL:
     L.ka_attn_rope_rows.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p]
     L.ka_attn_rope_rows.restype = c_int32
     L.ka_attn_prefill_workspace_bytes.argtypes = [P, c_int32]
+    L.ka_attn_prefill_workspace_need.restype = c_size_t
+    L.ka_attn_prefill_workspace_need.argtypes = [P, c_int32, c_int32]
     L.ka_attn_prefill_chunk.restype = c_int32
     L.ka_attn_prefill_chunk.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                         c_float, c_void_p, c_size_t, c_void_p]
@@ -258,6 +260,11 @@ def rope_rows(shape: Shape, x: torch.Tensor, y: torch.Tensor, rope_cos: torch.Te
 
 def prefill_workspace_bytes(shape: Shape, max_rows: int) -> int:
     return int(lib().ka_attn_prefill_workspace_bytes(ctypes.byref(shape), int(max_rows)))
+
+
+def prefill_workspace_need(shape: Shape, start_pos: int, row_count: int) -> int:
+    return int(lib().ka_attn_prefill_workspace_need(ctypes.byref(shape), int(start_pos),
+                                                    int(row_count)))
 
 
 def prefill_chunk(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

@@ -196,6 +196,14 @@ size_t ka_attn_prefill_workspace_bytes(const ka_attn_shape* s, int32_t max_rows)
   return ka::prefill_workspace_bound(sh, max_rows);
 }
 
+size_t ka_attn_prefill_workspace_need(const ka_attn_shape* s, int32_t start_pos,
+                                      int32_t row_count) {
+  ka::Shape sh;
+  if (check_shape(s, &sh) != KA_OK) return 0;
+  if (start_pos < 0 || row_count <= 0 || (long long)start_pos + row_count > sh.capacity) return 0;
+  return ka::plan_prefill(sh, start_pos, row_count).workspace_bytes;
+}
+
 ka_status ka_attn_prefill_chunk(const ka_attn_shape* s, const float* q, const void* k_cache,
                                 const void* v_cache, float* out, int32_t start_pos,
                                 int32_t row_count, float scale, void* workspace,

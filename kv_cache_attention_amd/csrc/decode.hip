@@ -478,7 +478,7 @@ struct DecTile {
   float4 sk[I8 ? 2 : 1];  // I8: scales of positions 16 kb + 4 r + 0..3
 };
 
-template <int D, bool I8>
+template <int D, bool I8, bool ROWS>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(
     const float* __restrict__ q, void* k_cache, void* v_cache, float* __restrict__ out,
     float* __restrict__ part, float* __restrict__ part_ml, const float* __restrict__ k_new,
@@ -623,6 +623,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) acc[db] = v4f{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  int nf_tile = 0;      // R > 1: the tile whose non-finite values were left out
+  uint32_t nf_pos = 0;  // and their positions in it
 
   // One tile; x is reloaded with tile t + 2 once its operands are consumed.
   // The decode step's new row (position ctx - 1, given by k_new / v_new).
@@ -831,6 +833,69 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         x.v[db].x &= keep[0]; x.v[db].y &= keep[1]; x.v[db].z &= keep[2]; x.v[db].w &= keep[3];
       }
     }
+    // Several rows (R > 1): in a tile past the first row's limit the columns
+    // share one value product in which a key past a column's limit weighs
+    // 0, and 0 * NaN or 0 * inf is NaN.  A non-finite value at such a
+    // position (ctx - R < p < ctx) is zeroed for the product; its class and
+    // the columns' weights of its position go to this wave's LDS slot (idle
+    // until the merge: no new row in this mode), and after the last tile the
+    // value reaches only the columns that see it (see class_bf16).  This
+    // lane's operand holds dim 16 db + lc of the positions of group r.  The
+    // tiles past the first limit all belong to different waves.
+    if (ROWS && R > 1 && kDecTile * t + kDecTile - 1 > ctx - R) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int p = vbf16_pos(t, r, e);
+        const bool inr = p > ctx - R && p < ctx;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+          const uint32_t wd = (e >> 1) == 0 ? x.v[db].x : (e >> 1) == 1 ? x.v[db].y
+                            : (e >> 1) == 2 ? x.v[db].z : x.v[db].w;
+          if (inr && bf16_nonfinite(wd >> (16 * (e & 1)))) bits |= 1u << (p - kDecTile * t);
+        }
+      }
+      const uint32_t nf = wave_or(bits);
+      if (nf != 0) {
+        nf_tile = t;
+        nf_pos = nf;
+        uint32_t* tab = reinterpret_cast<uint32_t*>(sacc[w]);  // [32][D / 16] classes
+        float* wtab = sacc[w] + kDecTile * (D / 16);           // [32][16] weights
+        for (int j = lane; j < kDecTile * (D / 16); j += kWave)
+          if ((nf >> (j / (D / 16))) & 1u) tab[j] = 0u;
+        wave_lds_sync();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int p = vbf16_pos(t, r, e);
+          const bool inr = p > ctx - R && p < ctx;
+          const uint32_t sh = 16 * (e & 1);
+#pragma unroll
+          for (int db = 0; db < D / 16; ++db) {
+            uint32_t wd = (e >> 1) == 0 ? x.v[db].x : (e >> 1) == 1 ? x.v[db].y
+                        : (e >> 1) == 2 ? x.v[db].z : x.v[db].w;
+            if (inr && bf16_nonfinite(wd >> sh)) {
+              atomicOr(tab + (p - kDecTile * t) * (D / 16) + db, class_bf16(wd >> sh) << (2 * lc));
+              wd &= ~(0xffffu << sh);
+              if ((e >> 1) == 0) x.v[db].x = wd;
+              else if ((e >> 1) == 1) x.v[db].y = wd;
+              else if ((e >> 1) == 2) x.v[db].z = wd;
+              else x.v[db].w = wd;
+            }
+          }
+        }
+        // weights of this lane's positions 16 kb + 4 r + i (column lc)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k = 16 * kb + 4 * r + i;
+            const uint32_t pw = pk[kb][i >> 1];
+            if ((nf >> k) & 1u)
+              wtab[k * kDecCols + lc] = __uint_as_float((i & 1) ? (pw & 0xffff0000u) : (pw << 16));
+          }
+        wave_lds_sync();
+      }
+    }
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
       acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -840,6 +905,31 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   for (int t = t0; t < t1; t += 2) {
     tile(ta_, t);
     if (t + 1 < t1) tile(tb_, t + 1);
+  }
+  // values left out of a tile's shared product (R > 1, rare): into the
+  // columns that see them; lane (lc, r) holds dims 16 db + 4 r + 0..3
+  if (ROWS && nf_pos != 0) {
+    const uint32_t* tab = reinterpret_cast<const uint32_t*>(sacc[w]);
+    const float* wtab = sacc[w] + kDecTile * (D / 16);
+    uint32_t cls[D / 64];  // dims 16 db + 4 r + i at bits 8 (db % 4) + 2 i of cls[db / 4]
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) cls[j] = 0u;
+    uint32_t m = nf_pos;
+    while (m != 0) {
+      const int k = __builtin_ctz(m);
+      m &= m - 1;
+      if (!hv || kDecTile * nf_tile + k > lim) continue;
+      const bool zero_w = wtab[k * kDecCols + lc] == 0.f;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        uint32_t byte = (tab[k * (D / 16) + db] >> (8 * r)) & 0xffu;
+        if (zero_w) byte = all_nan(byte);
+        cls[db >> 2] |= byte << (8 * (db & 3));
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) apply_classes<4>(cls[db >> 2] >> (8 * (db & 3)), acc[db], 0);
+    wave_lds_sync();  // the slot takes the accumulators next
   }
 
   // ---- merge the four waves
@@ -1008,13 +1098,13 @@ hipError_t launch_rows(const Shape& s, const DecodePlan& p, const float* q, cons
 #define KA_D(DD)                                                                               \
   case DD:                                                                                     \
     if (s.kv_dtype == kI8K)                                                                    \
-      hipLaunchKernelGGL((decode_mfma_kernel<DD, true>), mfma_grid(nb, s.num_kv_heads, HG, S), \
+      hipLaunchKernelGGL((decode_mfma_kernel<DD, true, true>), mfma_grid(nb, s.num_kv_heads, HG, S), \
                          dim3(256), 0, stream, q, kc, vc, out, part,                           \
                          part + (size_t)s.batch * s.num_kv_heads * HG * S * hpw * DD, nullptr, \
                          nullptr, k_scale_array(s, kc), ca, b0, nb, s.num_q_heads,             \
                          s.num_kv_heads, HG, hpw, s.capacity, S, sl2e, R);                     \
     else                                                                                       \
-      hipLaunchKernelGGL((decode_mfma_kernel<DD, false>), mfma_grid(nb, s.num_kv_heads, HG, S),\
+      hipLaunchKernelGGL((decode_mfma_kernel<DD, false, true>), mfma_grid(nb, s.num_kv_heads, HG, S),\
                          dim3(256), 0, stream, q, kc, vc, out, part,                           \
                          part + (size_t)s.batch * s.num_kv_heads * HG * S * hpw * DD, nullptr, \
                          nullptr, nullptr, ca, b0, nb, s.num_q_heads, s.num_kv_heads, HG, hpw, \
@@ -1056,14 +1146,14 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, vo
 #define KA_D(DD)                                                                               \
   case DD:                                                                                     \
     if (bf16)                                                                                  \
-      hipLaunchKernelGGL((decode_mfma_kernel<DD, false>), mfma_grid(nb, s.num_kv_heads, HG, S),\
+      hipLaunchKernelGGL((decode_mfma_kernel<DD, false, false>), mfma_grid(nb, s.num_kv_heads, HG, S),\
                          dim3(256), 0, stream, q, k_cache, v_cache, out, part,                 \
                          part + (size_t)s.batch * s.num_kv_heads * HG * S * p.heads_per_wg * DD, \
                          k_new, v_new, nullptr, ca, b0, nb, s.num_q_heads, s.num_kv_heads, HG, \
                          p.heads_per_wg,                                                       \
                          s.capacity, S, sl2e, 1);                                              \
     else if (i8)                                                                               \
-      hipLaunchKernelGGL((decode_mfma_kernel<DD, true>), mfma_grid(nb, s.num_kv_heads, HG, S), \
+      hipLaunchKernelGGL((decode_mfma_kernel<DD, true, false>), mfma_grid(nb, s.num_kv_heads, HG, S), \
                          dim3(256), 0, stream, q, k_cache, v_cache, out, part,                 \
                          part + (size_t)s.batch * s.num_kv_heads * HG * S * p.heads_per_wg * DD, \
                          k_new, v_new, k_scale_array(s, k_cache), ca, b0, nb,                  \

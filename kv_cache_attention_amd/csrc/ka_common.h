@@ -133,6 +133,62 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Bitwise OR across the 64 lanes of a wavefront (every lane ends with it).
+__device__ __forceinline__ uint32_t wave_or(uint32_t x) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) x |= (uint32_t)__shfl_xor((int)x, m, kWave);
+  return x;
+}
+
+// ------------------------------------------------- non-finite cache values
+// bf16 (low 16 bits of h) and f32 bit patterns whose exponent is all ones:
+// NaN or an infinity.
+__device__ __forceinline__ bool bf16_nonfinite(uint32_t h) { return (h & 0x7f80u) == 0x7f80u; }
+__device__ __forceinline__ bool f32_nonfinite(uint32_t u) {
+  return (u & 0x7f800000u) == 0x7f800000u;
+}
+
+// The V cache's value at position p, dim d of one (session, KV head) slab, as
+// f32 (plain loads: for the rare paths that add non-finite values back).
+template <bool BF16>
+__device__ __forceinline__ float v_at(const void* slab, int p, int d, int D) {
+  if constexpr (BF16) {
+    const uint16_t* s = reinterpret_cast<const uint16_t*>(slab);
+    return __uint_as_float((uint32_t)s[((size_t)vbf16_group(p) * D + d) * 8 + vbf16_slot(p)] << 16);
+  } else {
+    const float* s = reinterpret_cast<const float*>(slab);
+    return s[vf32_vec_index(p, d, D) * 4 + (p & 3)];
+  }
+}
+
+// Class codes of a non-finite cache value: 1 +inf, 2 -inf, 3 NaN.  Terms
+// w * v of such values summed into one accumulator combine by OR (+inf and
+// -inf give NaN, as does NaN with anything).  A class table of a tile holds
+// 2 bits per (position, dim): word p * D / 16 + d / 16, bits 2 (d % 16).
+__device__ __forceinline__ uint32_t class_bf16(uint32_t h) {
+  return (h & 0x7fu) != 0 ? 3u : ((h & 0x8000u) ? 2u : 1u);
+}
+__device__ __forceinline__ uint32_t class_f32(uint32_t u) {
+  return (u & 0x7fffffu) != 0 ? 3u : ((u & 0x80000000u) ? 2u : 1u);
+}
+// Widens a byte of four class codes to NaN (3) where a code is set: a zero
+// weight times an infinity is NaN.
+__device__ __forceinline__ uint32_t all_nan(uint32_t byte) {
+  return ((byte | (byte >> 1)) & 0x55u) * 3u;
+}
+
+// Adds the classes cls (2 bits per value of v: value i at bits 2 i) to the
+// accumulator values: + inf, - inf or NaN.
+template <int N, typename V>
+__device__ __forceinline__ void apply_classes(uint32_t cls, V& v, int i0) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t c = (cls >> (2 * i)) & 3u;
+    const float add = c == 1u ? INFINITY : (c == 2u ? -INFINITY : __builtin_nanf(""));
+    v[i0 + i] = c != 0u ? v[i0 + i] + add : v[i0 + i];
+  }
+}
+
 // ------------------------------------------------------- int8 K rows
 // Symmetric int8 quantisation of one row (Karume v0.8.0 release notes,
 // "Fixes": the activation-quantisation scale is amax times the f32 value of

@@ -329,6 +329,144 @@ __device__ __forceinline__ void zero_v_beyond(uint4* v_lds, int kt, int kend, in
   }
 }
 
+// Causality under non-finite values.  The columns of a tile that crosses a
+// row's causal limit share one value product, in which a key past a
+// column's limit carries weight 0 -- and 0 * NaN or 0 * inf is NaN.  So a
+// non-finite V value at a position that some column of the tile cannot see
+// must not enter the shared product: such tiles are scanned, those values
+// are zeroed for the product, and each reaches only the columns whose limit
+// reaches it, as the IEEE sum would: acc + w * v is NaN for a NaN v, for
+// +inf and -inf together and for w = 0; otherwise it is +-inf.  Positions at
+// or below lo are seen by every column of the tile; positions at or beyond
+// hi (the chunk's end) are zeroed already.  (Class codes and tables: see
+// class_bf16.)
+//
+// Any non-finite element in a 16-byte vector of the V layout.
+template <bool BF16>
+__device__ __forceinline__ bool any_nonfinite(const uint4& v) {
+  if constexpr (BF16) {
+    auto two = [](uint32_t w) { return bf16_nonfinite(w) || bf16_nonfinite(w >> 16); };
+    return two(v.x) || two(v.y) || two(v.z) || two(v.w);
+  } else {
+    return f32_nonfinite(v.x) || f32_nonfinite(v.y) || f32_nonfinite(v.z) || f32_nonfinite(v.w);
+  }
+}
+
+// Scan of the staged V tile kt, this thread's share of its 16-byte vectors:
+// the mask of tile positions (bit p - 64 kt) holding a non-finite value with
+// lo < p < hi.  With MARK it also zeroes those values in LDS and ORs their
+// classes into the table.
+template <int D, bool BF16, int NT, bool MARK>
+__device__ __forceinline__ uint64_t nonfinite_v(uint4* v_lds, int kt, int lo, int hi, int tid,
+                                                uint32_t* tab) {
+  constexpr int VVEC = PrefillCfg<D, BF16>::VVEC;
+  constexpr int NE = BF16 ? 8 : 4;
+  uint64_t bits = 0;
+#pragma unroll 1
+  for (int i = tid; i < VVEC; i += NT) {
+    const uint4 v = v_lds[i];
+    if (!any_nonfinite<BF16>(v)) continue;
+    const int gi = i / D, d = i - gi * D;
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+      int pl;
+      uint32_t x;
+      if constexpr (BF16) {
+        pl = vbf16_pos(gi >> 2, gi & 3, e);
+        x = (w[e >> 1] >> (16 * (e & 1))) & 0xffffu;
+      } else {
+        pl = gi * 4 + e;
+        x = w[e];
+      }
+      const int p = kt * kNTile + pl;
+      const bool nf = BF16 ? bf16_nonfinite(x) : f32_nonfinite(x);
+      if (nf && p > lo && p < hi) {
+        bits |= 1ull << pl;
+        if constexpr (MARK) {
+          atomicOr(tab + pl * (D / 16) + d / 16,
+                   (BF16 ? class_bf16(x) : class_f32(x)) << (2 * (d % 16)));
+          if constexpr (BF16) w[e >> 1] &= ~(0xffffu << (16 * (e & 1)));
+          else w[e] = 0u;
+        }
+      }
+    }
+    if (MARK) v_lds[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  return bits;
+}
+
+// The block's mask of such positions in tile kt (an OR over the waves
+// through nfm[2 * waves]); when it is not 0 (rare), the flagged values are
+// zeroed in LDS and their classes entered in tab (rows of flagged positions
+// cleared first).  Every thread calls this; after it returns the tile and
+// the table are visible to every wave.
+template <int D, bool BF16, int NT>
+__device__ __forceinline__ uint64_t sanitize_tile(uint4* v_lds, int kt, int lo, int hi, int tid,
+                                                  uint32_t* nfm, uint32_t* tab) {
+  constexpr int NW = NT / kWave;
+  const uint64_t bits = nonfinite_v<D, BF16, NT, false>(v_lds, kt, lo, hi, tid, tab);
+  const uint32_t b0 = wave_or((uint32_t)bits), b1 = wave_or((uint32_t)(bits >> 32));
+  const int w = tid / kWave;
+  if ((tid & (kWave - 1)) == 0) {
+    nfm[2 * w] = b0;
+    nfm[2 * w + 1] = b1;
+  }
+  __syncthreads();
+  uint64_t nf = 0;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) nf |= (uint64_t)nfm[2 * k] | ((uint64_t)nfm[2 * k + 1] << 32);
+  if (nf != 0) {
+    for (int i = tid; i < kNTile * (D / 16); i += NT)
+      if ((nf >> (i / (D / 16))) & 1) tab[i] = 0u;
+    __syncthreads();
+    nonfinite_v<D, BF16, NT, true>(v_lds, kt, lo, hi, tid, tab);
+    __syncthreads();
+  }
+  return nf;
+}
+
+// f32 kernels: the flagged values of tile kt, into the columns that see them.
+// p: the tile's weights (lane (lr, lg) holds keys 16 kb + 4 lg + i of its
+// columns), acc_o: dims 16 db + 4 lg + 0..3.
+template <int D>
+__device__ __forceinline__ void add_nonfinite_f32(uint64_t nf, int kt, const Tiling& t, int start,
+                                                  const v4f (&p)[4][2], const uint32_t* tab,
+                                                  v4f (&acc_o)[D / 16][2]) {
+  // [mb][db / 4]: dims 16 db + 4 lg + 0..3 at bits 8 (db % 4) .., 2 bits each
+  uint32_t cls[2][D / 64];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) cls[mb][j] = 0u;
+  while (nf != 0) {
+    const int pl = __builtin_ctzll(nf);
+    nf &= nf - 1;
+    const int key = kt * kNTile + pl;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      float sel = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sel = (kb == (pl >> 4) && i == (pl & 3)) ? p[kb][mb][i] : sel;
+      const float wgt = __shfl(sel, t.lr + 16 * ((pl >> 2) & 3), kWave);
+      if (!t.valid_col[mb] || key > start + t.row_col[mb]) continue;
+#pragma unroll
+      for (int db = 0; db < D / 16; ++db) {
+        uint32_t byte = (tab[pl * (D / 16) + db] >> (8 * t.lg)) & 0xffu;
+        if (wgt == 0.f) byte = all_nan(byte);
+        cls[mb][db >> 2] |= byte << (8 * (db & 3));
+      }
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+      apply_classes<4>(cls[mb][db >> 2] >> (8 * (db & 3)), acc_o[db][mb], 0);
+}
+
 // Epilogue: normalised output (one split) or the split's partial.
 template <int D>
 __device__ __forceinline__ void store_result(const Tiling& t, float* __restrict__ out,
@@ -491,6 +629,8 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char kb1[TB];
   __shared__ __attribute__((aligned(16))) unsigned char vb0[TB];
   __shared__ __attribute__((aligned(16))) unsigned char vb1[TB];
+  __shared__ uint32_t nfm[8];                  // non-finite value masks, [wave][2]
+  __shared__ uint32_t nf_tab[kNTile * D / 16];  // and their classes
 
   Tiling t;
   if (!make_tiling(ca, Hq, Hkv, t)) return;
@@ -536,6 +676,12 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
       zero_v_beyond<D, false>(reinterpret_cast<uint4*>(v_cur), kt, t.kend, t.tid);
       __syncthreads();
     }
+    // a tile crossing a row's limit: non-finite values only where seen
+    const bool cross = kt * kNTile + kNTile - 1 > start + t.row_lo;
+    uint64_t nf = 0;
+    if (cross)
+      nf = sanitize_tile<D, false, 256>(reinterpret_cast<uint4*>(v_cur), kt, start + t.row_lo,
+                                        t.kend, t.tid, nfm, nf_tab);
     // The next tile's score MFMAs and this tile's softmax are independent
     // and run interleaved (the last step computes one spare tile of scores
     // from a stale buffer, which is never used).
@@ -544,6 +690,7 @@ __global__ __launch_bounds__(256) void prefill_pipe_kernel(
                                  start, sl2e, m_run, l_run, alpha);
     rescale_acc<NDB>(alpha, acc_o);
     pv_tile<D>(reinterpret_cast<const uint4*>(v_cur), cur, acc_o, t.lr, t.lg);
+    if (nf != 0) add_nonfinite_f32<D>(nf, kt, t, start, cur, nf_tab, acc_o);
   };
   for (int i = 0; i < n; i += 2) {
     step(std::integral_constant<int, 0>(), i, sa, sb);
@@ -943,6 +1090,42 @@ __device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
   if constexpr (I8) scale_scores<D>(nxt, k_lds, kh, c, sq);
 }
 
+// 8-wave kernel: the flagged values of tile kt (see sanitize_tile), into the
+// columns that see them.  xw: the tile's bf16 weights in exchange buffer 0
+// (written by every wave; see fused_step_b for the slots), acc: dims
+// kh D/2 + 32 db + 8 a + 4 h + 0..3 of the lane's column.
+template <int D>
+__device__ __forceinline__ void add_nonfinite_b(uint64_t nf, int kt, const uint4* __restrict__ xw,
+                                                const uint32_t* __restrict__ tab, int cb, int kh,
+                                                const ColB& c, v16f (&acc)[D / 64]) {
+  uint32_t cls[D / 64];  // [db]: dims 32 db + 8 a + 4 h + e of this half at bits 2 (4 a + e)
+#pragma unroll
+  for (int db = 0; db < D / 64; ++db) cls[db] = 0u;
+  while (nf != 0) {
+    const int pl = __builtin_ctzll(nf);
+    nf &= nf - 1;
+    if (!c.valid || kt * kNTile + pl > c.lim) continue;
+    // key pl of the tile: wave cb + 4 (pl / 32) holds it, in register 4 a + e
+    // (k = pl % 32 = 8 a + 4 h + e) of lane lc + 32 h
+    const int k = pl & 31;
+    const uint4 wq = xw[xp_slot(0, cb + 4 * (pl >> 5), k >> 4, c.lc + 32 * ((k >> 2) & 1))];
+    const int el = 4 * ((k >> 3) & 1) + (k & 3);
+    const uint32_t word = (el >> 1) == 0 ? wq.x : (el >> 1) == 1 ? wq.y : (el >> 1) == 2 ? wq.z : wq.w;
+    const bool zero_w = ((word >> (16 * (el & 1))) & 0x7fffu) == 0u;
+#pragma unroll
+    for (int db = 0; db < D / 64; ++db)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d0 = kh * (D / 2) + 32 * db + 8 * a + 4 * c.lh;
+        uint32_t byte = (tab[pl * (D / 16) + d0 / 16] >> (2 * (d0 % 16))) & 0xffu;
+        if (zero_w) byte = all_nan(byte);
+        cls[db] |= byte << (8 * a);
+      }
+  }
+#pragma unroll
+  for (int db = 0; db < D / 64; ++db) apply_classes<16>(cls[db], acc[db], 0);
+}
+
 // Stores the workgroup's 128 columns: the normalised output (one split) or
 // the split's partial.  Partials: acc [tile][S][128 columns][D] as binary16,
 // each lane's D / 4 values scaled by 2^-e so that the largest finite one lies
@@ -1067,7 +1250,9 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
   const TileSrc ssrc = tile_src(I8 ? k_scales + slab_i * C : nullptr, I8 ? (size_t)C * 4 : 0);
   const TileSrc vsrc = tile_src(reinterpret_cast<const unsigned char*>(v_cache) + slab_i * C * D * 2,
                                 (size_t)C * D * 2);
+  const unsigned char* v_slab_b = reinterpret_cast<const unsigned char*>(v_cache) + slab_i * C * D * 2;
   const int n = t.kt1 - t.kt0;
+  const int vis_all = start + t.row_lo;  // positions every column of the tile sees
 
   typename Cfg::QOp qreg[Cfg::NQS];
   float sq = 0.f;  // I8: s_q * scale * log2 e of this lane's column
@@ -1096,7 +1281,10 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
   bf16x8 pw[2], pc[2], po[2];
   bool redo = false;
 
-  // Pipelined pass in the frame of the first tile (see above).
+  // Pipelined pass in the frame of the first tile (see above).  A
+  // non-finite V value that some column of a crossing tile cannot see (vbad)
+  // also sends the range to the redo pass, which leaves it out of the shared
+  // product (see nonfinite_v).
   if (n > 0) {
     bool ovf = false;
     wait_vmem();
@@ -1180,13 +1368,27 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
       zero_v_beyond<D, true, NT>(reinterpret_cast<uint4*>(v_last), kt, t.kend, t.tid);
       __syncthreads();
     }
+    // Crossing tiles are the last of the range: V(n-1) and V(n-2) are still
+    // in LDS; an older one (an M-tile of more than 64 rows) is read again
+    // from the cache.
+    bool vbad = false;
+    if (kt * kNTile + kNTile - 1 > vis_all)
+      vbad = nonfinite_v<D, true, NT, false>(reinterpret_cast<uint4*>(v_last), kt, vis_all, t.kend,
+                                             t.tid, nullptr) != 0;
+    if (n > 1 && (kt - 1) * kNTile + kNTile - 1 > vis_all)
+      vbad = vbad || nonfinite_v<D, true, NT, false>(reinterpret_cast<uint4*>(pl ? vb0 : vb1),
+                                                     kt - 1, vis_all, t.kend, t.tid, nullptr) != 0;
+    for (int k2 = kt - 2; k2 >= t.kt0 && k2 * kNTile + kNTile - 1 > vis_all; --k2)
+      vbad = vbad || nonfinite_v<D, true, NT, false>(
+                         const_cast<uint4*>(reinterpret_cast<const uint4*>(v_slab_b) + (size_t)k2 * (VTB / 16)),
+                         k2, vis_all, t.kend, t.tid, nullptr) != 0;
     const uint4* vl = reinterpret_cast<const uint4*>(v_last);
 #pragma unroll
     for (int j = 0; j < D / 16; ++j) pv_chunk_b<D>(j, vl[pv_op_b<D>(j, kh, c.lc, c.lh)], pw, po, acc);
     // votes, largest scores and sums, in exchange buffer 1 - pl (free since
     // the barrier above)
     const int px = 1 - pl;
-    *xf(px, t.w, 1) = __any(ovf) ? 1.f : 0.f;
+    *xf(px, t.w, 1) = __any(ovf || vbad) ? 1.f : 0.f;
     *xf(px, t.w, 2) = m_all;
     *xf(px, t.w, 3) = l_run;
     __syncthreads();
@@ -1196,9 +1398,16 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
     if (redo) m_ref = fmaxf(m_all, *xf(px, partner, 2));
   }
 
-  // Rare: a score left the frame.  The range is redone, tile by tile without
-  // pipelining, in the frame of its largest score.
+  // Rare: a score left the frame, or a crossing tile holds a non-finite
+  // value that some of its columns cannot see.  The range is redone, tile by
+  // tile without pipelining, in the frame of its largest score, and such
+  // values are left out of the shared product and added back where seen.
   if (redo) {
+    // exchange buffer 1 (free until the sums below): the masks, then the
+    // class table of a flagged tile (kNTile D / 4 bytes)
+    uint32_t* const nfm = reinterpret_cast<uint32_t*>(xp + xp_slot(1, 0, 0, 0));
+    uint32_t* const nf_tab = nfm + 64;
+    static_assert(256 + kNTile * D / 4 <= 16384, "class table fits exchange buffer 1");
     l_run = 0.f;
 #pragma unroll
     for (int db = 0; db < D / 64; ++db)
@@ -1218,6 +1427,9 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
         zero_v_beyond<D, true, NT>(vl, kt, t.kend, t.tid);
         __syncthreads();
       }
+      uint64_t nf = 0;
+      if (kt * kNTile + kNTile - 1 > vis_all)
+        nf = sanitize_tile<D, true, NT>(vl, kt, vis_all, t.kend, t.tid, nfm, nf_tab);
       v16f s;
       qk_tile_b<D, I8>(kl, qreg, s, kh, c, sq);
       if (kt * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(s, kt * kNTile + 32 * kh, c);
@@ -1242,6 +1454,7 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
         po[s2] = __builtin_bit_cast(bf16x8, xp[xp_slot(0, partner, s2, t.lane)]);
 #pragma unroll
       for (int j = 0; j < D / 16; ++j) pv_chunk_b<D>(j, vl[pv_op_b<D>(j, kh, c.lc, c.lh)], pw, po, acc);
+      if (nf != 0) add_nonfinite_b<D>(nf, kt, xp, nf_tab, t.w & 3, kh, c, acc);
     }
     __syncthreads();
     *xf(1, t.w, 3) = l_run;
@@ -1267,6 +1480,8 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
   constexpr int NDB = Cfg::NDB, TB = Cfg::TILE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char kb[TB];
   __shared__ __attribute__((aligned(16))) unsigned char vb[TB];
+  __shared__ uint32_t nfm[8];                  // non-finite value masks, [wave][2]
+  __shared__ uint32_t nf_tab[kNTile * D / 16];  // and their classes
 
   Tiling t;
   if (!make_tiling(ca, Hq, Hkv, t)) return;
@@ -1295,11 +1510,16 @@ __global__ __launch_bounds__(256) void prefill_seq_kernel(
       zero_v_beyond<D, false>(reinterpret_cast<uint4*>(vb), kt, t.kend, t.tid);
       __syncthreads();
     }
+    uint64_t nf = 0;
+    if (kt * kNTile + kNTile - 1 > start + t.row_lo)  // crosses a row's limit
+      nf = sanitize_tile<D, false, 256>(reinterpret_cast<uint4*>(vb), kt, start + t.row_lo,
+                                        t.kend, t.tid, nfm, nf_tab);
     qk_tile<D>(reinterpret_cast<const uint4*>(kb), qreg, sacc, t.lr, t.lg);
     float alpha[2];
     softmax_tile(t, kt, start, sl2e, sacc, m_run, l_run, alpha);
     rescale_acc<NDB>(alpha, acc_o);
     pv_tile<D>(reinterpret_cast<const uint4*>(vb), sacc, acc_o, t.lr, t.lg);
+    if (nf != 0) add_nonfinite_f32<D>(nf, kt, t, start, sacc, nf_tab, acc_o);
   }
   store_result<D>(t, out, part, part_ml, acc_o, m_run, l_run, R, Hq, Hkv, m_tiles, S);
 }

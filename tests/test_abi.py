@@ -146,11 +146,15 @@ def test_prefill_argument_errors():
     assert _prefill(s, 0, 1, q=None) == 1
     assert _prefill(s, 0, 1, out=FAKE) == 1      # out aliases q
     assert _prefill(s, 0, 0) == 0                # empty chunk is a no-op
-    # a long chunk needs a workspace; a missing or short one is rejected
-    need = ka.prefill_workspace_bytes(s, 768)
-    assert need > 0
+    # a long chunk needs a workspace; a missing or short one is rejected.  The
+    # exact need of this call gates the fake-pointer calls: with none needed
+    # they would pass validation and enqueue kernels on fake addresses.
+    need = ka.prefill_workspace_need(s, 3000, 768)
+    assert 0 < need <= ka.prefill_workspace_bytes(s, 768)
     assert _prefill(s, 3000, 768) == 4
-    assert _prefill(s, 3000, 768, ws=FAKE, ws_bytes=16) == 4
+    assert _prefill(s, 3000, 768, ws=FAKE, ws_bytes=need - 1) == 4
+    assert ka.prefill_workspace_need(s, 3000, 0) == 0
+    assert ka.prefill_workspace_need(s, 4000, 97) == 0       # past the capacity
 
 
 def test_decode_argument_errors():
@@ -225,12 +229,13 @@ def test_ragged_argument_errors():
     assert pre([0, 0, 0], [1, 1, 1], out=FAKE) == 1   # out aliases q
     assert L.ka_attn_prefill_ragged(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.c_void_p(0x2000),
                                     None, _i32([1, 1, 1]), 0.1, None, 0, None) == 1
-    # long chunks need a workspace: the bound for their total covers them
+    # long chunks need a workspace: the exact need of this call (which the
+    # bound for their total covers) gates the fake-pointer calls
     starts, rows = [3000, 0, 1000], [768, 0, 500]
-    need = ka.prefill_ragged_workspace_bytes(s, sum(rows))
-    assert need > 0
+    need = ka.prefill_ragged_workspace_need(s, starts, rows)
+    assert 0 < need <= ka.prefill_ragged_workspace_bytes(s, sum(rows))
     assert pre(starts, rows) == 4
-    assert pre(starts, rows, ws=FAKE, ws_bytes=16) == 4
+    assert pre(starts, rows, ws=FAKE, ws_bytes=need - 1) == 4
     assert app([0, 0, 0], [1, 0, -1]) == 1
     assert app([0, 4090, 0], [1, 7, 1]) == 2
     assert app([0, 0, 0], [1, 1, 1], cos=FAKE) == 1   # only one rotary table
