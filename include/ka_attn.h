@@ -263,6 +263,32 @@ ka_status ka_attn_decode_step(const ka_attn_shape* s, const float* q, const floa
                               size_t workspace_bytes, void* stream);
 
 /*
+ * The decode step without any allocation and without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc.  Same
+ * arguments, result and errors as ka_attn_decode_step, minus the workspace.
+ *
+ * The split partials live in a scratch array inside the library, one per
+ * device (the current device at the call; stream must belong to it), of
+ * ka_attn_decode_step_noalloc_max_bytes() bytes (8 MiB), held until the
+ * process ends.  Its address on a device is looked up once, at the first
+ * call on that device.  A call whose partials would not fit (only f32 caches
+ * with several hundred (session, KV head) slabs) returns KA_ERR_WORKSPACE
+ * before anything is enqueued.  The call allocates nothing and needs nothing
+ * cleared: every partial it reads was written by the same call.  Every call
+ * on one device shares that device's array: calls that may overlap in time
+ * on one device (different streams without ordering between them) race and
+ * must not be issued.  int8-K caches: the device self-test runs at the first
+ * int8 call on a device (it copies its result to the host), so run
+ * ka_attn_int8_self_test once before capturing such calls into a graph.
+ */
+size_t ka_attn_decode_step_noalloc_max_bytes(void);
+ka_status ka_attn_decode_step_noalloc(const ka_attn_shape* s, const float* q,
+                                      const float* k_new, const float* v_new, void* k_cache,
+                                      void* v_cache, float* out, const int32_t* pos, float scale,
+                                      void* stream);
+
+/*
  * Ragged batches: sessions at different positions in one call (several
  * conversations served together, each continuing its own KV cache across
  * turns; Karume v0.8.0 release notes, "Features": the multi-turn chat session

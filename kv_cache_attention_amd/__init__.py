@@ -22,7 +22,8 @@ __all__ = ["Shape", "KaAttnError", "KaAttnUnavailable", "lib", "lib_path", "F32"
            "last_error", "abi_version", "EXPORTED_SYMBOLS", "decode_step", "append_kv_rope",
            "rope_rows", "append_kv_ragged", "prefill_ragged_workspace_bytes",
            "prefill_ragged_workspace_need", "prefill_ragged",
-           "Memory", "session_memory", "cache_resize", "I8K", "int8_self_test"]
+           "Memory", "session_memory", "cache_resize", "I8K", "int8_self_test",
+           "decode_step_noalloc", "decode_step_noalloc_max_bytes"]
 
 F32 = 0
 BF16 = 1
@@ -36,6 +37,7 @@ EXPORTED_SYMBOLS = (
     "ka_attn_rope_rows",
     "ka_attn_prefill_workspace_bytes", "ka_attn_prefill_workspace_need", "ka_attn_prefill_chunk",
     "ka_attn_decode_workspace_bytes", "ka_attn_decode", "ka_attn_decode_step",
+    "ka_attn_decode_step_noalloc", "ka_attn_decode_step_noalloc_max_bytes",
     "ka_attn_append_kv_ragged", "ka_attn_prefill_ragged_workspace_bytes",
     "ka_attn_prefill_ragged_workspace_need", "ka_attn_prefill_ragged",
     "ka_attn_session_memory", "ka_attn_cache_resize", "ka_attn_int8_self_test",
@@ -122,6 +124,12 @@ def lib() -> ctypes.CDLL:
     L.ka_attn_decode_step.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, ctypes.POINTER(c_int32), ctypes.c_float,
                                       c_void_p, c_size_t, c_void_p]
+    L.ka_attn_decode_step_noalloc.restype = c_int32
+    L.ka_attn_decode_step_noalloc.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_void_p, ctypes.POINTER(c_int32), ctypes.c_float,
+                                              c_void_p]
+    L.ka_attn_decode_step_noalloc_max_bytes.restype = c_size_t
+    L.ka_attn_decode_step_noalloc_max_bytes.argtypes = []
     I32P = ctypes.POINTER(c_int32)
     L.ka_attn_append_kv_ragged.restype = c_int32
     L.ka_attn_append_kv_ragged.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -326,6 +334,29 @@ def decode_step(shape: Shape, q: torch.Tensor, k_new: torch.Tensor, v_new: torch
     _check(lib().ka_attn_decode_step(ctypes.byref(shape), _ptr(q), _ptr(k_new), _ptr(v_new),
                                      _ptr(k_cache), _ptr(v_cache), _ptr(out), arr, float(scale),
                                      _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def decode_step_noalloc_max_bytes() -> int:
+    return int(lib().ka_attn_decode_step_noalloc_max_bytes())
+
+
+def decode_step_noalloc(shape: Shape, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                        k_cache: torch.Tensor, v_cache: torch.Tensor, out: torch.Tensor,
+                        pos: Sequence[int], scale: float, stream=None) -> None:
+    """decode_step without a workspace (ka_attn_decode_step_noalloc): the
+    partials go to the library's own per-device scratch array."""
+    n = shape.batch * shape.num_q_heads * shape.head_dim
+    nk = shape.batch * shape.num_kv_heads * shape.head_dim
+    _need(q, "q", torch.float32, n)
+    _need(out, "out", torch.float32, n)
+    _need(k_new, "k_new", torch.float32, nk)
+    _need(v_new, "v_new", torch.float32, nk)
+    if len(pos) != shape.batch:
+        raise ValueError(f"pos has {len(pos)} entries, expected {shape.batch}")
+    arr = (ctypes.c_int32 * shape.batch)(*[int(p) for p in pos])
+    _check(lib().ka_attn_decode_step_noalloc(ctypes.byref(shape), _ptr(q), _ptr(k_new),
+                                             _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                             arr, float(scale), _stream(stream)))
 
 
 def _int32_array(xs: Sequence[int], n: int, name: str):

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "ka_attn.h"
@@ -98,6 +99,35 @@ ka_status check_int8(const ka::Shape& sh) {
   const hipError_t e = ka::int8_self_test(&passed, &why);
   if (e != hipSuccess) return hip_fail(e, "int8 self-test");
   if (!passed) return fail(KA_ERR_UNSUPPORTED, "%s", why);
+  return KA_OK;
+}
+
+// Scratch of the allocation-free decode step: the split partials live in this
+// file-scope device array instead of a caller's workspace.  Each device that
+// runs the library holds its own copy until the process ends; in host code
+// the name stands for no device address, so its address on a device is taken
+// once (hipGetSymbolAddress, with that device current) and kept per device.
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+ka_status scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
   return KA_OK;
 }
 
@@ -430,6 +460,39 @@ ka_status ka_attn_decode_step(const ka_attn_shape* s, const float* q, const floa
                                    workspace, reinterpret_cast<hipStream_t>(stream), k_new, v_new);
   if (e != hipSuccess) return hip_fail(e, "decode step launch");
   return ok();
+}
+
+size_t ka_attn_decode_step_noalloc_max_bytes(void) { return kScratchBytes; }
+
+ka_status ka_attn_decode_step_noalloc(const ka_attn_shape* s, const float* q, const float* k_new,
+                                      const float* v_new, void* k_cache, void* v_cache,
+                                      float* out, const int32_t* pos, float scale, void* stream) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  if (!pos) return fail(KA_ERR_INVALID_ARGUMENT, "pos is NULL");
+  int max_ctx = 0;
+  for (int b = 0; b < sh.batch; ++b) {
+    if (pos[b] < 0 || pos[b] >= sh.capacity)
+      return fail(KA_ERR_OUT_OF_RANGE, "pos[%d] = %d outside 0..capacity-1 (%d)", b, pos[b],
+                  sh.capacity - 1);
+    if (pos[b] + 1 > max_ctx) max_ctx = pos[b] + 1;
+  }
+  if ((st = check_scale(scale)) != KA_OK) return st;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if ((const void*)q == (const void*)out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "out must not alias q");
+  const size_t need = ka::plan_decode(sh, max_ctx).workspace_bytes;
+  if (need > kScratchBytes)
+    return fail(KA_ERR_WORKSPACE,
+                "decode step needs %zu scratch bytes, more than the %zu the allocation-free "
+                "variant holds; use ka_attn_decode_step with a workspace",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_of_current_device(&ws)) != KA_OK) return st;
+  return ka_attn_decode_step(s, q, k_new, v_new, k_cache, v_cache, out, pos, scale, ws, need,
+                             stream);
 }
 
 const char* ka_attn_status_string(int32_t status) {

@@ -357,3 +357,27 @@ def test_int8_k_layout_reader():
     codes, scales = unpack_k_i8(raw, B, Hkv, C, D)
     assert np.array_equal(codes, want_c)
     assert np.array_equal(scales.reshape(-1), sc)
+
+
+def test_noalloc_decode_step_validation():
+    """The allocation-free decode step validates as the decode step does, and
+    rejects partials beyond its scratch (f32 caches with 511 slabs split
+    into 1022 partials of 8 heads), all before anything is enqueued."""
+    _lib_or_skip()
+    L = ka.lib()
+    out = ctypes.c_void_p(0x2000)
+
+    def call(s, pos, scale=0.1, q=FAKE, o=out):
+        arr = (ctypes.c_int32 * len(pos))(*pos)
+        return L.ka_attn_decode_step_noalloc(ctypes.byref(s), q, FAKE, FAKE, FAKE, FAKE, o, arr,
+                                             ctypes.c_float(scale), None)
+    s = S(batch=2)
+    assert call(s, [0, 4096]) == 2
+    assert call(s, [5, 5], scale=float("nan")) == 1
+    assert call(s, [5, 5], q=None) == 1
+    assert call(s, [5, 5], o=FAKE) == 1            # out aliases q
+    assert call(S(head_dim=96), [5]) == 3
+    big = S(batch=511, kv_dtype=ka.F32)
+    assert ka.decode_workspace_bytes(big, 4096) > ka.decode_step_noalloc_max_bytes()
+    assert call(big, [4095] * 511) == 4 and "scratch" in ka.last_error()
+    assert ka.decode_step_noalloc_max_bytes() == 8 << 20
