@@ -17,8 +17,12 @@ timed on a bounded sample of the same workload.
 
 GPU times come from HIP events recorded on the stream the library launches
 on.  While the host enqueues a timed phase the GPU is held by a short spin
-kernel (recorded before the phase's first event), so per-call times measure
-the GPU, not Python's call overhead.
+kernel (recorded before the phase's first event), so the events time the
+GPU, not Python's call overhead.  A timed phase carries events at its two
+ends only: an event recorded between two calls stalls the queue (about 5 us
+on this GPU), so per-call figures come from separate runs of the same call
+repeated back to back, as (time of 2n calls - time of n calls) / n, which
+cancels the fixed cost of the bracketing events.
 """
 from __future__ import annotations
 
@@ -154,80 +158,109 @@ class Session16K:
         for t, p in enumerate(w.decode_positions):
             self.dec_views.append((p, self.k[:, p:p + 1], self.v[:, p:p + 1], self.q[0, qrow + t]))
 
-    def prefill_phase(self, ev=None):
+    def prefill_phase(self):
+        """22 chunk calls, each an append of the chunk's rows and a prefill."""
         sh = self.shape
-        for i, (s, R, kk, vv, qq, oo) in enumerate(self.chunk_views):
+        for s, R, kk, vv, qq, oo in self.chunk_views:
             ka.append_kv(sh, self.kc, self.vc, kk, vv, s, R)
-            if ev is not None:
-                ev[i][0].record()
             ka.prefill_chunk(sh, qq, self.kc, self.vc, oo, s, R, self.w.scale, self.ws)
-            if ev is not None:
-                ev[i][1].record()
 
-    def decode_phase(self, ev=None):
+    def decode_phase(self):
         """64 decode steps, each one ka_attn_decode_step (append + attend)."""
         sh = self.shape
-        for i, (p, kk, vv, qq) in enumerate(self.dec_views):
-            if ev is not None:
-                ev[i][0].record()
+        for p, kk, vv, qq in self.dec_views:
             ka.decode_step(sh, qq, kk, vv, self.kc, self.vc, self.out_d, [p], self.w.scale, self.ws)
-            if ev is not None:
-                ev[i][1].record()
 
 
 def ev_pair():
     return (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
 
 
+def span_ms(f, n, hold, hold_ms=2.0):
+    """GPU time of n back-to-back calls f(i), events at the two ends only.
+    The spin kernel before the first event must outlast the host's enqueue
+    of the n calls, or the GPU would wait for the host."""
+    a, b = ev_pair()
+    hold(hold_ms)
+    a.record()
+    for i in range(n):
+        f(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
+
+
+def per_call_ms(f, hold, n=8, reps=5):
+    """Per-call GPU time of f, back to back: median over reps of
+    (span of 2n calls - span of n calls) / n."""
+    f(0)
+    torch.cuda.synchronize()
+    hold_ms = 1.0 + 0.15 * 2 * n
+    ts = []
+    for _ in range(reps):
+        t1 = span_ms(f, n, hold, hold_ms)
+        t2 = span_ms(f, 2 * n, hold, hold_ms)
+        ts.append((t2 - t1) / n)
+    return float(np.median(ts))
+
+
 def bench_session(steps, warmup, hold):
+    """The timed steps: the 22 chunk calls and the 64 decode steps, each phase
+    back to back with events at its two ends.  Then, untimed for the step,
+    each chunk's prefill call and the last decode step alone (per_call_ms)."""
     s = Session16K()
     log("16K session: inputs resident")
     for _ in range(warmup):
         s.prefill_phase()
         s.decode_phase()
     torch.cuda.synchronize()
-    nch, ndec = len(s.chunk_views), len(s.dec_views)
     rec = []
     t0 = time.perf_counter()
     for _ in range(steps):
-        pe = [ev_pair() for _ in range(nch)]
-        de = [ev_pair() for _ in range(ndec)]
         ph, dh = ev_pair(), ev_pair()
-        hold(3.0)
+        hold(6.0)
         ph[0].record()
-        s.prefill_phase(pe)
+        s.prefill_phase()
         ph[1].record()
-        hold(8.0)
+        hold(10.0)
         dh[0].record()
-        s.decode_phase(de)
+        s.decode_phase()
         dh[1].record()
-        rec.append((ph, dh, pe, de))
+        rec.append((ph, dh))
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     phase_p = [r[0][0].elapsed_time(r[0][1]) for r in rec]
     phase_d = [r[1][0].elapsed_time(r[1][1]) for r in rec]
-    pre_calls = np.array([[a.elapsed_time(b) for a, b in r[2]] for r in rec])     # [steps][22]
-    dec_calls = np.array([[a.elapsed_time(b) for a, b in r[3]] for r in rec])     # [steps][64]
-    return dict(w=s.w, wall_ms=wall * 1e3, prefill_phase_ms=float(np.mean(phase_p)),
-                decode_phase_ms=float(np.mean(phase_d)), prefill_calls_ms=pre_calls,
-                decode_calls_ms=dec_calls, session=s)
+    log("16K session: timed steps done")
+    sh = s.shape
+    pre_calls = []
+    for (st, R, kk, vv, qq, oo) in s.chunk_views:
+        pre_calls.append(per_call_ms(
+            lambda i: ka.prefill_chunk(sh, qq, s.kc, s.vc, oo, st, R, s.w.scale, s.ws), hold, n=6, reps=3))
+    p, kk, vv, qq = s.dec_views[-1]
+    dec_call = per_call_ms(
+        lambda i: ka.decode_step(sh, qq, kk, vv, s.kc, s.vc, s.out_d, [p], s.w.scale, s.ws), hold, n=16)
+    return dict(w=s.w, wall_ms=wall * 1e3, prefill_phase_ms=float(np.median(phase_p)),
+                decode_phase_ms=float(np.median(phase_d)), prefill_calls_ms=np.array(pre_calls),
+                decode_call_ms=dec_call, session=s)
 
 
 def bench_decode_cold_16k(s, hold, copies=64, reps=3):
-    """Decode at 16K over `copies` caches in rotation (more bytes than the MALL)."""
+    """The decode step at 16K over `copies` caches in rotation (more bytes
+    than the MALL), back to back: GPU time per step."""
     w = s.w
     p = w.decode_positions[-1]
     kcs = [s.kc.clone() for _ in range(copies)]
     vcs = [s.vc.clone() for _ in range(copies)]
-    qq = s.dec_views[-1][3]
+    _, kk, vv, qq = s.dec_views[-1]
     torch.cuda.synchronize()
     times = []
     for r in range(reps + 1):
         a, b = ev_pair()
-        hold(3.0)
+        hold(10.0)
         a.record()
         for i in range(copies):
-            ka.decode(s.shape, qq, kcs[i], vcs[i], s.out_d, [p + 1], w.scale, s.ws)
+            ka.decode_step(s.shape, qq, kk, vv, kcs[i], vcs[i], s.out_d, [p], w.scale, s.ws)
         b.record()
         torch.cuda.synchronize()
         if r:
@@ -282,37 +315,27 @@ def bench_decode_128k(hold, steps=32, kv_dtype="bf16"):
     del c
     log("128K: filled")
 
-    def run(ev):
-        for t, p in enumerate(w.decode_positions[:steps]):
-            if ev is not None:
-                ev[t][0].record()
-            ka.decode_step(shape, qd[t], kd[t], vd[t], kc, vc, out, [p] * w.batch, w.scale, ws)
-            if ev is not None:
-                ev[t][1].record()
+    def step(t):
+        p = w.decode_positions[t % steps]
+        ka.decode_step(shape, qd[t % steps], kd[t % steps], vd[t % steps], kc, vc, out,
+                       [p] * w.batch, w.scale, ws)
 
-    run(None)
+    step(0)
     torch.cuda.synchronize()
-    reps = []
-    step_ms = []
-    for _ in range(3):
-        ev = [ev_pair() for _ in range(steps)]
-        a, b = ev_pair()
-        hold(5.0)
-        a.record()
-        run(ev)
-        b.record()
-        torch.cuda.synchronize()
-        reps.append([x.elapsed_time(y) for x, y in ev])
-        step_ms.append(a.elapsed_time(b) / steps)
-    dec = np.array(reps)
+    # the 32 steps back to back, events at the ends
+    step_ms = [span_ms(step, steps, hold, 6.0) / steps for _ in range(5)]
+    # one step alone: the last one (context 131072), repeated (it re-appends
+    # the same row, so every repeat does the same work)
+    last = lambda i: step(steps - 1)
+    call_ms = per_call_ms(last, hold, n=8)
     ctx_mean = int(np.mean([p + 1 for p in w.decode_positions[:steps]]))
-    return dict(w=w, decode_ms=float(np.median(dec)), step_ms=float(np.median(step_ms)),
+    return dict(w=w, step_ms=float(np.median(step_ms)), call_ms=call_ms,
                 bytes=decode_bytes(w, ctx_mean, w.batch, kv_dtype), ctx_mean=ctx_mean)
 
 
 def bench_prefill_f32(hold, reps=10):
     """The f32 chunk workload: a 768-row chunk at 3072 over 3072 cached rows
-    (8 query heads / 1 KV head, head_dim 256, f32 cache); median of reps."""
+    (8 query heads / 1 KV head, head_dim 256, f32 cache): per-call time."""
     w = WORKLOADS[3]
     c = draw_batch(w)
     shape = ka.Shape(1, 8, 1, 256, w.capacity, "f32")
@@ -324,27 +347,48 @@ def bench_prefill_f32(hold, reps=10):
     out = torch.empty(R * 8 * 256, device="cuda")
     ws = torch.empty(max(ka.prefill_workspace_bytes(shape, R), 1), dtype=torch.uint8, device="cuda")
     del c
-    ka.prefill_chunk(shape, q, kc, vc, out, s0, R, w.scale, ws)
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(reps):
-        a, b = ev_pair()
-        hold(0.5)
-        a.record()
-        ka.prefill_chunk(shape, q, kc, vc, out, s0, R, w.scale, ws)
-        b.record()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    ms = float(np.median(times))
+    ms = per_call_ms(lambda i: ka.prefill_chunk(shape, q, kc, vc, out, s0, R, w.scale, ws), hold,
+                     n=6, reps=reps)
     pairs = R * s0 + R * (R + 1) // 2
     flops = pairs * 8 * 256 * 4
     return dict(ms=ms, rows=R, flops=flops)
 
 
+def bench_decode_f32_4k(hold, copies=64):
+    """The f32 decode workload: 8 query heads on one KV head, head_dim 256,
+    4096 cached rows; each step appends row 4096 and attends to 4097 keys
+    (ka_attn_decode_step on an f32 cache).  Warm: one cache, the step
+    repeated (8.4 MB of K/V, resident in the 256 MB MALL); cold: `copies`
+    caches in rotation (545 MB), back to back."""
+    w = WORKLOADS[2]
+    c = draw_batch(w)
+    shape = ka.Shape(1, 8, 1, 256, w.capacity, "f32")
+    kc = ka.alloc_cache(shape, fill_byte=0xFF)
+    vc = ka.alloc_cache(shape, fill_byte=0xFF)
+    ka.append_kv(shape, kc, vc, dev(c.k[:, :w.fill_rows]), dev(c.v[:, :w.fill_rows]), 0, w.fill_rows)
+    p = w.decode_positions[0]
+    kn, vn, q = dev(c.k[:, p]), dev(c.v[:, p]), dev(c.q[:, 0])
+    out = torch.empty(8 * 256, device="cuda")
+    ws = torch.empty(max(ka.decode_workspace_bytes(shape, p + 1), 1), dtype=torch.uint8, device="cuda")
+    del c
+    warm = per_call_ms(lambda i: ka.decode_step(shape, q, kn, vn, kc, vc, out, [p], w.scale, ws), hold,
+                       n=16)
+    kcs = [kc.clone() for _ in range(copies)]
+    vcs = [vc.clone() for _ in range(copies)]
+    torch.cuda.synchronize()
+    f = lambda i: ka.decode_step(shape, q, kn, vn, kcs[i % copies], vcs[i % copies], out, [p],
+                                 w.scale, ws)
+    f(0)
+    cold = float(np.median([span_ms(f, copies, hold, 10.0) / copies for _ in range(3)]))
+    del kcs, vcs
+    torch.cuda.empty_cache()
+    return dict(warm_ms=warm, cold_ms=cold, bytes=decode_bytes(w, p + 1, 1, "f32"))
+
+
 def bench_rope(hold, reps=20):
     """Rotary entry points at the session's chunk shape: a 768-row append
     whose K rows are rotated on the way into the bf16 cache, and the rotation
-    of the chunk's 768 x 8 query rows (medians of reps, event-timed)."""
+    of the chunk's 768 x 8 query rows (per-call times, back to back)."""
     w = WORKLOADS[4]
     shape = ka.Shape(1, 8, 1, 256, w.capacity, "bf16")
     kc = ka.alloc_cache(shape)
@@ -365,18 +409,7 @@ def bench_rope(hold, reps=20):
              "append_kv_768_us": lambda: ka.append_kv(shape, kc, vc, k, v, s0, R)}
     res = {}
     for name, f in calls.items():
-        f()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
-            a, b = ev_pair()
-            hold(0.2)
-            a.record()
-            f()
-            b.record()
-            torch.cuda.synchronize()
-            ts.append(a.elapsed_time(b) * 1e3)
-        res[name] = round(float(np.median(ts)), 2)
+        res[name] = round(per_call_ms(lambda i, f=f: f(), hold, n=16) * 1e3, 2)
     return res
 
 
@@ -391,27 +424,22 @@ def bench_int8(hold):
     torch.cuda.synchronize()
     pre, dec = [], []
     for _ in range(3):
-        pe = [ev_pair() for _ in s.chunk_views]
-        de = [ev_pair() for _ in s.dec_views]
-        hold(3.0)
-        s.prefill_phase(pe)
-        hold(3.0)
-        s.decode_phase(de)
-        torch.cuda.synchronize()
-        pre.append(sum(a.elapsed_time(b) for a, b in pe))
-        dec.append([a.elapsed_time(b) * 1e3 for a, b in de])
+        pre.append(span_ms(lambda i: s.prefill_phase(), 1, hold, 6.0))
+        dec.append(span_ms(lambda i: s.decode_phase(), 1, hold, 10.0) / len(s.dec_views))
     rows = sum(R for _, R in s.w.chunks)
     pm = float(np.median(pre))
     res = {"prefill_16k_ms": round(pm, 4), "prefill_16k_rows_per_s": round(rows / (pm * 1e-3), 1),
-           "decode_us_per_token_16k_kernel_median": round(float(np.median(dec)), 3)}
+           "decode_us_per_token_16k": round(float(np.median(dec)) * 1e3, 3)}
     del s
     torch.cuda.empty_cache()
     d = bench_decode_128k(hold, kv_dtype="i8k")
-    gbs = d["bytes"] / (d["decode_ms"] * 1e-3) / 1e9
-    res["decode_us_per_step_128k_x4"] = round(d["decode_ms"] * 1e3, 3)
+    gbs = d["bytes"] / (d["step_ms"] * 1e-3) / 1e9
+    res["decode_us_per_step_128k_x4"] = round(d["step_ms"] * 1e3, 3)
+    res["decode_us_per_call_128k_x4"] = round(d["call_ms"] * 1e3, 3)
     res["roofline_decode_128k"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                    "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                   "algorithmic_bytes_per_launch": d["bytes"]}
+                                   "algorithmic_bytes_per_launch": d["bytes"],
+                                   "time": "32 steps back to back"}
     torch.cuda.empty_cache()
     return res
 
@@ -419,7 +447,7 @@ def bench_int8(hold):
 def bench_few_rows(hold, reps=20):
     """Chunks of 1 .. 15 rows (the band between decode and the M-tile
     prefill) ending at context 16384 and 131072 of one session, 8 query heads
-    on one KV head, head_dim 256, bf16 cache: event-timed medians per call."""
+    on one KV head, head_dim 256, bf16 cache: per-call times, back to back."""
     res = {}
     for ctx in (16384, 131072):
         shape = ka.Shape(1, 8, 1, 256, ctx, "bf16")
@@ -438,19 +466,8 @@ def bench_few_rows(hold, reps=20):
         row = {}
         for R in (1, 2, 4, 8, 15):
             n = R * 8 * 256
-            f = lambda: ka.prefill_chunk(shape, q[:n], kc, vc, o[:n], ctx - R, R, 1 / 16, ws)
-            f()
-            torch.cuda.synchronize()
-            ts = []
-            for _ in range(reps):
-                a, b = ev_pair()
-                hold(0.2)
-                a.record()
-                f()
-                b.record()
-                torch.cuda.synchronize()
-                ts.append(a.elapsed_time(b) * 1e3)
-            row[str(R)] = round(float(np.median(ts)), 2)
+            f = lambda i, n=n, R=R: ka.prefill_chunk(shape, q[:n], kc, vc, o[:n], ctx - R, R, 1 / 16, ws)
+            row[str(R)] = round(per_call_ms(f, hold, n=12) * 1e3, 2)
         res[f"ctx_{ctx}_us_by_rows"] = row
         del kc, vc, q, o, ws
         torch.cuda.empty_cache()
@@ -460,7 +477,7 @@ def bench_few_rows(hold, reps=20):
 def bench_ragged(hold, reps=20):
     """Eight sessions of one 16K-capacity bf16 cache (8 query heads, one KV
     head, head_dim 256), each with a chunk at its own position: one ragged
-    call against one chunk call per session (event-timed medians)."""
+    call against one chunk call per session (per-call times, back to back)."""
     B, C = 8, 16384
     shape = ka.Shape(B, 8, 1, 256, C, "bf16")
     one = ka.Shape(1, 8, 1, 256, C, "bf16")
@@ -496,18 +513,7 @@ def bench_ragged(hold, reps=20):
 
         row = {"rows": rows}
         for nm, f in (("ragged_call_us", ragged), ("per_session_calls_us", per_session)):
-            f()
-            torch.cuda.synchronize()
-            ts = []
-            for _ in range(reps):
-                a, b_ = ev_pair()
-                hold(0.2)
-                a.record()
-                f()
-                b_.record()
-                torch.cuda.synchronize()
-                ts.append(a.elapsed_time(b_) * 1e3)
-            row[nm] = round(float(np.median(ts)), 2)
+            row[nm] = round(per_call_ms(lambda i, f=f: f(), hold, n=8) * 1e3, 2)
         res[name] = row
     del kc, vc
     torch.cuda.empty_cache()
@@ -552,6 +558,17 @@ def cpu_baseline(session_w, budget_s=15.0):
             ctxm.__exit__(None, None, None)
     n = nblocks * 16
     extras = oracle_extras(oracle, threadpool_limits, cores)
+    # the scalar oracle (pure Python, one core) on the tiny workload in full
+    w1 = WORKLOADS[1]
+    c1 = draw_batch(w1)
+    (s1, R1), = w1.chunks
+    t = time.perf_counter()
+    oracle.attend_rows_scalar(c1.q[0], c1.k[0], c1.v[0], list(range(s1, s1 + R1)), w1.scale)
+    extras["scalar_tiny_prefill_1_core"] = {
+        "rows_per_s": round(R1 / (time.perf_counter() - t), 2),
+        "seconds": round(time.perf_counter() - t, 2),
+        "sample": "all 128 rows of the tiny f32 prefill (2 query heads, head_dim 64), "
+                  "pure-Python math.fsum oracle, one core"}
     return {"value": round(n / dt, 2), "unit": "rows/s", "cores": cores, "kind": "oracle",
             "sample": (f"{n} of the 16384 prompt rows of the 16K session (16-row blocks evenly spaced "
                        f"over positions 0..16383, each row against its full causal context; 8 heads, "
@@ -622,14 +639,13 @@ def main():
     r = bench_session(args.steps, args.warmup, hold)
     w = r["w"]
     flops, pairs = prefill_flops(w)
-    pre_calls = r["prefill_calls_ms"]                   # prefill calls only (no append)
-    pre_kernel_ms = float(pre_calls.sum(axis=1).mean())
+    pre_calls = r["prefill_calls_ms"]                   # [22] prefill calls alone (no append)
+    pre_kernel_ms = float(pre_calls.sum())
     achieved_tf = flops / (pre_kernel_ms * 1e-3) / 1e12
     rows = sum(R for _, R in w.chunks)
     value = rows / (r["prefill_phase_ms"] * 1e-3)        # append + prefill, 22 chunks
-    dec16 = r["decode_calls_ms"]
-    dec16_step = float(np.median(r["decode_phase_ms"])) / len(w.decode_positions)
-    last_chunk_ms = float(np.median(pre_calls[:, -2]))
+    dec16_step = r["decode_phase_ms"] / len(w.decode_positions)
+    last_chunk_ms = float(pre_calls[-2])
     s_last, R_last = w.chunks[-2]
     flops_last = (R_last * s_last + R_last * (R_last + 1) // 2) * 8 * 256 * 4
 
@@ -649,15 +665,15 @@ def main():
                      "kernel": "prefill chunk call (prefill_mtile_kernel<256, false> + its merge kernel), "
                                "average over the 22 chunks",
                      "algorithmic_flops_per_step": flops, "causal_pairs": pairs,
-                     "avg_launch_ms": round(pre_kernel_ms / len(w.chunks), 5)},
+                     "avg_launch_ms": round(pre_kernel_ms / len(w.chunks), 5),
+                     "time": "each chunk's prefill call back to back, (2n - n calls) / n"},
         "wall_ms_per_step": round(r["wall_ms"], 3),
         "prefill_16k_ms": round(r["prefill_phase_ms"], 4),
+        "prefill_16k_ms_prefill_calls_only": round(pre_kernel_ms, 4),
         "prefill_last768_rows_per_s": round(R_last / (last_chunk_ms * 1e-3), 1),
         "prefill_last768_tflops": round(flops_last / (last_chunk_ms * 1e-3) / 1e12, 2),
         "decode_us_per_token_16k": round(dec16_step * 1e3, 3),
-        "decode_us_per_token_16k_kernel_median": round(float(np.median(dec16)) * 1e3, 3),
-        "decode_us_per_token_16k_p10_p90": [round(float(np.percentile(dec16, 10)) * 1e3, 3),
-                                            round(float(np.percentile(dec16, 90)) * 1e3, 3)],
+        "decode_us_per_call_16k": round(r["decode_call_ms"] * 1e3, 3),
     }
     out["copy_calibration"] = copy
     b16 = decode_bytes(w, w.decode_positions[-1] + 1, 1)
@@ -665,15 +681,15 @@ def main():
         cold = bench_decode_cold_16k(r["session"], hold)
         out["decode_us_per_token_16k_cold"] = round(cold * 1e3, 3)
         out["decode_16k_cold_hbm_frac"] = round(b16 / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
-    out["decode_16k_warm_hbm_frac"] = round(b16 / (float(np.median(dec16)) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    out["decode_16k_in_session_hbm_frac"] = round(b16 / (dec16_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
     del r
     torch.cuda.empty_cache()
     if not args.no_128k:
         d = bench_decode_128k(hold)
-        gbs = d["bytes"] / (d["decode_ms"] * 1e-3) / 1e9
-        out["decode_us_per_step_128k_x4"] = round(d["decode_ms"] * 1e3, 3)
-        out["decode_us_per_token_128k"] = round(d["decode_ms"] * 1e3 / d["w"].batch, 3)
-        out["decode_us_per_step_128k_x4_back_to_back"] = round(d["step_ms"] * 1e3, 3)
+        gbs = d["bytes"] / (d["step_ms"] * 1e-3) / 1e9
+        out["decode_us_per_step_128k_x4"] = round(d["step_ms"] * 1e3, 3)
+        out["decode_us_per_token_128k"] = round(d["step_ms"] * 1e3 / d["w"].batch, 3)
+        out["decode_us_per_call_128k_x4"] = round(d["call_ms"] * 1e3, 3)
         out["roofline_decode_128k"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                                        "frac_of_measured_copy": round(gbs / copy["gbs"], 4),
@@ -682,8 +698,17 @@ def main():
                                        "kernel": "decode step call (decode_mfma_kernel with the "
                                                  "row append + decode_merge_kernel), 4 sessions "
                                                  "at ctx 131041..131072",
-                                       "algorithmic_bytes_per_launch": d["bytes"]}
+                                       "algorithmic_bytes_per_launch": d["bytes"],
+                                       "time": "32 steps back to back"}
         torch.cuda.empty_cache()
+    d2 = bench_decode_f32_4k(hold)
+    out["decode_f32_4097"] = {
+        "us_per_step_warm": round(d2["warm_ms"] * 1e3, 3),
+        "hbm_frac_warm": round(d2["bytes"] / (d2["warm_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "us_per_step_cold": round(d2["cold_ms"] * 1e3, 3),
+        "hbm_frac_cold": round(d2["bytes"] / (d2["cold_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes": d2["bytes"],
+        "note": "warm: 8.4 MB of K/V resident in the 256 MB MALL; cold: 64 caches in rotation"}
     f = bench_prefill_f32(hold)
     tf = f["flops"] / (f["ms"] * 1e-3) / 1e12
     out["prefill_f32_3072_768_us"] = round(f["ms"] * 1e3, 2)
