@@ -358,84 +358,88 @@ void decode_split_kernel(
 }
 
 // Combines the S split partials of one (session, KV head, head group) for
-// one head and 32 dims.  Thread (d, r) sums splits r, r + 8, ...; the loads
-// of its first 32 splits (all of them up to 256 splits, the most the MFMA
-// kernel's plans use) go out together with the (m, l) loads, so the merge
-// waits on memory about once.  The eight partial sums are added in a fixed
-// order, so the result does not depend on timing.
+// one head and 32 dims.  Thread (d, r) takes splits r, r + 8, r + 16, ...:
+// it loads their accumulators and (m, l) records together (the first kEarly
+// of them before using any, so the merge waits on memory about once) and sums
+// them in its own frame; the eight threads of a dim then combine their
+// (m, l, acc) through LDS in the fixed order r = 0 .. 7 (one barrier), so the
+// result does not depend on timing.  A split that saw no key (l = 0) adds
+// nothing; one whose sum is NaN (NaN scores, even with m = -inf) makes the
+// result NaN.
+constexpr int kMergeEarly = 32;
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
     int b0, int Hq, int Hkv, int HG, int hpw, int S, int R) {
-  __shared__ float wgt[kMaxSplits];
-  __shared__ float red[8][32];
-  __shared__ float wmax[4], wsum[4];
+  __shared__ float red_a[8][32];
+  __shared__ float red_m[8], red_l[8];
   constexpr int NS = D / 32;
-  constexpr int EARLY = 32;
   const int h = blockIdx.x / NS, ds = blockIdx.x % NS;
   const int gh = blockIdx.y, bl = blockIdx.z, b = b0 + bl;
   const int g = gh / HG, hg = gh % HG;
   const int G = Hq / Hkv;
   const int gq = b * (Hkv * HG) + gh;
   const int ph = hg * hpw + h;  // (row, head) pair of the group: row ph / G, head ph % G
-  if (ph >= R * G) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const float* ml = part_ml + ((size_t)gq * hpw + h) * S * 2;
+  if (ph >= R * G) return;      // block-uniform: before the barrier
+  const int tid = threadIdx.x;
+  const float2* ml = reinterpret_cast<const float2*>(part_ml + ((size_t)gq * hpw + h) * S * 2);
   const int dl = tid & 31, r = tid >> 5;
   const int d = ds * 32 + dl;
   const float* pa = part + ((size_t)gq * S * hpw + h) * D + d;
   const size_t PS = (size_t)hpw * D;
-  float av[EARLY];
+  float av[kMergeEarly];
+  float2 mlv[kMergeEarly];
 #pragma unroll
-  for (int k = 0; k < EARLY; ++k) {
+  for (int k = 0; k < kMergeEarly; ++k) {
     const int s = r + 8 * k;
     av[k] = s < S ? pa[(size_t)s * PS] : 0.f;
+    mlv[k] = s < S ? ml[s] : make_float2(-INFINITY, 0.f);
   }
-  // (m, l) of splits tid, tid + 256, ... (S <= kMaxSplits = 4 * 256)
-  float mv[kMaxSplits / 256], lv[kMaxSplits / 256];
+  float m = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kMaxSplits / 256; ++j) {
-    const int s = tid + 256 * j;
-    mv[j] = s < S ? ml[2 * s] : -INFINITY;
-    lv[j] = s < S ? ml[2 * s + 1] : 0.f;
+  for (int k = 0; k < kMergeEarly; ++k) m = fmaxf(m, mlv[k].x);
+  float l = 0.f, a = 0.f;
+#pragma unroll
+  for (int k = 0; k < kMergeEarly; ++k) {
+    if (mlv[k].y == 0.f) continue;
+    const float f = fast_exp2(mlv[k].x - m);
+    l += f * mlv[k].y;
+    a += f * av[k];
   }
-  // M = max_s m_s over the block, then w_s = 2^(m_s - M), L = sum_s w_s l_s
+  // more than 8 kMergeEarly splits (f32 plans): a running frame
+  for (int s = r + 8 * kMergeEarly; s < S; s += 8) {
+    const float2 x = ml[s];
+    if (x.y == 0.f) continue;
+    if (x.x > m) {
+      const float f = fast_exp2(m - x.x);  // 0 while m is -inf
+      l *= f;
+      a *= f;
+      m = x.x;
+    }
+    const float f = fast_exp2(x.x - m);
+    l += f * x.y;
+    a += f * pa[(size_t)s * PS];
+  }
+  red_a[r][dl] = a;
+  if (dl == 0) {
+    red_m[r] = m;
+    red_l[r] = l;
+  }
+  __syncthreads();
+  if (r != 0) return;
   float M = -INFINITY;
 #pragma unroll
-  for (int j = 0; j < kMaxSplits / 256; ++j) M = fmaxf(M, mv[j]);
-  M = group_max<64>(M);
-  if (lane == 0) wmax[w] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-  float L = 0.f;
+  for (int j = 0; j < 8; ++j) M = fmaxf(M, red_m[j]);
+  float A = 0.f, L = 0.f;
 #pragma unroll
-  for (int j = 0; j < kMaxSplits / 256; ++j) {
-    const int s = tid + 256 * j;
-    if (s < S) {
-      const float f = mv[j] == -INFINITY ? 0.f : fast_exp2(mv[j] - M);
-      wgt[s] = f;
-      L += f * lv[j];
-    }
+  for (int j = 0; j < 8; ++j) {
+    if (red_l[j] == 0.f) continue;
+    const float f = fast_exp2(red_m[j] - M);
+    A += f * red_a[j][dl];
+    L += f * red_l[j];
   }
-  L = group_sum<64>(L);
-  if (lane == 0) wsum[w] = L;
-  __syncthreads();
-  L = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-  // weighted sum of the accumulators
-  float a = 0.f;
-#pragma unroll
-  for (int k = 0; k < EARLY; ++k) {
-    const int s = r + 8 * k;
-    if (s < S) a += wgt[s] * av[k];
-  }
-  for (int s = r + 8 * EARLY; s < S; s += 8) a += wgt[s] * pa[(size_t)s * PS];
-  red[r][dl] = a;
-  __syncthreads();
-  if (r == 0) {
-    const float t = ((red[0][dl] + red[1][dl]) + (red[2][dl] + red[3][dl])) +
-                    ((red[4][dl] + red[5][dl]) + (red[6][dl] + red[7][dl]));
-    out[(((size_t)b * R + ph / G) * Hq + g * G + ph % G) * D + d] = t / L;
-  }
+  out[(((size_t)b * R + ph / G) * Hq + g * G + ph % G) * D + d] = A / L;
 }
 
 // ============================================================================

@@ -1589,6 +1589,7 @@ __global__ __launch_bounds__(256) void prefill_merge_few_kernel(
         ev[k][j] = H16 ? ml[ML * k + 2 + 2 * ((4 * v + 64 * j) / (D / 2)) + (v & 1)] : 0.f;
     } else {
       mv[k] = -INFINITY;
+      lv[k] = 0.f;
     }
   }
   float M = -INFINITY;
@@ -1600,7 +1601,9 @@ __global__ __launch_bounds__(256) void prefill_merge_few_kernel(
   float L = 0.f;
 #pragma unroll
   for (int k = 0; k < kMergeFew; ++k) {
-    if (mv[k] == -INFINITY) continue;  // past S, or a split that saw none of the column's keys
+    // past S, or a split that saw none of the column's keys (a NaN sum, even
+    // with m = -inf, still reaches the result)
+    if (lv[k] == 0.f) continue;
     const float f = fast_exp2(mv[k] - M);
     L += f * lv[k];
 #pragma unroll
@@ -1674,7 +1677,7 @@ __global__ __launch_bounds__(256) void prefill_merge_split_kernel(
       }
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) {
-        if (mv[k] != -INFINITY) {  // a split that saw none of the column's keys adds nothing
+        if (lv[k] != 0.f) {  // a split that saw none of the column's keys adds nothing
           float f = fast_exp2(mv[k] - mw);
           lw += f * lv[k];
           if constexpr (H16) f = ldexpf(f, (int)ev[k]);
@@ -1697,7 +1700,7 @@ __global__ __launch_bounds__(256) void prefill_merge_split_kernel(
   float L = 0.f;
 #pragma unroll
   for (int w = 0; w < kMergeGroups; ++w) {
-    if (red_m[w][c] == -INFINITY) continue;
+    if (red_l[w][c] == 0.f) continue;
     const float f = fast_exp2(red_m[w][c] - M);
     const float4 x = red[w][c][v];
     o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;

@@ -134,3 +134,30 @@ def test_nonfinite_values_in_a_ragged_batch(dt):
     ks, vs = oracle.stored_values(c.k, dt), oracle.stored_values(c.v, dt)
     ref = oracle.prefill_ragged(q, ks, vs, starts, rows, 1 / np.sqrt(D))
     _compare(got, ref, vs, dt, f"ragged {dt} starts {starts} rows {rows}")
+
+
+@pytest.mark.parametrize("dt", ["bf16", "i8k", "f32"])
+def test_a_whole_key_range_of_nan_rows(dt):
+    """256 consecutive NaN key rows (more than a split's share of keys): every
+    row that sees them is NaN in full, on the decode path and on the chunk
+    path, even where a whole split sees nothing but NaN scores; rows that
+    cannot see them match the oracle."""
+    B, Hq, Hkv, D, C = 1, 8, 1, 256, 8192
+    c = random_case(47, B, Hq, Hkv, D, 8192, 4)
+    c.k[0, 4096:4352] = np.nan
+    caches = DevCaches(B, Hq, Hkv, D, C, dt)
+    caches.append(c.k, c.v, 0)
+    got = caches.decode(c.q[:, 0], [8192], 1 / 16)
+    assert np.isnan(got).all()
+    got = caches.decode(c.q[:, 0], [4000], 1 / 16)
+    vs = oracle.stored_values(c.v, "f32" if dt == "f32" else "bf16")
+    ks = oracle.stored_values(c.k, "f32" if dt == "f32" else "bf16")
+    if dt == "i8k":
+        ref = oi8.decode_i8(c.q[:, 0], c.k, vs, [4000], 1 / 16)
+    else:
+        ref = oracle.decode(c.q[:, 0], ks, vs, [4000], 1 / 16)
+    assert oracle.rel_error(got, ref, vs[:, :4000]) <= TOL[dt]
+    # a chunk straddling the NaN range: rows before 4096 finite, rows after NaN
+    q = c.q[:, :4].repeat(10, axis=1)[:, :40]
+    got = caches.prefill(q, 4076, 1 / 16)
+    assert np.isfinite(got[:, :20]).all() and np.isnan(got[:, 20:]).all()
