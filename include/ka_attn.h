@@ -252,7 +252,7 @@ ka_status ka_attn_decode(const ka_attn_shape* s, const float* q,
  * rounding, same bits), and the query row q[b] at that position attends to
  * cache positions 0 .. pos[b].  Equivalent to one ka_attn_append_kv per
  * session followed by ka_attn_decode with ctx_len[b] = pos[b] + 1, and bitwise
- * equal to it, in one launch for bf16 and int8-K caches (the attention kernel writes the
+ * equal to it, in one attention launch on every cache dtype (the attention kernel writes the
  * row it uses).  pos is a HOST array of B entries, 0 <= pos[b] < C.  The
  * workspace is ka_attn_decode's for max_b pos[b] + 1.  k_new, v_new and q may
  * not overlap the caches or out.  Errors as ka_attn_decode.

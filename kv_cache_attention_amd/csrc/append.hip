@@ -377,93 +377,4 @@ hipError_t launch_rope_rows(const float* x, float* y, const float* rope_cos,
   return hipGetLastError();
 }
 
-// One new row per session at its own position (the decode step's append):
-// k_new / v_new [B][Hkv][D] f32 -> cache position pos[b].  Thread i writes
-// one K vector or one V element (a V vector spans E positions, so only the
-// row's own element of it is stored).
-template <int MODE>
-__global__ __launch_bounds__(256) void append_row_kernel(
-    void* __restrict__ k_cache, void* __restrict__ v_cache, const float* __restrict__ k_new,
-    const float* __restrict__ v_new, float* __restrict__ k_scales, const CtxArg pos, int b0,
-    int nb, int Hkv, int D, int C) {
-  constexpr bool BF16 = MODE != kF32;
-  constexpr int E = MODE == kI8K ? 16 : MODE == kBF16 ? 8 : 4;  // K elements per vector
-  const int cpr = D / E;
-  const long long nk = (long long)nb * Hkv * cpr, nv = (long long)nb * Hkv * D;
-  const long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long stride = (long long)gridDim.x * blockDim.x;
-  long long first = tid;
-  if constexpr (MODE == kI8K) {
-    // K rows one per wave, then the V elements
-    const int lane = threadIdx.x & (kWave - 1);
-    for (long long rt = tid / kWave; rt < (long long)nb * Hkv; rt += stride / kWave) {
-      const int g = (int)(rt % Hkv), bl = (int)(rt / Hkv), b = b0 + bl;
-      const int j = pos.ctx[bl];
-      const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;  // bytes
-      quantise_row_wave<false>(k_new + ((size_t)b * Hkv + g) * D, nullptr, nullptr, D, lane,
-                               reinterpret_cast<int8_t*>(k_cache) + slab, k_vec_index(j, 0, D, 16),
-                               k_scales + ((size_t)b * Hkv + g) * C + j);
-    }
-    first = tid + nk;
-  }
-  for (long long i = first; i < nk + nv; i += stride) {
-    if (i < nk) {
-      const int c = (int)(i % cpr);
-      const long long t = i / cpr;
-      const int g = (int)(t % Hkv), bl = (int)(t / Hkv), b = b0 + bl;
-      const int j = pos.ctx[bl];
-      const float* src = k_new + ((size_t)b * Hkv + g) * D + c * E;
-      const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;
-      const size_t vi = k_vec_index(j, c, D, E);
-      if constexpr (BF16) {
-        const float4 a = *reinterpret_cast<const float4*>(src);
-        const float4 bq = *reinterpret_cast<const float4*>(src + 4);
-        uint4 o;
-        o.x = pack_bf16x2(a.x, a.y);
-        o.y = pack_bf16x2(a.z, a.w);
-        o.z = pack_bf16x2(bq.x, bq.y);
-        o.w = pack_bf16x2(bq.z, bq.w);
-        reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_cache) + slab)[vi] = o;
-      } else {
-        reinterpret_cast<float4*>(reinterpret_cast<float*>(k_cache) + slab)[vi] =
-            *reinterpret_cast<const float4*>(src);
-      }
-    } else {
-      const long long iv = i - nk;
-      const int d = (int)(iv % D);
-      const long long t = iv / D;
-      const int g = (int)(t % Hkv), bl = (int)(t / Hkv), b = b0 + bl;
-      const int j = pos.ctx[bl];
-      const float x = v_new[((size_t)b * Hkv + g) * D + d];
-      const size_t slab = ((size_t)b * Hkv + g) * (size_t)C * D;
-      if constexpr (BF16) {
-        uint16_t* base = reinterpret_cast<uint16_t*>(v_cache) + slab;
-        base[((size_t)vbf16_group(j) * D + d) * 8 + vbf16_slot(j)] = (uint16_t)f32_to_bf16_bits(x);
-      } else {
-        float* base = reinterpret_cast<float*>(v_cache) + slab;
-        base[vf32_vec_index(j, d, D) * 4 + (j & 3)] = x;
-      }
-    }
-  }
-}
-
-hipError_t launch_append_rows(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
-                              const float* v_new, const CtxArg& pos, int b0, int nb,
-                              hipStream_t stream) {
-  const int E = s.kv_dtype == kI8K ? 16 : s.kv_dtype == kBF16 ? 8 : 4;
-  const long long total = (long long)nb * s.num_kv_heads *
-                          ((s.kv_dtype == kI8K ? kWave : s.head_dim / E) + s.head_dim);
-  long long blocks = (total + 255) / 256;
-  if (blocks > 65536) blocks = 65536;
-  float* k_scales = k_scale_array(s, k_cache);
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k_cache, v_cache,
-                       k_new, v_new, k_scales, pos, b0, nb, s.num_kv_heads, s.head_dim, s.capacity);
-  };
-  if (s.kv_dtype == kI8K) go(append_row_kernel<kI8K>);
-  else if (s.kv_dtype == kBF16) go(append_row_kernel<kBF16>);
-  else go(append_row_kernel<kF32>);
-  return hipGetLastError();
-}
-
 }  // namespace ka

@@ -242,10 +242,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kSplitWaves
 void decode_split_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, float* __restrict__ out, float* __restrict__ part,
-    float* __restrict__ part_ml, const CtxArg ctxa, int b0, int Hq, int Hkv, int HG, int C,
-    int S, float sl2e) {
+    float* __restrict__ part_ml, const float* __restrict__ k_new, const float* __restrict__ v_new,
+    const CtxArg ctxa, int b0, int Hq, int Hkv, int HG, int C, int S, float sl2e) {
+  static_assert(!BF16, "bf16 caches decode on the MFMA kernel");
   using R = UnitRegs<D, BF16>;
-  constexpr int ND = R::ND;
+  constexpr int ND = R::ND, NCH = R::NCH;
   using T = typename Elem<BF16>::T;
   __shared__ DecodeSmem<D, HPW, BF16> sm;
 
@@ -265,6 +266,49 @@ void decode_split_kernel(
   const int n_units = units_for(ctx);
   const int u0 = (int)((long long)split * n_units / S);
   const int u1 = (int)((long long)(split + 1) * n_units / S);
+
+  // The decode step's new row (k_new / v_new, position ctx - 1): the wave
+  // whose unit holds it stores it as the append kernel would (an f32 copy;
+  // head group 0 of the slab only) and takes its values in registers in
+  // place of what its loads of that unit bring in, so no wave waits on the
+  // store and no other wave reads that position.
+  const int p_new = ctx - 1, u_new = p_new / kUnit;
+  const bool owns_new = k_new != nullptr && u_new >= u0 && u_new < u1 &&
+                        (u_new - u0) % kWaves == w;
+  const float* kn = owns_new ? k_new + ((size_t)b * Hkv + g) * D : nullptr;
+  const float* vn = owns_new ? v_new + ((size_t)b * Hkv + g) * D : nullptr;
+  if (owns_new && hg == 0) {
+    float* kw = reinterpret_cast<float*>(const_cast<void*>(k_cache)) + slab;
+    float* vw = reinterpret_cast<float*>(const_cast<void*>(v_cache)) + slab;
+    for (int c = lane; c < D / 4; c += kWave)
+      *reinterpret_cast<float4*>(kw + k_vec_index(p_new, c, D, 4) * 4) =
+          *reinterpret_cast<const float4*>(kn + 4 * c);
+    for (int d = lane; d < D; d += kWave) vw[vf32_vec_index(p_new, d, D) * 4 + (p_new & 3)] = vn[d];
+  }
+  auto take_new_row = [&](R& r) {
+    if ((lane & 15) == (p_new & 15)) {  // this lane's K slices are of the new position
+      const int qd = lane >> 4;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const float4 x = *reinterpret_cast<const float4*>(kn + 4 * (qd * NCH + i));
+        r.k[i] = make_uint4(__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z),
+                            __float_as_uint(x.w));
+      }
+    }
+    const int gi = (p_new & 15) >> 2, e = p_new & 3;  // V: group gi of the unit, slot e
+#pragma unroll
+    for (int t = 0; t < ND; ++t) {
+      const uint32_t x = __float_as_uint(vn[lane + 64 * t]);
+#pragma unroll
+      for (int g2 = 0; g2 < R::NG; ++g2) {
+        if (g2 != gi) continue;
+        r.v[g2][t].x = e == 0 ? x : r.v[g2][t].x;
+        r.v[g2][t].y = e == 1 ? x : r.v[g2][t].y;
+        r.v[g2][t].z = e == 2 ? x : r.v[g2][t].z;
+        r.v[g2][t].w = e == 3 ? x : r.v[g2][t].w;
+      }
+    }
+  };
 
   // first unit's loads go out before q, so the two latencies overlap
   R ra;
@@ -317,6 +361,7 @@ void decode_split_kernel(
       load_unit_v<D, BF16>(ra, u, lane, vc);
     }
     first = false;
+    if (owns_new && u == u_new) take_new_row(ra);
     process_unit<D, HPW, BF16>(ra, u, lane, ctx, sl2e, sm.q, sm.p[w], m_run, l_run, acc);
   }
 
@@ -993,23 +1038,23 @@ int heads_per_wg(int G) {
 
 template <int D, int HPW, bool BF16>
 void launch_split(dim3 grid, hipStream_t st, const float* q, const void* kc, const void* vc,
-                  float* out, float* part, const CtxArg& ca, int b0, const Shape& s, int HG,
-                  int S, float sl2e) {
+                  float* out, float* part, const float* k_new, const float* v_new,
+                  const CtxArg& ca, int b0, const Shape& s, int HG, int S, float sl2e) {
   float* part_ml = part + (size_t)s.batch * s.num_kv_heads * HG * S * HPW * D;
   hipLaunchKernelGGL((decode_split_kernel<D, HPW, BF16>), grid, dim3(256), 0, st, q, kc, vc, out,
-                     part, part_ml, ca, b0, s.num_q_heads, s.num_kv_heads, HG, s.capacity, S,
-                     sl2e);
+                     part, part_ml, k_new, v_new, ca, b0, s.num_q_heads, s.num_kv_heads, HG,
+                     s.capacity, S, sl2e);
 }
 
 template <int D, bool BF16>
 void dispatch_hpw(int hpw, dim3 grid, hipStream_t st, const float* q, const void* kc,
-                  const void* vc, float* out, float* part, const CtxArg& ca, int b0,
-                  const Shape& s, int HG, int S, float sl2e) {
+                  const void* vc, float* out, float* part, const float* k_new, const float* v_new,
+                  const CtxArg& ca, int b0, const Shape& s, int HG, int S, float sl2e) {
   switch (hpw) {
-    case 8: launch_split<D, 8, BF16>(grid, st, q, kc, vc, out, part, ca, b0, s, HG, S, sl2e); break;
-    case 4: launch_split<D, 4, BF16>(grid, st, q, kc, vc, out, part, ca, b0, s, HG, S, sl2e); break;
-    case 2: launch_split<D, 2, BF16>(grid, st, q, kc, vc, out, part, ca, b0, s, HG, S, sl2e); break;
-    default: launch_split<D, 1, BF16>(grid, st, q, kc, vc, out, part, ca, b0, s, HG, S, sl2e); break;
+    case 8: launch_split<D, 8, BF16>(grid, st, q, kc, vc, out, part, k_new, v_new, ca, b0, s, HG, S, sl2e); break;
+    case 4: launch_split<D, 4, BF16>(grid, st, q, kc, vc, out, part, k_new, v_new, ca, b0, s, HG, S, sl2e); break;
+    case 2: launch_split<D, 2, BF16>(grid, st, q, kc, vc, out, part, k_new, v_new, ca, b0, s, HG, S, sl2e); break;
+    default: launch_split<D, 1, BF16>(grid, st, q, kc, vc, out, part, k_new, v_new, ca, b0, s, HG, S, sl2e); break;
   }
 }
 
@@ -1053,7 +1098,10 @@ DecodePlan plan_decode(const Shape& s, int max_ctx) {
     const int units = units_for(max_ctx);
     const long long slabs = (long long)s.batch * s.num_kv_heads * p.head_groups;
     S = (kTargetWgs + slabs - 1) / slabs;
-    const long long by_units = units / kWaves;  // at least one unit per wave
+    // at most about one unit per wave: with floor(units / 4) splits some
+    // workgroup gets a fifth unit, and its wave runs two dependent
+    // load-then-compute rounds (4097 keys: 21.4 us against 16.9 us)
+    const long long by_units = (units + kWaves - 1) / kWaves;
     if (S > by_units) S = by_units;
   }
   if (S > kMaxSplits) S = kMaxSplits;
@@ -1139,13 +1187,6 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, vo
     CtxArg ca;
     for (int i = 0; i < kMaxDecodeBatchPerLaunch; ++i) ca.ctx[i] = i < nb ? ctx_host[b0 + i] : 0;
     dim3 grid(S, s.num_kv_heads * HG, nb);
-    if (k_new != nullptr && s.kv_dtype == kF32) {
-      // f32 caches: the new rows go in first, by their own kernel
-      CtxArg pos;
-      for (int i = 0; i < kMaxDecodeBatchPerLaunch; ++i) pos.ctx[i] = i < nb ? ca.ctx[i] - 1 : 0;
-      const hipError_t e = launch_append_rows(s, k_cache, v_cache, k_new, v_new, pos, b0, nb, stream);
-      if (e != hipSuccess) return e;
-    }
     switch (s.head_dim) {
 #define KA_D(DD)                                                                               \
   case DD:                                                                                     \
@@ -1164,7 +1205,7 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, vo
                          s.num_q_heads, s.num_kv_heads, HG, p.heads_per_wg, s.capacity, S,     \
                          sl2e, 1);                                                             \
     else dispatch_hpw<DD, false>(p.heads_per_wg, grid, stream, q, k_cache, v_cache, out, part, \
-                                 ca, b0, s, HG, S, sl2e);                                      \
+                                 k_new, v_new, ca, b0, s, HG, S, sl2e);                        \
     if (S > 1) launch_merge<DD>(p.heads_per_wg,                                               \
                                 dim3(p.heads_per_wg * (DD / 32), s.num_kv_heads * HG, nb),     \
                                 stream, part, out, b0, s, HG, S);                              \

@@ -44,10 +44,6 @@ hipError_t launch_append_ragged(const Shape& s, void* k_cache, void* v_cache, co
 hipError_t launch_rope_rows(const float* x, float* y, const float* rope_cos,
                             const float* rope_sin, int B, int R, int H, int D,
                             hipStream_t stream);
-// One row per session at position pos.ctx[b - b0], sessions b0 .. b0 + nb - 1.
-hipError_t launch_append_rows(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
-                              const float* v_new, const CtxArg& pos, int b0, int nb,
-                              hipStream_t stream);
 
 // Split-context plan of the decode kernels.  On the bf16 MFMA kernel a
 // workgroup's columns are heads_per_wg (row, head) pairs -- one row: heads.
@@ -83,8 +79,8 @@ hipError_t launch_prefill_ragged(const Shape& s, const float* q, const void* k_c
 // ---- decode
 DecodePlan plan_decode(const Shape& s, int max_ctx);
 // k_new / v_new (optional, [B][Hkv][D] f32): the decode step's new rows, at
-// position ctx - 1 of each session; they are appended before they are
-// attended to (fused into the attention kernel for bf16 caches).
+// position ctx - 1 of each session; the attention kernel stores them as the
+// append would and attends to them (no separate append launch).
 hipError_t launch_decode(const Shape& s, const DecodePlan& p, const float* q, void* k_cache,
                          void* v_cache, float* out, const int32_t* ctx_host, float scale,
                          void* workspace, hipStream_t stream, const float* k_new = nullptr,

@@ -321,6 +321,8 @@ DECODE_STEP_CASES = [
     ("bf16", 2, 8, 2, 256, 1024, [64, 1000]),
     ("f32", 2, 8, 1, 128, 512, [5, 300]),
     ("f32", 1, 4, 2, 64, 128, [0]),
+    ("f32", 3, 16, 1, 256, 1088, [0, 517, 1087]),  # two head groups per KV head
+    ("f32", 2, 8, 2, 256, 4160, [4096, 33]),
 ]
 
 
