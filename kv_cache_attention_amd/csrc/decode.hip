@@ -1075,10 +1075,55 @@ void launch_merge(int hpw, dim3 grid, hipStream_t st, const float* part, float* 
 
 }  // namespace
 
+// f32 caches (VALU kernel): heads per workgroup and splits for a context of
+// `units` 16-position units.  A wave's work per unit grows with the heads it
+// serves, and short steps are bound by that chain of one wave, not by bytes:
+// while the whole step is small (every slab's units together at most
+// kF32FewUnits, e.g. one session at 4097 keys) a workgroup serves a quarter
+// of the heads and two units, so four times as many waves each do an eighth
+// of the work (4097 keys: 12.5 us against 17.4 us with all 8 heads and four
+// units); up to kF32MidUnits, half the heads (one session at 16K: 20.7
+// against 22.2 us).  Past that the step streams the cache, and every head
+// group would read it again, so a workgroup serves all heads (4 sessions at
+// 64K: 108 us against 136 us with half).
+constexpr long long kF32FewUnits = 512, kF32MidUnits = 2048;
+
+struct F32Plan {
+  int hpw;
+  long long S;
+};
+
+static F32Plan plan_f32(const Shape& s, int units) {
+  const int G = s.num_q_heads / s.num_kv_heads;
+  const int h0 = heads_per_wg(G);
+  const long long work = (long long)s.batch * s.num_kv_heads * units;
+  int hpw = h0, upw = kWaves;
+  if (work <= kF32FewUnits) {
+    hpw = h0 >= 4 ? h0 / 4 : 1;
+    upw = 2;
+  } else if (work <= kF32MidUnits) {
+    hpw = h0 >= 2 ? h0 / 2 : 1;
+  }
+  const long long slabs = (long long)s.batch * s.num_kv_heads * (G / hpw);
+  long long S = (kTargetWgs + slabs - 1) / slabs;
+  // at most about one unit per active wave: with fewer splits some wave gets
+  // a second unit and runs two dependent load-then-compute rounds
+  const long long by_units = (units + upw - 1) / upw;
+  if (S > by_units) S = by_units;
+  if (S > kMaxSplits) S = kMaxSplits;
+  if (S < 1) S = 1;
+  return {hpw, S};
+}
+
+// Partial bytes of a split plan: acc [slab][S][HPW][D], then (m, l)
+// [slab][HPW][S][2]; none with one split.
+static size_t part_bytes(const Shape& s, long long slabs, int hpw, long long S) {
+  return S == 1 ? 0 : (size_t)slabs * S * hpw * (s.head_dim + 2) * sizeof(float);
+}
+
 DecodePlan plan_decode(const Shape& s, int max_ctx) {
   DecodePlan p;
   const int G = s.num_q_heads / s.num_kv_heads;
-  long long S;
   if (s.kv_dtype != kF32) {
     // MFMA path (bf16 and int8-K caches): up to 16 heads share a workgroup's columns; one round of
     // 256 workgroups (one per CU: a wave's operand registers fill its SIMD),
@@ -1089,28 +1134,36 @@ DecodePlan plan_decode(const Shape& s, int max_ctx) {
     p.heads_per_wg = G / hg;
     const long long slabs = (long long)s.batch * s.num_kv_heads * hg;
     const long long tiles = (max_ctx + kDecTile - 1) / kDecTile;
-    S = 256 / slabs;  // a 257th workgroup would start a second round
+    long long S = 256 / slabs;  // a 257th workgroup would start a second round
     const long long by_tiles = (tiles + kWaves - 1) / kWaves;
     if (S > by_tiles) S = by_tiles;
-  } else {
-    p.heads_per_wg = heads_per_wg(G);
-    p.head_groups = G / p.heads_per_wg;
-    const int units = units_for(max_ctx);
-    const long long slabs = (long long)s.batch * s.num_kv_heads * p.head_groups;
-    S = (kTargetWgs + slabs - 1) / slabs;
-    // at most about one unit per wave: with floor(units / 4) splits some
-    // workgroup gets a fifth unit, and its wave runs two dependent
-    // load-then-compute rounds (4097 keys: 21.4 us against 16.9 us)
-    const long long by_units = (units + kWaves - 1) / kWaves;
-    if (S > by_units) S = by_units;
+    if (S > kMaxSplits) S = kMaxSplits;
+    if (S < 1) S = 1;
+    p.splits = (int)S;
+    // S grows with the context, so this also covers every shorter context
+    p.workspace_bytes = part_bytes(s, slabs, p.heads_per_wg, S);
+    return p;
   }
-  if (S > kMaxSplits) S = kMaxSplits;
-  if (S < 1) S = 1;
-  p.splits = (int)S;
-  const long long slabs = (long long)s.batch * s.num_kv_heads * p.head_groups;
-  p.workspace_bytes = p.splits == 1 ? 0
-      : (size_t)slabs * p.splits * p.heads_per_wg * (s.head_dim + 2) * sizeof(float);
-  // layout: acc [slab][S][HPW][D], then (m, l) [slab][HPW][S][2]
+  const int units = units_for(max_ctx);
+  const F32Plan f = plan_f32(s, units);
+  p.heads_per_wg = f.hpw;
+  p.head_groups = G / f.hpw;
+  p.splits = (int)f.S;
+  // The workspace bound covers every context up to max_ctx (a caller sizes
+  // it once, at the longest): within one regime S grows with the context,
+  // but a step into the next regime can lower it, so the last context of
+  // each shorter regime is taken too.
+  const long long per = (long long)s.batch * s.num_kv_heads;
+  size_t ws = 0;
+  for (const long long lim : {kF32FewUnits, kF32MidUnits}) {
+    const long long u = lim / per;  // the last unit count of that regime
+    if (u < 1 || u >= units) continue;
+    const F32Plan e = plan_f32(s, (int)u);
+    const size_t b = part_bytes(s, per * (G / e.hpw), e.hpw, e.S);
+    if (b > ws) ws = b;
+  }
+  const size_t own = part_bytes(s, per * p.head_groups, f.hpw, f.S);
+  p.workspace_bytes = own > ws ? own : ws;
   return p;
 }
 

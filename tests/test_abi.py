@@ -206,6 +206,26 @@ def test_workspace_sizes_cover_smaller_requests():
         assert ka.prefill_workspace_bytes(s, r) <= p
 
 
+@pytest.mark.parametrize("kv", ["f32", "bf16", "i8k"])
+@pytest.mark.parametrize("batch,hq,hkv", [(1, 8, 1), (2, 8, 1), (4, 8, 2), (1, 1, 1), (3, 2, 1),
+                                          (16, 16, 1), (1, 12, 3)])
+def test_decode_workspace_never_shrinks_with_the_context(kv, batch, hq, hkv):
+    """A workspace sized for the longest context serves every shorter one:
+    the f32 plan changes its heads per workgroup with the step's size, and
+    its reported bound must still grow with the context."""
+    _lib_or_skip()
+    s = ka.Shape(batch, hq, hkv, 128, 70016, kv)
+    cs = sorted(set(list(range(1, 70016, 97)) + [16 * u + d for u in (512, 1024, 2048, 4096)
+                                                 for k in (1, 2, 3, 4, 8, 16)
+                                                 for u in [u // k] for d in (-1, 0, 1)
+                                                 if 1 <= 16 * u + d <= 70016]))
+    prev = 0
+    for c in cs:
+        b = ka.decode_workspace_bytes(s, c)
+        assert b >= prev, (c, b, prev)
+        prev = b
+
+
 def _i32(xs):
     return (ctypes.c_int32 * len(xs))(*xs)
 

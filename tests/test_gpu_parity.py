@@ -255,6 +255,9 @@ DECODE_CASES = [
     ("bf16", 2, 32, 4, 128, 128, [100, 128]),
     ("bf16", 1, 16, 1, 64, 256, [250]),
     ("f32", 1, 3, 1, 64, 128, [77]),
+    # f32 plans by the step's size (8 heads: 2, 4 or 8 heads per workgroup)
+    ("f32", 2, 8, 1, 128, 16448, [16385, 9000]),
+    ("f32", 1, 8, 1, 64, 16448, [16385]),
 ]
 
 
@@ -323,6 +326,8 @@ DECODE_STEP_CASES = [
     ("f32", 1, 4, 2, 64, 128, [0]),
     ("f32", 3, 16, 1, 256, 1088, [0, 517, 1087]),  # two head groups per KV head
     ("f32", 2, 8, 2, 256, 4160, [4096, 33]),
+    ("f32", 1, 8, 1, 64, 40000, [39000]),          # all heads per workgroup
+    ("f32", 1, 8, 1, 256, 4160, [4096]),           # two heads per workgroup
 ]
 
 
