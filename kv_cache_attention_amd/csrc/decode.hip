@@ -404,14 +404,16 @@ void decode_split_kernel(
 
 // Combines the S split partials of one (session, KV head, head group) for
 // one head and 32 dims.  Thread (d, r) takes splits r, r + 8, r + 16, ...:
-// it loads their accumulators and (m, l) records together (the first kEarly
-// of them before using any, so the merge waits on memory about once) and sums
-// them in its own frame; the eight threads of a dim then combine their
+// it loads the accumulators and (m, l) records of its first kMergeEarly
+// splits before using any (every MFMA plan fits, so the merge waits on
+// memory about once; the f32 plans' longer split lists follow in batches of
+// kMergeTail), and sums them in its own frame; the eight threads of a dim then combine their
 // (m, l, acc) through LDS in the fixed order r = 0 .. 7 (one barrier), so the
 // result does not depend on timing.  A split that saw no key (l = 0) adds
 // nothing; one whose sum is NaN (NaN scores, even with m = -inf) makes the
 // result NaN.
 constexpr int kMergeEarly = 32;
+constexpr int kMergeTail = 16;
 
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
@@ -452,19 +454,34 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     l += f * mlv[k].y;
     a += f * av[k];
   }
-  // more than 8 kMergeEarly splits (f32 plans): a running frame
-  for (int s = r + 8 * kMergeEarly; s < S; s += 8) {
-    const float2 x = ml[s];
-    if (x.y == 0.f) continue;
-    if (x.x > m) {
-      const float f = fast_exp2(m - x.x);  // 0 while m is -inf
+  // more than 8 kMergeEarly splits (f32 plans): further batches of kMergeTail
+  // splits per thread, each batch's loads issued together, in a running
+  // frame that moves to the batch's largest m
+  for (int s0 = r + 8 * kMergeEarly; s0 < S; s0 += 8 * kMergeTail) {
+    float bv[kMergeTail];
+    float2 bml[kMergeTail];
+#pragma unroll
+    for (int k = 0; k < kMergeTail; ++k) {
+      const int s = s0 + 8 * k;
+      bv[k] = s < S ? pa[(size_t)s * PS] : 0.f;
+      bml[k] = s < S ? ml[s] : make_float2(-INFINITY, 0.f);
+    }
+    float mb = m;
+#pragma unroll
+    for (int k = 0; k < kMergeTail; ++k) mb = fmaxf(mb, bml[k].x);
+    if (mb > m) {
+      const float f = fast_exp2(m - mb);  // 0 while m is -inf
       l *= f;
       a *= f;
-      m = x.x;
+      m = mb;
     }
-    const float f = fast_exp2(x.x - m);
-    l += f * x.y;
-    a += f * pa[(size_t)s * PS];
+#pragma unroll
+    for (int k = 0; k < kMergeTail; ++k) {
+      if (bml[k].y == 0.f) continue;
+      const float f = fast_exp2(bml[k].x - m);
+      l += f * bml[k].y;
+      a += f * bv[k];
+    }
   }
   red_a[r][dl] = a;
   if (dl == 0) {

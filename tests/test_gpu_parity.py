@@ -258,6 +258,7 @@ DECODE_CASES = [
     # f32 plans by the step's size (8 heads: 2, 4 or 8 heads per workgroup)
     ("f32", 2, 8, 1, 128, 16448, [16385, 9000]),
     ("f32", 1, 8, 1, 64, 16448, [16385]),
+    ("f32", 1, 1, 1, 64, 19264, [19200]),          # 300 splits: the merge's later batches
 ]
 
 
@@ -326,7 +327,7 @@ DECODE_STEP_CASES = [
     ("f32", 1, 4, 2, 64, 128, [0]),
     ("f32", 3, 16, 1, 256, 1088, [0, 517, 1087]),  # two head groups per KV head
     ("f32", 2, 8, 2, 256, 4160, [4096, 33]),
-    ("f32", 1, 8, 1, 64, 40000, [39000]),          # all heads per workgroup
+    ("f32", 1, 8, 1, 64, 40000, [39000]),          # all heads per workgroup, 512 splits
     ("f32", 1, 8, 1, 256, 4160, [4096]),           # two heads per workgroup
 ]
 
