@@ -106,13 +106,17 @@ __device__ __forceinline__ void load_unit_v(UnitRegs<D, BF16>& r, int u, int lan
   }
 }
 
-// Scores, online softmax and value accumulation of one unit.
+// Scores, online softmax and value accumulation of one unit.  Once the
+// scores have used the K registers, the K of unit next_u (if >= 0) is loaded
+// into them.
 template <int D, int HPW, bool BF16>
 __device__ __forceinline__ void process_unit(UnitRegs<D, BF16>& r, int u, int lane, int ctx,
                                              float sl2e, const typename Elem<BF16>::T* q_lds,
                                              typename Elem<BF16>::T* p_lds, float (&m_run)[HPW],
                                              float (&l_run)[HPW],
-                                             float (&acc)[HPW][UnitRegs<D, BF16>::ND]) {
+                                             float (&acc)[HPW][UnitRegs<D, BF16>::ND],
+                                             int next_u,
+                                             const typename Elem<BF16>::T* __restrict__ kc) {
   using R = UnitRegs<D, BF16>;
   constexpr int NCH = R::NCH, ND = R::ND, NG = R::NG;
   const int kk = lane & 15, qd = lane >> 4;
@@ -154,6 +158,10 @@ __device__ __forceinline__ void process_unit(UnitRegs<D, BF16>& r, int u, int la
     a += xor_shfl(a, 32);
     s[h] = pos < ctx ? a * sl2e : -INFINITY;
   }
+  // the next loads may not move above the last use of the K registers
+  __builtin_amdgcn_sched_barrier(0);
+  if (next_u >= 0) load_unit_k<D, BF16>(r, next_u, lane, kc);
+  __builtin_amdgcn_sched_barrier(0);
   // ---- online softmax over the unit (16-lane butterfly max)
   float p[HPW];
 #pragma unroll
@@ -352,17 +360,19 @@ void decode_split_kernel(
     for (int t = 0; t < ND; ++t) acc[h][t] = 0.f;
   }
 
-  // Latency is hidden by occupancy (several waves per SIMD, each with one
-  // unit's loads in flight) rather than by a second register set per wave.
-  bool first = true;
+  // One register set per wave (the operands of a unit fill most of it): the
+  // next unit's K goes into the K registers as soon as the scores have used
+  // them, so it arrives during this unit's softmax and value product, and a
+  // unit's V is loaded ahead of its scores; the other waves of the SIMD
+  // cover the rest of the latency.  (Loading the next V at the end of a unit
+  // instead made the compiler keep far more registers live: 129 -> 255 at
+  // D = 64, spills at D = 256.)
   for (; u < u1; u += kWaves) {
-    if (!first) {
-      load_unit_k<D, BF16>(ra, u, lane, kc);
-      load_unit_v<D, BF16>(ra, u, lane, vc);
-    }
-    first = false;
+    const int nu = u + kWaves;
+    if (u != u0 + w) load_unit_v<D, BF16>(ra, u, lane, vc);  // the first unit's went out early
     if (owns_new && u == u_new) take_new_row(ra);
-    process_unit<D, HPW, BF16>(ra, u, lane, ctx, sl2e, sm.q, sm.p[w], m_run, l_run, acc);
+    process_unit<D, HPW, BF16>(ra, u, lane, ctx, sl2e, sm.q, sm.p[w], m_run, l_run, acc,
+                               nu < u1 ? nu : -1, kc);
   }
 
   // ---- merge the four waves
