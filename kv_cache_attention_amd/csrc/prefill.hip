@@ -152,8 +152,9 @@ __device__ __forceinline__ bool make_tiling(const ChunkArg& ca, int Hq, int Hkv,
   t.row_lo = t.m_base / t.G;
   const int row_hi = min(R - 1, (t.m_base + kMTile - 1) / t.G);
   const int nkt = (start + row_hi) / kNTile + 1;
-  t.kt0 = (int)((long long)t.split * nkt / S);
-  t.kt1 = (int)((long long)(t.split + 1) * nkt / S);
+  // split * nkt stays below 2^31 (at most 64 splits of 2048 key tiles)
+  t.kt0 = t.split * nkt / S;
+  t.kt1 = (t.split + 1) * nkt / S;
   t.kend = start + R;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
@@ -835,13 +836,27 @@ __device__ __forceinline__ void dma_q(const Tiling& t, const float* __restrict__
   const int row_hi = min(t.R - 1, (t.m_base + kMTile - 1) / t.G);
   const float* base = q + ((size_t)t.row0 + t.row_lo) * Hq * D;
   const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, (size_t)(row_hi - t.row_lo + 1) * Hq * D * 4);
+  if constexpr (GR == kWave) {
+    // one column per wave instruction (column 8 i + w): its (row, head), and
+    // so the start of its D values, are the same for every lane of the wave
+    // and are worked out once per instruction on the scalar unit
 #pragma unroll
-  for (int i = 0; i < kMTile * GR / NT; ++i) {
-    const int p = i * NT + t.w * 64 + t.lane;  // LDS granule this lane fills
-    const int col = p / GR, j = (p % GR) ^ (col & (GR - 1));
-    const int m = min(t.m_base + col, t.M_total - 1);
-    const int off = (((m / t.G - t.row_lo) * Hq + t.g * t.G + m % t.G) * D + 4 * j) * 4;
-    dma16(rs, dst + (size_t)(i * NT + t.w * 64) * 16, off);
+    for (int i = 0; i < kMTile * GR / NT; ++i) {
+      const int col = __builtin_amdgcn_readfirstlane(i * (NT / GR) + t.w);
+      const int m = min(t.m_base + col, t.M_total - 1);
+      const int cbase = __builtin_amdgcn_readfirstlane(
+          ((m / t.G - t.row_lo) * Hq + t.g * t.G + m % t.G) * D * 4);
+      dma16(rs, dst + (size_t)(i * NT + t.w * 64) * 16, cbase + 16 * (t.lane ^ (col & (GR - 1))));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kMTile * GR / NT; ++i) {
+      const int p = i * NT + t.w * 64 + t.lane;  // LDS granule this lane fills
+      const int col = p / GR, j = (p % GR) ^ (col & (GR - 1));
+      const int m = min(t.m_base + col, t.M_total - 1);
+      const int off = (((m / t.G - t.row_lo) * Hq + t.g * t.G + m % t.G) * D + 4 * j) * 4;
+      dma16(rs, dst + (size_t)(i * NT + t.w * 64) * 16, off);
+    }
   }
 }
 
