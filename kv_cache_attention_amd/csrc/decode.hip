@@ -625,6 +625,33 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
                      vrs, ((4 * t + r) * D + 16 * db + lc) * 16, 0, kStreamAux));
   };
 
+  // The decode step's new row (position ctx - 1, given by k_new / v_new; its
+  // handling is described below).  The wave that owns it loads it before
+  // anything else: k_new and v_new come from the caller's last kernel and may
+  // be far from this CU, and their latency should run alongside the tiles'
+  // and q's, not after them (one 16K step with inputs not in cache: 17.9 us
+  // with these loads after q, as the other inputs' latency allows).
+  const int p_new = ctx - 1, t_new = p_new / kDecTile;
+  const bool owns_new = k_new != nullptr && t_new % NW == j0;
+  // K: lane l holds dims 8 l .. 8 l + 7 (bf16, lanes below D / 8) or 4 l ..
+  // 4 l + 3 (int8-K, lanes below D / 4); V: dims l + 64 i
+  float4 nk0 = make_float4(0.f, 0.f, 0.f, 0.f), nk1 = nk0;
+  float nv[D / 64];
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) nv[i] = 0.f;
+  if (owns_new) {
+    const float* kn = k_new + ((size_t)b * Hkv + g) * D;
+    const float* vn = v_new + ((size_t)b * Hkv + g) * D;
+    if constexpr (I8) {
+      if (4 * lane < D) nk0 = *reinterpret_cast<const float4*>(kn + 4 * lane);
+    } else if (lane < D / 8) {
+      nk0 = *reinterpret_cast<const float4*>(kn + 8 * lane);
+      nk1 = *reinterpret_cast<const float4*>(kn + 8 * lane + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) nv[i] = vn[lane + 64 * i];
+  }
+
   DecTile<D, I8> ta_, tb_;
   if (t0 < t1) load(ta_, t0);
   if (t0 + 1 < t1) load(tb_, t0 + 1);
@@ -703,29 +730,24 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   uint32_t nf_pos = 0;  // and their positions in it
 
   // One tile; x is reloaded with tile t + 2 once its operands are consumed.
-  // The decode step's new row (position ctx - 1, given by k_new / v_new).
-  // The wave whose turn covers its tile rounds it exactly as the append
-  // kernel rounds, writes it to the cache at once (its loads overlap the
-  // first tiles) and keeps the bf16 row in its LDS merge slot, idle until the
-  // end; when it reaches that tile it uses those values in place of what its
-  // loads of the tile brought in.  No other wave touches that position.
-  const int p_new = ctx - 1, t_new = p_new / kDecTile;
-  // int8-K: the wave quantises the row as the append kernel does and keeps
-  // its codes (as bf16 keeps its rounded row) and its scale s_new.
-  const bool owns_new = k_new != nullptr && t_new % NW == j0;
+  // The decode step's new row: the wave whose turn covers its tile rounds it
+  // exactly as the append kernel rounds, writes it to the cache at once (its
+  // loads overlap the first tiles) and keeps the bf16 row in its LDS merge
+  // slot, idle until the end; when it reaches that tile it uses those values
+  // in place of what its loads of the tile brought in.  No other wave
+  // touches that position.  int8-K: the wave quantises the row as the append
+  // kernel does and keeps its codes (as bf16 keeps its rounded row) and its
+  // scale s_new.
   uint16_t* row_lds = reinterpret_cast<uint16_t*>(sacc[w]);  // [K row][V row D bf16]
   float s_new = 0.f;
   if (owns_new) {
     const size_t slab_el = ((size_t)b * Hkv + g) * (size_t)C * D;
-    const float* kn = k_new + ((size_t)b * Hkv + g) * D;
-    const float* vn = v_new + ((size_t)b * Hkv + g) * D;
     uint16_t* vw = reinterpret_cast<uint16_t*>(v_cache) + slab_el;
     const int gv = vbf16_group(p_new), e = vbf16_slot(p_new);
     if constexpr (I8) {
       // lane l: dims 4 l .. 4 l + 3; amax and NaN flag across the wave
       const bool mine = 4 * lane < D;
-      const float4 x = mine ? *reinterpret_cast<const float4*>(kn + 4 * lane)
-                            : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 x = nk0;
       AbsMax am;
       am.add(x.x); am.add(x.y); am.add(x.z); am.add(x.w);
       float m = am.m, nf = am.nan ? 1.f : 0.f;
@@ -753,17 +775,17 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
       if (lane == 0) k_scales[slab_i * C + p_new] = s_new;
     } else {
       uint4* kw = reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(k_cache) + slab_el);
-      for (int c = lane; c < D / 8; c += 64) {  // K: one 8-dim vector per lane
-        const float4 x0 = *reinterpret_cast<const float4*>(kn + 8 * c);
-        const float4 x1 = *reinterpret_cast<const float4*>(kn + 8 * c + 4);
-        const uint4 o = make_uint4(pack_bf16x2(x0.x, x0.y), pack_bf16x2(x0.z, x0.w),
-                                   pack_bf16x2(x1.x, x1.y), pack_bf16x2(x1.z, x1.w));
-        kw[k_vec_index(p_new, c, D, 8)] = o;
-        reinterpret_cast<uint4*>(row_lds)[c] = o;
+      if (lane < D / 8) {  // K: one 8-dim vector per lane
+        const uint4 o = make_uint4(pack_bf16x2(nk0.x, nk0.y), pack_bf16x2(nk0.z, nk0.w),
+                                   pack_bf16x2(nk1.x, nk1.y), pack_bf16x2(nk1.z, nk1.w));
+        kw[k_vec_index(p_new, lane, D, 8)] = o;
+        reinterpret_cast<uint4*>(row_lds)[lane] = o;
       }
     }
-    for (int d = lane; d < D; d += 64) {  // V: the row's element of each vector
-      const uint16_t h = (uint16_t)f32_to_bf16_bits(vn[d]);
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) {  // V: the row's element of each vector
+      const int d = lane + 64 * i;
+      const uint16_t h = (uint16_t)f32_to_bf16_bits(nv[i]);
       vw[((size_t)gv * D + d) * 8 + e] = h;
       row_lds[D + d] = h;
     }
