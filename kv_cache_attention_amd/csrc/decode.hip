@@ -65,6 +65,8 @@ struct alignas(16) DecodeSmem {
   float m[kWaves][HPW];
   float l[kWaves][HPW];
   float acc[kWaves][HPW * D];
+  // the decode step's new K and V rows (f32), for the wave that owns them
+  float row[2][D];
 };
 
 // K / V registers of one unit for one lane
@@ -276,29 +278,32 @@ void decode_split_kernel(
   const int u1 = (int)((long long)(split + 1) * n_units / S);
 
   // The decode step's new row (k_new / v_new, position ctx - 1): the wave
-  // whose unit holds it stores it as the append kernel would (an f32 copy;
-  // head group 0 of the slab only) and takes its values in registers in
-  // place of what its loads of that unit bring in, so no wave waits on the
-  // store and no other wave reads that position.
+  // whose unit holds it loads it before anything else (the caller's last
+  // kernel wrote it, so it may be far from this CU, and its latency should
+  // run alongside the first unit's and q's), keeps it in LDS, stores it as
+  // the append kernel would (an f32 copy; head group 0 of the slab only),
+  // and takes its values in place of what its loads of that unit bring in,
+  // so no wave waits on the store and no other wave reads that position.
   const int p_new = ctx - 1, u_new = p_new / kUnit;
   const bool owns_new = k_new != nullptr && u_new >= u0 && u_new < u1 &&
                         (u_new - u0) % kWaves == w;
-  const float* kn = owns_new ? k_new + ((size_t)b * Hkv + g) * D : nullptr;
-  const float* vn = owns_new ? v_new + ((size_t)b * Hkv + g) * D : nullptr;
-  if (owns_new && hg == 0) {
-    float* kw = reinterpret_cast<float*>(const_cast<void*>(k_cache)) + slab;
-    float* vw = reinterpret_cast<float*>(const_cast<void*>(v_cache)) + slab;
-    for (int c = lane; c < D / 4; c += kWave)
-      *reinterpret_cast<float4*>(kw + k_vec_index(p_new, c, D, 4) * 4) =
-          *reinterpret_cast<const float4*>(kn + 4 * c);
-    for (int d = lane; d < D; d += kWave) vw[vf32_vec_index(p_new, d, D) * 4 + (p_new & 3)] = vn[d];
+  float4 nk = make_float4(0.f, 0.f, 0.f, 0.f);  // K dims 4 lane .. 4 lane + 3 (lanes below D / 4)
+  float nv[ND];                                  // V dims lane + 64 t
+#pragma unroll
+  for (int t = 0; t < ND; ++t) nv[t] = 0.f;
+  if (owns_new) {
+    const float* kn = k_new + ((size_t)b * Hkv + g) * D;
+    const float* vn = v_new + ((size_t)b * Hkv + g) * D;
+    if (4 * lane < D) nk = *reinterpret_cast<const float4*>(kn + 4 * lane);
+#pragma unroll
+    for (int t = 0; t < ND; ++t) nv[t] = vn[lane + 64 * t];
   }
   auto take_new_row = [&](R& r) {
     if ((lane & 15) == (p_new & 15)) {  // this lane's K slices are of the new position
       const int qd = lane >> 4;
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const float4 x = *reinterpret_cast<const float4*>(kn + 4 * (qd * NCH + i));
+        const float4 x = *reinterpret_cast<const float4*>(&sm.row[0][4 * (qd * NCH + i)]);
         r.k[i] = make_uint4(__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z),
                             __float_as_uint(x.w));
       }
@@ -306,7 +311,7 @@ void decode_split_kernel(
     const int gi = (p_new & 15) >> 2, e = p_new & 3;  // V: group gi of the unit, slot e
 #pragma unroll
     for (int t = 0; t < ND; ++t) {
-      const uint32_t x = __float_as_uint(vn[lane + 64 * t]);
+      const uint32_t x = __float_as_uint(sm.row[1][lane + 64 * t]);
 #pragma unroll
       for (int g2 = 0; g2 < R::NG; ++g2) {
         if (g2 != gi) continue;
@@ -324,6 +329,20 @@ void decode_split_kernel(
   if (u < u1) {
     load_unit_k<D, BF16>(ra, u, lane, kc);
     load_unit_v<D, BF16>(ra, u, lane, vc);
+  }
+  if (owns_new) {
+    if (4 * lane < D) *reinterpret_cast<float4*>(&sm.row[0][4 * lane]) = nk;
+#pragma unroll
+    for (int t = 0; t < ND; ++t) sm.row[1][lane + 64 * t] = nv[t];
+    if (hg == 0) {
+      float* kw = reinterpret_cast<float*>(const_cast<void*>(k_cache)) + slab;
+      float* vw = reinterpret_cast<float*>(const_cast<void*>(v_cache)) + slab;
+      if (4 * lane < D) *reinterpret_cast<float4*>(kw + k_vec_index(p_new, lane, D, 4) * 4) = nk;
+#pragma unroll
+      for (int t = 0; t < ND; ++t)
+        vw[vf32_vec_index(p_new, lane + 64 * t, D) * 4 + (p_new & 3)] = nv[t];
+    }
+    wave_lds_sync();
   }
 
   // ---- q -> LDS (bf16 with RNE, or f32 copy); all loads issued first
