@@ -83,8 +83,10 @@
  *   Cache contents beyond the rows appended so far are never read into a
  *   result (they may hold anything, NaN included).
  *
- * Limits: 1 <= Hkv, Hkv divides Hq, D in {64, 128, 256}, C a multiple of 64
- * with 64 <= C <= 131072, batch >= 1.
+ * Limits: 1 <= Hkv, Hkv divides Hq, Hq <= 1024, D in {64, 128, 256}, C a
+ * multiple of 64 with 64 <= C <= 131072, 1 <= batch <= 65536.  (With these
+ * every size, index and launch grid the library forms stays far inside its
+ * integer types; a shape beyond them is rejected as KA_ERR_OUT_OF_RANGE.)
  */
 #ifndef KA_ATTN_H_
 #define KA_ATTN_H_
@@ -98,11 +100,13 @@ extern "C" {
 
 #define KA_ATTN_ABI_VERSION 1
 #define KA_ATTN_MAX_CAPACITY 131072
+#define KA_ATTN_MAX_Q_HEADS 1024
+#define KA_ATTN_MAX_BATCH 65536
 
 typedef enum ka_status {
   KA_OK = 0,
   KA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad count, Hq % Hkv != 0, bad scale */
-  KA_ERR_OUT_OF_RANGE = 2,     /* start + R > C, ctx < 1 or ctx > C, C too large  */
+  KA_ERR_OUT_OF_RANGE = 2,     /* start + R > C, ctx < 1 or ctx > C, C, Hq or B too large */
   KA_ERR_UNSUPPORTED = 3,      /* head_dim or kv dtype not built                  */
   KA_ERR_WORKSPACE = 4,        /* workspace smaller than required                 */
   KA_ERR_HIP = 5               /* a HIP runtime error; text in ka_attn_last_error */

@@ -47,6 +47,11 @@ ka_status check_shape(const ka_attn_shape* s, ka::Shape* out) {
   if (s->kv_dtype != KA_DTYPE_F32 && s->kv_dtype != KA_DTYPE_BF16 && s->kv_dtype != KA_DTYPE_I8K)
     return fail(KA_ERR_UNSUPPORTED, "kv_dtype %d not supported (0 = f32, 1 = bf16, 2 = int8 K)",
                 s->kv_dtype);
+  if (s->num_q_heads > KA_ATTN_MAX_Q_HEADS)
+    return fail(KA_ERR_OUT_OF_RANGE, "num_q_heads %d exceeds %d", s->num_q_heads,
+                KA_ATTN_MAX_Q_HEADS);
+  if (s->batch > KA_ATTN_MAX_BATCH)
+    return fail(KA_ERR_OUT_OF_RANGE, "batch %d exceeds %d", s->batch, KA_ATTN_MAX_BATCH);
   if (s->capacity > KA_ATTN_MAX_CAPACITY)
     return fail(KA_ERR_OUT_OF_RANGE, "capacity %d exceeds %d", s->capacity, KA_ATTN_MAX_CAPACITY);
   if (s->capacity < 64 || s->capacity % 64 != 0)

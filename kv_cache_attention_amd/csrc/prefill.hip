@@ -1946,11 +1946,13 @@ PrefillPlan plan_prefill(const Shape& s, int start, int R) {
 
 size_t prefill_workspace_bound(const Shape& s, int max_rows) {
   if (max_rows <= 0) return 0;
+  if (max_rows > s.capacity) max_rows = s.capacity;  // no chunk holds more rows
   const int G = s.num_q_heads / s.num_kv_heads;
   const int mt_max = (int)(((long long)max_rows * G + kMTile - 1) / kMTile);
   size_t best = 0;
   for (int mt = 1; mt <= mt_max; ++mt) {
     const long long units = (long long)s.batch * s.num_kv_heads * mt;
+    if (units >= (long long)kMaxWgRounds * kCUs) break;  // from here on no chunk splits
     const int S = max_splits(units);  // choose_splits never exceeds it
     if (S <= 1) continue;
     const size_t bytes = (size_t)units * S * kMTile * partial_bytes(s);
@@ -1992,6 +1994,8 @@ size_t prefill_ragged_workspace(const Shape& s, const int32_t* start, const int3
 // Hkv (ceil(T G / 128) + min(B, T)) for T rows in all.
 size_t prefill_ragged_workspace_bound(const Shape& s, long long max_total_rows) {
   if (max_total_rows <= 0) return 0;
+  // no valid call holds more rows than every session's full capacity
+  if (max_total_rows > (long long)s.batch * s.capacity) max_total_rows = (long long)s.batch * s.capacity;
   const int G = s.num_q_heads / s.num_kv_heads;
   const long long sessions = max_total_rows < s.batch ? max_total_rows : s.batch;
   const long long u_max = (long long)s.num_kv_heads * ((max_total_rows * G + kMTile - 1) / kMTile + sessions);

@@ -71,6 +71,10 @@ def test_cache_bytes():
     assert ka.cache_bytes(S(kv_dtype=ka.F32, batch=3, num_kv_heads=2)) == 3 * 2 * 4096 * 256 * 4
     assert ka.cache_bytes(S(head_dim=96)) == 0
     assert ka.cache_bytes(S(capacity=100)) == 0
+    # the largest shape the ABI takes: sizes stay exact
+    big = S(batch=65536, num_q_heads=1024, num_kv_heads=1024, capacity=131072, kv_dtype=ka.F32)
+    assert ka.cache_bytes(big) == 65536 * 1024 * 131072 * 256 * 4
+    assert ka.cache_bytes(S(batch=65537)) == 0 and ka.cache_bytes(S(num_q_heads=1032)) == 0
 
 
 FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
@@ -94,6 +98,8 @@ def _decode(shape, ctx, scale=0.0625, ws=None, ws_bytes=0, q=FAKE, out=ctypes.c_
 @pytest.mark.parametrize("shape,status", [
     (S(batch=0), 1), (S(num_q_heads=0), 1), (S(num_kv_heads=3), 1), (S(head_dim=80), 3),
     (S(kv_dtype=7), 3), (S(capacity=131072 + 64), 2), (S(capacity=1000), 1), (S(capacity=0), 1),
+    (S(num_q_heads=1025, num_kv_heads=1025), 2), (S(num_q_heads=2048, num_kv_heads=2), 2),
+    (S(batch=65537), 2),
 ])
 def test_bad_shapes_rejected_everywhere(shape, status):
     _lib_or_skip()
