@@ -1028,8 +1028,13 @@ __device__ __forceinline__ void pv_chunk_b(int j, uint4 vop, const bf16x8 (&p_ow
 // multiplied into acc with the V tile in v_lds (skipped when FIRST).
 //
 // Chunk c (c < NC = D/16) carries the score MFMA of k-step c, the value MFMA
-// of chunk c, the LDS reads of chunk c+2 and softmax phase slices; a
-// scheduling fence closes it.
+// of chunk c, the LDS reads of a later chunk and softmax phase slices; a
+// scheduling fence closes it.  A wave raises its issue priority for the
+// chunk's LDS reads and MFMAs and lowers it again for the softmax slice.
+// Without that the older of the two waves sharing a SIMD wins every MFMA
+// slot both want, runs ahead and then waits at the next barrier while the
+// younger one finishes the tile alone, one wave deep; with it the pair tends
+// to alternate (one issuing MFMAs while the other runs its softmax slice).
 //   phases: 0 max; 1 cross-half max, largest score and frame check;
 //   2..9 exponentials (2 each); 10, 11 bf16 conversion of the weights;
 //   12 running sum.
@@ -1043,7 +1048,9 @@ __device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
                                              const ColB& c, int kh, float m_use, float m_ref,
                                              float& m_all, float& l_run, bool& ovf) {
   constexpr int NC = D / 16;
-  constexpr int DIST = 1;
+  // operand reads run one chunk ahead (two for int8 K, whose score
+  // k-steps span two chunks: measured 0.7% faster there, no change for bf16)
+  constexpr int DIST = I8 ? 2 : 1;
   constexpr int NPH = 13;
 #pragma unroll
   for (int i = 0; i < 16; ++i) nxt[i] = 0.f;
@@ -1093,10 +1100,14 @@ __device__ __forceinline__ void fused_step_b(const uint4* __restrict__ k_lds,
   for (int cc = 0; cc < DIST; ++cc) issue(cc);
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
     if (cc + DIST < NC) issue(cc + DIST);
     const uint4(&r)[2] = ring[cc % (DIST + 1)];
     if (!I8 || (cc & 1) == 0) score_mfma<I8>(nxt, r[0], qreg[I8 ? cc / 2 : cc]);
     if (!FIRST) pv_chunk_b<D>(cc, r[1], p_prev, p_oth, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int ph = 0; ph < NPH; ++ph)
       if (ph * NC / NPH == cc) phase(ph);
