@@ -772,10 +772,10 @@ struct MtCfg {
 
 // Asynchronous copy of K tile kt into LDS: codes (and, I8, the tile's 64
 // scales behind them) or bf16 values.
-template <int D, bool I8>
+template <int D, bool I8, int NT = kBf16Threads>
 __device__ __forceinline__ void load_k(const TileSrc& ksrc, const TileSrc& ssrc, int kt,
                                        unsigned char* dst, int w, int lane) {
-  constexpr int KTB = MtCfg<D, I8>::KTB, NT = kBf16Threads;
+  constexpr int KTB = MtCfg<D, I8>::KTB;
 #pragma unroll
   for (int i = 0; i < (KTB + NT * 16 - 1) / (NT * 16); ++i) {
     const int off = (i * NT + w * 64) * 16;
@@ -1352,8 +1352,12 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
       wait_vmem();
       __syncthreads();
       wait_lgkm();
-      if (i + 2 < n) load_k<D, I8>(ksrc, ssrc, kt + 2, k_load, t.w, t.lane);
-      load_tile<VTB, NT>(vsrc, kt, v_load, t.w, t.lane);
+      // the older wave of each SIMD (waves 0-3) issues the tile copies: it
+      // reaches the step barrier first (see fused_step_b)
+      if (t.w < 4) {
+        if (i + 2 < n) load_k<D, I8, NT / 2>(ksrc, ssrc, kt + 2, k_load, t.w, t.lane);
+        load_tile<VTB, NT / 2>(vsrc, kt, v_load, t.w, t.lane);
+      }
       if (FIRST) {
         m_ref = fmaxf(m_ref, *xf(1, partner, 0));
         m_use = m_ref == -INFINITY ? 0.f : m_ref;
