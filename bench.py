@@ -2,14 +2,15 @@
 
 One step = one pass of the whole path over the 16K session workload: a
 16384-token prompt (8 query heads sharing 1 KV head, head_dim 256, bf16
-cache) prefilled as 21 chunks of 768 rows plus one of 256 -- each chunk an
-append of its K/V rows and a prefill of its query rows -- followed by 64
-decode steps, each one ka_attn_decode_step call (the append of the step's
-row and its decode).  Inputs are
+cache) prefilled as 21 chunks of 768 rows plus one of 256 -- each chunk one
+ka_attn_append_prefill_chunk call (the append of its K/V rows and the prefill
+of its query rows) -- followed by 64 decode steps, each one
+ka_attn_decode_step call (the append of the step's row and its decode).  Inputs are
 seeded synthetic draws (module ``synth``), resident in HBM before timing.
 
 Printed: one JSON line.  ``value`` is the 16K prefill throughput in rows/s
-(16384 rows / GPU time of the 22 append + prefill calls).  The line also
+(16384 rows / GPU time of the 22 chunk calls; the same chunks as separate
+append and prefill calls are reported beside it).  The line also
 carries the decode time per token at 16K (in-session, and cache-cold over 64
 rotated cache copies) and at 128K (4 sessions batched), the roofline of the
 prefill kernel (bf16 MFMA) and of the 128K decode (HBM), and the CPU oracle
@@ -144,7 +145,8 @@ class Session16K:
         self.vc = ka.alloc_cache(self.shape, fill_byte=0xFF)
         self.out_p = torch.empty(768 * 8 * 256, device="cuda")
         self.out_d = torch.empty(8 * 256, device="cuda")
-        n = max(ka.prefill_workspace_bytes(self.shape, 768),
+        n = max(ka.append_prefill_workspace_bytes(self.shape, 768),
+                ka.prefill_workspace_bytes(self.shape, 768),
                 ka.decode_workspace_bytes(self.shape, w.capacity), 1)
         self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
         # contiguous per-call views
@@ -159,7 +161,15 @@ class Session16K:
             self.dec_views.append((p, self.k[:, p:p + 1], self.v[:, p:p + 1], self.q[0, qrow + t]))
 
     def prefill_phase(self):
-        """22 chunk calls, each an append of the chunk's rows and a prefill."""
+        """22 chunk calls, each ka_attn_append_prefill_chunk (the chunk's append
+        and its prefill in one call)."""
+        sh = self.shape
+        for s, R, kk, vv, qq, oo in self.chunk_views:
+            ka.append_prefill_chunk(sh, qq, kk, vv, self.kc, self.vc, oo, s, R, self.w.scale,
+                                    self.ws)
+
+    def prefill_phase_separate(self):
+        """The same 22 chunks as ka_attn_append_kv + ka_attn_prefill_chunk."""
         sh = self.shape
         for s, R, kk, vv, qq, oo in self.chunk_views:
             ka.append_kv(sh, self.kc, self.vc, kk, vv, s, R)
@@ -232,15 +242,21 @@ def bench_session(steps, warmup, hold):
     phase_p = [r[0][0].elapsed_time(r[0][1]) for r in rec]
     phase_d = [r[1][0].elapsed_time(r[1][1]) for r in rec]
     log("16K session: timed steps done")
+    sep = [span_ms(lambda i: s.prefill_phase_separate(), 1, hold, 6.0) for _ in range(3)]
     sh = s.shape
-    pre_calls = []
+    fused_calls, pre_calls = [], []
     for (st, R, kk, vv, qq, oo) in s.chunk_views:
+        # each call appends the same rows again: the cache ends as one pass leaves it
+        fused_calls.append(per_call_ms(
+            lambda i: ka.append_prefill_chunk(sh, qq, kk, vv, s.kc, s.vc, oo, st, R, s.w.scale, s.ws),
+            hold, n=6, reps=3))
         pre_calls.append(per_call_ms(
             lambda i: ka.prefill_chunk(sh, qq, s.kc, s.vc, oo, st, R, s.w.scale, s.ws), hold, n=6, reps=3))
     p, kk, vv, qq = s.dec_views[-1]
     dec_call = per_call_ms(
         lambda i: ka.decode_step(sh, qq, kk, vv, s.kc, s.vc, s.out_d, [p], s.w.scale, s.ws), hold, n=16)
     return dict(w=s.w, wall_ms=wall * 1e3, prefill_phase_ms=float(np.median(phase_p)),
+                prefill_phase_separate_ms=float(np.median(sep)), fused_calls_ms=np.array(fused_calls),
                 decode_phase_ms=float(np.median(phase_d)), prefill_calls_ms=np.array(pre_calls),
                 decode_call_ms=dec_call, session=s)
 
@@ -639,11 +655,13 @@ def main():
     r = bench_session(args.steps, args.warmup, hold)
     w = r["w"]
     flops, pairs = prefill_flops(w)
+    fused_calls = r["fused_calls_ms"]                   # [22] fused append + prefill calls
+    fused_ms = float(fused_calls.sum())
     pre_calls = r["prefill_calls_ms"]                   # [22] prefill calls alone (no append)
     pre_kernel_ms = float(pre_calls.sum())
     achieved_tf = flops / (pre_kernel_ms * 1e-3) / 1e12
     rows = sum(R for _, R in w.chunks)
-    value = rows / (r["prefill_phase_ms"] * 1e-3)        # append + prefill, 22 chunks
+    value = rows / (r["prefill_phase_ms"] * 1e-3)        # 22 fused append + prefill calls
     dec16_step = r["decode_phase_ms"] / len(w.decode_positions)
     last_chunk_ms = float(pre_calls[-2])
     s_last, R_last = w.chunks[-2]
@@ -657,19 +675,25 @@ def main():
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": ("16K session: 8 query heads / 1 KV head, head_dim 256, bf16 KV "
                                 "cache (f32 accumulate), 16384-row prompt as 21x768 + 256 chunks "
-                                "(append + prefill each), then 64 decode steps (one fused append + decode call each)"),
+                                "(one fused append + prefill call each), then 64 decode steps "
+                                "(one fused append + decode call each)"),
                    "global_batch": 1, "seq_len": 16384, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved_tf, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved_tf / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic.get("prefill_call_bytes_per_launch"), "traffic_unit": "B/launch",
-                     "kernel": "prefill chunk call (prefill_mtile_kernel<256, false> + its merge kernel), "
-                               "average over the 22 chunks",
+                     "kernel": "prefill call (ka_attn_prefill_chunk: prefill_mtile_kernel<256, false, "
+                               "false>, which stages f32 Q, and its merge kernel), average over the "
+                               "22 chunks; the session's fused chunk call runs the same loop on a "
+                               "bf16 Q copy its append writes",
                      "algorithmic_flops_per_step": flops, "causal_pairs": pairs,
                      "avg_launch_ms": round(pre_kernel_ms / len(w.chunks), 5),
                      "time": "each chunk's prefill call back to back, (2n - n calls) / n"},
         "wall_ms_per_step": round(r["wall_ms"], 3),
         "prefill_16k_ms": round(r["prefill_phase_ms"], 4),
+        "prefill_16k_ms_separate_calls": round(r["prefill_phase_separate_ms"], 4),
+        "prefill_16k_ms_chunk_calls_only": round(fused_ms, 4),
         "prefill_16k_ms_prefill_calls_only": round(pre_kernel_ms, 4),
+        "prefill_last768_chunk_call_us": round(float(fused_calls[-2]) * 1e3, 2),
         "prefill_last768_rows_per_s": round(R_last / (last_chunk_ms * 1e-3), 1),
         "prefill_last768_tflops": round(flops_last / (last_chunk_ms * 1e-3) / 1e12, 2),
         "decode_us_per_token_16k": round(dec16_step * 1e3, 3),

@@ -224,6 +224,44 @@ ka_status ka_attn_prefill_chunk(const ka_attn_shape* s, const float* q,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * A chunk's append and its prefill in one call: the same result, bit for
+ * bit, as ka_attn_append_kv(s, k_cache, v_cache, k_new, v_new, start_pos,
+ * row_count, stream) followed by ka_attn_prefill_chunk(s, q, k_cache, v_cache,
+ * out, start_pos, row_count, scale, ...) -- the chunk's rows enter the state
+ * before they are attended (Karume v0.8.0 release notes, "Features": sessions
+ * continue the KV cache; v0.12.0, "Performance": the tiled states-form
+ * prefill).  On bf16 caches, where the M-tile kernel serves the chunk, the
+ * append kernel also stores the chunk's Q rows as bf16 of q * scale * log2(e),
+ * rounded exactly as the prefill rounds its Q operands, in the workspace; the
+ * prefill then reads those (half the bytes of f32 Q, and no conversion).
+ * Arguments and layouts as for the two calls; out may not alias q.
+ * workspace: device scratch of at least
+ * ka_attn_append_prefill_workspace_bytes(s, row_count) bytes (may be NULL
+ * when that is 0).  Errors: those of the two calls.
+ */
+ka_status ka_attn_append_prefill_chunk(const ka_attn_shape* s, const float* q,
+                                       const float* k_new, const float* v_new, void* k_cache,
+                                       void* v_cache, float* out, int32_t start_pos,
+                                       int32_t row_count, float scale, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes that ka_attn_append_prefill_chunk needs for any chunk of at
+ * most max_rows rows at any start position of shape s (0 if none is needed):
+ * ka_attn_prefill_workspace_bytes(s, max_rows) rounded up to 256, plus B *
+ * max_rows * Hq * D * 2 on bf16 caches.
+ */
+size_t ka_attn_append_prefill_workspace_bytes(const ka_attn_shape* s, int32_t max_rows);
+
+/*
+ * Workspace bytes one ka_attn_append_prefill_chunk call with these arguments
+ * needs (at most ka_attn_append_prefill_workspace_bytes(s, row_count); 0 if
+ * none is needed or the arguments are invalid).  Host only.
+ */
+size_t ka_attn_append_prefill_workspace_need(const ka_attn_shape* s, int32_t start_pos,
+                                             int32_t row_count);
+
+/*
  * Workspace bytes that ka_attn_decode needs when no session's context length
  * exceeds max_ctx_len.
  */

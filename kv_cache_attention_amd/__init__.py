@@ -23,7 +23,8 @@ __all__ = ["Shape", "KaAttnError", "KaAttnUnavailable", "lib", "lib_path", "F32"
            "rope_rows", "append_kv_ragged", "prefill_ragged_workspace_bytes",
            "prefill_ragged_workspace_need", "prefill_ragged",
            "Memory", "session_memory", "cache_resize", "I8K", "int8_self_test",
-           "decode_step_noalloc", "decode_step_noalloc_max_bytes"]
+           "decode_step_noalloc", "decode_step_noalloc_max_bytes", "append_prefill_chunk",
+           "append_prefill_workspace_bytes", "append_prefill_workspace_need"]
 
 F32 = 0
 BF16 = 1
@@ -36,6 +37,8 @@ EXPORTED_SYMBOLS = (
     "ka_attn_abi_version", "ka_attn_cache_bytes", "ka_attn_append_kv", "ka_attn_append_kv_rope",
     "ka_attn_rope_rows",
     "ka_attn_prefill_workspace_bytes", "ka_attn_prefill_workspace_need", "ka_attn_prefill_chunk",
+    "ka_attn_append_prefill_chunk", "ka_attn_append_prefill_workspace_bytes",
+    "ka_attn_append_prefill_workspace_need",
     "ka_attn_decode_workspace_bytes", "ka_attn_decode", "ka_attn_decode_step",
     "ka_attn_decode_step_noalloc", "ka_attn_decode_step_noalloc_max_bytes",
     "ka_attn_append_kv_ragged", "ka_attn_prefill_ragged_workspace_bytes",
@@ -115,6 +118,14 @@ def lib() -> ctypes.CDLL:
     L.ka_attn_prefill_chunk.restype = c_int32
     L.ka_attn_prefill_chunk.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32,
                                         c_float, c_void_p, c_size_t, c_void_p]
+    L.ka_attn_append_prefill_chunk.restype = c_int32
+    L.ka_attn_append_prefill_chunk.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                               c_void_p, c_int32, c_int32, ctypes.c_float,
+                                               c_void_p, c_size_t, c_void_p]
+    L.ka_attn_append_prefill_workspace_bytes.restype = c_size_t
+    L.ka_attn_append_prefill_workspace_bytes.argtypes = [P, c_int32]
+    L.ka_attn_append_prefill_workspace_need.restype = c_size_t
+    L.ka_attn_append_prefill_workspace_need.argtypes = [P, c_int32, c_int32]
     L.ka_attn_decode_workspace_bytes.restype = c_size_t
     L.ka_attn_decode_workspace_bytes.argtypes = [P, c_int32]
     L.ka_attn_decode.restype = c_int32
@@ -288,6 +299,41 @@ def prefill_chunk(shape: Shape, q: torch.Tensor, k_cache: torch.Tensor, v_cache:
     _check(lib().ka_attn_prefill_chunk(ctypes.byref(shape), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                        _ptr(out), int(start_pos), int(row_count), float(scale),
                                        _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def append_prefill_workspace_bytes(shape: Shape, max_rows: int) -> int:
+    return int(lib().ka_attn_append_prefill_workspace_bytes(ctypes.byref(shape), int(max_rows)))
+
+
+def append_prefill_workspace_need(shape: Shape, start_pos: int, row_count: int) -> int:
+    return int(lib().ka_attn_append_prefill_workspace_need(ctypes.byref(shape), int(start_pos),
+                                                           int(row_count)))
+
+
+def append_prefill_chunk(shape: Shape, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                         k_cache: torch.Tensor, v_cache: torch.Tensor, out: torch.Tensor,
+                         start_pos: int, row_count: int, scale: float,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """ka_attn_append_prefill_chunk: append_kv then prefill_chunk in one call."""
+    n = shape.batch * row_count * shape.num_q_heads * shape.head_dim
+    _need(q, "q", torch.float32, n)
+    _need(out, "out", torch.float32, n)
+    nk = shape.batch * row_count * shape.num_kv_heads * shape.head_dim
+    for t, nm in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, nm, torch.float32, nk)
+    cb = cache_bytes(shape)
+    for t, nm in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, nm, None)
+        if t.numel() * t.element_size() < cb:
+            raise ValueError(f"{nm} is smaller than {cb} bytes")
+    ws_bytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", None)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().ka_attn_append_prefill_chunk(ctypes.byref(shape), _ptr(q), _ptr(k_new),
+                                              _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                              int(start_pos), int(row_count), float(scale),
+                                              _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def decode_workspace_bytes(shape: Shape, max_ctx_len: int) -> int:

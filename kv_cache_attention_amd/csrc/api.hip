@@ -268,6 +268,89 @@ ka_status ka_attn_prefill_chunk(const ka_attn_shape* s, const float* q, const vo
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// The fused append and prefill: on bf16 caches with an M-tile plan the append
+// also writes the chunk's Q, scaled and rounded, for the prefill kernel to
+// read (half the bytes of f32 Q, and no conversion in the prefill); it sits in
+// the workspace behind the split partials, from a 256-byte boundary.
+size_t round_up_256(size_t n) { return (n + 255) & ~(size_t)255; }
+bool fused_uses_qb(const ka::Shape& sh, const ka::PrefillPlan& plan) {
+  return sh.kv_dtype == KA_DTYPE_BF16 && plan.m_tiles > 0;
+}
+size_t qb_bytes(const ka::Shape& sh, long long rows) {
+  return (size_t)sh.batch * (size_t)rows * sh.num_q_heads * sh.head_dim * 2;
+}
+size_t fused_need(const ka::Shape& sh, const ka::PrefillPlan& plan, int rows) {
+  if (!fused_uses_qb(sh, plan)) return plan.workspace_bytes;
+  return round_up_256(plan.workspace_bytes) + qb_bytes(sh, rows);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ka_attn_append_prefill_workspace_bytes(const ka_attn_shape* s, int32_t max_rows) {
+  ka::Shape sh;
+  if (check_shape(s, &sh) != KA_OK || max_rows <= 0) return 0;
+  const int rows = max_rows < sh.capacity ? max_rows : sh.capacity;
+  const size_t part = ka::prefill_workspace_bound(sh, rows);
+  if (sh.kv_dtype != KA_DTYPE_BF16) return part;
+  return round_up_256(part) + qb_bytes(sh, rows);
+}
+
+size_t ka_attn_append_prefill_workspace_need(const ka_attn_shape* s, int32_t start_pos,
+                                             int32_t row_count) {
+  ka::Shape sh;
+  if (check_shape(s, &sh) != KA_OK) return 0;
+  if (start_pos < 0 || row_count <= 0 || (long long)start_pos + row_count > sh.capacity) return 0;
+  return fused_need(sh, ka::plan_prefill(sh, start_pos, row_count), row_count);
+}
+
+ka_status ka_attn_append_prefill_chunk(const ka_attn_shape* s, const float* q, const float* k_new,
+                                       const float* v_new, void* k_cache, void* v_cache,
+                                       float* out, int32_t start_pos, int32_t row_count,
+                                       float scale, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  ka::Shape sh;
+  ka_status st = check_shape(s, &sh);
+  if (st != KA_OK) return st;
+  if (row_count < 0) return fail(KA_ERR_INVALID_ARGUMENT, "row_count %d < 0", row_count);
+  if (start_pos < 0) return fail(KA_ERR_INVALID_ARGUMENT, "start_pos %d < 0", start_pos);
+  if ((long long)start_pos + row_count > sh.capacity)
+    return fail(KA_ERR_OUT_OF_RANGE, "start_pos %d + row_count %d exceeds capacity %d",
+                start_pos, row_count, sh.capacity);
+  if ((st = check_scale(scale)) != KA_OK) return st;
+  if (row_count == 0) return ok();
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "null tensor pointer");
+  if ((const void*)q == (const void*)out)
+    return fail(KA_ERR_INVALID_ARGUMENT, "out must not alias q");
+  const ka::PrefillPlan plan = ka::plan_prefill(sh, start_pos, row_count);
+  const size_t need = fused_need(sh, plan, row_count);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(KA_ERR_WORKSPACE, "append and prefill need %zu workspace bytes, got %zu", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((st = check_int8(sh)) != KA_OK) return st;
+  const hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  void* qb = nullptr;
+  hipError_t e;
+  if (fused_uses_qb(sh, plan)) {
+    qb = static_cast<unsigned char*>(workspace) + round_up_256(plan.workspace_bytes);
+    e = ka::launch_append_q(sh, k_cache, v_cache, k_new, v_new, start_pos, row_count, q, qb, scale,
+                            hs);
+  } else {
+    e = ka::launch_append(sh, k_cache, v_cache, k_new, v_new, start_pos, row_count, hs);
+  }
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  e = ka::launch_prefill(sh, plan, q, k_cache, v_cache, out, start_pos, row_count, scale,
+                         workspace, hs, qb);
+  if (e != hipSuccess) return hip_fail(e, "prefill launch");
+  return ok();
+}
+
 size_t ka_attn_prefill_ragged_workspace_bytes(const ka_attn_shape* s, int64_t max_total_rows) {
   ka::Shape sh;
   if (check_shape(s, &sh) != KA_OK) return 0;

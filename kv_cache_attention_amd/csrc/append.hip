@@ -121,13 +121,18 @@ __device__ __forceinline__ void quantise_row_wave(const float* rowp, const float
 // ROPE: each new K row is rotated by its position's angles (cos / sin rows of
 // D/2 values, one per appended row) before it is stored; V as given.  MODE
 // (KvMode): f32 K / V; bf16 K / V; int8 K codes with their row scales in
-// k_scales ([B][Hkv][C] f32) and bf16 V.
-template <int MODE, bool ROPE>
+// k_scales ([B][Hkv][C] f32) and bf16 V.  QB (bf16, for the fused append and
+// prefill): the chunk's Q rows q ([rows][Hq][D] f32, packed like k_new) also
+// go to qb as bf16 of q * sl2e, with the rounding the prefill kernel applies
+// to its Q operands, 8 dims per 16-byte vector.
+template <int MODE, bool ROPE, bool QB = false>
 __global__ __launch_bounds__(256) void append_kernel(
     void* __restrict__ k_cache, void* __restrict__ v_cache,
     const float* __restrict__ k_new, const float* __restrict__ v_new,
     const float* __restrict__ rope_cos, const float* __restrict__ rope_sin,
-    float* __restrict__ k_scales, int Hkv, int D, int C, const AppendArg aa) {
+    float* __restrict__ k_scales, int Hkv, int D, int C, const AppendArg aa,
+    const float* __restrict__ q, uint4* __restrict__ qb, int Hq, float sl2e) {
+  static_assert(!QB || MODE == kBF16, "prepared Q only with bf16 caches");
   constexpr bool BF16 = MODE != kF32;             // V (and bf16 K) in the bf16 layouts
   constexpr int E = BF16 ? 8 : 4;                 // V elements per 16-byte vector
   constexpr int EK = MODE == kI8K ? 16 : E;       // K elements per 16-byte vector
@@ -139,6 +144,7 @@ __global__ __launch_bounds__(256) void append_kernel(
   v_groups(BF16, start, R, v_group0, v_groups_per_slab);
   const long long n_k_vecs = (long long)R * Hkv * cpr;
   const long long n_v_vecs = (long long)Hkv * v_groups_per_slab * D;
+  const long long n_q_vecs = QB ? (long long)R * Hq * (D / 8) : 0;
   long long tid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   const long long stride = (long long)gridDim.x * blockDim.x;
   long long first = tid;
@@ -158,8 +164,20 @@ __global__ __launch_bounds__(256) void append_kernel(
     }
     first = tid + n_k_vecs;  // the vector loop below does V only
   }
-  for (long long i = first; i < n_k_vecs + n_v_vecs; i += stride) {
-    if (i < n_k_vecs) {
+  for (long long i = first; i < n_k_vecs + n_v_vecs + n_q_vecs; i += stride) {
+    if (QB && i >= n_k_vecs + n_v_vecs) {
+      // Q vector: (row, head, c) with c innermost
+      const long long iq = i - n_k_vecs - n_v_vecs;
+      const int c = (int)(iq % (D / 8));
+      const long long t = iq / (D / 8);
+      const size_t qrow = ((size_t)row0 + t / Hq) * Hq + (size_t)(t % Hq);
+      const float4 a = *reinterpret_cast<const float4*>(q + qrow * D + 8 * c);
+      const float4 b = *reinterpret_cast<const float4*>(q + qrow * D + 8 * c + 4);
+      float f[8];
+      f[0] = a.x * sl2e; f[1] = a.y * sl2e; f[2] = a.z * sl2e; f[3] = a.w * sl2e;
+      f[4] = b.x * sl2e; f[5] = b.y * sl2e; f[6] = b.z * sl2e; f[7] = b.w * sl2e;
+      qb[qrow * (D / 8) + c] = __builtin_bit_cast(uint4, to_bf16x8(f));
+    } else if (i < n_k_vecs) {
       // K vector: (row, g, c) with c innermost
       const int c = (int)(i % cpr);
       long long t = i / cpr;
@@ -260,7 +278,9 @@ __global__ __launch_bounds__(256) void append_kernel(
 static hipError_t launch_append_tables(const Shape& s, void* k_cache, void* v_cache,
                                        const float* k_new, const float* v_new,
                                        const float* rope_cos, const float* rope_sin,
-                                       const std::vector<AppendArg>& L, hipStream_t stream) {
+                                       const std::vector<AppendArg>& L, hipStream_t stream,
+                                       const float* q = nullptr, void* qb = nullptr,
+                                       float sl2e = 0.f) {
   const int mode = s.kv_dtype;
   const bool bf16 = mode != kF32;                      // V layout
   const int E = mode == kF32 ? 4 : mode == kBF16 ? 8 : 16;   // K elements per vector
@@ -274,7 +294,8 @@ static hipError_t launch_append_tables(const Shape& s, void* k_cache, void* v_ca
       // threads: one per K vector (int8 K: one wave per row) and per V vector
       const long long nk = mode == kI8K ? (long long)aa.rows[i] * s.num_kv_heads * kWave
                                         : (long long)aa.rows[i] * s.num_kv_heads * (s.head_dim / E);
-      const long long n = nk + (long long)s.num_kv_heads * ng * s.head_dim;
+      const long long nq = qb ? (long long)aa.rows[i] * s.num_q_heads * (s.head_dim / 8) : 0;
+      const long long n = nk + (long long)s.num_kv_heads * ng * s.head_dim + nq;
       if (n > most) most = n;
     }
     long long blocks = (most + 255) / 256;
@@ -282,9 +303,13 @@ static hipError_t launch_append_tables(const Shape& s, void* k_cache, void* v_ca
     const dim3 grid((unsigned)blocks, aa.n);
     auto go = [&](auto kernel) {
       hipLaunchKernelGGL(kernel, grid, dim3(256), 0, stream, k_cache, v_cache, k_new, v_new,
-                         rope_cos, rope_sin, k_scales, s.num_kv_heads, s.head_dim, s.capacity, aa);
+                         rope_cos, rope_sin, k_scales, s.num_kv_heads, s.head_dim, s.capacity, aa,
+                         q, static_cast<uint4*>(qb), s.num_q_heads, sl2e);
     };
-    if (mode == kI8K) rope ? go(append_kernel<kI8K, true>) : go(append_kernel<kI8K, false>);
+    if (qb) {
+      if (mode != kBF16 || rope) return hipErrorInvalidValue;
+      go(append_kernel<kBF16, false, true>);
+    } else if (mode == kI8K) rope ? go(append_kernel<kI8K, true>) : go(append_kernel<kI8K, false>);
     else if (mode == kBF16) rope ? go(append_kernel<kBF16, true>) : go(append_kernel<kBF16, false>);
     else rope ? go(append_kernel<kF32, true>) : go(append_kernel<kF32, false>);
     const hipError_t e = hipGetLastError();
@@ -327,6 +352,15 @@ hipError_t launch_append(const Shape& s, void* k_cache, void* v_cache, const flo
   const auto L = append_tables(
       s.batch, [&](int) { return R; }, [&](int) { return start; }, true);
   return launch_append_tables(s, k_cache, v_cache, k_new, v_new, rope_cos, rope_sin, L, stream);
+}
+
+hipError_t launch_append_q(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
+                           const float* v_new, int start, int R, const float* q, void* qb,
+                           float scale, hipStream_t stream) {
+  const auto L = append_tables(
+      s.batch, [&](int) { return R; }, [&](int) { return start; }, true);
+  return launch_append_tables(s, k_cache, v_cache, k_new, v_new, nullptr, nullptr, L, stream, q,
+                              qb, scale * kLog2e);
 }
 
 hipError_t launch_append_ragged(const Shape& s, void* k_cache, void* v_cache, const float* k_new,

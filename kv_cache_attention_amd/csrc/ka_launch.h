@@ -33,6 +33,12 @@ inline float* k_scale_array(const Shape& s, const void* k_cache) {
 hipError_t launch_append(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
                          const float* v_new, int start, int R, hipStream_t stream,
                          const float* rope_cos = nullptr, const float* rope_sin = nullptr);
+// The append of a uniform chunk on a bf16 cache that also writes the chunk's
+// Q rows (f32 [B][R][Hq][D]) to qb as bf16 of q * scale * log2 e, rounded as
+// the prefill kernel rounds its Q operands (for launch_prefill's qb).
+hipError_t launch_append_q(const Shape& s, void* k_cache, void* v_cache, const float* k_new,
+                           const float* v_new, int start, int R, const float* q, void* qb,
+                           float scale, hipStream_t stream);
 // Ragged: session b appends rows[b] rows (0: none) at positions start[b] ..,
 // rows packed in session order in k_new / v_new ([sum rows][Hkv][D]) and in
 // rope_cos / rope_sin when given.  start / rows are host arrays [B].
@@ -63,9 +69,12 @@ struct PrefillPlan {
 };
 PrefillPlan plan_prefill(const Shape& s, int start, int R);
 size_t prefill_workspace_bound(const Shape& s, int max_rows);
+// qb (bf16 caches, M-tile plans only; null otherwise): Q already scaled and
+// rounded by launch_append_q, [B][R][Hq][D] bf16, read instead of q.
 hipError_t launch_prefill(const Shape& s, const PrefillPlan& p, const float* q,
                           const void* k_cache, const void* v_cache, float* out, int start, int R,
-                          float scale, void* workspace, hipStream_t stream);
+                          float scale, void* workspace, hipStream_t stream,
+                          const void* qb = nullptr);
 // Ragged prefill: session b's rows[b] rows (0: none) at positions start[b] ..,
 // packed in session order in q / out ([sum rows][Hq][D]); all sessions' tiles
 // share each launch.  start / rows are host arrays [B].

@@ -880,6 +880,44 @@ __device__ __forceinline__ void take_q(const ColB& c, int cb, float sl2e,
   }
 }
 
+// Prepared Q (the fused append-and-prefill call): the append kernel has
+// already multiplied each f32 Q value by scale * log2 e and rounded it to
+// bf16 with the same converter take_q uses, into qb ([packed rows][Hq][D]
+// bf16).  The M-tile's columns are staged as 16-byte granules of 8 dims, D / 8
+// per column, granule j of column col at LDS granule col D/8 + (j ^ (col %
+// (D/8))); a column past the chunk repeats the last one (its result is never
+// stored).
+template <int D>
+__device__ __forceinline__ void dma_qb(const Tiling& t, const void* __restrict__ qb, int Hq,
+                                       unsigned char* dst) {
+  constexpr int NT = kBf16Threads, GR = D / 8;
+  static_assert(kMTile * GR % NT == 0, "whole granules per thread");
+  const int row_hi = min(t.R - 1, (t.m_base + kMTile - 1) / t.G);
+  const unsigned char* base =
+      static_cast<const unsigned char*>(qb) + ((size_t)t.row0 + t.row_lo) * Hq * D * 2;
+  const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(base, (size_t)(row_hi - t.row_lo + 1) * Hq * D * 2);
+#pragma unroll
+  for (int i = 0; i < kMTile * GR / NT; ++i) {
+    const int p = i * NT + t.w * 64 + t.lane;  // LDS granule this lane fills
+    const int col = p / GR, j = (p % GR) ^ (col & (GR - 1));
+    const int m = min(t.m_base + col, t.M_total - 1);
+    const int off = (((m / t.G - t.row_lo) * Hq + t.g * t.G + m % t.G) * D + 8 * j) * 2;
+    dma16(rs, dst + (size_t)(i * NT + t.w * 64) * 16, off);
+  }
+}
+
+// The B operands of this lane's column from the staged granules: k-step ks
+// takes dims 16 ks + 8 lh .. + 7, granule 2 ks + lh (as take_q).
+template <int D>
+__device__ __forceinline__ void take_qb(const ColB& c, int cb, const uint4* __restrict__ q_lds,
+                                        bf16x8 (&qreg)[D / 16]) {
+  constexpr int GR = D / 8;
+  const int col = 32 * cb + c.lc, sw = col & (GR - 1);
+  const uint4* qc = q_lds + col * GR;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qreg[ks] = __builtin_bit_cast(bf16x8, qc[(2 * ks + c.lh) ^ sw]);
+}
+
 // int8 form: the column's symmetric codes (as the append quantises K rows)
 // and sq = s_q * scale * log2 e.  Lane (l % 32, h) holds the 16 codes of dims
 // 32 ks + 16 h .. 32 ks + 16 h + 15 for each k-step.  The amax covers the
@@ -1244,7 +1282,8 @@ __device__ __forceinline__ void store_result_b(const Tiling& t, const ColB& c, i
   }
 }
 
-template <int D, bool I8>
+// QB (bf16 caches): q points at prepared bf16 Q (see dma_qb) instead of f32.
+template <int D, bool I8, bool QB = false>
 __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
     const float* __restrict__ q, const void* __restrict__ k_cache,
     const void* __restrict__ v_cache, float* __restrict__ out, void* __restrict__ part,
@@ -1291,11 +1330,19 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
   // Q (f32) is staged behind K(0): kb1 onwards, up to the end of the
   // exchange buffers (512 D bytes), which hold nothing until every wave has
   // taken its operands
-  unsigned char* const q_lds = kb1;
+  // Prepared bf16 Q takes half that, V(0) and V(1)'s buffers, so K(1) can
+  // be fetched at once too.
+  unsigned char* const q_lds = QB ? vb0 : kb1;
   static_assert(KTB_LDS + kMTile * D * 4 <= Cfg::LDS, "Q staging fits behind K(0)");
+  static_assert(!QB || (!I8 && kMTile * D * 2 <= 2 * VTB), "bf16 Q fits the V buffers");
   if (n > 0) {
     load_k<D, I8>(ksrc, ssrc, t.kt0, kb0, t.w, t.lane);
-    dma_q<D>(t, q, Hq, q_lds);
+    if constexpr (QB) {
+      if (n > 1) load_k<D, I8>(ksrc, ssrc, t.kt0 + 1, kb1, t.w, t.lane);
+      dma_qb<D>(t, q, Hq, q_lds);
+    } else {
+      dma_q<D>(t, q, Hq, q_lds);
+    }
   }
   // per-pass exchange area (floats) in the exchange buffer that holds no
   // weights at that moment: [wave][slot][lane]
@@ -1314,13 +1361,18 @@ __global__ __launch_bounds__(kBf16Threads) void prefill_mtile_kernel(
   if (n > 0) {
     bool ovf = false;
     wait_vmem();
-    __syncthreads();  // K(0) and Q are in LDS
-    if constexpr (I8)
-      take_q_i8<D>(c, t.w & 3, kh, t.w, t.lane, sl2e, reinterpret_cast<float4*>(q_lds), qreg, sq);
-    else
-      take_q<D>(c, t.w & 3, sl2e, reinterpret_cast<const float4*>(q_lds), qreg);
-    __syncthreads();  // every wave holds its Q: kb1 and the exchange buffers are free
-    if (n > 1) load_k<D, I8>(ksrc, ssrc, t.kt0 + 1, kb1, t.w, t.lane);
+    __syncthreads();  // K(0) and Q (QB: and K(1)) are in LDS
+    if constexpr (QB) {
+      // the V buffers are next written at the first step, after its barrier
+      take_qb<D>(c, t.w & 3, reinterpret_cast<const uint4*>(q_lds), qreg);
+    } else {
+      if constexpr (I8)
+        take_q_i8<D>(c, t.w & 3, kh, t.w, t.lane, sl2e, reinterpret_cast<float4*>(q_lds), qreg, sq);
+      else
+        take_q<D>(c, t.w & 3, sl2e, reinterpret_cast<const float4*>(q_lds), qreg);
+      __syncthreads();  // every wave holds its Q: kb1 and the exchange buffers are free
+      if (n > 1) load_k<D, I8>(ksrc, ssrc, t.kt0 + 1, kb1, t.w, t.lane);
+    }
     // scores of the first tile (no softmax to overlap with yet)
     qk_tile_b<D, I8>(reinterpret_cast<const uint4*>(kb0), qreg, sa, kh, c, sq);
     if (t.kt0 * kNTile + kNTile - 1 > start + t.row_lo) mask_tile_b(sa, t.kt0 * kNTile + 32 * kh, c);
@@ -1785,10 +1837,12 @@ struct ChunkLaunch {
   int max_m, max_s;
 };
 
+// qb (bf16 caches only, may be null): Q prepared by the fused append (see
+// dma_qb), read in place of q.
 template <int D, int MODE>
 hipError_t launch_chunks(const Shape& s, const ChunkLaunch* L, int nl, long long total_slots,
                          const float* q, const void* kc, const void* vc, float* out, float scale,
-                         void* ws, hipStream_t st) {
+                         void* ws, hipStream_t st, const void* qb = nullptr) {
   constexpr bool H16 = MODE != kF32;  // binary16 partials (the 8-wave kernel)
   using Cfg = PrefillCfg<D, false>;
   // partials: binary16 accumulators for bf16 and int8-K caches, f32 otherwise, one
@@ -1803,10 +1857,16 @@ hipError_t launch_chunks(const Shape& s, const ChunkLaunch* L, int nl, long long
     if (items == 0) continue;
     // padded to whole rounds of the 8 XCDs (see make_tiling)
     const dim3 grid(8 * ((items + 7) / 8));
-    if constexpr (MODE == kBF16)
-      hipLaunchKernelGGL((prefill_mtile_kernel<D, false>), grid, dim3(kBf16Threads), 0, st, q, kc,
-                         vc, out, part, part_ml, nullptr, s.num_q_heads, s.num_kv_heads,
-                         s.capacity, ca, scale * kLog2e);
+    if constexpr (MODE == kBF16) {
+      if (qb)
+        hipLaunchKernelGGL((prefill_mtile_kernel<D, false, true>), grid, dim3(kBf16Threads), 0, st,
+                           static_cast<const float*>(qb), kc, vc, out, part, part_ml, nullptr,
+                           s.num_q_heads, s.num_kv_heads, s.capacity, ca, scale * kLog2e);
+      else
+        hipLaunchKernelGGL((prefill_mtile_kernel<D, false>), grid, dim3(kBf16Threads), 0, st, q,
+                           kc, vc, out, part, part_ml, nullptr, s.num_q_heads, s.num_kv_heads,
+                           s.capacity, ca, scale * kLog2e);
+    }
     else if constexpr (MODE == kI8K)
       hipLaunchKernelGGL((prefill_mtile_kernel<D, true>), grid, dim3(kBf16Threads), 0, st, q, kc,
                          vc, out, part, part_ml, k_scale_array(s, kc), s.num_q_heads,
@@ -1879,10 +1939,10 @@ long long build_launches(const Shape& s, Rows rows_of, Start start_of, Splits sp
 template <int D>
 hipError_t launch_mode(const Shape& s, const std::vector<ChunkLaunch>& L, long long slots,
                        const float* q, const void* kc, const void* vc, float* out, float scale,
-                       void* ws, hipStream_t st) {
+                       void* ws, hipStream_t st, const void* qb = nullptr) {
   const int n = (int)L.size();
   switch (s.kv_dtype) {
-    case kBF16: return launch_chunks<D, kBF16>(s, L.data(), n, slots, q, kc, vc, out, scale, ws, st);
+    case kBF16: return launch_chunks<D, kBF16>(s, L.data(), n, slots, q, kc, vc, out, scale, ws, st, qb);
     case kI8K: return launch_chunks<D, kI8K>(s, L.data(), n, slots, q, kc, vc, out, scale, ws, st);
     default: return launch_chunks<D, kF32>(s, L.data(), n, slots, q, kc, vc, out, scale, ws, st);
   }
@@ -1891,11 +1951,11 @@ hipError_t launch_mode(const Shape& s, const std::vector<ChunkLaunch>& L, long l
 template <int D>
 hipError_t launch_t(const Shape& s, const PrefillPlan& p, const float* q, const void* kc,
                     const void* vc, float* out, int start, int R, float scale, void* ws,
-                    hipStream_t st) {
+                    hipStream_t st, const void* qb) {
   std::vector<ChunkLaunch> L;
   const long long slots = build_launches(
       s, [&](int) { return R; }, [&](int) { return start; }, [&](int, int) { return p.splits; }, L);
-  return launch_mode<D>(s, L, slots, q, kc, vc, out, scale, ws, st);
+  return launch_mode<D>(s, L, slots, q, kc, vc, out, scale, ws, st, qb);
 }
 
 }  // namespace
@@ -2039,13 +2099,14 @@ hipError_t launch_prefill_ragged(const Shape& s, const float* q, const void* k_c
 
 hipError_t launch_prefill(const Shape& s, const PrefillPlan& p, const float* q,
                           const void* k_cache, const void* v_cache, float* out, int start, int R,
-                          float scale, void* workspace, hipStream_t stream) {
+                          float scale, void* workspace, hipStream_t stream, const void* qb) {
   if (p.m_tiles == 0)
     return launch_rows(s, p.rows, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
+  if (qb && s.kv_dtype != kBF16) return hipErrorInvalidValue;
   switch (s.head_dim) {
-    case 64: return launch_t<64>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
-    case 128: return launch_t<128>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
-    case 256: return launch_t<256>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream);
+    case 64: return launch_t<64>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream, qb);
+    case 128: return launch_t<128>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream, qb);
+    case 256: return launch_t<256>(s, p, q, k_cache, v_cache, out, start, R, scale, workspace, stream, qb);
     default: return hipErrorInvalidValue;
   }
 }

@@ -75,6 +75,7 @@ static void size_queries(void) {
             for (unsigned ri = 0; ri < sizeof kRows / sizeof *kRows; ++ri) {
               const int r = kRows[ri];
               const size_t pw = ka_attn_prefill_workspace_bytes(&s, r);
+              const size_t fw = ka_attn_append_prefill_workspace_bytes(&s, r);
               const size_t dw = ka_attn_decode_workspace_bytes(&s, r);
               (void)dw;
               const size_t rw = ka_attn_prefill_ragged_workspace_bytes(&s, (int64_t)r * 3);
@@ -82,8 +83,12 @@ static void size_queries(void) {
               const int starts[] = {0, 1, c / 2, c - 1, c, INT_MAX};
               for (unsigned si = 0; si < sizeof starts / sizeof *starts; ++si) {
                 const size_t need = ka_attn_prefill_workspace_need(&s, starts[si], r);
+                const size_t fneed = ka_attn_append_prefill_workspace_need(&s, starts[si], r);
                 /* a valid call never needs more than the bound for its rows */
-                if (cb != 0 && r > 0 && (long long)starts[si] + r <= c) EXPECT(need <= pw);
+                if (cb != 0 && r > 0 && (long long)starts[si] + r <= c) {
+                  EXPECT(need <= pw);
+                  EXPECT(fneed <= fw && need <= fneed);
+                }
               }
               ka_attn_memory m;
               memset(&m, 0, sizeof m);
@@ -171,6 +176,23 @@ static void rejections(void) {
     if (need > 0)
       REJECTS(ka_attn_prefill_chunk(&ok, FAKEF, FAKE, FAKE, FAKEO, 3000, 768, 0.1f, FAKE, need - 1,
                                     NULL),
+              KA_ERR_WORKSPACE);
+  }
+  REJECTS(ka_attn_append_prefill_chunk(&ok, FAKEF, FAKEF, FAKEF, FAKE, FAKE, FAKEO, 4000, 161, 0.1f,
+                                       FAKE, 1 << 30, NULL),
+          KA_ERR_OUT_OF_RANGE);
+  REJECTS(ka_attn_append_prefill_chunk(&ok, FAKEF, NULL, FAKEF, FAKE, FAKE, FAKEO, 0, 16, 0.1f, FAKE,
+                                       1 << 30, NULL),
+          KA_ERR_INVALID_ARGUMENT);
+  REJECTS(ka_attn_append_prefill_chunk(&ok, FAKEF, FAKEF, FAKEF, FAKE, FAKE, FAKEF, 0, 16, 0.1f, FAKE,
+                                       1 << 30, NULL),
+          KA_ERR_INVALID_ARGUMENT);
+  {
+    const size_t need = ka_attn_append_prefill_workspace_need(&ok, 3000, 768);
+    EXPECT(need > 0 && need <= ka_attn_append_prefill_workspace_bytes(&ok, 768));
+    if (need > 0)
+      REJECTS(ka_attn_append_prefill_chunk(&ok, FAKEF, FAKEF, FAKEF, FAKE, FAKE, FAKEO, 3000, 768,
+                                           0.1f, FAKE, need - 1, NULL),
               KA_ERR_WORKSPACE);
   }
   REJECTS(ka_attn_decode(&ok, FAKEF, FAKE, FAKE, FAKEO, NULL, 0.1f, FAKE, 1 << 30, NULL),

@@ -163,6 +163,55 @@ def test_prefill_argument_errors():
     assert ka.prefill_workspace_need(s, 4000, 97) == 0       # past the capacity
 
 
+def _fused(shape, start, rows, scale=0.0625, ws=None, ws_bytes=0, q=FAKE, kn=FAKE,
+           out=ctypes.c_void_p(0x2000)):
+    return ka.lib().ka_attn_append_prefill_chunk(ctypes.byref(shape), q, kn, FAKE, FAKE, FAKE,
+                                                 out, start, rows, scale, ws, ws_bytes, None)
+
+
+def test_fused_append_prefill_argument_errors():
+    _lib_or_skip()
+    s = S()
+    assert _fused(s, 0, 1, scale=float("nan")) == 1
+    assert _fused(s, 0, 1, scale=0.0) == 1
+    assert _fused(s, 4090, 7) == 2
+    assert _fused(s, -1, 7) == 1
+    assert _fused(s, 0, -1) == 1
+    assert _fused(s, 0, 1, q=None) == 1
+    assert _fused(s, 0, 1, kn=None) == 1
+    assert _fused(s, 0, 1, out=FAKE) == 1       # out aliases q
+    assert _fused(s, 0, 0) == 0                 # empty chunk is a no-op
+    assert _fused(S(head_dim=80), 0, 1) == 3
+    assert ka.last_error() != ""
+    # the exact need gates the fake-pointer calls (see the prefill test)
+    for kv in (ka.BF16, ka.I8K, ka.F32):
+        sk = S(kv_dtype=kv)
+        need = ka.append_prefill_workspace_need(sk, 3000, 768)
+        assert 0 < need <= ka.append_prefill_workspace_bytes(sk, 768)
+        assert _fused(sk, 3000, 768) == 4
+        assert _fused(sk, 3000, 768, ws=FAKE, ws_bytes=need - 1) == 4
+        part = ka.prefill_workspace_need(sk, 3000, 768)
+        if kv == ka.BF16:   # the bf16 Q copy behind the partials
+            assert need == ((part + 255) // 256) * 256 + 768 * 8 * 256 * 2
+        else:
+            assert need == part
+    assert ka.append_prefill_workspace_need(s, 4000, 97) == 0
+    assert ka.append_prefill_workspace_bytes(s, 0) == 0
+
+
+def test_fused_workspace_bound_covers_every_chunk():
+    _lib_or_skip()
+    rng = np.random.default_rng(7)
+    for kv in (ka.BF16, ka.I8K, ka.F32):
+        for B, hq, hkv, D in ((1, 8, 1, 256), (3, 8, 2, 128), (2, 2, 1, 64)):
+            s = S(batch=B, num_q_heads=hq, num_kv_heads=hkv, head_dim=D, kv_dtype=kv)
+            for R in (1, 15, 16, 100, 768, 4096):
+                bound = ka.append_prefill_workspace_bytes(s, R)
+                for start in rng.integers(0, 4096 - R + 1, size=6):
+                    for r in (R, max(1, R // 2)):
+                        assert ka.append_prefill_workspace_need(s, int(start), r) <= bound
+
+
 def test_decode_argument_errors():
     _lib_or_skip()
     s = S(batch=2)
