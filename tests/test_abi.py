@@ -221,6 +221,9 @@ def test_decode_argument_errors():
     arr = None
     assert ka.lib().ka_attn_decode(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.c_void_p(0x2000), arr,
                                    0.1, None, 0, None) == 1
+    # the bound at this call's longest context is the call's own need (the
+    # plan depends on the shape and that context only), 0 for a one-split
+    # plan: need > 0 gates the fake-pointer calls
     need = ka.decode_workspace_bytes(s, 4096)
     assert need > 0
     assert _decode(s, [4096, 10]) == 4
@@ -243,7 +246,7 @@ def test_decode_step_argument_errors():
     assert _step(s, [5, 5], out=FAKE) == 1   # out aliases q
     assert ka.lib().ka_attn_decode_step(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE,
                                         ctypes.c_void_p(0x2000), None, 0.1, None, 0, None) == 1
-    need = ka.decode_workspace_bytes(s, 4096)
+    need = ka.decode_workspace_bytes(s, 4096)   # the call's own need (ctx 4096), as above
     assert need > 0
     assert _step(s, [4095, 10]) == 4
     assert _step(s, [4095, 10], ws=FAKE, ws_bytes=need - 1) == 4
