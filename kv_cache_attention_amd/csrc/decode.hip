@@ -453,7 +453,7 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   constexpr int NS = D / 32;
   const int h = blockIdx.x / NS, ds = blockIdx.x % NS;
   const int gh = blockIdx.y, bl = blockIdx.z, b = b0 + bl;
-  const int g = gh / HG, hg = gh % HG;
+  const int g = HG == 1 ? gh : gh / HG, hg = HG == 1 ? 0 : gh % HG;  // no division for one group
   const int G = Hq / Hkv;
   const int gq = b * (Hkv * HG) + gh;
   const int ph = hg * hpw + h;  // (row, head) pair of the group: row ph / G, head ph % G
@@ -530,7 +530,8 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
     A += f * red_a[j][dl];
     L += f * red_l[j];
   }
-  out[(((size_t)b * R + ph / G) * Hq + g * G + ph % G) * D + d] = A / L;
+  const int prow = R == 1 ? 0 : ph / G, phead = R == 1 ? ph : ph % G;
+  out[(((size_t)b * R + prow) * Hq + g * G + phead) * D + d] = A / L;
 }
 
 // ============================================================================
@@ -591,14 +592,25 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // XCDs in turn, so workgroup x takes item (x % 8) per + x / 8 and each XCD
   // holds a contiguous run of items -- the head groups of a split together,
   // reading the same K / V lines through one L2.  Items past the end exit.
-  int item = blockIdx.x;
+  // One head group: the grid is (split, KV head, session), read straight
+  // from the block index, so the context length's load needs no other
+  // argument first.
+  int hg = 0, split, g, bl;
   if (HG > 1) {
     const int per = (int)((gridDim.x + 7) / 8);
-    item = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    const int item = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (item >= nb * Hkv * S * HG) return;
+    hg = item % HG;
+    split = (item / HG) % S;
+    const int gb = item / (HG * S);
+    g = gb % Hkv;
+    bl = gb / Hkv;
+  } else {
+    split = blockIdx.x;
+    g = blockIdx.y;
+    bl = blockIdx.z;
   }
-  const int hg = item % HG, split = (item / HG) % S, gb = item / (HG * S);
-  const int g = gb % Hkv, bl = gb / Hkv, b = b0 + bl;
+  const int b = b0 + bl;
   const int gh = g * HG + hg;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -610,7 +622,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // j + 2 NW, ...), so at any moment they read one contiguous stretch of the
   // cache; a wave's tiles need no order (the softmax is online).
   const int NW = S * kWaves, j0 = split * kWaves + w;
-  const int t0 = 0, t1 = j0 < nt ? (nt - 1 - j0) / NW + 1 : 0;  // local tile counts
+  // Local tile counts from one division of the workgroup: with nt - 1 =
+  // qn NW + rn, a wave j0 <= rn has qn + 1 tiles, one above it qn, and the
+  // last tile (that of the decode step's new row) is wave rn's.
+  const int qn = (nt - 1) / NW, rn = nt - 1 - qn * NW;
+  const int t0 = 0, t1 = qn + (j0 <= rn ? 1 : 0);
+  // whether the wave has a first and a second tile, without waiting for t1
+  const bool has0 = j0 < nt, has1 = j0 + NW < nt;
 
   const size_t slab_bytes = (size_t)C * D * 2;                 // V (and bf16 K)
   const size_t k_slab_bytes = (size_t)C * D * (I8 ? 1 : 2);
@@ -651,7 +669,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // and q's, not after them (one 16K step with inputs not in cache: 17.9 us
   // with these loads after q, as the other inputs' latency allows).
   const int p_new = ctx - 1, t_new = p_new / kDecTile;
-  const bool owns_new = k_new != nullptr && t_new % NW == j0;
+  const bool owns_new = k_new != nullptr && j0 == rn;  // t_new = nt - 1
   // K: lane l holds dims 8 l .. 8 l + 7 (bf16, lanes below D / 8) or 4 l ..
   // 4 l + 3 (int8-K, lanes below D / 4); V: dims l + 64 i
   float4 nk0 = make_float4(0.f, 0.f, 0.f, 0.f), nk1 = nk0;
@@ -672,8 +690,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   }
 
   DecTile<D, I8> ta_, tb_;
-  if (t0 < t1) load(ta_, t0);
-  if (t0 + 1 < t1) load(tb_, t0 + 1);
+  if (has0) load(ta_, t0);
+  if (has1) load(tb_, t0 + 1);
 
   // stationary Q^T: column lc is (row, head) pair pc = hg hpw + lc of the KV
   // group -- query row pc / G of the session's R rows (the last of which sits
@@ -684,11 +702,13 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   float sq = 0.f;                // I8: the column's scale times scale * log2 e
   const int pc = hg * hpw + lc;
   const bool hv = lc < hpw && pc < R * G;
-  const int lim = ctx - R + (hv ? pc / G : 0);
+  // the column's query row and head (one row without ROWS: row 0, head pc)
+  const int prow = ROWS ? (hv ? pc / G : 0) : 0, phead = ROWS ? (hv ? pc % G : 0) : (hv ? pc : 0);
+  const int lim = ctx - R + prow;
   if constexpr (I8) {
     // symmetric int8 codes of the column's query row: amax over its D dims
     // (this lane's D / 4 and the three lanes 16 and 32 apart), then codes
-    const float* qp = q + (((size_t)b * R + (hv ? pc / G : 0)) * Hq + g * G + (hv ? pc % G : 0)) * D + 16 * r;
+    const float* qp = q + (((size_t)b * R + prow) * Hq + g * G + phead) * D + 16 * r;
     float4 xq[D / 64][4];
     AbsMax am;
 #pragma unroll
@@ -724,7 +744,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     }
     sq = s * sl2e;
   } else {
-    const float* qp = q + (((size_t)b * R + (hv ? pc / G : 0)) * Hq + g * G + (hv ? pc % G : 0)) * D + 8 * r;
+    const float* qp = q + (((size_t)b * R + prow) * Hq + g * G + phead) * D + 8 * r;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
       float f[8];
@@ -1085,7 +1105,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     }
     if (S == 1) {
       const float inv = 1.f / l;
-      *reinterpret_cast<float4*>(out + (((size_t)b * R + ph / G) * Hq + g * G + ph % G) * D + d) =
+      *reinterpret_cast<float4*>(out + (((size_t)b * R + (ROWS ? ph / G : 0)) * Hq + g * G +
+                                        (ROWS ? ph % G : ph)) * D + d) =
           make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
     } else {
       *reinterpret_cast<float4*>(part + (((size_t)gq * S + split) * hpw + h) * D + d) = a;
@@ -1129,8 +1150,9 @@ void dispatch_hpw(int hpw, dim3 grid, hipStream_t st, const float* q, const void
 // 1-D grid of the MFMA kernel: one workgroup per item, padded to whole
 // rounds of the 8 XCDs when head groups are remapped
 dim3 mfma_grid(int nb, int Hkv, int HG, int S) {
+  if (HG == 1) return dim3((unsigned)S, (unsigned)Hkv, (unsigned)nb);
   const long long n = (long long)nb * Hkv * HG * S;
-  return dim3((unsigned)(HG > 1 ? 8 * ((n + 7) / 8) : n));
+  return dim3((unsigned)(8 * ((n + 7) / 8)));
 }
 
 template <int D>
