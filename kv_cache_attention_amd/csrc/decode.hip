@@ -954,7 +954,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
       const auto x1 = __builtin_amdgcn_permlane32_swap(pk[0][1], pk[1][1], false, false);
       pb = make_uint4(x0[0], x1[0], x0[1], x1[1]);
     }
-    if (__any(alpha != 1.f)) {
+    // (the wave's first tile: the sums are still 0, nothing to rescale)
+    if (i > 0 && __any(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < D / 16; ++db) acc[db] *= alpha;
     }
