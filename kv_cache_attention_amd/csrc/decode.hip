@@ -444,7 +444,9 @@ void decode_split_kernel(
 constexpr int kMergeEarly = 32;
 constexpr int kMergeTail = 16;
 
-template <int D>
+// NB: batches of 8 splits that every thread loads at once (8 NB >= S up to
+// kMergeEarly batches; the host picks it from S).
+template <int D, int NB>
 __global__ __launch_bounds__(256) void decode_merge_kernel(
     const float* __restrict__ part, const float* __restrict__ part_ml, float* __restrict__ out,
     int b0, int Hq, int Hkv, int HG, int hpw, int S, int R) {
@@ -462,22 +464,36 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   const float2* ml = reinterpret_cast<const float2*>(part_ml + ((size_t)gq * hpw + h) * S * 2);
   const int dl = tid & 31, r = tid >> 5;
   const int d = ds * 32 + dl;
-  const float* pa = part + ((size_t)gq * S * hpw + h) * D + d;
-  const size_t PS = (size_t)hpw * D;
-  float av[kMergeEarly];
-  float2 mlv[kMergeEarly];
+  // a base common to the block and 32-bit offsets (s PS + d < 2^31: at most
+  // 1024 splits of 16 heads of 256 dims)
+  const float* pa = part + ((size_t)gq * S * hpw + h) * D;
+  const int PS = hpw * D;
+  // The loads first, all of them in flight together and with no condition
+  // around them: a thread whose split of a batch is past the end loads split
+  // S - 1 and its value is replaced afterwards.  (A per-thread or per-batch
+  // condition around the loads lets the compiler copy a loaded register at
+  // the join, waiting for that load before it issues the rest: a second
+  // memory round trip.)
+  float av[NB];
+  float2 mlv[NB];
 #pragma unroll
-  for (int k = 0; k < kMergeEarly; ++k) {
-    const int s = r + 8 * k;
-    av[k] = s < S ? pa[(size_t)s * PS] : 0.f;
-    mlv[k] = s < S ? ml[s] : make_float2(-INFINITY, 0.f);
+  for (int k = 0; k < NB; ++k) {
+    const int s = min(r + 8 * k, S - 1);
+    av[k] = pa[s * PS + d];
+    mlv[k] = ml[s];
+  }
+#pragma unroll
+  for (int k = 0; k < NB; ++k) {
+    const bool in = r + 8 * k < S;
+    av[k] = in ? av[k] : 0.f;
+    mlv[k] = in ? mlv[k] : make_float2(-INFINITY, 0.f);
   }
   float m = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < kMergeEarly; ++k) m = fmaxf(m, mlv[k].x);
+  for (int k = 0; k < NB; ++k) m = fmaxf(m, mlv[k].x);
   float l = 0.f, a = 0.f;
 #pragma unroll
-  for (int k = 0; k < kMergeEarly; ++k) {
+  for (int k = 0; k < NB; ++k) {
     if (mlv[k].y == 0.f) continue;
     const float f = fast_exp2(mlv[k].x - m);
     l += f * mlv[k].y;
@@ -486,14 +502,20 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(
   // more than 8 kMergeEarly splits (f32 plans): further batches of kMergeTail
   // splits per thread, each batch's loads issued together, in a running
   // frame that moves to the batch's largest m
-  for (int s0 = r + 8 * kMergeEarly; s0 < S; s0 += 8 * kMergeTail) {
+  for (int sb = 8 * NB; sb < S; sb += 8 * kMergeTail) {  // the same batches for all threads
     float bv[kMergeTail];
     float2 bml[kMergeTail];
 #pragma unroll
     for (int k = 0; k < kMergeTail; ++k) {
-      const int s = s0 + 8 * k;
-      bv[k] = s < S ? pa[(size_t)s * PS] : 0.f;
-      bml[k] = s < S ? ml[s] : make_float2(-INFINITY, 0.f);
+      const int s = min(sb + r + 8 * k, S - 1);
+      bv[k] = pa[s * PS + d];
+      bml[k] = ml[s];
+    }
+#pragma unroll
+    for (int k = 0; k < kMergeTail; ++k) {
+      const bool in = sb + r + 8 * k < S;
+      bv[k] = in ? bv[k] : 0.f;
+      bml[k] = in ? bml[k] : make_float2(-INFINITY, 0.f);
     }
     float mb = m;
 #pragma unroll
@@ -1159,9 +1181,24 @@ dim3 mfma_grid(int nb, int Hkv, int HG, int S) {
 template <int D>
 void launch_merge(int hpw, dim3 grid, hipStream_t st, const float* part, float* out, int b0,
                   const Shape& s, int HG, int S, int R = 1) {
-  hipLaunchKernelGGL((decode_merge_kernel<D>), grid, dim3(256), 0, st, part,
-                     part + (size_t)s.batch * s.num_kv_heads * HG * S * hpw * D, out, b0,
-                     s.num_q_heads, s.num_kv_heads, HG, hpw, S, R);
+  const float* ml = part + (size_t)s.batch * s.num_kv_heads * HG * S * hpw * D;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, grid, dim3(256), 0, st, part, ml, out, b0, s.num_q_heads,
+                       s.num_kv_heads, HG, hpw, S, R);
+  };
+  // batches of 8 splits loaded at once: ceil(S / 8), rounded up to 1, 2, 4
+  // or a multiple of 4 (at most 3 batches loaded for nothing)
+  const int nb = (S + 7) / 8;
+  if (nb <= 1) go(decode_merge_kernel<D, 1>);
+  else if (nb <= 2) go(decode_merge_kernel<D, 2>);
+  else if (nb <= 4) go(decode_merge_kernel<D, 4>);
+  else if (nb <= 8) go(decode_merge_kernel<D, 8>);
+  else if (nb <= 12) go(decode_merge_kernel<D, 12>);
+  else if (nb <= 16) go(decode_merge_kernel<D, 16>);
+  else if (nb <= 20) go(decode_merge_kernel<D, 20>);
+  else if (nb <= 24) go(decode_merge_kernel<D, 24>);
+  else if (nb <= 28) go(decode_merge_kernel<D, 28>);
+  else go(decode_merge_kernel<D, kMergeEarly>);
 }
 
 }  // namespace
