@@ -314,11 +314,13 @@ void decode_split_kernel(
       const uint32_t x = __float_as_uint(sm.row[1][lane + 64 * t]);
 #pragma unroll
       for (int g2 = 0; g2 < R::NG; ++g2) {
-        if (g2 != gi) continue;
-        r.v[g2][t].x = e == 0 ? x : r.v[g2][t].x;
-        r.v[g2][t].y = e == 1 ? x : r.v[g2][t].y;
-        r.v[g2][t].z = e == 2 ? x : r.v[g2][t].z;
-        r.v[g2][t].w = e == 3 ? x : r.v[g2][t].w;
+        // a select per element (a skipped iteration became a runtime index
+        // into a stack copy of the registers at D = 64)
+        const bool sg = g2 == gi;
+        r.v[g2][t].x = sg && e == 0 ? x : r.v[g2][t].x;
+        r.v[g2][t].y = sg && e == 1 ? x : r.v[g2][t].y;
+        r.v[g2][t].z = sg && e == 2 ? x : r.v[g2][t].z;
+        r.v[g2][t].w = sg && e == 3 ? x : r.v[g2][t].w;
       }
     }
   };

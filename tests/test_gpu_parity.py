@@ -328,6 +328,7 @@ DECODE_STEP_CASES = [
     ("f32", 3, 16, 1, 256, 1088, [0, 517, 1087]),  # two head groups per KV head
     ("f32", 2, 8, 2, 256, 4160, [4096, 33]),
     ("f32", 1, 8, 1, 64, 40000, [39000]),          # all heads per workgroup, 512 splits
+    ("f32", 2, 8, 1, 64, 512, [7, 298]),           # new row in slots 3 and 2 of its V group
     ("f32", 1, 8, 1, 256, 4160, [4096]),           # two heads per workgroup
 ]
 
