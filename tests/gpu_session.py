@@ -56,6 +56,18 @@ class DevCaches:
             torch.cuda.synchronize()
         return out.cpu().numpy()
 
+    def append_prefill(self, q, k_rows, v_rows, start, scale):
+        """ka_attn_append_prefill_chunk: the chunk's K / V rows appended and its
+        q rows ([B][R][Hq][D] float32) attended, in one call -> out numpy."""
+        R = q.shape[1]
+        qt = dev(q)
+        out = torch.full_like(qt, float("nan"))
+        ws = self.workspace(ka.append_prefill_workspace_bytes(self.shape, R))
+        ka.append_prefill_chunk(self.shape, qt, dev(k_rows), dev(v_rows), self.k, self.v, out,
+                                start, R, scale, ws)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
     def decode(self, q, ctx, scale):
         """q: [B][Hq][D] float32, ctx: list of B ints -> out numpy [B][Hq][D]."""
         qt = dev(q)

@@ -1,8 +1,8 @@
 """GPU parity at the benchmark's full sizes, through the calls the benchmark
 times, with the same shapes and schedule:
 
-  * 16K session, bf16 cache: 21 chunks of 768 rows + one of 256, each an
-    append then a prefill call (ka_attn_append_kv, ka_attn_prefill_chunk);
+  * 16K session, bf16 cache: 21 chunks of 768 rows + one of 256, each one
+    ka_attn_append_prefill_chunk call (the chunk's append and prefill);
     the last 768-row chunk and the 256-row chunk are compared in full, the
     others on sampled rows.  Then 64 decode steps, each one
     ka_attn_decode_step call (append of the step's row + decode), every step
@@ -54,8 +54,8 @@ def test_long_session_16k(dt):
     qrow = 0
     last = len(w.chunks) - 1
     for ci, (start, R) in enumerate(w.chunks):
-        caches.append(c.k[:, start:start + R], c.v[:, start:start + R], start)
-        got = caches.prefill(c.q[:, qrow:qrow + R], start, w.scale)
+        got = caches.append_prefill(c.q[:, qrow:qrow + R], c.k[:, start:start + R],
+                                    c.v[:, start:start + R], start, w.scale)
         assert np.isfinite(got).all(), f"chunk {ci}: non-finite output"
         if ci >= last - 1:
             rows = list(range(R))          # the last 768-row chunk and the 256-row chunk
