@@ -666,7 +666,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // operand loads of this wave's i-th tile, tile j0 + i NW (K layout
   // [C/64][D/KE][64][KE], V [C/32][4][D][8]); every cache byte is read once per
   // step, so the loads are marked non-temporal
-  auto load = [&](DecTile<D, I8>& x, int i) {
+  auto load_k = [&](DecTile<D, I8>& x, int i) {
     const int t = j0 + i * NW;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -679,11 +679,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
       if constexpr (I8)
         x.sk[kb] = *reinterpret_cast<const float4*>(sk_row + kDecTile * t + 16 * kb + 4 * r);
     }
+  };
+  auto load_v = [&](DecTile<D, I8>& x, int i) {
+    const int t = j0 + i * NW;
 #pragma unroll
     for (int db = 0; db < D / 16; ++db)
       x.v[db] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(
                      vrs, ((4 * t + r) * D + 16 * db + lc) * 16, 0, kStreamAux));
+  };
+  auto load = [&](DecTile<D, I8>& x, int i) {
+    load_k(x, i);
+    load_v(x, i);
   };
 
   // The decode step's new row (position ctx - 1, given by k_new / v_new; its
@@ -713,10 +720,6 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     for (int i = 0; i < D / 64; ++i) nv[i] = vn[lane + 64 * i];
   }
 
-  DecTile<D, I8> ta_, tb_;
-  if (has0) load(ta_, t0);
-  if (has1) load(tb_, t0 + 1);
-
   // stationary Q^T: column lc is (row, head) pair pc = hg hpw + lc of the KV
   // group -- query row pc / G of the session's R rows (the last of which sits
   // at position ctx - 1), head g G + pc % G -- and zero past the pairs.  Its
@@ -729,18 +732,37 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
   // the column's query row and head (one row without ROWS: row 0, head pc)
   const int prow = ROWS ? (hv ? pc / G : 0) : 0, phead = ROWS ? (hv ? pc % G : 0) : (hv ? pc : 0);
   const int lim = ctx - R + prow;
+
+  // The first tile's K, then this column's q (f32; converted or quantised
+  // below), then that tile's V and the second tile.  Loads return in issue
+  // order, so the first tile's scores wait for its K and q only and run
+  // while its V arrives (with q issued after both tiles, they waited for
+  // all of them: a 16K step 13.8 -> 12.5 us).  Lane (lc, r) takes the dims
+  // of its MFMA operand: float4 n holds dims 32 (n / 2) + 8 r + 4 (n % 2)
+  // (bf16) or 64 (n / 4) + 16 r + 4 (n % 4) (int8 codes).
+  DecTile<D, I8> ta_, tb_;
+  float4 qraw[D / 16];
+  if (has0) load_k(ta_, t0);
+  {
+    const float* qp = q + (((size_t)b * R + prow) * Hq + g * G + phead) * D + (I8 ? 16 : 8) * r;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) {
+      const int off = I8 ? 64 * (n >> 2) + 4 * (n & 3) : 32 * (n >> 1) + 4 * (n & 1);
+      qraw[n] = hv ? *reinterpret_cast<const float4*>(qp + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+  if (has0) load_v(ta_, t0);
+  if (has1) load(tb_, t0 + 1);
   if constexpr (I8) {
     // symmetric int8 codes of the column's query row: amax over its D dims
     // (this lane's D / 4 and the three lanes 16 and 32 apart), then codes
-    const float* qp = q + (((size_t)b * R + prow) * Hq + g * G + phead) * D + 16 * r;
     float4 xq[D / 64][4];
     AbsMax am;
 #pragma unroll
     for (int ks = 0; ks < D / 64; ++ks)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        xq[ks][e] = hv ? *reinterpret_cast<const float4*>(qp + 64 * ks + 4 * e)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
+        xq[ks][e] = qraw[4 * ks + e];
         am.add(xq[ks][e].x); am.add(xq[ks][e].y); am.add(xq[ks][e].z); am.add(xq[ks][e].w);
       }
     float m = am.m, nf = am.nan ? 1.f : 0.f;
@@ -768,19 +790,12 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     }
     sq = s * sl2e;
   } else {
-    const float* qp = q + (((size_t)b * R + prow) * Hq + g * G + phead) * D + 8 * r;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) {
+      const float4 x = qraw[2 * ks], y = qraw[2 * ks + 1];
       float f[8];
-      if (hv) {
-        const float4 x = *reinterpret_cast<const float4*>(qp + 32 * ks);
-        const float4 y = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
-        f[0] = x.x * sl2e; f[1] = x.y * sl2e; f[2] = x.z * sl2e; f[3] = x.w * sl2e;
-        f[4] = y.x * sl2e; f[5] = y.y * sl2e; f[6] = y.z * sl2e; f[7] = y.w * sl2e;
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) f[j] = 0.f;
-      }
+      f[0] = x.x * sl2e; f[1] = x.y * sl2e; f[2] = x.z * sl2e; f[3] = x.w * sl2e;
+      f[4] = y.x * sl2e; f[5] = y.y * sl2e; f[6] = y.z * sl2e; f[7] = y.w * sl2e;
       qreg[ks] = to_bf16x8(f);
     }
   }
