@@ -325,13 +325,23 @@ void decode_split_kernel(
     }
   };
 
-  // first unit's loads go out before q, so the two latencies overlap
+  // The first unit's K, then q, then that unit's V: loads return in issue
+  // order, so q reaches LDS, and the first scores start, while V is still
+  // arriving (with q after V, both waited for the whole unit)
   R ra;
   int u = u0 + w;
-  if (u < u1) {
-    load_unit_k<D, BF16>(ra, u, lane, kc);
-    load_unit_v<D, BF16>(ra, u, lane, vc);
+  if (u < u1) load_unit_k<D, BF16>(ra, u, lane, kc);
+  constexpr int QV = HPW * D / 2 / 256 > 0 ? HPW * D / 2 / 256 : 1;
+  float2 qv[QV];
+#pragma unroll
+  for (int j = 0; j < QV; ++j) {
+    const int i = tid + 256 * j;
+    if (i < HPW * D / 2) {
+      const int h = (2 * i) / D, d = (2 * i) % D;
+      qv[j] = *reinterpret_cast<const float2*>(q + ((size_t)b * Hq + h0 + h) * D + d);
+    }
   }
+  if (u < u1) load_unit_v<D, BF16>(ra, u, lane, vc);
   if (owns_new) {
     if (4 * lane < D) *reinterpret_cast<float4*>(&sm.row[0][4 * lane]) = nk;
 #pragma unroll
@@ -347,17 +357,7 @@ void decode_split_kernel(
     wave_lds_sync();
   }
 
-  // ---- q -> LDS (bf16 with RNE, or f32 copy); all loads issued first
-  constexpr int QV = HPW * D / 2 / 256 > 0 ? HPW * D / 2 / 256 : 1;
-  float2 qv[QV];
-#pragma unroll
-  for (int j = 0; j < QV; ++j) {
-    const int i = tid + 256 * j;
-    if (i < HPW * D / 2) {
-      const int h = (2 * i) / D, d = (2 * i) % D;
-      qv[j] = *reinterpret_cast<const float2*>(q + ((size_t)b * Hq + h0 + h) * D + d);
-    }
-  }
+  // ---- q -> LDS (bf16 with RNE, or f32 copy)
 #pragma unroll
   for (int j = 0; j < QV; ++j) {
     const int i = tid + 256 * j;
